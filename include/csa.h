@@ -1,0 +1,228 @@
+/*
+ * csa.h -- C ABI of the Compressed Sparse Attention (CSA) hot path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (DeepSeek-V4's CSA and HCA) as the source pages describe it:
+ *   - "DeepSeek V4 technical review" (takeshell.com), section 2.1 "CSA":
+ *     every m tokens' KV become one entry by weighted aggregation; a
+ *     Lightning Indexer scores each query against the compressed entries and
+ *     keeps the top-k; core attention runs over the selected entries only.
+ *     Section 2.2 "HCA": m' = 128, dense attention over all entries.
+ *   - "DeepSeek V4: Compressed Sparse Attention and the Million-Token
+ *     Context" (octagono.org), "Hybrid Attention: CSA and HCA": top-1024,
+ *     a sliding window of 128 recent tokens, HCA has no selection.
+ *   - dataforcee.us "Hybrid Attention: CSA and HCA": both CSA and HCA carry
+ *     a sliding-window branch over the most recent raw tokens.
+ *   - takeshell.com section 5 and dataforcee.us "Muon Optimizer and FP4
+ *     QAT": the indexer's query-key path runs in low precision.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor pointers are DEVICE pointers, row-major and contiguous in the
+ *   stated shape unless a batch stride argument says otherwise.  The caller
+ *   owns every buffer; no call allocates or frees device memory.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   Every call is asynchronous on that stream: it only enqueues kernels.
+ * - Arguments are validated on the host before anything is enqueued.  A
+ *   failed validation returns a negative status and enqueues nothing;
+ *   csa_last_error() then describes the problem (thread-local).  Nothing
+ *   aborts or throws across this ABI.  A launch failure reported by the HIP
+ *   runtime returns CSA_ERR_HIP.  Faults inside kernels surface at the
+ *   caller's next synchronisation of the stream.
+ * - Query token i (0 <= i < T) of sequence b sits at absolute position
+ *   t = pos0[b] + i (pos0 is a DEVICE array of B int64).  The compressed
+ *   entries visible to position t are j < V(t) = floor((t + 1) / m): block
+ *   j covers raw positions j*m .. j*m+m-1 and is visible once it is
+ *   complete.  Kernels clamp V(t) to n_cap so that no access leaves the
+ *   buffers; positions with V(t) > n_cap are a caller error.
+ * - Scores must be finite; -0.0 is ranked equal to +0.0.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define CSA_F32 0      /* IEEE binary32 */
+#define CSA_BF16 1     /* bfloat16, stored as 16-bit words */
+#define CSA_FP8_E4M3 2 /* OCP FP8 E4M3FN byte codes (max 448, no inf) */
+
+/* indexer nonlinearity */
+#define CSA_ACT_RELU 0
+#define CSA_ACT_IDENTITY 1
+
+/* status codes */
+#define CSA_OK 0
+#define CSA_ERR_NULL (-1)        /* a required pointer is NULL */
+#define CSA_ERR_SHAPE (-2)       /* a size or position argument is invalid */
+#define CSA_ERR_DTYPE (-3)       /* unsupported element type or combination */
+#define CSA_ERR_UNSUPPORTED (-4) /* valid, but outside what the kernels support */
+#define CSA_ERR_WORKSPACE (-5)   /* workspace missing or too small */
+#define CSA_ERR_HIP (-6)         /* the HIP runtime reported an error */
+
+/* Human-readable name of a status code (static string). */
+const char* csa_status_string(int status);
+/* Message describing the last failed call on this thread ("" if none). */
+const char* csa_last_error(void);
+/* ABI version of this library (incremented on incompatible changes). */
+int csa_abi_version(void);
+
+/*
+ * csa_compress -- the token-level compressor (takeshell.com 2.1: every m
+ * tokens' KV entries are compressed into one entry by weighted
+ * aggregation; octagono.org: a learned token-level compressor).
+ *
+ * For sequence b, block j < n_tok/m and channel c:
+ *   w_i = softmax over i < m of logits[b, j*m + i, c]
+ *   cache[b, first_entry + j, c] = sum_i w_i * x[b, j*m + i, c]
+ * computed in fp32 and rounded to nearest-even when the cache is bf16.
+ *
+ *   x       [B][x_batch_stride] elements; row i (i < n_tok) of sequence b
+ *           starts at x + b*x_batch_stride + i*d.  dtype x_dtype.
+ *   logits  fp32, same indexing with z_batch_stride.
+ *   cache   [B][n_cap][d] of cache_dtype (must equal x_dtype); entries
+ *           first_entry .. first_entry + n_tok/m - 1 are written, nothing
+ *           else is touched.
+ * Requirements: n_tok % m == 0 (only complete blocks), m >= 1, d >= 1,
+ * first_entry >= 0, first_entry + n_tok/m <= n_cap, strides >= n_tok*d.
+ * dtypes: (F32 -> F32), (BF16 -> BF16).  n_tok == 0 is a no-op.
+ */
+int csa_compress(const void* x, int x_dtype, const float* logits,
+                 int64_t B, int64_t n_tok, int64_t d, int m,
+                 int64_t x_batch_stride, int64_t z_batch_stride,
+                 void* cache, int cache_dtype, int64_t n_cap,
+                 int64_t first_entry, void* stream);
+
+/*
+ * csa_quantize_fp8_rows -- FP8 storage of indexer keys and queries (the
+ * pages quantize the indexer's QK path; takeshell.com section 5).  For each
+ * row r of x [rows][d]:
+ *   scale[r] = max_c |x[r,c]| / 448   (correctly rounded fp32; 1 if zero)
+ *   codes[r,c] = E4M3FN(x[r,c] / scale[r])  (correctly rounded fp32
+ *                quotient, round to nearest even, saturate to +-448)
+ * dequantized value = decode(code) * scale.  x_dtype F32 or BF16;
+ * 1 <= d <= 1024.  rows == 0 is a no-op.
+ */
+int csa_quantize_fp8_rows(const void* x, int x_dtype, int64_t rows, int64_t d,
+                          uint8_t* codes, float* scales, void* stream);
+
+/*
+ * csa_index_scores -- the Lightning Indexer (takeshell.com 2.1: indexer
+ * queries per query token, scored against the compressed entries; 64 heads
+ * x 128 dims for V4-Pro).  For query (b, i) at position t and j < V(t):
+ *   scores[b,i,j] = sum_h w[b,i,h] * phi( qi[b,i,h,:] . ki[b,j,:] )
+ * phi = ReLU (act = CSA_ACT_RELU) or identity (CSA_ACT_IDENTITY).  With
+ * FP8 inputs the operands are decode(code) * scale, i.e.
+ *   scores = ki_scale[b,j] * sum_h (w * qi_scale[b,i,h]) * phi(q~ . k~).
+ * Entries j >= V(t) of a score row are not written.
+ *
+ *   qi        [B][T][H_I][d_I]      qi_dtype
+ *   qi_scale  [B][T][H_I] fp32      FP8 only (else ignored, may be NULL)
+ *   w         [B][T][H_I] fp32
+ *   ki        [B][n_cap][d_I]       ki_dtype (== qi_dtype)
+ *   ki_scale  [B][n_cap] fp32       FP8 only (else ignored, may be NULL)
+ *   pos0      [B] int64 (device)
+ *   scores    [B][T][n_cap] fp32
+ * Supported: dtypes F32, BF16 (d_I % 32 == 0, d_I <= 256) and FP8_E4M3
+ * (d_I == 128); 1 <= H_I <= 64; m >= 1; T >= 1, B >= 1.
+ */
+int csa_index_scores(const void* qi, int qi_dtype, const float* qi_scale,
+                     const float* w, const void* ki, int ki_dtype,
+                     const float* ki_scale, const int64_t* pos0,
+                     int64_t B, int64_t T, int64_t H_I, int64_t d_I,
+                     int64_t n_cap, int m, int act, float* scores,
+                     void* stream);
+
+/*
+ * csa_topk -- per-query top-k selection (takeshell.com 2.1: the k most
+ * relevant compressed blocks are kept; k = 1024 for V4-Pro).  For query
+ * (b, i) at position t the min(k, V(t)) visible entries with the largest
+ * score are kept; equal scores go to the lower entry index.  idx[b,i,:]
+ * lists them in ascending index order, padded with -1 to length k.
+ *
+ *   scores [B][T][n_cap] fp32 (only j < V(t) is read)
+ *   idx    [B][T][k] int32
+ *   ws     device workspace of at least csa_topk_workspace_size() bytes;
+ *          its contents on entry do not matter.
+ * 1 <= k <= 4096.
+ */
+size_t csa_topk_workspace_size(int64_t B, int64_t T, int64_t n_cap, int k);
+int csa_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T,
+             int64_t n_cap, int m, int k, int32_t* idx, void* ws,
+             size_t ws_bytes, void* stream);
+
+/*
+ * csa_index_topk -- csa_index_scores followed by csa_topk on the same
+ * stream.  scores may be NULL, in which case the score matrix lives in the
+ * workspace (csa_index_topk_workspace_size accounts for it).
+ */
+size_t csa_index_topk_workspace_size(int64_t B, int64_t T, int64_t n_cap,
+                                     int k, int scores_in_workspace);
+int csa_index_topk(const void* qi, int qi_dtype, const float* qi_scale,
+                   const float* w, const void* ki, int ki_dtype,
+                   const float* ki_scale, const int64_t* pos0,
+                   int64_t B, int64_t T, int64_t H_I, int64_t d_I,
+                   int64_t n_cap, int m, int act, int k, float* scores,
+                   int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa_attend -- core attention over the selected compressed entries plus
+ * the sliding window, in one softmax (octagono.org "Hybrid Attention":
+ * attend only to the selected entries, with a 128-token window for local
+ * context; dataforcee.us: the window branch covers the most recent raw
+ * tokens).  One KV head is shared by all H query heads.  For query (b, i)
+ * at position t and head h the key set is
+ *   { kc[b, j] : j = idx[b,i,s] >= 0 }  followed by
+ *   { kr[b, p - raw_pos0[b]] : max(0, t-W+1) <= p <= t }
+ * (the window is not de-duplicated against the selected entries), with
+ * values from vc / vr at the same rows:
+ *   out[b,i,h,:] = softmax_keys(scale * q[b,i,h,:] . key) @ values
+ *   lse[b,i,h]   = natural-log sum of exp(scale * q . key)
+ *
+ *   q     [B][T][H][d]         q_dtype (== kv_dtype)
+ *   kc,vc [B][n_cap][d]        kv_dtype
+ *   idx   [B][T][k] int32      entries < 0 or >= n_cap are skipped
+ *   kr,vr [B][R][d]            kv_dtype; row r holds position raw_pos0[b]+r
+ *   raw_pos0 [B] int64 (device); window positions outside the raw buffer
+ *          are a caller error and are skipped (never read out of bounds)
+ *   out   [B][T][H][d] fp32;  lse [B][T][H] fp32 or NULL
+ *   ws    device workspace of csa_attend_workspace_size() bytes
+ * Supported: dtypes F32, BF16; d in {64, 128}; 1 <= H <= 64 (H % 16 == 0
+ * or H < 16); 0 <= W <= 4096; 0 <= k <= 65536.  A query whose key set is
+ * empty gets out = 0 and lse = -inf.
+ */
+size_t csa_attend_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d,
+                                 int k, int W);
+int csa_attend(const void* q, int q_dtype, const void* kc, const void* vc,
+               int kv_dtype, const int32_t* idx, int k, const void* kr,
+               const void* vr, const int64_t* raw_pos0, int64_t R,
+               const int64_t* pos0, int64_t B, int64_t T, int64_t H,
+               int64_t d, int64_t n_cap, int W, float scale, float* out,
+               float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * hca_attend -- Heavily Compressed Attention (takeshell.com 2.2: m' = 128;
+ * octagono.org: dense attention over the heavily compressed entries, no
+ * sparse selection), with the same sliding-window branch.  Identical to
+ * csa_attend with idx[b,i] = 0 .. V(t)-1, V(t) = floor((t+1)/m), clamped
+ * to n_cap.  Same layouts and support limits as csa_attend.
+ */
+size_t hca_attend_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d,
+                                 int64_t n_cap, int W);
+int hca_attend(const void* q, int q_dtype, const void* kc, const void* vc,
+               int kv_dtype, int m, const void* kr, const void* vr,
+               const int64_t* raw_pos0, int64_t R, const int64_t* pos0,
+               int64_t B, int64_t T, int64_t H, int64_t d, int64_t n_cap,
+               int W, float scale, float* out, float* lse, void* ws,
+               size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H */

@@ -1,0 +1,315 @@
+// C ABI of the CSA hot path: argument validation (pure host code, runs
+// before anything is enqueued) and dispatch to the HIP kernels.  The
+// contract of every call is documented in include/csa.h.
+#include "../../include/csa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return CSA_OK;
+}
+
+int hip_result(int rc, const char* what) {
+  if (rc == 0) return ok();
+  if (rc == -2) return fail(CSA_ERR_UNSUPPORTED, "%s: no kernel variant for these arguments", what);
+  return fail(CSA_ERR_HIP, "%s: kernel launch failed: %s", what,
+              hipGetErrorString(hipGetLastError()));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxGridY = 65535;
+constexpr int64_t kMaxIndex = 0x7fffffffLL;
+
+size_t round_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+#define CSA_REQUIRE(cond, code, ...) \
+  do {                               \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+int check_index_args(const void* qi, int qi_dtype, const float* qi_scale, const float* w,
+                     const void* ki, int ki_dtype, const float* ki_scale, const int64_t* pos0,
+                     int64_t B, int64_t T, int64_t H_I, int64_t d_I, int64_t n_cap, int m, int act,
+                     const float* scores, const char* fn) {
+  CSA_REQUIRE(qi && w && ki && pos0 && scores, CSA_ERR_NULL,
+              "%s: qi, w, ki, pos0 and scores must be non-NULL", fn);
+  CSA_REQUIRE(qi_dtype == ki_dtype, CSA_ERR_DTYPE, "%s: qi_dtype (%d) must equal ki_dtype (%d)", fn,
+              qi_dtype, ki_dtype);
+  CSA_REQUIRE(qi_dtype == CSA_F32 || qi_dtype == CSA_BF16 || qi_dtype == CSA_FP8_E4M3,
+              CSA_ERR_DTYPE, "%s: unknown dtype %d", fn, qi_dtype);
+  if (qi_dtype == CSA_FP8_E4M3)
+    CSA_REQUIRE(qi_scale && ki_scale, CSA_ERR_NULL, "%s: FP8 inputs need qi_scale and ki_scale", fn);
+  CSA_REQUIRE(act == CSA_ACT_RELU || act == CSA_ACT_IDENTITY, CSA_ERR_SHAPE, "%s: unknown act %d",
+              fn, act);
+  CSA_REQUIRE(B >= 1 && T >= 1, CSA_ERR_SHAPE, "%s: B and T must be >= 1", fn);
+  CSA_REQUIRE(B * T <= kMaxGridY, CSA_ERR_UNSUPPORTED, "%s: B*T must be <= %lld", fn,
+              static_cast<long long>(kMaxGridY));
+  CSA_REQUIRE(m >= 1, CSA_ERR_SHAPE, "%s: m must be >= 1", fn);
+  CSA_REQUIRE(n_cap >= 1 && n_cap <= kMaxIndex, CSA_ERR_SHAPE, "%s: n_cap must be in [1, 2^31)",
+              fn);
+  CSA_REQUIRE(H_I >= 1 && H_I <= 64, CSA_ERR_UNSUPPORTED, "%s: H_I must be in [1, 64]", fn);
+  if (qi_dtype == CSA_F32)
+    CSA_REQUIRE(d_I == 64 || d_I == 128, CSA_ERR_UNSUPPORTED, "%s: fp32 needs d_I in {64, 128}", fn);
+  else if (qi_dtype == CSA_BF16)
+    CSA_REQUIRE(d_I == 64 || d_I == 128 || d_I == 256, CSA_ERR_UNSUPPORTED,
+                "%s: bf16 needs d_I in {64, 128, 256}", fn);
+  else
+    CSA_REQUIRE(d_I == 128, CSA_ERR_UNSUPPORTED, "%s: fp8 needs d_I == 128", fn);
+  CSA_REQUIRE(aligned16(qi) && aligned16(ki), CSA_ERR_SHAPE, "%s: qi and ki must be 16-byte aligned",
+              fn);
+  return CSA_OK;
+}
+
+int check_topk_args(const float* scores, const int64_t* pos0, int64_t B, int64_t T, int64_t n_cap,
+                    int m, int k, const int32_t* idx, const char* fn) {
+  CSA_REQUIRE(scores && pos0 && idx, CSA_ERR_NULL, "%s: scores, pos0 and idx must be non-NULL", fn);
+  CSA_REQUIRE(B >= 1 && T >= 1, CSA_ERR_SHAPE, "%s: B and T must be >= 1", fn);
+  CSA_REQUIRE(B * T <= kMaxGridY, CSA_ERR_UNSUPPORTED, "%s: B*T must be <= %lld", fn,
+              static_cast<long long>(kMaxGridY));
+  CSA_REQUIRE(m >= 1, CSA_ERR_SHAPE, "%s: m must be >= 1", fn);
+  CSA_REQUIRE(n_cap >= 1 && n_cap <= kMaxIndex, CSA_ERR_SHAPE, "%s: n_cap must be in [1, 2^31)",
+              fn);
+  CSA_REQUIRE(k >= 1 && k <= 4096, CSA_ERR_UNSUPPORTED, "%s: k must be in [1, 4096]", fn);
+  return CSA_OK;
+}
+
+int check_attend_args(const void* q, int q_dtype, const void* kc, const void* vc, int kv_dtype,
+                      const void* kr, const void* vr, const int64_t* raw_pos0, int64_t R,
+                      const int64_t* pos0, int64_t B, int64_t T, int64_t H, int64_t d,
+                      int64_t n_cap, int W, const float* out, const char* fn) {
+  CSA_REQUIRE(q && kc && vc && pos0 && out, CSA_ERR_NULL,
+              "%s: q, kc, vc, pos0 and out must be non-NULL", fn);
+  CSA_REQUIRE(W == 0 || (kr && vr && raw_pos0), CSA_ERR_NULL,
+              "%s: kr, vr and raw_pos0 must be non-NULL when W > 0", fn);
+  CSA_REQUIRE(q_dtype == kv_dtype, CSA_ERR_DTYPE, "%s: q_dtype (%d) must equal kv_dtype (%d)", fn,
+              q_dtype, kv_dtype);
+  CSA_REQUIRE(q_dtype == CSA_F32 || q_dtype == CSA_BF16, CSA_ERR_DTYPE,
+              "%s: dtype must be F32 or BF16, got %d", fn, q_dtype);
+  CSA_REQUIRE(B >= 1 && T >= 1, CSA_ERR_SHAPE, "%s: B and T must be >= 1", fn);
+  CSA_REQUIRE(B * T <= kMaxGridY, CSA_ERR_UNSUPPORTED, "%s: B*T must be <= %lld", fn,
+              static_cast<long long>(kMaxGridY));
+  CSA_REQUIRE(H >= 1 && H <= 64, CSA_ERR_UNSUPPORTED, "%s: H must be in [1, 64]", fn);
+  CSA_REQUIRE(d == 64 || d == 128, CSA_ERR_UNSUPPORTED, "%s: d must be 64 or 128", fn);
+  CSA_REQUIRE(n_cap >= 1 && n_cap <= kMaxIndex, CSA_ERR_SHAPE, "%s: n_cap must be in [1, 2^31)",
+              fn);
+  CSA_REQUIRE(W >= 0 && W <= 4096, CSA_ERR_UNSUPPORTED, "%s: W must be in [0, 4096]", fn);
+  CSA_REQUIRE(R >= 0 && (W == 0 || R >= 1), CSA_ERR_SHAPE, "%s: R must be >= 1 when W > 0", fn);
+  CSA_REQUIRE(aligned16(q) && aligned16(kc) && aligned16(vc) && aligned16(out) &&
+                  (W == 0 || (aligned16(kr) && aligned16(vr))),
+              CSA_ERR_SHAPE, "%s: q, kc, vc, kr, vr and out must be 16-byte aligned", fn);
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa_status_string(int status) {
+  switch (status) {
+    case CSA_OK: return "CSA_OK";
+    case CSA_ERR_NULL: return "CSA_ERR_NULL";
+    case CSA_ERR_SHAPE: return "CSA_ERR_SHAPE";
+    case CSA_ERR_DTYPE: return "CSA_ERR_DTYPE";
+    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED";
+    case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE";
+    case CSA_ERR_HIP: return "CSA_ERR_HIP";
+    default: return "CSA_ERR_UNKNOWN";
+  }
+}
+
+const char* csa_last_error(void) { return g_last_error; }
+
+int csa_abi_version(void) { return 1; }
+
+int csa_compress(const void* x, int x_dtype, const float* logits, int64_t B, int64_t n_tok,
+                 int64_t d, int m, int64_t x_batch_stride, int64_t z_batch_stride, void* cache,
+                 int cache_dtype, int64_t n_cap, int64_t first_entry, void* stream) {
+  const char* fn = "csa_compress";
+  CSA_REQUIRE(x && logits && cache, CSA_ERR_NULL, "%s: x, logits and cache must be non-NULL", fn);
+  CSA_REQUIRE(x_dtype == cache_dtype, CSA_ERR_DTYPE, "%s: x_dtype must equal cache_dtype", fn);
+  CSA_REQUIRE(x_dtype == CSA_F32 || x_dtype == CSA_BF16, CSA_ERR_DTYPE,
+              "%s: dtype must be F32 or BF16, got %d", fn, x_dtype);
+  CSA_REQUIRE(B >= 1 && B <= kMaxGridY, CSA_ERR_SHAPE, "%s: B must be in [1, 65535]", fn);
+  CSA_REQUIRE(m >= 1, CSA_ERR_SHAPE, "%s: m must be >= 1", fn);
+  CSA_REQUIRE(d >= 1, CSA_ERR_SHAPE, "%s: d must be >= 1", fn);
+  CSA_REQUIRE(n_tok >= 0 && n_tok % m == 0, CSA_ERR_SHAPE,
+              "%s: n_tok (%lld) must be a non-negative multiple of m (%d)", fn,
+              static_cast<long long>(n_tok), m);
+  CSA_REQUIRE(x_batch_stride >= n_tok * d && z_batch_stride >= n_tok * d, CSA_ERR_SHAPE,
+              "%s: batch strides must be >= n_tok*d", fn);
+  CSA_REQUIRE(first_entry >= 0 && n_cap >= 1 && first_entry + n_tok / m <= n_cap, CSA_ERR_SHAPE,
+              "%s: entries [%lld, %lld) do not fit n_cap=%lld", fn,
+              static_cast<long long>(first_entry), static_cast<long long>(first_entry + n_tok / m),
+              static_cast<long long>(n_cap));
+  CSA_REQUIRE((n_tok / m) * d <= 0x7fffffffLL * 256, CSA_ERR_UNSUPPORTED, "%s: too many entries",
+              fn);
+  if (n_tok == 0) return ok();
+  return hip_result(csa::launch_compress(x, x_dtype, logits, B, n_tok, d, m, x_batch_stride,
+                                         z_batch_stride, cache, n_cap, first_entry,
+                                         static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int csa_quantize_fp8_rows(const void* x, int x_dtype, int64_t rows, int64_t d, uint8_t* codes,
+                          float* scales, void* stream) {
+  const char* fn = "csa_quantize_fp8_rows";
+  CSA_REQUIRE(x && codes && scales, CSA_ERR_NULL, "%s: x, codes and scales must be non-NULL", fn);
+  CSA_REQUIRE(x_dtype == CSA_F32 || x_dtype == CSA_BF16, CSA_ERR_DTYPE,
+              "%s: dtype must be F32 or BF16, got %d", fn, x_dtype);
+  CSA_REQUIRE(rows >= 0, CSA_ERR_SHAPE, "%s: rows must be >= 0", fn);
+  CSA_REQUIRE(d >= 1 && d <= 1024, CSA_ERR_UNSUPPORTED, "%s: d must be in [1, 1024]", fn);
+  CSA_REQUIRE(rows / 4 < 0x7fffffffLL, CSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  if (rows == 0) return ok();
+  return hip_result(csa::launch_quantize_fp8_rows(x, x_dtype, rows, d, codes, scales,
+                                                  static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int csa_index_scores(const void* qi, int qi_dtype, const float* qi_scale, const float* w,
+                     const void* ki, int ki_dtype, const float* ki_scale, const int64_t* pos0,
+                     int64_t B, int64_t T, int64_t H_I, int64_t d_I, int64_t n_cap, int m, int act,
+                     float* scores, void* stream) {
+  const char* fn = "csa_index_scores";
+  int rc = check_index_args(qi, qi_dtype, qi_scale, w, ki, ki_dtype, ki_scale, pos0, B, T, H_I,
+                            d_I, n_cap, m, act, scores, fn);
+  if (rc) return rc;
+  return hip_result(csa::launch_index_scores(qi, qi_dtype, qi_scale, w, ki, ki_scale, pos0, B, T,
+                                             H_I, d_I, n_cap, m, act, scores,
+                                             static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+size_t csa_topk_workspace_size(int64_t B, int64_t T, int64_t n_cap, int k) {
+  if (B < 1 || T < 1) return 0;
+  return round_up(csa::topk_workspace_bytes(B, T, n_cap, k));
+}
+
+int csa_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, int64_t n_cap, int m,
+             int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "csa_topk";
+  int rc = check_topk_args(scores, pos0, B, T, n_cap, m, k, idx, fn);
+  if (rc) return rc;
+  const size_t need = csa_topk_workspace_size(B, T, n_cap, k);
+  CSA_REQUIRE(need == 0 || (ws && ws_bytes >= need), CSA_ERR_WORKSPACE,
+              "%s: workspace of %zu bytes needed, got %zu", fn, need, ws ? ws_bytes : 0);
+  CSA_REQUIRE(ws == nullptr || aligned16(ws), CSA_ERR_WORKSPACE, "%s: ws must be 16-byte aligned",
+              fn);
+  return hip_result(
+      csa::launch_topk(scores, pos0, B, T, n_cap, m, k, idx, ws, static_cast<hipStream_t>(stream)),
+      fn);
+}
+
+size_t csa_index_topk_workspace_size(int64_t B, int64_t T, int64_t n_cap, int k,
+                                     int scores_in_workspace) {
+  if (B < 1 || T < 1 || n_cap < 1) return 0;
+  size_t s = csa_topk_workspace_size(B, T, n_cap, k);
+  if (scores_in_workspace) s += round_up(static_cast<size_t>(B * T) * n_cap * sizeof(float));
+  return s;
+}
+
+int csa_index_topk(const void* qi, int qi_dtype, const float* qi_scale, const float* w,
+                   const void* ki, int ki_dtype, const float* ki_scale, const int64_t* pos0,
+                   int64_t B, int64_t T, int64_t H_I, int64_t d_I, int64_t n_cap, int m, int act,
+                   int k, float* scores, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "csa_index_topk";
+  const bool scores_in_ws = scores == nullptr;
+  const size_t need = csa_index_topk_workspace_size(B, T, n_cap, k, scores_in_ws ? 1 : 0);
+  CSA_REQUIRE(need == 0 || (ws && ws_bytes >= need), CSA_ERR_WORKSPACE,
+              "%s: workspace of %zu bytes needed, got %zu", fn, need, ws ? ws_bytes : 0);
+  CSA_REQUIRE(ws == nullptr || aligned16(ws), CSA_ERR_WORKSPACE, "%s: ws must be 16-byte aligned",
+              fn);
+  float* sc = scores;
+  char* topk_ws = static_cast<char*>(ws);
+  if (scores_in_ws && ws) {
+    sc = static_cast<float*>(ws);
+    topk_ws += round_up(static_cast<size_t>(B * T) * n_cap * sizeof(float));
+  }
+  int rc = check_index_args(qi, qi_dtype, qi_scale, w, ki, ki_dtype, ki_scale, pos0, B, T, H_I,
+                            d_I, n_cap, m, act, sc, fn);
+  if (rc) return rc;
+  rc = check_topk_args(sc, pos0, B, T, n_cap, m, k, idx, fn);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = hip_result(csa::launch_index_scores(qi, qi_dtype, qi_scale, w, ki, ki_scale, pos0, B, T,
+                                           H_I, d_I, n_cap, m, act, sc, s),
+                  fn);
+  if (rc) return rc;
+  return hip_result(csa::launch_topk(sc, pos0, B, T, n_cap, m, k, idx, topk_ws, s), fn);
+}
+
+size_t csa_attend_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d, int k, int W) {
+  if (B < 1 || T < 1 || H < 1 || d < 1 || k < 0 || W < 0) return 0;
+  return round_up(csa::attend_workspace_bytes(B * T, H, d, static_cast<int64_t>(k) + W));
+}
+
+int csa_attend(const void* q, int q_dtype, const void* kc, const void* vc, int kv_dtype,
+               const int32_t* idx, int k, const void* kr, const void* vr,
+               const int64_t* raw_pos0, int64_t R, const int64_t* pos0, int64_t B, int64_t T,
+               int64_t H, int64_t d, int64_t n_cap, int W, float scale, float* out, float* lse,
+               void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "csa_attend";
+  int rc = check_attend_args(q, q_dtype, kc, vc, kv_dtype, kr, vr, raw_pos0, R, pos0, B, T, H, d,
+                             n_cap, W, out, fn);
+  if (rc) return rc;
+  CSA_REQUIRE(k >= 0 && k <= 65536, CSA_ERR_UNSUPPORTED, "%s: k must be in [0, 65536]", fn);
+  CSA_REQUIRE(k == 0 || idx, CSA_ERR_NULL, "%s: idx must be non-NULL when k > 0", fn);
+  CSA_REQUIRE(k + W >= 1, CSA_ERR_SHAPE, "%s: k + W must be >= 1", fn);
+  const size_t need = csa_attend_workspace_size(B, T, H, d, k, W);
+  CSA_REQUIRE(need == 0 || (ws && ws_bytes >= need), CSA_ERR_WORKSPACE,
+              "%s: workspace of %zu bytes needed, got %zu", fn, need, ws ? ws_bytes : 0);
+  CSA_REQUIRE(ws == nullptr || aligned16(ws), CSA_ERR_WORKSPACE, "%s: ws must be 16-byte aligned",
+              fn);
+  return hip_result(csa::launch_attend(q, q_dtype, kc, vc, idx, k, 0, kr, vr, raw_pos0, R, pos0, B,
+                                       T, H, d, n_cap, W, scale, out, lse, ws,
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+size_t hca_attend_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d, int64_t n_cap,
+                                 int W) {
+  if (B < 1 || T < 1 || H < 1 || d < 1 || n_cap < 1 || W < 0) return 0;
+  return round_up(csa::attend_workspace_bytes(B * T, H, d, n_cap + W));
+}
+
+int hca_attend(const void* q, int q_dtype, const void* kc, const void* vc, int kv_dtype, int m,
+               const void* kr, const void* vr, const int64_t* raw_pos0, int64_t R,
+               const int64_t* pos0, int64_t B, int64_t T, int64_t H, int64_t d, int64_t n_cap,
+               int W, float scale, float* out, float* lse, void* ws, size_t ws_bytes,
+               void* stream) {
+  const char* fn = "hca_attend";
+  int rc = check_attend_args(q, q_dtype, kc, vc, kv_dtype, kr, vr, raw_pos0, R, pos0, B, T, H, d,
+                             n_cap, W, out, fn);
+  if (rc) return rc;
+  CSA_REQUIRE(m >= 1, CSA_ERR_SHAPE, "%s: m must be >= 1", fn);
+  const size_t need = hca_attend_workspace_size(B, T, H, d, n_cap, W);
+  CSA_REQUIRE(need == 0 || (ws && ws_bytes >= need), CSA_ERR_WORKSPACE,
+              "%s: workspace of %zu bytes needed, got %zu", fn, need, ws ? ws_bytes : 0);
+  CSA_REQUIRE(ws == nullptr || aligned16(ws), CSA_ERR_WORKSPACE, "%s: ws must be 16-byte aligned",
+              fn);
+  return hip_result(csa::launch_attend(q, q_dtype, kc, vc, nullptr, 0, m, kr, vr, raw_pos0, R,
+                                       pos0, B, T, H, d, n_cap, W, scale, out, lse, ws,
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+}  // extern "C"

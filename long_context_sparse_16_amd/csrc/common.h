@@ -1,0 +1,104 @@
+// Shared device helpers for the CSA kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bfloat16
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ----------------------------------------------------------------- fp8 e4m3
+
+// fp32 -> OCP E4M3FN code, round to nearest even, saturating at 448.
+__device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
+  uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  float a = fabsf(v);
+  uint32_t mag;
+  if (a >= 448.0f) {
+    mag = 0x7eu;  // every value >= 448 rounds (or saturates) to 448
+  } else if (a < 0.015625f) {
+    // subnormal range: value = f * 2^-9, f = 0..7; 2^-6 itself is code 8
+    mag = static_cast<uint32_t>(rintf(a * 512.0f));
+  } else {
+    uint32_t u = __float_as_uint(a);
+    u += 0x7ffffu + ((u >> 20) & 1u);  // round to 3 fraction bits, ties even
+    uint32_t e = (u >> 23) - 127u + 7u;
+    mag = (e << 3) | ((u >> 20) & 7u);
+    if (mag > 0x7eu) mag = 0x7eu;
+  }
+  return static_cast<uint8_t>(sign | mag);
+}
+
+// ------------------------------------------------------- order-preserving key
+
+// Map a finite float to a uint32 whose unsigned order is the float order;
+// -0.0 and +0.0 map to the same key.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0u) return 0x80000000u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// ------------------------------------------------------------- MFMA wrappers
+//
+// 16x16 output tiles.  In every flavour lane l holds column (l % 16) of B
+// and row (l % 16) of A, and lane group g = l / 16 holds one quarter of the
+// reduction (k) dimension; A and B lanes with the same (g, element) meet in
+// the same product, so any consistent assignment of k to (g, element) gives
+// the same sum.  The accumulator holds D[4*g + i][l % 16], i = 0..3.
+
+__device__ __forceinline__ f32x4 mma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// 16x16x128 FP8 (E4M3 x E4M3), fp32 accumulate, unit block scales.
+__device__ __forceinline__ f32x4 mma_fp8(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ int64_t visible_entries(int64_t t, int m, int64_t n_cap) {
+  int64_t v = (t + 1) / m;
+  if (v < 0) v = 0;
+  return v < n_cap ? v : n_cap;
+}
+
+}  // namespace csa

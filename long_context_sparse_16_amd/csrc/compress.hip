@@ -1,0 +1,110 @@
+// Token-level compressor and FP8 row quantizer.
+//
+// Compressor: every m tokens of K (or V) become one cache entry, a weighted
+// aggregation over the block ("DeepSeek V4 technical review", takeshell.com,
+// section 2.1 CSA; octagono.org "Hybrid Attention: CSA and HCA" calls it a
+// learned token-level compressor).  The weights are a softmax over the m
+// tokens of caller-supplied logits, independently per channel.
+//
+// Layout: one thread per (entry, channel).  Consecutive lanes take
+// consecutive channels, so every token row of x and of the logits is read
+// with fully coalesced loads; the m-token loop is the only serial part.
+#include "common.h"
+#include "kernels.h"
+
+namespace csa {
+
+template <typename T>
+__device__ __forceinline__ float load_elem(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_elem<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+template <typename T>
+__device__ __forceinline__ void store_elem(T* p, int64_t i, float v);
+template <>
+__device__ __forceinline__ void store_elem<float>(float* p, int64_t i, float v) { p[i] = v; }
+template <>
+__device__ __forceinline__ void store_elem<uint16_t>(uint16_t* p, int64_t i, float v) {
+  p[i] = f32_to_bf16(v);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void compress_kernel(
+    const T* __restrict__ x, const float* __restrict__ z, T* __restrict__ cache,
+    int64_t n_blocks, int64_t d, int m, int64_t x_sb, int64_t z_sb, int64_t n_cap,
+    int64_t first_entry) {
+  const int64_t b = blockIdx.y;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= n_blocks * d) return;
+  const int64_t j = e / d;
+  const int64_t c = e - j * d;
+  const T* xb = x + b * x_sb + (j * m) * d + c;
+  const float* zb = z + b * z_sb + (j * m) * d + c;
+  float zmax = -INFINITY;
+  for (int i = 0; i < m; ++i) zmax = fmaxf(zmax, zb[static_cast<int64_t>(i) * d]);
+  float num = 0.f, den = 0.f;
+  for (int i = 0; i < m; ++i) {
+    const float a = expf(zb[static_cast<int64_t>(i) * d] - zmax);
+    den += a;
+    num = fmaf(a, load_elem<T>(xb, static_cast<int64_t>(i) * d), num);
+  }
+  store_elem<T>(cache, b * n_cap * d + (first_entry + j) * d + c, num / den);
+}
+
+int launch_compress(const void* x, int dtype, const float* z, int64_t B, int64_t n_tok,
+                    int64_t d, int m, int64_t x_sb, int64_t z_sb, void* cache,
+                    int64_t n_cap, int64_t first_entry, hipStream_t s) {
+  const int64_t nb = n_tok / m;
+  const int64_t total = nb * d;
+  dim3 grid(static_cast<unsigned>((total + 255) / 256), static_cast<unsigned>(B));
+  if (dtype == 0) {
+    compress_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), z,
+                                                static_cast<float*>(cache), nb, d, m, x_sb,
+                                                z_sb, n_cap, first_entry);
+  } else {
+    compress_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), z,
+                                                   static_cast<uint16_t*>(cache), nb, d, m,
+                                                   x_sb, z_sb, n_cap, first_entry);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// FP8 row quantizer: one wave per row.  scale = amax / 448 and the code
+// quotient x / scale are correctly rounded fp32 divisions (the default HIP
+// division), then rounded to E4M3 (nearest even, saturating).
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict__ x,
+                                                            uint8_t* __restrict__ codes,
+                                                            float* __restrict__ scales,
+                                                            int64_t rows, int d) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const T* xr = x + r * d;
+  float amax = 0.f;
+  for (int c = lane; c < d; c += 64) amax = fmaxf(amax, fabsf(load_elem<T>(xr, c)));
+  amax = wave_max(amax);
+  const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+  for (int c = lane; c < d; c += 64) codes[r * d + c] = f32_to_e4m3(load_elem<T>(xr, c) / scale);
+  if (lane == 0) scales[r] = scale;
+}
+
+int launch_quantize_fp8_rows(const void* x, int dtype, int64_t rows, int64_t d,
+                             uint8_t* codes, float* scales, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+  if (dtype == 0) {
+    quantize_rows_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), codes,
+                                                     scales, rows, static_cast<int>(d));
+  } else {
+    quantize_rows_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x),
+                                                        codes, scales, rows,
+                                                        static_cast<int>(d));
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace csa

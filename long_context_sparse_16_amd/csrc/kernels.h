@@ -1,0 +1,44 @@
+// Internal launchers of the CSA kernels (not part of the public ABI).
+// Each returns 0 on success, -1 if the HIP runtime reported a launch error,
+// -2 if no kernel variant matches the (already validated) arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+int launch_compress(const void* x, int dtype, const float* z, int64_t B, int64_t n_tok, int64_t d,
+                    int m, int64_t x_sb, int64_t z_sb, void* cache, int64_t n_cap,
+                    int64_t first_entry, hipStream_t s);
+
+int launch_quantize_fp8_rows(const void* x, int dtype, int64_t rows, int64_t d, uint8_t* codes,
+                             float* scales, hipStream_t s);
+
+int launch_index_scores(const void* qi, int dtype, const float* qs, const float* w,
+                        const void* ki, const float* ks, const int64_t* pos0, int64_t B,
+                        int64_t T, int64_t H_I, int64_t d_I, int64_t n_cap, int m, int act,
+                        float* scores, hipStream_t s);
+
+// Rows (B*T) up to this count use the multi-workgroup split top-k, which
+// needs a workspace; more rows use one workgroup per row and none.
+constexpr int64_t kTopkSplitMaxRows = 256;
+size_t topk_workspace_bytes(int64_t B, int64_t T, int64_t n_cap, int k);
+int launch_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, int64_t n_cap,
+                int m, int k, int32_t* idx, void* ws, hipStream_t s);
+
+struct AttSplit {
+  int splits;
+  int chunks_per_split;
+};
+AttSplit attend_split(int64_t rows, int64_t n_slots_max);
+size_t attend_workspace_bytes(int64_t rows, int64_t H, int64_t D, int64_t n_slots_max);
+// hca_m > 0 selects HCA (all visible entries, idx ignored).
+int launch_attend(const void* q, int dtype, const void* kc, const void* vc, const int32_t* idx,
+                  int k, int hca_m, const void* kr, const void* vr, const int64_t* raw_pos0,
+                  int64_t R, const int64_t* pos0, int64_t B, int64_t T, int64_t H, int64_t D,
+                  int64_t n_cap, int W, float scale, float* out, float* lse, void* ws,
+                  hipStream_t stream);
+
+}  // namespace csa

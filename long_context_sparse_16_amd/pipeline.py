@@ -1,0 +1,135 @@
+"""One CSA (or HCA) attention step over a batch, driven through the C ABI.
+
+``CSAStep`` holds device-resident inputs, outputs and workspaces for one
+batch and exposes the hot-path stages as separate calls so that callers can
+time them individually:
+
+  compress()  new raw tokens -> appended compressed K/V entries
+  index()     Lightning Indexer scores
+  topk()      per-query top-k entry indices
+  attend()    attention over the selected entries + sliding window
+              (HCA: dense attention over every visible entry + window)
+
+Every stage is one library call; this module only allocates tensors and
+passes them on.  Inputs are given in storage form: float32 arrays, or uint16
+arrays holding bf16 codes.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (csa_attend, csa_compress, csa_index_scores, csa_quantize_fp8_rows, csa_topk,
+               csa_topk_workspace_size, csa_attend_workspace_size, hca_attend,
+               hca_attend_workspace_size)
+
+
+def to_device(a: np.ndarray, device, storage: str) -> torch.Tensor:
+    """Upload a storage-form array (float32, int, or uint16 bf16 codes)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def bf16_codes_of(t: torch.Tensor) -> np.ndarray:
+    """uint16 codes of a device bf16 tensor."""
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class CSAStep:
+    def __init__(self, cfg, batch: dict, device="cuda:0", act: str = "relu"):
+        self.cfg = cfg
+        self.act = act
+        self.device = torch.device(device)
+        dev = self.device
+        st = cfg.storage
+        B, T, d = cfg.B, cfg.T, cfg.d
+        n_cap = cfg.n_cap
+        kv_dtype = torch.float32 if st == "f32" else torch.bfloat16
+        self.kc = torch.zeros((B, n_cap, d), dtype=kv_dtype, device=dev)
+        self.vc = torch.zeros((B, n_cap, d), dtype=kv_dtype, device=dev)
+        if cfg.n_ctx_entries:
+            self.kc[:, :cfg.n_ctx_entries] = to_device(batch["kc"], dev, st)
+            self.vc[:, :cfg.n_ctx_entries] = to_device(batch["vc"], dev, st)
+        self.kr = to_device(batch["kr"], dev, st)
+        self.vr = to_device(batch["vr"], dev, st)
+        self.z = to_device(batch["z"], dev, st) if cfg.n_new_tokens else None
+        self.q = to_device(batch["q"], dev, st)
+        self.pos0 = torch.full((B,), cfg.pos0, dtype=torch.int64, device=dev)
+        self.raw_pos0 = torch.full((B,), cfg.raw_pos0, dtype=torch.int64, device=dev)
+        self.out = torch.empty((B, T, cfg.H, d), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, T, cfg.H), dtype=torch.float32, device=dev)
+        if cfg.hca:
+            self.att_ws = torch.empty(
+                max(1, hca_attend_workspace_size(B, T, cfg.H, d, n_cap, cfg.W)),
+                dtype=torch.uint8, device=dev)
+            self.idx = None
+            return
+        self.qi = to_device(batch["qi"], dev, st)
+        self.w = to_device(batch["w"], dev, "f32")
+        self.qi_scale = None
+        self.ki_codes = None
+        self.ki_scale = None
+        if cfg.ki_fp8:
+            self.qi_codes, self.qi_scale = csa_quantize_fp8_rows(self.qi)
+            self.ki_codes = torch.empty((B, n_cap, cfg.d_I), dtype=torch.uint8, device=dev)
+            self.ki_scale = torch.ones((B, n_cap), dtype=torch.float32, device=dev)
+            if cfg.n_ctx_entries:
+                self.quantize_keys(0, cfg.n_ctx_entries)
+        self.scores = torch.empty((B, T, n_cap), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((B, T, cfg.k), dtype=torch.int32, device=dev)
+        self.topk_ws = torch.empty(max(1, csa_topk_workspace_size(B, T, n_cap, cfg.k)),
+                                   dtype=torch.uint8, device=dev)
+        self.att_ws = torch.empty(
+            max(1, csa_attend_workspace_size(B, T, cfg.H, d, cfg.k, cfg.W)),
+            dtype=torch.uint8, device=dev)
+
+    # ------------------------------------------------------------ stages
+    def quantize_keys(self, first: int, last: int) -> None:
+        """FP8 copy (codes + per-entry scale) of compressed keys [first, last)."""
+        codes, scales = csa_quantize_fp8_rows(self.kc[:, first:last].contiguous())
+        self.ki_codes[:, first:last] = codes
+        self.ki_scale[:, first:last] = scales
+
+    def compress(self) -> None:
+        cfg = self.cfg
+        if not cfg.n_new_tokens:
+            return
+        x_k = self.kr[:, cfg.raw_before:cfg.raw_before + cfg.n_new_tokens]
+        x_v = self.vr[:, cfg.raw_before:cfg.raw_before + cfg.n_new_tokens]
+        csa_compress(x_k, self.z, self.kc, cfg.m, cfg.n_ctx_entries)
+        csa_compress(x_v, self.z, self.vc, cfg.m, cfg.n_ctx_entries)
+        if cfg.ki_fp8:
+            self.quantize_keys(cfg.n_ctx_entries, cfg.n_cap)
+
+    def index(self) -> None:
+        cfg = self.cfg
+        if cfg.ki_fp8:
+            csa_index_scores(self.qi_codes, self.w, self.ki_codes, self.pos0, cfg.m, self.act,
+                             qi_scale=self.qi_scale, ki_scale=self.ki_scale, scores=self.scores)
+        else:
+            csa_index_scores(self.qi, self.w, self.kc, self.pos0, cfg.m, self.act,
+                             scores=self.scores)
+
+    def topk(self) -> None:
+        csa_topk(self.scores, self.pos0, self.cfg.m, self.cfg.k, idx=self.idx, ws=self.topk_ws)
+
+    def attend(self) -> None:
+        cfg = self.cfg
+        if cfg.hca:
+            hca_attend(self.q, self.kc, self.vc, cfg.m, self.kr, self.vr, self.raw_pos0,
+                       self.pos0, cfg.W, cfg.scale, out=self.out, lse=self.lse, ws=self.att_ws)
+        else:
+            csa_attend(self.q, self.kc, self.vc, self.idx, self.kr, self.vr, self.raw_pos0,
+                       self.pos0, cfg.W, cfg.scale, out=self.out, lse=self.lse, ws=self.att_ws)
+
+    def run(self) -> None:
+        """The whole step: compress (if the step completes blocks), then
+        indexer + top-k + attention (CSA) or dense attention (HCA)."""
+        self.compress()
+        if not self.cfg.hca:
+            self.index()
+            self.topk()
+        self.attend()

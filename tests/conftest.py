@@ -23,3 +23,12 @@ def golden(name):
 @pytest.fixture
 def load_golden():
     return golden
+
+
+def ensure_library():
+    """Build libcsa.so if it is not there yet (hipcc cross-compiles on CPU)."""
+    lib = os.path.join(ROOT, "long_context_sparse_16_amd", "libcsa.so")
+    if not os.path.exists(lib):
+        from long_context_sparse_16_amd import build as _b
+        _b.build()
+    return lib

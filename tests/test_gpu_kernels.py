@@ -1,0 +1,301 @@
+"""Stage-wise parity of the HIP kernels against the fp64 oracle, at sizes the
+oracle finishes in seconds that still span several tiles / workgroups and a
+ragged tail.  Every call goes through the C ABI (via the ctypes binding)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import ensure_library
+from gpu_util import (DEV, bf16_codes, compress_bound, decode, from_dev, rel_l2, say,
+                      score_close, to_dev)
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+ensure_library()
+import long_context_sparse_16_amd as csa  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _store(x, storage):
+    return x.astype(np.float32) if storage == "f32" else bf16_codes(x)
+
+
+# ------------------------------------------------------------- fp8 quantizer
+
+@pytest.mark.parametrize("storage", ["f32", "bf16"])
+def test_quantize_fp8_rows_bitexact(storage):
+    say("quantize", storage)
+    rng = np.random.default_rng(100)
+    x = rng.standard_normal((997, 128)).astype(np.float32) * 3
+    x[0] = 0.0                                  # zero row -> scale 1
+    x[1] = rng.standard_normal(128) * 1e-30     # tiny values: subnormal codes
+    x[2, :] = 1.0
+    x[2, 7] = -448.0                            # exact scale 1
+    # values whose quotient lands on exact e4m3 midpoints (ties to even)
+    mids = (oracle.e4m3_decode(np.arange(0x7e)) + oracle.e4m3_decode(np.arange(1, 0x7f))) / 2
+    x[3, :] = 0.0
+    x[3, :100] = mids[:100]
+    x[3, 100] = 448.0
+    xs = _store(x, storage)
+    codes, scales = csa.csa_quantize_fp8_rows(to_dev(xs))
+    torch.cuda.synchronize()
+    ref_codes, ref_scales = oracle.quantize_fp8_rows(decode(xs).astype(np.float32))
+    assert np.array_equal(from_dev(scales), ref_scales)
+    assert np.array_equal(from_dev(codes), ref_codes)
+
+
+# ---------------------------------------------------------------- compressor
+
+@pytest.mark.parametrize("storage", ["f32", "bf16"])
+@pytest.mark.parametrize("m,d,nb", [(4, 64, 37), (4, 128, 600), (128, 128, 5), (1, 64, 9)])
+def test_compress_parity(storage, m, d, nb):
+    say("compress", storage, m, d, nb)
+    rng = np.random.default_rng(200 + m + d)
+    B, first, extra = 2, 5, 3
+    n_tok = nb * m
+    n_cap = first + nb + extra
+    x = _store(rng.standard_normal((B, n_tok, d)), storage)
+    z = (rng.standard_normal((B, n_tok, d)) * 2).astype(np.float32)
+    sentinel = np.full((B, n_cap, d), 7.0, np.float32)
+    cache = to_dev(_store(sentinel, storage))
+    csa.csa_compress(to_dev(x), to_dev(z), cache, m, first)
+    got = decode(from_dev(cache))
+    for b in range(B):
+        xv = decode(x[b])
+        ref = oracle.compress(xv, z[b], m)
+        g = got[b, first:first + nb]
+        if storage == "f32":
+            assert np.max(np.abs(g - ref)) <= 1e-5 * max(1.0, np.max(np.abs(ref)))
+        else:
+            assert np.all(np.abs(g - ref) <= compress_bound(ref, xv.reshape(nb, m, d), m))
+        assert np.all(got[b, :first] == 7.0) and np.all(got[b, first + nb:] == 7.0)
+
+
+@pytest.mark.parametrize("storage", ["f32", "bf16"])
+def test_compress_one_hot_and_chunked_append(storage):
+    say("compress one-hot / chunked", storage)
+    rng = np.random.default_rng(300)
+    B, m, d, nb = 3, 4, 128, 50
+    x = _store(rng.standard_normal((B, nb * m, d)), storage)
+    pick = rng.integers(0, m, size=(B, nb, d))
+    z = np.full((B, nb, m, d), -1e30, np.float32)
+    np.put_along_axis(z, pick[:, :, None, :], 0.0, axis=2)
+    z = z.reshape(B, nb * m, d)
+    cache = to_dev(_store(np.zeros((B, nb, d)), storage))
+    csa.csa_compress(to_dev(x), to_dev(z), cache, m, 0)
+    got = from_dev(cache)
+    want = np.take_along_axis(x.reshape(B, nb, m, d), pick[:, :, None, :], axis=2)[:, :, 0]
+    assert np.array_equal(got, want)  # exact subsampling, bit for bit
+    # appending in two chunks (first_entry = entries already present) equals
+    # one call, bit for bit
+    z2 = rng.standard_normal((B, nb * m, d)).astype(np.float32)
+    xd, zd = to_dev(x), to_dev(z2)
+    whole = to_dev(_store(np.zeros((B, nb, d)), storage))
+    parts = to_dev(_store(np.zeros((B, nb, d)), storage))
+    csa.csa_compress(xd, zd, whole, m, 0)
+    cut = 23 * m
+    csa.csa_compress(xd[:, :cut], zd[:, :cut], parts, m, 0)
+    csa.csa_compress(xd[:, cut:], zd[:, cut:], parts, m, cut // m)
+    assert np.array_equal(from_dev(whole), from_dev(parts))
+
+
+# ------------------------------------------------------------------- indexer
+
+@pytest.mark.parametrize("kind,H_I,d_I", [("f32", 4, 64), ("f32", 64, 128), ("bf16", 64, 128),
+                                         ("bf16", 20, 64), ("fp8", 64, 128), ("fp8", 7, 128)])
+@pytest.mark.parametrize("act", ["relu", "identity"])
+def test_indexer_parity(kind, H_I, d_I, act):
+    say("indexer", kind, H_I, d_I, act)
+    rng = np.random.default_rng(400 + H_I + d_I)
+    B, T, m, n_cap = 2, 3, 4, 5000
+    pos0 = np.array([4 * n_cap - 3, 37], np.int64)   # full cache / a short prefix
+    storage = "f32" if kind == "f32" else "bf16"
+    qi = _store(rng.standard_normal((B, T, H_I, d_I)), storage)
+    ki = _store(rng.standard_normal((B, n_cap, d_I)), storage)
+    w = rng.random((B, T, H_I)).astype(np.float32)
+    qi_d, ki_d = to_dev(qi), to_dev(ki)
+    qs = ks = None
+    qv, kv = decode(qi), decode(ki)
+    if kind == "fp8":
+        qi_d, qs = csa.csa_quantize_fp8_rows(qi_d)
+        ki_d, ks = csa.csa_quantize_fp8_rows(ki_d)
+        qc, qsc = oracle.quantize_fp8_rows(qv.astype(np.float32))
+        kcode, ksc = oracle.quantize_fp8_rows(kv.astype(np.float32))
+        assert np.array_equal(from_dev(qi_d), qc) and np.array_equal(from_dev(ki_d), kcode)
+        qv = oracle.e4m3_decode(qc) * qsc[..., None]
+        kv = oracle.e4m3_decode(kcode) * ksc[..., None]
+    scores = torch.full((B, T, n_cap), float("nan"), device=DEV)
+    csa.csa_index_scores(qi_d, to_dev(w), ki_d, to_dev(pos0), m, act, qi_scale=qs, ki_scale=ks,
+                         scores=scores)
+    got = from_dev(scores)
+    worst = 0.0
+    for b in range(B):
+        pos = pos0[b] + np.arange(T)
+        ref = oracle.indexer_scores(qv[b], w[b], kv[b], pos, m, act)
+        V = oracle.visible_count(pos, m)
+        for i in range(T):
+            worst = max(worst, score_close(got[b, i, :V[i]], ref[i, :V[i]]))
+            assert np.all(np.isnan(got[b, i, V[i]:])), "wrote past the visible entries"
+    assert worst <= 1.0, worst
+
+
+# --------------------------------------------------------------------- top-k
+
+def _topk_case(scores, V, k):
+    """Run csa_topk with m = 1 so that V(t) = t + 1 is set through pos0."""
+    B, T, n_cap = scores.shape
+    pos0 = (V[:, 0] - 1).astype(np.int64)
+    assert np.all(V == (pos0[:, None] + np.arange(T) + 1))
+    idx = csa.csa_topk(to_dev(scores.astype(np.float32)), to_dev(pos0), 1, k)
+    got = from_dev(idx)
+    for b in range(B):
+        for i in range(T):
+            want = oracle.topk_select(scores[b, i].astype(np.float64), int(min(V[b, i], n_cap)), k)
+            assert np.array_equal(got[b, i], want), (b, i)
+    return got
+
+
+@pytest.mark.parametrize("path", ["split", "row"])
+def test_topk_random_and_ties(path):
+    say("topk", path)
+    rng = np.random.default_rng(500)
+    k = 100
+    if path == "split":
+        B, T, n_cap = 5, 4, 9000
+    else:
+        B, T, n_cap = 1, 300, 3000
+    s = rng.standard_normal((B, T, n_cap)).astype(np.float32) * 30 + 140
+    s[:, 1] = rng.integers(0, 40, size=s[:, 1].shape)          # heavy ties
+    s[:, 2] = np.where(rng.random(s[:, 2].shape) < 0.5, -0.0, 0.0)  # signed zeros
+    s[:, 2, ::7] = rng.standard_normal(s[:, 2, ::7].shape)
+    V = np.zeros((B, T), np.int64)
+    for b in range(B):
+        start = n_cap - T - 3 * b if path == "split" else 40
+        V[b] = start + np.arange(T)
+    _topk_case(s, np.minimum(V, n_cap), k)
+
+
+def test_topk_edge_rows():
+    say("topk edges")
+    rng = np.random.default_rng(501)
+    # V <= k (all kept, -1 padding), V = k + 1, k = 1, and a row of equal
+    # scores longer than the LDS candidate buffer (global fallback)
+    cases = [(1, 64, 50), (1, 64, 64), (1, 64, 65), (1, 1, 3000), (2, 1024, 1025)]
+    for B, k, v in cases:
+        s = rng.standard_normal((B, 1, v + 5)).astype(np.float32)
+        _topk_case(s, np.full((B, 1), v, np.int64), k)
+    s = np.zeros((2, 1, 20000), np.float32)
+    got = _topk_case(s, np.full((2, 1), 20000, np.int64), 1024)
+    assert np.array_equal(got[0, 0], np.arange(1024))
+    s = np.zeros((1, 300, 20000), np.float32)
+    s[0, :, 5000] = 1.0
+    got = _topk_case(s, np.arange(19700, 20000)[None], 16)
+    assert np.array_equal(got[0, 0], np.r_[np.arange(15), 5000])
+
+
+def test_topk_long_rows_decode_shape():
+    say("topk long rows")
+    rng = np.random.default_rng(502)
+    s = (rng.standard_normal((4, 1, 262144)) * 31 + 141).astype(np.float32)
+    _topk_case(s, np.full((4, 1), 262144, np.int64), 1024)
+
+
+# ----------------------------------------------------------------- attention
+
+def _attend_case(storage, B, T, H, d, N, k, W, R, raw_off, seed, hca_m=0, fill=0.8):
+    rng = np.random.default_rng(seed)
+    kc = _store(rng.standard_normal((B, N, d)), storage)
+    vc = _store(rng.standard_normal((B, N, d)), storage)
+    kr = _store(rng.standard_normal((B, R, d)), storage)
+    vr = _store(rng.standard_normal((B, R, d)), storage)
+    q = _store(rng.standard_normal((B, T, H, d)), storage)
+    m = hca_m if hca_m else 4
+    pos0 = np.array([raw_off[b] + R - T for b in range(B)], np.int64)
+    raw_pos0 = np.array(raw_off, np.int64)
+    scale = 1.0 / math.sqrt(d)
+    idx = None
+    if not hca_m:
+        idx = np.full((B, T, k), -1, np.int32)
+        for b in range(B):
+            for i in range(T):
+                V = int(min(N, (pos0[b] + i + 1) // m))
+                n = min(V, int(rng.integers(int(fill * k), k + 1)))
+                idx[b, i, :n] = np.sort(rng.choice(V, size=n, replace=False))
+    args = (to_dev(q), to_dev(kc), to_dev(vc))
+    if hca_m:
+        out, lse = csa.hca_attend(*args, hca_m, to_dev(kr), to_dev(vr), to_dev(raw_pos0),
+                                  to_dev(pos0), W, scale)
+    else:
+        out, lse = csa.csa_attend(*args, to_dev(idx), to_dev(kr), to_dev(vr), to_dev(raw_pos0),
+                                  to_dev(pos0), W, scale)
+    out, lse = from_dev(out), from_dev(lse)
+    errs, rels = [], []
+    for b in range(B):
+        pos = pos0[b] + np.arange(T)
+        if hca_m:
+            ref, ref_lse = oracle.hca_attend(decode(q[b]), decode(kc[b]), decode(vc[b]),
+                                             decode(kr[b]), decode(vr[b]), raw_pos0[b], pos,
+                                             hca_m, W, scale)
+        else:
+            ref, ref_lse = oracle.attend(decode(q[b]), decode(kc[b]), decode(vc[b]), idx[b],
+                                         decode(kr[b]), decode(vr[b]), raw_pos0[b], pos, W, scale)
+        errs.append(np.max(np.abs(out[b] - ref)))
+        errs.append(np.max(np.abs(lse[b] - ref_lse)))
+        rels.append(rel_l2(out[b], ref))
+    return max(errs), max(rels)
+
+
+@pytest.mark.parametrize("storage,H,d", [("f32", 8, 64), ("f32", 64, 128), ("bf16", 64, 128),
+                                         ("bf16", 16, 64), ("bf16", 40, 128)])
+@pytest.mark.parametrize("rows", ["few", "many"])
+def test_attend_parity(storage, H, d, rows):
+    say("attend", storage, H, d, rows)
+    if rows == "few":   # split over several workgroups + merge
+        B, T, k, N, W, R = 3, 2, 700, 3000, 128, 200
+    else:               # one workgroup per query
+        B, T, k, N, W, R = 1, 300, 64, 600, 32, 400
+    err, rel = _attend_case(storage, B, T, H, d, N, k, W, R, [100 * b + 2500 for b in range(B)]
+                            if rows == "few" else [2000], seed=600 + H + d)
+    tol = 1e-4 if storage == "f32" else 2e-2
+    assert err <= tol, err
+    assert rel <= (1e-5 if storage == "f32" else 1e-2), rel
+
+
+@pytest.mark.parametrize("storage", ["f32", "bf16"])
+def test_attend_window_edges(storage):
+    """Queries near position 0 (window shorter than W, nothing compressed
+    yet) and an empty selection."""
+    say("attend edges", storage)
+    err, _ = _attend_case(storage, 1, 9, 16, 64, 8, 4, 5, 9, [0], seed=700, fill=0.0)
+    assert err <= (1e-4 if storage == "f32" else 2e-2)
+    # t = 0: the only key is raw token 0, so O = v_0 exactly
+    rng = np.random.default_rng(701)
+    d, H = 64, 16
+    q = _store(rng.standard_normal((1, 1, H, d)), storage)
+    v = _store(rng.standard_normal((1, 1, d)), storage)
+    kk = _store(rng.standard_normal((1, 1, d)), storage)
+    kc = to_dev(_store(np.zeros((1, 4, d)), storage))
+    zero = to_dev(np.zeros(1, np.int64))
+    out, lse = csa.csa_attend(to_dev(q), kc, kc, to_dev(np.full((1, 1, 4), -1, np.int32)),
+                              to_dev(kk), to_dev(v), zero, zero, 32, 0.125)
+    assert np.array_equal(from_dev(out)[0, 0], np.tile(decode(v)[0, 0], (H, 1)).astype(np.float32))
+
+
+@pytest.mark.parametrize("storage,m", [("bf16", 128), ("bf16", 4), ("f32", 4)])
+def test_hca_parity(storage, m):
+    say("hca", storage, m)
+    B, T, H, d, N, W, R = 2, 2, 64, 128, 1500, 128, 300
+    raw = [N * m - 5 - R + T, 40 * m]
+    err, rel = _attend_case(storage, B, T, H, d, N, 0, W, R, raw, seed=800 + m, hca_m=m)
+    assert err <= (1e-4 if storage == "f32" else 2e-2), err
+    assert rel <= (1e-5 if storage == "f32" else 1e-2), rel
