@@ -33,6 +33,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="csa_decode_128k_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch stages directly, no HIP graphs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle sample")
     return ap.parse_args()
@@ -107,46 +108,58 @@ def main():
 
     import workloads as WL
     if not os.path.exists(os.path.join(ROOT, "long_context_sparse_16_amd", "libcsa.so")):
-        from long_context_sparse_16_amd import build as _b
-        _b.build()
+        import __graft_entry__
+        __graft_entry__._build_module().build()
     from long_context_sparse_16_amd.pipeline import CSAStep
 
     cfg = WL.BY_NAME[args.workload]
     batch = WL.make_batch(cfg)
     step = CSAStep(cfg, batch)
     del batch
-    stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
 
+    # one HIP graph per stage: replays carry almost no host launch cost, and
+    # events between replays on the same stream time each stage
+    stages = ([step.compress] if cfg.n_new_tokens else []) + \
+        ([step.index, step.topk] if not cfg.hca else []) + [step.attend]
+    names = (["compress"] if cfg.n_new_tokens else []) + \
+        (["index", "topk"] if not cfg.hca else []) + ["attend"]
+    run_stage = stages
+    if not args.eager:
+        graphs = []
+        for fn in stages:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            graphs.append(g)
+        run_stage = [g.replay for g in graphs]
+        for _ in range(args.warmup):
+            for r in run_stage:
+                r()
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    n_ev = len(run_stage) + 1
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
         e = ev[s]
         e[0].record(stream)
-        step.compress()
-        e[1].record(stream)
-        if not cfg.hca:
-            step.index()
-            e[2].record(stream)
-            step.topk()
-            e[3].record(stream)
-        else:
-            e[2].record(stream)
-            e[3].record(stream)
-        step.attend()
-        e[4].record(stream)
+        for j, r in enumerate(run_stage):
+            r()
+            e[j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     def stage(a, b):
         return float(np.mean([ev[s][a].elapsed_time(ev[s][b]) for s in range(K)]))
 
-    st = {"compress": stage(0, 1), "index": stage(1, 2), "topk": stage(2, 3),
-          "attend": stage(3, 4), "step_events": stage(0, 4)}
+    st = {nm: stage(j, j + 1) for j, nm in enumerate(names)}
+    st["step_events"] = stage(0, n_ev - 1)
     queries = cfg.B * cfg.T
     V = int(min(cfg.n_cap, (cfg.pos0 + cfg.T) // cfg.m))
     ms_per_step = wall * 1e3 / K
@@ -178,6 +191,7 @@ def main():
                    "top_k": cfg.k, "heads": cfg.H, "head_dim": cfg.d, "window": cfg.W},
         "entries_scored_per_s": (cfg.B * cfg.T * V * K / wall) if not cfg.hca else None,
         "stage_ms": st,
+        "launch": "eager" if args.eager else "hip_graph_per_stage",
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

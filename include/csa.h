@@ -36,6 +36,14 @@
  *   complete.  Kernels clamp V(t) to n_cap so that no access leaves the
  *   buffers; positions with V(t) > n_cap are a caller error.
  * - Scores must be finite; -0.0 is ranked equal to +0.0.
+ * - Workspaces (`ws`): device memory owned by the caller, sized by the
+ *   matching *_workspace_size() query.  Top-k workspaces follow an
+ *   all-zero protocol: zero before first use (a zero-filled allocation, or
+ *   csa_workspace_clear), and every call returns them to all-zero, so they
+ *   are reused call after call without clearing.  Attention workspaces
+ *   hold per-call partial results and may contain anything on entry.
+ *   Calls that share a workspace must be ordered (same stream); concurrent
+ *   calls on one workspace race.
  */
 #ifndef CSA_H
 #define CSA_H
@@ -71,6 +79,10 @@ const char* csa_status_string(int status);
 const char* csa_last_error(void);
 /* ABI version of this library (incremented on incompatible changes). */
 int csa_abi_version(void);
+
+/* Zero `ws_bytes` bytes of a device workspace on `stream` (a kernel, so it
+ * may be captured in a HIP graph).  ws 16-byte aligned, ws_bytes % 4 == 0. */
+int csa_workspace_clear(void* ws, size_t ws_bytes, void* stream);
 
 /*
  * csa_compress -- the token-level compressor (takeshell.com 2.1: every m
@@ -121,6 +133,14 @@ int csa_quantize_fp8_rows(const void* x, int x_dtype, int64_t rows, int64_t d,
  *   scores = ki_scale[b,j] * sum_h (w * qi_scale[b,i,h]) * phi(q~ . k~).
  * Entries j >= V(t) of a score row are not written.
  *
+ * Optional fusion with csa_topk: when topk_ws is non-NULL, the call also
+ * accumulates into topk_ws the first-digit histogram of the top-k
+ * selection with this k (saves csa_topk one pass over the scores); the
+ * next call must then be csa_topk(..., topk_ws, ..., hist_ready = 1) with
+ * the same B, T, n_cap, m, k, which consumes it.  topk_ws must be in its
+ * all-zero state and at least csa_topk_workspace_size() bytes.  With
+ * topk_ws == NULL, k is ignored.
+ *
  *   qi        [B][T][H_I][d_I]      qi_dtype
  *   qi_scale  [B][T][H_I] fp32      FP8 only (else ignored, may be NULL)
  *   w         [B][T][H_I] fp32
@@ -135,8 +155,8 @@ int csa_index_scores(const void* qi, int qi_dtype, const float* qi_scale,
                      const float* w, const void* ki, int ki_dtype,
                      const float* ki_scale, const int64_t* pos0,
                      int64_t B, int64_t T, int64_t H_I, int64_t d_I,
-                     int64_t n_cap, int m, int act, float* scores,
-                     void* stream);
+                     int64_t n_cap, int m, int act, float* scores, int k,
+                     void* topk_ws, size_t topk_ws_bytes, void* stream);
 
 /*
  * csa_topk -- per-query top-k selection (takeshell.com 2.1: the k most
@@ -147,19 +167,25 @@ int csa_index_scores(const void* qi, int qi_dtype, const float* qi_scale,
  *
  *   scores [B][T][n_cap] fp32 (only j < V(t) is read)
  *   idx    [B][T][k] int32
- *   ws     device workspace of at least csa_topk_workspace_size() bytes;
- *          its contents on entry do not matter.
+ *   ws     device workspace of csa_topk_workspace_size() bytes (all-zero
+ *          protocol above; the size is 0, and ws may be NULL, when B*T is
+ *          large enough for one workgroup per query row).
+ *   hist_ready  1 if the directly preceding csa_index_scores was given
+ *          this ws (and k) and so already built the first-digit
+ *          histogram; 0 otherwise.
  * 1 <= k <= 4096.
  */
 size_t csa_topk_workspace_size(int64_t B, int64_t T, int64_t n_cap, int k);
 int csa_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T,
              int64_t n_cap, int m, int k, int32_t* idx, void* ws,
-             size_t ws_bytes, void* stream);
+             size_t ws_bytes, int hist_ready, void* stream);
 
 /*
  * csa_index_topk -- csa_index_scores followed by csa_topk on the same
- * stream.  scores may be NULL, in which case the score matrix lives in the
- * workspace (csa_index_topk_workspace_size accounts for it).
+ * stream, with the top-k histogram fused into the indexer.  scores may be
+ * NULL, in which case the score matrix lives in the workspace
+ * (csa_index_topk_workspace_size accounts for it).  Same all-zero
+ * workspace protocol.
  */
 size_t csa_index_topk_workspace_size(int64_t B, int64_t T, int64_t n_cap,
                                      int k, int scores_in_workspace);
@@ -191,9 +217,11 @@ int csa_index_topk(const void* qi, int qi_dtype, const float* qi_scale,
  *   raw_pos0 [B] int64 (device); window positions outside the raw buffer
  *          are a caller error and are skipped (never read out of bounds)
  *   out   [B][T][H][d] fp32;  lse [B][T][H] fp32 or NULL
- *   ws    device workspace of csa_attend_workspace_size() bytes
- * Supported: dtypes F32, BF16; d in {64, 128}; 1 <= H <= 64 (H % 16 == 0
- * or H < 16); 0 <= W <= 4096; 0 <= k <= 65536.  A query whose key set is
+ *   ws    device workspace of csa_attend_workspace_size() bytes (contents
+ *         on entry do not matter; size 0 and ws may be NULL when each query
+ *         fits one workgroup)
+ * Supported: dtypes F32, BF16; d in {64, 128}; 1 <= H <= 64;
+ * 0 <= W <= 4096; 0 <= k <= 65536; k + W >= 1.  A query whose key set is
  * empty gets out = 0 and lse = -inf.
  */
 size_t csa_attend_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d,

@@ -47,12 +47,13 @@ _SIGNATURES = {
     "csa_status_string": (ctypes.c_char_p, [_i]),
     "csa_last_error": (ctypes.c_char_p, []),
     "csa_abi_version": (_i, []),
+    "csa_workspace_clear": (_i, [_vp, _sz, _vp]),
     "csa_compress": (_i, [_vp, _i, _vp, _i64, _i64, _i64, _i, _i64, _i64, _vp, _i, _i64, _i64, _vp]),
     "csa_quantize_fp8_rows": (_i, [_vp, _i, _i64, _i64, _vp, _vp, _vp]),
     "csa_index_scores": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
-                              _i, _i, _vp, _vp]),
+                              _i, _i, _vp, _i, _vp, _sz, _vp]),
     "csa_topk_workspace_size": (_sz, [_i64, _i64, _i64, _i]),
-    "csa_topk": (_i, [_vp, _vp, _i64, _i64, _i64, _i, _i, _vp, _vp, _sz, _vp]),
+    "csa_topk": (_i, [_vp, _vp, _i64, _i64, _i64, _i, _i, _vp, _vp, _sz, _i, _vp]),
     "csa_index_topk_workspace_size": (_sz, [_i64, _i64, _i64, _i, _i]),
     "csa_index_topk": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i,
                             _i, _i, _vp, _vp, _vp, _sz, _vp]),
@@ -201,8 +202,12 @@ def _index_shapes(qi, w, ki, pos0):
 
 
 def csa_index_scores(qi, w, ki, pos0, m: int, act="relu", qi_scale=None, ki_scale=None,
-                     scores=None, stream=None) -> torch.Tensor:
-    """Lightning Indexer scores [B, T, n_cap] (entries j >= V(t) untouched)."""
+                     scores=None, topk_ws=None, k: int = 0, stream=None) -> torch.Tensor:
+    """Lightning Indexer scores [B, T, n_cap] (entries j >= V(t) untouched).
+
+    With ``topk_ws`` (a clean top-k workspace) and ``k``, the first-digit
+    histogram of the top-k is built on the way; follow with
+    ``csa_topk(..., ws=topk_ws, hist_ready=True)``."""
     dev = _dev(qi, w, ki, pos0)
     B, T, H_I, d_I, n_cap = _index_shapes(qi, w, ki, pos0)
     if scores is None:
@@ -210,10 +215,11 @@ def csa_index_scores(qi, w, ki, pos0, m: int, act="relu", qi_scale=None, ki_scal
     _contig("scores", scores)
     if scores.shape != (B, T, n_cap) or scores.dtype != torch.float32:
         raise ValueError("scores must be float32 [B, T, n_cap]")
+    nbytes = 0 if topk_ws is None else topk_ws.numel() * topk_ws.element_size()
     _check("csa_index_scores", _lib.csa_index_scores(
         _ptr(qi), _dtype_code(qi), _ptr(qi_scale), _ptr(w), _ptr(ki), _dtype_code(ki),
         _ptr(ki_scale), _ptr(pos0), B, T, H_I, d_I, n_cap, int(m), _act_code(act), _ptr(scores),
-        _stream(stream, dev)))
+        int(k), _ptr(topk_ws), nbytes, _stream(stream, dev)))
     return scores
 
 
@@ -221,17 +227,28 @@ def csa_topk_workspace_size(B: int, T: int, n_cap: int, k: int) -> int:
     return int(_lib.csa_topk_workspace_size(B, T, n_cap, k))
 
 
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled workspace (the state every call expects and leaves)."""
+    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def csa_workspace_clear(ws: torch.Tensor, stream=None) -> None:
+    _check("csa_workspace_clear", _lib.csa_workspace_clear(
+        _ptr(ws), ws.numel() * ws.element_size() // 4 * 4, _stream(stream, ws.device)))
+
+
 def _workspace(ws, need, dev):
     if need == 0:
-        return ws, 0
+        return ws, 0 if ws is None else ws.numel() * ws.element_size()
     if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws = workspace(need, dev)
     if ws.numel() * ws.element_size() < need:
         raise ValueError(f"workspace needs {need} bytes")
     return ws, ws.numel() * ws.element_size()
 
 
-def csa_topk(scores, pos0, m: int, k: int, idx=None, ws=None, stream=None) -> torch.Tensor:
+def csa_topk(scores, pos0, m: int, k: int, idx=None, ws=None, hist_ready=False,
+             stream=None) -> torch.Tensor:
     """Top-k entry indices [B, T, k] int32, ascending, padded with -1."""
     dev = _dev(scores, pos0)
     _contig("scores", scores)
@@ -242,7 +259,7 @@ def csa_topk(scores, pos0, m: int, k: int, idx=None, ws=None, stream=None) -> to
     ws, nbytes = _workspace(ws, csa_topk_workspace_size(B, T, n_cap, k), dev)
     _check("csa_topk", _lib.csa_topk(
         _ptr(scores), _ptr(pos0), B, T, n_cap, int(m), int(k), _ptr(idx), _ptr(ws), nbytes,
-        _stream(stream, dev)))
+        int(bool(hist_ready)), _stream(stream, dev)))
     return idx
 
 
@@ -348,7 +365,8 @@ def hca_attend(q, kc, vc, m: int, kr, vr, raw_pos0, pos0, W: int, scale: float, 
 
 
 __all__ = [
-    "CSAError", "LIB_PATH", "abi_version", "last_error", "header_functions",
+    "CSAError", "LIB_PATH", "abi_version", "last_error", "header_functions", "workspace",
+    "csa_workspace_clear",
     "csa_compress", "csa_quantize_fp8_rows", "csa_index_scores", "csa_topk",
     "csa_topk_workspace_size", "csa_index_topk", "csa_index_topk_workspace_size",
     "csa_attend", "csa_attend_workspace_size", "hca_attend", "hca_attend_workspace_size",

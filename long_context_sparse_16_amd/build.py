@@ -1,9 +1,10 @@
 """Build libcsa.so (the C ABI of include/csa.h) for gfx950 with hipcc.
 
 Every source is compiled to an object under _build/ (in parallel) and the
-objects are linked into long_context_sparse_16_amd/libcsa.so.  Run as
-``python -m long_context_sparse_16_amd.build`` or through
-``__graft_entry__.build()``.
+objects are linked into long_context_sparse_16_amd/libcsa.so.  Run as a
+script (``python long_context_sparse_16_amd/build.py``) or through
+``__graft_entry__.build()``; it imports nothing from the package, whose
+import needs the library built here.
 """
 
 from __future__ import annotations

@@ -141,6 +141,15 @@ const char* csa_last_error(void) { return g_last_error; }
 
 int csa_abi_version(void) { return 1; }
 
+int csa_workspace_clear(void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "csa_workspace_clear";
+  if (ws_bytes == 0) return ok();
+  CSA_REQUIRE(ws, CSA_ERR_NULL, "%s: ws must be non-NULL", fn);
+  CSA_REQUIRE(aligned16(ws) && ws_bytes % 4 == 0, CSA_ERR_WORKSPACE,
+              "%s: ws must be 16-byte aligned and a multiple of 4 bytes", fn);
+  return hip_result(csa::launch_clear(ws, ws_bytes, static_cast<hipStream_t>(stream)), fn);
+}
+
 int csa_compress(const void* x, int x_dtype, const float* logits, int64_t B, int64_t n_tok,
                  int64_t d, int m, int64_t x_batch_stride, int64_t z_batch_stride, void* cache,
                  int cache_dtype, int64_t n_cap, int64_t first_entry, void* stream) {
@@ -188,13 +197,22 @@ int csa_quantize_fp8_rows(const void* x, int x_dtype, int64_t rows, int64_t d, u
 int csa_index_scores(const void* qi, int qi_dtype, const float* qi_scale, const float* w,
                      const void* ki, int ki_dtype, const float* ki_scale, const int64_t* pos0,
                      int64_t B, int64_t T, int64_t H_I, int64_t d_I, int64_t n_cap, int m, int act,
-                     float* scores, void* stream) {
+                     float* scores, int k, void* topk_ws, size_t topk_ws_bytes, void* stream) {
   const char* fn = "csa_index_scores";
   int rc = check_index_args(qi, qi_dtype, qi_scale, w, ki, ki_dtype, ki_scale, pos0, B, T, H_I,
                             d_I, n_cap, m, act, scores, fn);
   if (rc) return rc;
+  uint32_t* hist = nullptr;
+  if (topk_ws) {
+    CSA_REQUIRE(k >= 1 && k <= 4096, CSA_ERR_UNSUPPORTED, "%s: k must be in [1, 4096]", fn);
+    const size_t need = csa_topk_workspace_size(B, T, n_cap, k);
+    CSA_REQUIRE(topk_ws_bytes >= need, CSA_ERR_WORKSPACE,
+                "%s: top-k workspace of %zu bytes needed, got %zu", fn, need, topk_ws_bytes);
+    CSA_REQUIRE(aligned16(topk_ws), CSA_ERR_WORKSPACE, "%s: ws must be 16-byte aligned", fn);
+    hist = need ? csa::topk_hist_ptr(topk_ws, B, T) : nullptr;
+  }
   return hip_result(csa::launch_index_scores(qi, qi_dtype, qi_scale, w, ki, ki_scale, pos0, B, T,
-                                             H_I, d_I, n_cap, m, act, scores,
+                                             H_I, d_I, n_cap, m, act, scores, hist, k,
                                              static_cast<hipStream_t>(stream)),
                     fn);
 }
@@ -205,7 +223,7 @@ size_t csa_topk_workspace_size(int64_t B, int64_t T, int64_t n_cap, int k) {
 }
 
 int csa_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, int64_t n_cap, int m,
-             int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+             int k, int32_t* idx, void* ws, size_t ws_bytes, int hist_ready, void* stream) {
   const char* fn = "csa_topk";
   int rc = check_topk_args(scores, pos0, B, T, n_cap, m, k, idx, fn);
   if (rc) return rc;
@@ -214,9 +232,9 @@ int csa_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, int
               "%s: workspace of %zu bytes needed, got %zu", fn, need, ws ? ws_bytes : 0);
   CSA_REQUIRE(ws == nullptr || aligned16(ws), CSA_ERR_WORKSPACE, "%s: ws must be 16-byte aligned",
               fn);
-  return hip_result(
-      csa::launch_topk(scores, pos0, B, T, n_cap, m, k, idx, ws, static_cast<hipStream_t>(stream)),
-      fn);
+  return hip_result(csa::launch_topk(scores, pos0, B, T, n_cap, m, k, idx, ws, hist_ready != 0,
+                                     static_cast<hipStream_t>(stream)),
+                    fn);
 }
 
 size_t csa_index_topk_workspace_size(int64_t B, int64_t T, int64_t n_cap, int k,
@@ -250,11 +268,13 @@ int csa_index_topk(const void* qi, int qi_dtype, const float* qi_scale, const fl
   rc = check_topk_args(sc, pos0, B, T, n_cap, m, k, idx, fn);
   if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* hist = csa::topk_hist_ptr(topk_ws, B, T);
   rc = hip_result(csa::launch_index_scores(qi, qi_dtype, qi_scale, w, ki, ki_scale, pos0, B, T,
-                                           H_I, d_I, n_cap, m, act, sc, s),
+                                           H_I, d_I, n_cap, m, act, sc, hist, k, s),
                   fn);
   if (rc) return rc;
-  return hip_result(csa::launch_topk(sc, pos0, B, T, n_cap, m, k, idx, topk_ws, s), fn);
+  return hip_result(csa::launch_topk(sc, pos0, B, T, n_cap, m, k, idx, topk_ws, hist != nullptr, s),
+                    fn);
 }
 
 size_t csa_attend_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d, int k, int W) {

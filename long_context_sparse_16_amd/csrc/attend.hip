@@ -24,6 +24,7 @@
 namespace csa {
 
 constexpr int kAttChunk = 64;  // keys per LDS chunk
+constexpr int kMergeMaxSplits = 64;  // partials merged per row
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int DTYPE, int D>
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15;
   const int g = lane >> 4;
   const int64_t row = blockIdx.y;
@@ -106,26 +107,26 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
     for (int v = 0; v < kQVec; ++v) qf[v] = src[v];
   }
 
-  // source row of slot s (nullptr if absent)
-  auto slot_rows = [&](int64_t s, const uint8_t*& krow, const uint8_t*& vrow) {
-    krow = nullptr;
-    vrow = nullptr;
-    if (s < n_ent) {
-      int64_t e = HCA ? s : static_cast<int64_t>(p.idx[row * p.k + s]);
-      if (e >= 0 && e < p.n_cap) {
-        krow = p.kc + (b * p.n_cap + e) * RB;
-        vrow = p.vc + (b * p.n_cap + e) * RB;
-      }
-    } else if (s < n_slots) {
-      const int64_t pos = t - p.W + 1 + (s - n_ent);
-      const int64_t r = pos - rp0;
-      if (pos >= 0 && r >= 0 && r < p.R) {
-        krow = p.kr + (b * p.R + r) * RB;
-        vrow = p.vr + (b * p.R + r) * RB;
+  // Every thread gathers kPerThread 16-byte pieces of K and of V per chunk.
+  // Absent slots (padding, positions outside the raw buffer) read row 0 of
+  // the sequence's cache instead, so every load is issued unconditionally;
+  // they are masked out of the softmax and their values get weight 0.
+  const uint8_t* kc_b = p.kc + b * p.n_cap * RB;
+  const uint8_t* vc_b = p.vc + b * p.n_cap * RB;
+  const int64_t idx_row = row * p.k;
+  int32_t ent[kPerThread];  // the chunk's entry index per piece (CSA)
+  auto fetch_idx = [&](int64_t chunk) {
+#pragma unroll
+    for (int r = 0; r < kPerThread; ++r) {
+      const int64_t s = chunk * kAttChunk + (tid + 256 * r) / kPieces;
+      if (HCA) {
+        ent[r] = static_cast<int32_t>(s);
+      } else {
+        const int64_t sc = s < n_ent ? s : n_ent - 1;
+        ent[r] = n_ent > 0 ? p.idx[idx_row + sc] : -1;
       }
     }
   };
-
   u32x4 kreg[kPerThread], vreg[kPerThread];
   bool vld[kPerThread];
   auto gather = [&](int64_t chunk) {
@@ -134,16 +135,29 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
       const int id = tid + 256 * r;
       const int key = id / kPieces;
       const int pc = id - key * kPieces;
-      const uint8_t *krow, *vrow;
-      slot_rows(chunk * kAttChunk + key, krow, vrow);
-      vld[r] = krow != nullptr;
-      if (krow) {
-        kreg[r] = *reinterpret_cast<const u32x4*>(krow + pc * 16);
-        vreg[r] = *reinterpret_cast<const u32x4*>(vrow + pc * 16);
+      const int64_t s = chunk * kAttChunk + key;
+      const uint8_t* krow = kc_b;
+      const uint8_t* vrow = vc_b;
+      bool ok = false;
+      if (s < n_ent) {
+        const int64_t e = ent[r];
+        ok = e >= 0 && e < p.n_cap;
+        if (ok) {
+          krow = kc_b + e * RB;
+          vrow = vc_b + e * RB;
+        }
       } else {
-        kreg[r] = u32x4{0u, 0u, 0u, 0u};
-        vreg[r] = u32x4{0u, 0u, 0u, 0u};
+        const int64_t pos = t - p.W + 1 + (s - n_ent);
+        const int64_t rr = pos - rp0;
+        ok = s < n_slots && pos >= 0 && rr >= 0 && rr < p.R;
+        if (ok) {
+          krow = p.kr + (b * p.R + rr) * RB;
+          vrow = p.vr + (b * p.R + rr) * RB;
+        }
       }
+      vld[r] = ok;
+      kreg[r] = *reinterpret_cast<const u32x4*>(krow + pc * 16);
+      vreg[r] = *reinterpret_cast<const u32x4*>(vrow + pc * 16);
     }
   };
   auto stage = [&]() {
@@ -177,12 +191,19 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
   float m_run = -INFINITY;  // running max (log2 domain), uniform per head
   float l_run = 0.f;        // this lane's partial sum of exp
 
-  if (c_begin < c_end) gather(c_begin);
+  if (c_begin < c_end) {
+    fetch_idx(c_begin);
+    gather(c_begin);
+    if (c_begin + 1 < c_end) fetch_idx(c_begin + 1);
+  }
   for (int64_t c = c_begin; c < c_end; ++c) {
     __syncthreads();
     stage();
     __syncthreads();
-    if (c + 1 < c_end) gather(c + 1);
+    if (c + 1 < c_end) {
+      gather(c + 1);
+      if (c + 2 < c_end) fetch_idx(c + 2);
+    }
     if (!has_heads) continue;
 
     // S^T tiles: 4 tiles of 16 keys x 16 heads
@@ -271,12 +292,12 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
     }
   }
 
-  if (!has_heads) return;
   float l_tot = l_run;
   l_tot += __shfl_xor(l_tot, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  if (head >= p.H) return;
+  const bool writer = has_heads && head < p.H;
   if (p.splits == 1) {
+    if (!writer) return;
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     float* orow = p.out + (row * p.H + head) * D;
 #pragma unroll
@@ -284,7 +305,9 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
       *reinterpret_cast<f32x4*>(orow + dt * 16 + 4 * g) = o[dt] * inv;
     if (p.lse && g == 0)
       p.lse[row * p.H + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) / kLog2e : -INFINITY;
-  } else {
+    return;
+  }
+  if (writer) {
     const int64_t pr = (row * p.splits + split) * p.H + head;
     float* orow = p.po + pr * D;
 #pragma unroll
@@ -296,44 +319,72 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
   }
 }
 
-// Fixed-order merge of the split partials: one thread per (head, dim).
+// Merge the split partials of one (query row, head): one thread per output
+// dim.  All split maxima and sums are fetched at once into LDS, the merge
+// weights follow from them, and each thread then issues its partial-output
+// loads for every split before using any (fixed split order, so the result
+// does not depend on scheduling).
 template <int D>
-__global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
-  const int64_t row = blockIdx.x;
-  const int64_t n = p.H * D;
-  for (int64_t e = threadIdx.x; e < n; e += 256) {
-    const int64_t h = e / D;
-    float M = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.pm[(row * p.splits + s) * p.H + h]);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < p.splits; ++s) {
-        const int64_t pr = (row * p.splits + s) * p.H + h;
-        const float wgt = exp2f(p.pm[pr] - M);
-        L = fmaf(p.pl[pr], wgt, L);
-        O = fmaf(p.po[pr * D + (e - h * D)], wgt, O);
-      }
+__global__ __launch_bounds__(D) void attend_merge_kernel(AttParams p) {
+  __shared__ float s_w[kMergeMaxSplits];
+  __shared__ float s_inv[2];
+  const int64_t row = blockIdx.y;
+  const int64_t h = blockIdx.x;
+  const int dd = threadIdx.x;
+  const int64_t base = row * p.splits * p.H + h;  // partial (row, split 0, head h)
+  if (dd < 64) {
+    // one wave: per-split weights exp2(m_s - M) and the merged normaliser
+    const bool on = dd < p.splits;
+    const float pm = on ? p.pm[base + dd * p.H] : -INFINITY;
+    const float pl = on ? p.pl[base + dd * p.H] : 0.f;
+    const float M = wave_max(pm);
+    const float wgt = (M == -INFINITY || pm == -INFINITY) ? 0.f : exp2f(pm - M);
+    const float L = wave_sum(pl * wgt);
+    if (on) s_w[dd] = wgt;
+    if (dd == 0) {
+      s_inv[0] = L > 0.f ? 1.0f / L : 0.f;
+      s_inv[1] = L > 0.f ? (M + log2f(L)) / kLog2e : -INFINITY;
     }
-    p.out[row * n + e] = L > 0.f ? O / L : 0.f;
-    if (p.lse && e - h * D == 0)
-      p.lse[row * p.H + h] = L > 0.f ? (M + log2f(L)) / kLog2e : -INFINITY;
   }
+  __syncthreads();
+  float po[kMergeMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMergeMaxSplits; ++s)
+    po[s] = s < p.splits ? p.po[(base + s * p.H) * D + dd] : 0.f;
+  float O = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMergeMaxSplits; ++s)
+    if (s < p.splits) O = fmaf(po[s], s_w[s], O);
+  p.out[(row * p.H + h) * D + dd] = O * s_inv[0];
+  if (p.lse && dd == 0) p.lse[row * p.H + h] = s_inv[1];
 }
 
 // ----------------------------------------------------------------- host side
 
 AttSplit attend_split(int64_t rows, int64_t n_slots_max) {
+  // A split's partial result (H x D fp32) is as large as 64 gathered K/V
+  // rows, so splits are kept at >= 4 chunks (256 keys) unless the batch is
+  // too small to occupy the GPU otherwise; enough splits are made to give
+  // roughly 256 workgroups.
   AttSplit s;
   int64_t chunks = (n_slots_max + kAttChunk - 1) / kAttChunk;
   if (chunks < 1) chunks = 1;
-  int64_t target = rows >= 256 ? 1 : (512 + rows - 1) / rows;
+  int64_t target = rows >= 256 ? 1 : (256 + rows - 1) / rows;
+  int64_t min_cps = rows >= 64 ? 4 : rows >= 16 ? 2 : 1;
   if (target > chunks) target = chunks;
-  const int64_t cps = (chunks + target - 1) / target;
+  int64_t cps = (chunks + target - 1) / target;
+  if (cps < min_cps) cps = min_cps;
+  // the merge handles at most kMergeMaxSplits partials per row
+  if (cps < (chunks + kMergeMaxSplits - 1) / kMergeMaxSplits)
+    cps = (chunks + kMergeMaxSplits - 1) / kMergeMaxSplits;
+  if (cps > chunks) cps = chunks;
   s.chunks_per_split = static_cast<int>(cps);
   s.splits = static_cast<int>((chunks + cps - 1) / cps);
   return s;
 }
 
+// Workspace: the split partials (O, max, sum); nothing in it is read before
+// being written in the same call.
 size_t attend_workspace_bytes(int64_t rows, int64_t H, int64_t D, int64_t n_slots_max) {
   const AttSplit s = attend_split(rows, n_slots_max);
   if (s.splits == 1) return 0;
@@ -385,7 +436,8 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
     else                                                                            \
       attend_kernel<DT, DD, false><<<grid, 256, 0, stream>>>(p);                    \
     if (sp.splits > 1)                                                              \
-      attend_merge_kernel<DD><<<static_cast<unsigned>(rows), 256, 0, stream>>>(p);  \
+      attend_merge_kernel<DD><<<dim3(static_cast<unsigned>(H), static_cast<unsigned>(rows)), \
+                                DD, 0, stream>>>(p);                                \
     return hipGetLastError() == hipSuccess ? 0 : -1;                                \
   }
   CSA_ATT_CASE(0, 64)

@@ -70,22 +70,30 @@ struct IdxTraits<2, DI> {  // fp8 e4m3, v_mfma_f32_16x16x128_f8f6f4
 
 constexpr int kIdxWaves = 4;
 constexpr int kIdxTile = 16;  // entries per MFMA column tile
+constexpr int kIdxMaxTilesPerWg = 128;  // 2048 entries per workgroup
 
 // grid: x = entry chunk, y = query row (b * T + i).  block: 4 waves.
-// Wave w of chunk c handles the 16-entry tiles c*tiles_per_wg + w + 4*n.
-template <int DTYPE, int DI, bool RELU>
+// The chunk's tiles are taken in groups of kGroup tiles (12 KiB of keys per
+// wave); wave w handles groups w, w+4, ...  While one group is multiplied,
+// the next group's loads are already in flight (two register buffers,
+// statically indexed so they stay in VGPRs).
+template <int DTYPE, int DI, bool RELU, bool HIST>
 __global__ __launch_bounds__(256) void indexer_kernel(
     const uint8_t* __restrict__ qi, const float* __restrict__ qi_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ ki,
     const float* __restrict__ ki_scale, const int64_t* __restrict__ pos0, int64_t T,
-    int H_I, int64_t n_cap, int m, int tiles_per_wg, float* __restrict__ scores) {
+    int H_I, int64_t n_cap, int m, int tiles_per_wg, float* __restrict__ scores,
+    uint32_t* __restrict__ hist, int topk_k) {
   using Tr = IdxTraits<DTYPE, DI>;
   constexpr int kVec = Tr::kLaneBytes / 16;  // 16-byte loads per lane per row
   constexpr int kRowBytes = DI * Tr::kElemBytes;
+  constexpr int kGroup = 12 / kVec > 0 ? 12 / kVec : 1;  // tiles per group: 12 loads per lane
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int col = lane & 15;
   const int g = lane >> 4;
+  __shared__ float s_scores[kIdxMaxTilesPerWg * kIdxTile];
+  __shared__ uint32_t s_hist[HIST ? kTopkHistBins : 1];
   const int64_t row = blockIdx.y;
   const int64_t b = row / T;
   const int64_t t = pos0[b] + (row - b * T);
@@ -94,6 +102,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const int64_t e_begin = tile0 * kIdxTile;
   if (e_begin >= V) return;
   const int64_t ntiles = min(static_cast<int64_t>(tiles_per_wg), (V - e_begin + kIdxTile - 1) / kIdxTile);
+  const int64_t ngroups = (ntiles + kGroup - 1) / kGroup;
 
   // A operand: 4 head tiles of 16 query heads, kept in registers.
   u32x4 a[4][kVec];
@@ -125,83 +134,152 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const uint8_t* kib = ki + b * n_cap * kRowBytes;
   float* srow = scores + row * n_cap;
 
-  auto load_tile = [&](int64_t tile, u32x4* dst) {
-    const int64_t e = (tile0 + tile) * kIdxTile + col;
-    if (e < V) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(kib + e * kRowBytes + g * Tr::kLaneBytes);
+  // Loads are issued unconditionally (past-the-end entries read the last
+  // visible row instead) so that the wait counts stay static and the next
+  // group's loads really overlap the current group's MFMAs.  A column only
+  // depends on its own key row, and past-the-end columns are never stored.
+  // Groups that lie entirely below V are loaded from a wave-uniform base
+  // pointer plus a constant per-lane offset, with no per-lane clamping, so
+  // the loop needs no address temporaries and its loads stay in flight
+  // across the previous group's MFMAs.  The prefetch of the next group is
+  // unconditional (the last full group re-reads itself, from cache) so the
+  // loop body is straight-line code with static wait counts.  A trailing
+  // partial group is loaded once with clamped addresses (past-the-end
+  // columns are computed from a valid row and never stored).
+  constexpr int kGroupEnt = kGroup * kIdxTile;
+  const int n_ent_wg =
+      static_cast<int>(min<int64_t>(V - e_begin, static_cast<int64_t>(tiles_per_wg) * kIdxTile));
+  const int n_full = n_ent_wg / kGroupEnt;
+  const int n_grp = (n_ent_wg + kGroupEnt - 1) / kGroupEnt;
+  const uint8_t* kwg = kib + e_begin * kRowBytes;          // wave-uniform
+  const uint32_t lane_off = static_cast<uint32_t>(col * kRowBytes + g * Tr::kLaneBytes);
+
+  auto load_full = [&](int grp, u32x4 (&dst)[kGroup][kVec]) {
+    const uint8_t* gb = kwg + static_cast<int64_t>(grp) * (kGroupEnt * kRowBytes);
 #pragma unroll
-      for (int v = 0; v < kVec; ++v) dst[v] = src[v];
-    } else {
+    for (int tt = 0; tt < kGroup; ++tt) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(gb + tt * (kIdxTile * kRowBytes) + lane_off);
 #pragma unroll
-      for (int v = 0; v < kVec; ++v) dst[v] = u32x4{0u, 0u, 0u, 0u};
+      for (int v = 0; v < kVec; ++v) dst[tt][v] = src[v];
+    }
+  };
+  auto load_tail = [&](int grp, u32x4 (&dst)[kGroup][kVec]) {
+#pragma unroll
+    for (int tt = 0; tt < kGroup; ++tt) {
+      int e = (grp * kGroup + tt) * kIdxTile + col;
+      e = e < n_ent_wg - 1 ? e : n_ent_wg - 1;
+      const u32x4* src = reinterpret_cast<const u32x4*>(
+          kwg + static_cast<uint32_t>(e) * kRowBytes + g * Tr::kLaneBytes);
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) dst[tt][v] = src[v];
     }
   };
 
-  u32x4 bcur[kVec], bnext[kVec];
-  int64_t tile = wave;
-  if (tile < ntiles) load_tile(tile, bcur);
-  for (; tile < ntiles; tile += kIdxWaves) {
-    if (tile + kIdxWaves < ntiles) load_tile(tile + kIdxWaves, bnext);
-    f32x4 acc[4];
+  auto compute_group = [&](int grp, const u32x4 (&bt)[kGroup][kVec]) {
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < kGroup; ++tt) {
+      f32x4 acc[4];
 #pragma unroll
-    for (int s = 0; s < Tr::kSteps; ++s) {
+      for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < Tr::kSteps; ++st) {
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) acc[ht] = Tr::mma(a[ht], bt[tt], st, acc[ht]);
+      }
+      float v = 0.f;
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) {
-        if (ht < n_ht) acc[ht] = Tr::mma(a[ht], bcur, s, acc[ht]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = RELU ? fmaxf(acc[ht][i], 0.f) : acc[ht][i];
+          v = fmaf(wq[ht][i], x, v);
+        }
       }
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (lane < 16) s_scores[(grp * kGroup + tt) * kIdxTile + col] = v;
     }
-    float v = 0.f;
-#pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = RELU ? fmaxf(acc[ht][i], 0.f) : acc[ht][i];
-        v = fmaf(wq[ht][i], x, v);
-      }
+  };
+
+  u32x4 buf0[kGroup][kVec], buf1[kGroup][kVec];
+  int grp = wave;
+  if (grp < n_full) {
+    const int last = n_full - 1 - ((n_full - 1 - wave) & (kIdxWaves - 1));  // this wave's last
+    load_full(grp, buf0);
+    while (true) {
+      load_full(grp + kIdxWaves <= last ? grp + kIdxWaves : last, buf1);
+      compute_group(grp, buf0);
+      grp += kIdxWaves;
+      if (grp > last) break;
+      load_full(grp + kIdxWaves <= last ? grp + kIdxWaves : last, buf0);
+      compute_group(grp, buf1);
+      grp += kIdxWaves;
+      if (grp > last) break;
     }
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    const int64_t e = (tile0 + tile) * kIdxTile + col;
-    if (lane < 16 && e < V) {
-      if (DTYPE == 2) v *= ki_scale[b * n_cap + e];
-      srow[e] = v;
+  }
+  if (n_full < n_grp && (n_full & (kIdxWaves - 1)) == wave) {
+    load_tail(n_full, buf0);
+    compute_group(n_full, buf0);
+  }
+  // Scores were staged in LDS; write this workgroup's slice out coalesced
+  // (and apply the per-entry key scale of the FP8 path here).  With HIST,
+  // the first-digit histogram of the top-k selection is accumulated on the
+  // way (rows that keep every visible entry need none).
+  const bool do_hist = HIST && V > topk_k;
+  if (do_hist)
+    for (int i = threadIdx.x; i < kTopkHistBins; i += 256) s_hist[i] = 0u;
+  __syncthreads();
+  float* dst = srow + e_begin;
+  for (int i = threadIdx.x; i < n_ent_wg; i += 256) {
+    float v = s_scores[i];
+    if (DTYPE == 2) v *= ki_scale[b * n_cap + e_begin + i];
+    dst[i] = v;
+    if (do_hist) atomicAdd(&s_hist[score_key(v) >> kTopkDigit1Shift], 1u);
+  }
+  if (do_hist) {
+    __syncthreads();
+    uint32_t* gh = hist + row * kTopkHistBins;
+    for (int i = threadIdx.x; i < kTopkHistBins; i += 256) {
+      const uint32_t c = s_hist[i];
+      if (c) atomicAdd(&gh[i], c);
     }
-#pragma unroll
-    for (int k = 0; k < kVec; ++k) bcur[k] = bnext[k];
   }
 }
 
 template <int DTYPE, int DI>
 static void launch_idx_t(const void* qi, const float* qs, const float* w, const void* ki,
                          const float* ks, const int64_t* pos0, int64_t B, int64_t T, int H_I,
-                         int64_t n_cap, int m, bool relu, float* scores, hipStream_t s) {
+                         int64_t n_cap, int m, bool relu, float* scores, uint32_t* hist, int k,
+                         hipStream_t s) {
   // 2048 entries per workgroup (32 tiles per wave) unless the cache is small.
   const int64_t tiles = (n_cap + kIdxTile - 1) / kIdxTile;
-  const int tiles_per_wg = static_cast<int>(tiles < 128 ? tiles : 128);
+  const int tiles_per_wg = static_cast<int>(tiles < kIdxMaxTilesPerWg ? tiles : kIdxMaxTilesPerWg);
   dim3 grid(static_cast<unsigned>((tiles + tiles_per_wg - 1) / tiles_per_wg),
             static_cast<unsigned>(B * T));
   auto q8 = static_cast<const uint8_t*>(qi);
   auto k8 = static_cast<const uint8_t*>(ki);
-  if (relu)
-    indexer_kernel<DTYPE, DI, true><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, pos0, T, H_I, n_cap,
-                                                         m, tiles_per_wg, scores);
-  else
-    indexer_kernel<DTYPE, DI, false><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, pos0, T, H_I,
-                                                          n_cap, m, tiles_per_wg, scores);
+#define CSA_IDX_GO(R, HST)                                                                 \
+  indexer_kernel<DTYPE, DI, R, HST><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, pos0, T, H_I,  \
+                                                         n_cap, m, tiles_per_wg, scores,   \
+                                                         hist, k)
+  if (relu) {
+    if (hist) CSA_IDX_GO(true, true); else CSA_IDX_GO(true, false);
+  } else {
+    if (hist) CSA_IDX_GO(false, true); else CSA_IDX_GO(false, false);
+  }
+#undef CSA_IDX_GO
 }
 
 int launch_index_scores(const void* qi, int dtype, const float* qs, const float* w,
                         const void* ki, const float* ks, const int64_t* pos0, int64_t B,
                         int64_t T, int64_t H_I, int64_t d_I, int64_t n_cap, int m, int act,
-                        float* scores, hipStream_t s) {
+                        float* scores, uint32_t* hist, int k, hipStream_t s) {
   const bool relu = act == 0;
   const int H = static_cast<int>(H_I);
-#define CSA_IDX_CASE(DT, DI)                                                             \
-  if (dtype == DT && d_I == DI) {                                                        \
-    launch_idx_t<DT, DI>(qi, qs, w, ki, ks, pos0, B, T, H, n_cap, m, relu, scores, s);   \
-    return hipGetLastError() == hipSuccess ? 0 : -1;                                     \
+#define CSA_IDX_CASE(DT, DI)                                                                  \
+  if (dtype == DT && d_I == DI) {                                                             \
+    launch_idx_t<DT, DI>(qi, qs, w, ki, ks, pos0, B, T, H, n_cap, m, relu, scores, hist, k, s); \
+    return hipGetLastError() == hipSuccess ? 0 : -1;                                          \
   }
   CSA_IDX_CASE(0, 64)
   CSA_IDX_CASE(0, 128)

@@ -16,17 +16,29 @@ int launch_compress(const void* x, int dtype, const float* z, int64_t B, int64_t
 int launch_quantize_fp8_rows(const void* x, int dtype, int64_t rows, int64_t d, uint8_t* codes,
                              float* scales, hipStream_t s);
 
+// Top-k first digit: the 12 most significant bits of the order-preserving
+// score key (4096 bins).
+constexpr int kTopkDigit1Shift = 20;
+constexpr int kTopkHistBins = 1 << (32 - kTopkDigit1Shift);
+
+// hist (nullable): per-row first-digit histogram accumulated for csa_topk
+// (rows with V <= k are skipped).  It must be zero on entry.
 int launch_index_scores(const void* qi, int dtype, const float* qs, const float* w,
                         const void* ki, const float* ks, const int64_t* pos0, int64_t B,
                         int64_t T, int64_t H_I, int64_t d_I, int64_t n_cap, int m, int act,
-                        float* scores, hipStream_t s);
+                        float* scores, uint32_t* hist, int k, hipStream_t s);
 
 // Rows (B*T) up to this count use the multi-workgroup split top-k, which
 // needs a workspace; more rows use one workgroup per row and none.
 constexpr int64_t kTopkSplitMaxRows = 256;
 size_t topk_workspace_bytes(int64_t B, int64_t T, int64_t n_cap, int k);
+// The first-digit histogram inside a top-k workspace (nullptr when the row
+// path, which keeps its histogram in LDS, will be used).
+uint32_t* topk_hist_ptr(void* ws, int64_t B, int64_t T);
 int launch_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, int64_t n_cap,
-                int m, int k, int32_t* idx, void* ws, hipStream_t s);
+                int m, int k, int32_t* idx, void* ws, bool hist_ready, hipStream_t s);
+// Zero-fill (a kernel, so it may be captured in a graph).
+int launch_clear(void* p, size_t bytes, hipStream_t s);
 
 struct AttSplit {
   int splits;

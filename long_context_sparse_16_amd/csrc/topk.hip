@@ -5,45 +5,51 @@
 // Order: larger score first, equal scores to the lower entry index.  Output:
 // the selected entry indices in ascending order, padded with -1.
 //
-// Algorithm (exact radix select on order-preserving 32-bit keys):
-//   1. 4096-bin histogram of the top 12 key bits over the visible entries;
-//      the bucket b1 holding the k-th largest key splits the row into
-//      entries that are surely selected (bucket > b1) and candidates
-//      (bucket == b1).
+// Exact radix select on order-preserving 32-bit keys:
+//   1. 4096-bin histogram of the top 12 key bits over the visible entries
+//      (fused into the indexer epilogue on the decode path).  The bucket b1
+//      holding the k-th largest key splits the row into entries that are
+//      surely selected (bucket > b1) and candidates (bucket == b1).
 //   2. The candidates are resolved in LDS by two more digit passes (10 + 10
-//      bits) that give the exact k-th key, and -- only when several entries
-//      share it -- three digit passes over the entry index that keep the
-//      lowest indices.
-//   3. The k winners are sorted ascending with a bitonic network in LDS.
-// If the candidate bucket is larger than the LDS buffer (e.g. a row of equal
-// scores) the same digit passes run directly over the row in global memory.
+//      bits) that give the exact k-th key and, only when several entries
+//      share it, three digit passes over the entry index that keep the
+//      lowest indices.  A candidate bucket larger than the LDS buffer (a row
+//      of equal scores, say) is resolved by the same passes reading the row
+//      from global memory.
+//   3. The winners are marked in an LDS bitmap over the row and emitted in
+//      ascending order by a prefix sum of per-word popcounts.
 //
-// Two drivers share the resolution code:
-//   * "row" path for many rows: one 1024-thread workgroup per row reads its
-//     score row twice (histogram, then sure/candidate split).
-//   * "split" path for few long rows (decode): the histogram and the split
-//     are spread over many workgroups per row (global integer atomics, whose
-//     final counts are order independent), then one workgroup per row
-//     resolves the candidates.
+// Drivers:
+//   * split path (few long rows, decode): many workgroups per row classify
+//     a 4096-entry slice each and append sure entries / candidates to
+//     per-row lists with one atomic per wave; a second kernel resolves each
+//     row in one workgroup and returns the row's workspace to all-zero.
+//     (A kernel boundary is the cheap way to make the lists visible: a
+//     last-workgroup hand-off would need device-scope fences, which write
+//     back and invalidate a whole XCD's L2.)
+//   * row path (many rows, prefill): one workgroup per row reads its score
+//     row twice (histogram, then classification) and resolves in LDS.
 #include "common.h"
 #include "kernels.h"
 
 namespace csa {
 
-constexpr int kTopkThreads = 1024;
-constexpr int kHistBins = 4096;  // top 12 key bits
-constexpr int kCandCap = 12288;  // candidates resolved in LDS
+constexpr int kHistBins = kTopkHistBins;        // 4096
+constexpr int kCandCap = 8192;                  // candidates resolved in LDS
 constexpr int kMaxK = 4096;
-constexpr int kSliceThreads = 256;
-constexpr int kSliceEntries = 2048;  // entries per workgroup in the split path
+constexpr int kBitmapMaxEntries = 262144;       // bitmap output up to this V
+constexpr int kSelThreads = 256;
+constexpr int kSelEntries = 4096;               // entries per select workgroup
+constexpr int kRowThreads = 512;
 
-struct TopkShared {
-  uint32_t hist[kHistBins];
+struct FinishShared {
+  uint32_t hist[2048];                    // digit passes 2.. (<= 2048 bins)
   uint32_t ckey[kCandCap];
   int32_t cidx[kCandCap];
   int32_t sel[kMaxK];
+  uint32_t bitmap[kBitmapMaxEntries / 32];  // also the 4096-bin first digit
   uint32_t scan[32];
-  uint32_t misc[8];
+  uint32_t misc[8];  // [0] bin [1] above [4] selected [5] candidates [7] flag
 };
 
 // ------------------------------------------------------------ block helpers
@@ -75,9 +81,9 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sm) {
   return base + x - v;
 }
 
-// Given a histogram in LDS, find the bin holding the r-th largest element
-// (1-based) and the number of elements in higher bins.  Results land in
-// out[0] (bin) and out[1] (count above).  Requires r <= total.
+// Find the bin holding the r-th largest element (1-based) of a histogram in
+// LDS and the number of elements in higher bins: out[0] = bin, out[1] =
+// count above.  Requires 1 <= r <= total and nb a multiple of NT (or <= NT).
 template <int NT>
 __device__ void block_find_top(const uint32_t* hist, int nb, uint32_t r, uint32_t* scan_sm,
                                uint32_t* out) {
@@ -103,32 +109,23 @@ __device__ void block_find_top(const uint32_t* hist, int nb, uint32_t r, uint32_
   __syncthreads();
 }
 
-template <int NT>
-__device__ void block_clear(uint32_t* a, int n) {
-  for (int i = threadIdx.x; i < n; i += NT) a[i] = 0u;
-  __syncthreads();
-}
-
 // One digit pass over a set of (key, index) items: histogram of
-// (key >> shift) & (nb-1) over the items accepted by `match`, then the bin
-// of the r-th largest.  `visit(f)` calls f(key, index) for every item.
+// (key >> shift) & (nb-1), then the bin of the r-th largest.  visit(f)
+// calls f(key, index) for every item.
 template <int NT, typename Visit>
-__device__ void digit_pass(TopkShared& sm, Visit visit, int shift, int nb, uint32_t r) {
-  block_clear<NT>(sm.hist, nb);
-  visit([&](uint32_t key, int32_t) {
-    atomicAdd(&sm.hist[(key >> shift) & (nb - 1)], 1u);
-  });
+__device__ void digit_pass(FinishShared& sm, Visit visit, int shift, int nb, uint32_t r) {
+  for (int i = threadIdx.x; i < nb; i += NT) sm.hist[i] = 0u;
+  __syncthreads();
+  visit([&](uint32_t key, int32_t) { atomicAdd(&sm.hist[(key >> shift) & (nb - 1)], 1u); });
   __syncthreads();
   block_find_top<NT>(sm.hist, nb, r, sm.scan, sm.misc);
 }
 
-// Resolve the exact selection among the items (all in bucket b1 of the
-// first digit) given by `visit_all`, needing r of them, and append the
-// winners to sm.sel starting at the current sm.misc[4] count.
+// Resolve the exact selection among items that all share the first digit,
+// needing r of them; winners are appended to sm.sel at sm.misc[4].
 template <int NT, typename Visit>
-__device__ void resolve_candidates(TopkShared& sm, Visit visit_all, uint32_t r) {
-  // digit 2: key bits 19..10
-  digit_pass<NT>(sm, visit_all, 10, 1024, r);
+__device__ void resolve_candidates(FinishShared& sm, Visit visit_all, uint32_t r) {
+  digit_pass<NT>(sm, visit_all, 10, 1024, r);  // key bits 19..10
   const uint32_t b2 = sm.misc[0];
   const uint32_t r2 = r - sm.misc[1];
   __syncthreads();
@@ -137,17 +134,16 @@ __device__ void resolve_candidates(TopkShared& sm, Visit visit_all, uint32_t r) 
       if (((key >> 10) & 1023u) == b2) f(key, j);
     });
   };
-  // digit 3: key bits 9..0 among bits 19..10 == b2
-  digit_pass<NT>(sm, visit_b2, 0, 1024, r2);
+  digit_pass<NT>(sm, visit_b2, 0, 1024, r2);   // key bits 9..0
   const uint32_t b3 = sm.misc[0];
-  const uint32_t r3 = r2 - sm.misc[1];   // ties needed at the exact key
+  const uint32_t r3 = r2 - sm.misc[1];        // entries needed at the exact key
   const uint32_t n_eq = sm.hist[b3];
-  const uint32_t low20 = (b2 << 10) | b3;  // the k-th key's low 20 bits
+  const uint32_t low20 = (b2 << 10) | b3;
   __syncthreads();
   int32_t jmax = 0x7fffffff;
   if (n_eq > r3) {
-    // keep the r3 lowest indices among the ties: select the top r3 of
-    // 0x7fffffff - j, three digits of 11 / 10 / 10 bits
+    // keep the r3 lowest indices among the ties: the top r3 of
+    // 0x7fffffff - j, in digits of 11 / 10 / 10 bits
     auto visit_eq = [&](auto f) {
       visit_all([&](uint32_t key, int32_t j) {
         if ((key & 0xfffffu) == low20) f(0x7fffffffu - static_cast<uint32_t>(j), j);
@@ -174,8 +170,7 @@ __device__ void resolve_candidates(TopkShared& sm, Visit visit_all, uint32_t r) 
     digit_pass<NT>(sm, visit_c2, 0, 1024, q2);
     const uint32_t c3 = sm.misc[0];
     __syncthreads();
-    const uint32_t k2star = (c1 << 20) | (c2 << 10) | c3;
-    jmax = static_cast<int32_t>(0x7fffffffu - k2star);
+    jmax = static_cast<int32_t>(0x7fffffffu - ((c1 << 20) | (c2 << 10) | c3));
   }
   visit_all([&](uint32_t key, int32_t j) {
     const uint32_t lo = key & 0xfffffu;
@@ -187,39 +182,71 @@ __device__ void resolve_candidates(TopkShared& sm, Visit visit_all, uint32_t r) 
   __syncthreads();
 }
 
-// Sort sm.sel[0..k) ascending and write it out.
+// Emit sm.sel[0..k) in ascending order to out[0..k).  Rows up to
+// kBitmapMaxEntries long use a bitmap over the row and a prefix sum of
+// popcounts; longer rows sort with a bitonic network.
 template <int NT>
-__device__ void sort_and_store(TopkShared& sm, int k, int32_t* out) {
-  int k2 = 1;
-  while (k2 < k) k2 <<= 1;
-  for (int i = threadIdx.x + k; i < k2; i += NT) sm.sel[i] = 0x7fffffff;
-  __syncthreads();
-  for (int size = 2; size <= k2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < k2; i += NT) {
-        const int p = i ^ stride;
-        if (p > i) {
-          const int32_t a = sm.sel[i], b = sm.sel[p];
-          const bool up = (i & size) == 0;
-          if ((a > b) == up) {
-            sm.sel[i] = b;
-            sm.sel[p] = a;
+__device__ void emit_sorted(FinishShared& sm, int k, int64_t V, int32_t* out) {
+  const int tid = threadIdx.x;
+  if (V <= kBitmapMaxEntries) {
+    const int nw = static_cast<int>((V + 31) >> 5);
+    for (int i = tid; i < nw; i += NT) sm.bitmap[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < k; i += NT) {
+      const int32_t j = sm.sel[i];
+      if (j >= 0 && j < V) atomicOr(&sm.bitmap[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+    const int per = (nw + NT - 1) / NT;
+    const int w0 = tid * per;
+    const int w1 = min(nw, w0 + per);
+    uint32_t cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(sm.bitmap[w]);
+    uint32_t pos = block_excl_scan<NT>(cnt, sm.scan);
+    if (tid == NT - 1) sm.misc[6] = pos + cnt;  // number of marked entries
+    for (int w = w0; w < w1; ++w) {
+      uint32_t bits = sm.bitmap[w];
+      while (bits) {
+        const int bit = __ffs(bits) - 1;
+        if (pos < static_cast<uint32_t>(k)) out[pos] = w * 32 + bit;
+        ++pos;
+        bits &= bits - 1;
+      }
+    }
+    __syncthreads();
+    for (int i = static_cast<int>(sm.misc[6]) + tid; i < k; i += NT) out[i] = -1;
+  } else {
+    int k2 = 1;
+    while (k2 < k) k2 <<= 1;
+    for (int i = tid + k; i < k2; i += NT) sm.sel[i] = 0x7fffffff;
+    __syncthreads();
+    for (int size = 2; size <= k2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < k2; i += NT) {
+          const int p = i ^ stride;
+          if (p > i) {
+            const int32_t a = sm.sel[i], b = sm.sel[p];
+            if ((a > b) == ((i & size) == 0)) {
+              sm.sel[i] = b;
+              sm.sel[p] = a;
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
+    for (int i = tid; i < k; i += NT) out[i] = sm.sel[i];
   }
-  for (int i = threadIdx.x; i < k; i += NT) out[i] = sm.sel[i];
 }
 
 __device__ __forceinline__ void write_iota(int32_t* out, int64_t V, int k) {
   for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = i < V ? i : -1;
 }
 
-// Candidates either in LDS (nc <= cap) or re-derived from the score row.
+// Resolve r winners among the candidates (first digit == b1), either from
+// LDS (nc <= kCandCap) or from the score row, then emit the row.
 template <int NT>
-__device__ void finish_row(TopkShared& sm, const float* srow, int64_t V, uint32_t b1,
+__device__ void finish_row(FinishShared& sm, const float* srow, int64_t V, uint32_t b1,
                            uint32_t r, uint32_t nc, int k, int32_t* out) {
   if (nc <= static_cast<uint32_t>(kCandCap)) {
     auto visit = [&](auto f) {
@@ -230,20 +257,20 @@ __device__ void finish_row(TopkShared& sm, const float* srow, int64_t V, uint32_
     auto visit = [&](auto f) {
       for (int64_t j = threadIdx.x; j < V; j += NT) {
         const uint32_t key = score_key(srow[j]);
-        if ((key >> 20) == b1) f(key, static_cast<int32_t>(j));
+        if ((key >> kTopkDigit1Shift) == b1) f(key, static_cast<int32_t>(j));
       }
     };
     resolve_candidates<NT>(sm, visit, r);
   }
-  sort_and_store<NT>(sm, k, out);
+  emit_sorted<NT>(sm, k, V, out);
 }
 
 // ------------------------------------------------------------- row path
 
-__global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ pos0, int64_t T,
     int64_t n_cap, int m, int k, int32_t* __restrict__ idx) {
-  __shared__ TopkShared sm;
+  __shared__ FinishShared sm;
   const int64_t row = blockIdx.x;
   const int64_t b = row / T;
   const int64_t t = pos0[b] + (row - b * T);
@@ -254,22 +281,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
     return;
   }
   const float* srow = scores + row * n_cap;
-  block_clear<kTopkThreads>(sm.hist, kHistBins);
-  for (int64_t j = threadIdx.x; j < V; j += kTopkThreads)
-    atomicAdd(&sm.hist[score_key(srow[j]) >> 20], 1u);
+  uint32_t* h1 = sm.bitmap;  // first-digit histogram (the bitmap is used later)
+  for (int i = threadIdx.x; i < kHistBins; i += kRowThreads) h1[i] = 0u;
+  if (threadIdx.x < 8) sm.misc[threadIdx.x] = 0u;
   __syncthreads();
-  block_find_top<kTopkThreads>(sm.hist, kHistBins, static_cast<uint32_t>(k), sm.scan, sm.misc);
+  for (int64_t j = threadIdx.x; j < V; j += kRowThreads)
+    atomicAdd(&h1[score_key(srow[j]) >> kTopkDigit1Shift], 1u);
+  __syncthreads();
+  block_find_top<kRowThreads>(h1, kHistBins, static_cast<uint32_t>(k), sm.scan, sm.misc);
   const uint32_t b1 = sm.misc[0];
   const uint32_t above = sm.misc[1];
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    sm.misc[4] = 0;  // selected so far
-    sm.misc[5] = 0;  // candidates
-  }
-  __syncthreads();
-  for (int64_t j = threadIdx.x; j < V; j += kTopkThreads) {
+  for (int64_t j = threadIdx.x; j < V; j += kRowThreads) {
     const uint32_t key = score_key(srow[j]);
-    const uint32_t bk = key >> 20;
+    const uint32_t bk = key >> kTopkDigit1Shift;
     if (bk > b1) {
       sm.sel[atomicAdd(&sm.misc[4], 1u)] = static_cast<int32_t>(j);
     } else if (bk == b1) {
@@ -282,34 +306,37 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
   }
   __syncthreads();
   const uint32_t nc = sm.misc[5];
-  finish_row<kTopkThreads>(sm, srow, V, b1, static_cast<uint32_t>(k) - above, nc, k, out);
+  finish_row<kRowThreads>(sm, srow, V, b1, static_cast<uint32_t>(k) - above, nc, k, out);
 }
 
 // ------------------------------------------------------------ split path
 //
-// Workspace per row: hist[4096] u32, counters[4] u32 (sure, candidates),
-// sure[kMaxK] i32, ckey[kCandCap] u32, cidx[kCandCap] i32.
+// Workspace per row, all-zero between calls: hist[4096] u32, ctrl[4] u32
+// (sure count, candidate count, first-digit bucket, count above it); then
+// the per-row lists
+// sure[kMaxK] i32, ckey[kCandCap] u32, cidx[kCandCap] i32, whose contents
+// never matter on entry.
 
 struct SplitWs {
   uint32_t* hist;
-  uint32_t* cnt;
+  uint32_t* ctrl;
   int32_t* sure;
   uint32_t* ckey;
   int32_t* cidx;
 };
 
-__host__ __device__ inline size_t split_ws_bytes(int64_t rows) {
+inline size_t split_ws_bytes(int64_t rows) {
   return static_cast<size_t>(rows) *
          (sizeof(uint32_t) * (kHistBins + 4) + sizeof(int32_t) * kMaxK +
           (sizeof(uint32_t) + sizeof(int32_t)) * kCandCap);
 }
 
-__host__ __device__ inline SplitWs split_ws(void* base, int64_t rows) {
+inline SplitWs split_ws(void* base, int64_t rows) {
   SplitWs w;
   char* p = static_cast<char*>(base);
   w.hist = reinterpret_cast<uint32_t*>(p);
   p += sizeof(uint32_t) * kHistBins * rows;
-  w.cnt = reinterpret_cast<uint32_t*>(p);
+  w.ctrl = reinterpret_cast<uint32_t*>(p);
   p += sizeof(uint32_t) * 4 * rows;
   w.sure = reinterpret_cast<int32_t*>(p);
   p += sizeof(int32_t) * kMaxK * rows;
@@ -319,13 +346,8 @@ __host__ __device__ inline SplitWs split_ws(void* base, int64_t rows) {
   return w;
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * 256)
-    p[i] = 0u;
-}
-
-__global__ __launch_bounds__(kSliceThreads) void topk_hist_kernel(
+// First-digit histogram of each row (when the indexer did not build it).
+__global__ __launch_bounds__(kSelThreads) void topk_hist_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ pos0, int64_t T,
     int64_t n_cap, int m, int k, SplitWs ws) {
   __shared__ uint32_t hist[kHistBins];
@@ -333,81 +355,119 @@ __global__ __launch_bounds__(kSliceThreads) void topk_hist_kernel(
   const int64_t b = row / T;
   const int64_t t = pos0[b] + (row - b * T);
   const int64_t V = visible_entries(t, m, n_cap);
-  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kSliceEntries;
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kSelEntries;
   if (V <= k || j0 >= V) return;
-  const int64_t j1 = min(V, j0 + kSliceEntries);
-  for (int i = threadIdx.x; i < kHistBins; i += kSliceThreads) hist[i] = 0u;
+  const int64_t j1 = min(V, j0 + kSelEntries);
+  for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) hist[i] = 0u;
   __syncthreads();
   const float* srow = scores + row * n_cap;
-  for (int64_t j = j0 + threadIdx.x; j < j1; j += kSliceThreads)
-    atomicAdd(&hist[score_key(srow[j]) >> 20], 1u);
+  for (int64_t j = j0 + threadIdx.x; j < j1; j += kSelThreads)
+    atomicAdd(&hist[score_key(srow[j]) >> kTopkDigit1Shift], 1u);
   __syncthreads();
   uint32_t* gh = ws.hist + row * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += kSliceThreads) {
+  for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) {
     const uint32_t c = hist[i];
     if (c) atomicAdd(&gh[i], c);
   }
 }
 
-__global__ __launch_bounds__(kSliceThreads) void topk_split_kernel(
+// Append the lanes whose flag is set to an LDS list with one LDS atomic per
+// wave; positions within the wave follow lane order.
+__device__ __forceinline__ void wave_append_lds(bool flag, uint32_t* counter, int32_t* list_idx,
+                                                uint32_t* list_key, int32_t j, uint32_t key) {
+  const unsigned long long mask = __ballot(flag);
+  if (mask == 0ull) return;
+  const int lane = threadIdx.x & 63;
+  const int leader = __ffsll(static_cast<long long>(mask)) - 1;
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(counter, static_cast<uint32_t>(__popcll(mask)));
+  base = __shfl(base, leader);
+  if (flag) {
+    const uint32_t p = base + static_cast<uint32_t>(__popcll(mask & ((1ull << lane) - 1ull)));
+    list_idx[p] = j;
+    if (list_key) list_key[p] = key;
+  }
+}
+
+// Classify one 4096-entry slice of a row: entries above the bucket of the
+// k-th largest key go to the row's "sure" list, entries in that bucket to
+// its candidate list.  Each workgroup collects its slice's entries in LDS
+// and reserves its range of the row's lists with one global atomic per
+// list.  The bucket and the count above it are also recorded for the
+// finishing kernel.
+__global__ __launch_bounds__(kSelThreads) void topk_classify_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ pos0, int64_t T,
     int64_t n_cap, int m, int k, SplitWs ws) {
   __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t scan_sm[32];
+  __shared__ uint32_t scan[32];
   __shared__ uint32_t res[8];
-  __shared__ int32_t l_sure[kSliceEntries];
-  __shared__ uint32_t l_ckey[kSliceEntries];
-  __shared__ int32_t l_cidx[kSliceEntries];
+  __shared__ int32_t l_sure[kSelEntries];
+  __shared__ int32_t l_cidx[kSelEntries];
+  __shared__ uint32_t l_ckey[kSelEntries];
   const int64_t row = blockIdx.y;
   const int64_t b = row / T;
   const int64_t t = pos0[b] + (row - b * T);
   const int64_t V = visible_entries(t, m, n_cap);
-  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kSliceEntries;
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kSelEntries;
   if (V <= k || j0 >= V) return;
-  const int64_t j1 = min(V, j0 + kSliceEntries);
   const uint32_t* gh = ws.hist + row * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += kSliceThreads) hist[i] = gh[i];
+  uint32_t* ctrl = ws.ctrl + row * 4;
+  for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) hist[i] = gh[i];
   if (threadIdx.x < 8) res[threadIdx.x] = 0u;
   __syncthreads();
-  block_find_top<kSliceThreads>(hist, kHistBins, static_cast<uint32_t>(k), scan_sm, res);
+  block_find_top<kSelThreads>(hist, kHistBins, static_cast<uint32_t>(k), scan, res);
   const uint32_t b1 = res[0];
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    ctrl[2] = b1;
+    ctrl[3] = res[1];
+  }
   const float* srow = scores + row * n_cap;
-  for (int64_t j = j0 + threadIdx.x; j < j1; j += kSliceThreads) {
-    const uint32_t key = score_key(srow[j]);
-    const uint32_t bk = key >> 20;
-    if (bk > b1) {
-      l_sure[atomicAdd(&res[2], 1u)] = static_cast<int32_t>(j);
-    } else if (bk == b1) {
-      const uint32_t p = atomicAdd(&res[3], 1u);
-      l_ckey[p] = key;
-      l_cidx[p] = static_cast<int32_t>(j);
-    }
+  const int64_t j1 = min(V, j0 + kSelEntries);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // all of this thread's scores are loaded before any is classified
+  constexpr int kIters = kSelEntries / kSelThreads;
+  float sv[kIters];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    int64_t j = j0 + it * kSelThreads + wave * 64 + lane;
+    sv[it] = srow[j < j1 ? j : j1 - 1];
+  }
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int64_t j = j0 + it * kSelThreads + wave * 64 + lane;
+    const bool valid = j < j1;
+    const uint32_t key = score_key(sv[it]);
+    const uint32_t bk = key >> kTopkDigit1Shift;
+    wave_append_lds(valid && bk > b1, &res[4], l_sure, nullptr, static_cast<int32_t>(j), key);
+    wave_append_lds(valid && bk == b1, &res[5], l_cidx, l_ckey, static_cast<int32_t>(j), key);
   }
   __syncthreads();
-  const uint32_t ns = res[2], nc = res[3];
+  const uint32_t ns = res[4], nc = res[5];
   if (threadIdx.x == 0) {
-    res[4] = ns ? atomicAdd(&ws.cnt[row * 4 + 0], ns) : 0u;
-    res[5] = nc ? atomicAdd(&ws.cnt[row * 4 + 1], nc) : 0u;
+    res[6] = ns ? atomicAdd(&ctrl[0], ns) : 0u;
+    res[7] = nc ? atomicAdd(&ctrl[1], nc) : 0u;
   }
   __syncthreads();
-  const uint32_t sbase = res[4], cbase = res[5];
+  const uint32_t sb = res[6], cb = res[7];
   int32_t* gs = ws.sure + row * kMaxK;
-  for (uint32_t i = threadIdx.x; i < ns; i += kSliceThreads)
-    if (sbase + i < static_cast<uint32_t>(kMaxK)) gs[sbase + i] = l_sure[i];
-  uint32_t* gk = ws.ckey + row * kCandCap;
+  for (uint32_t i = threadIdx.x; i < ns; i += kSelThreads)
+    if (sb + i < static_cast<uint32_t>(kMaxK)) gs[sb + i] = l_sure[i];
   int32_t* gi = ws.cidx + row * kCandCap;
-  for (uint32_t i = threadIdx.x; i < nc; i += kSliceThreads) {
-    if (cbase + i < static_cast<uint32_t>(kCandCap)) {
-      gk[cbase + i] = l_ckey[i];
-      gi[cbase + i] = l_cidx[i];
+  uint32_t* gk = ws.ckey + row * kCandCap;
+  for (uint32_t i = threadIdx.x; i < nc; i += kSelThreads) {
+    if (cb + i < static_cast<uint32_t>(kCandCap)) {
+      gi[cb + i] = l_cidx[i];
+      gk[cb + i] = l_ckey[i];
     }
   }
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_finish_kernel(
+// Resolve one row from its sure list and candidates, then return the row's
+// histogram and counters to zero for the next call.
+__global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ pos0, int64_t T,
     int64_t n_cap, int m, int k, SplitWs ws, int32_t* __restrict__ idx) {
-  __shared__ TopkShared sm;
+  __shared__ FinishShared sm;
   const int64_t row = blockIdx.x;
   const int64_t b = row / T;
   const int64_t t = pos0[b] + (row - b * T);
@@ -417,30 +477,35 @@ __global__ __launch_bounds__(kTopkThreads) void topk_finish_kernel(
     write_iota(out, V, k);
     return;
   }
-  const uint32_t* gh = ws.hist + row * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += kTopkThreads) sm.hist[i] = gh[i];
-  __syncthreads();
-  block_find_top<kTopkThreads>(sm.hist, kHistBins, static_cast<uint32_t>(k), sm.scan, sm.misc);
-  const uint32_t b1 = sm.misc[0];
-  const uint32_t above = sm.misc[1];
-  const uint32_t ns = min(ws.cnt[row * 4 + 0], static_cast<uint32_t>(kMaxK));
-  const uint32_t nc = ws.cnt[row * 4 + 1];
-  __syncthreads();
+  uint32_t* gh = ws.hist + row * kHistBins;
+  uint32_t* ctrl = ws.ctrl + row * 4;
+  const u32x4 cv = *reinterpret_cast<const u32x4*>(ctrl);  // sure, candidates, bucket, above
+  const uint32_t ns = min(cv[0], static_cast<uint32_t>(k));
+  const uint32_t nc = cv[1];
+  const uint32_t b1 = cv[2];
+  if (threadIdx.x < 8) sm.misc[threadIdx.x] = 0u;
   const int32_t* gs = ws.sure + row * kMaxK;
-  for (uint32_t i = threadIdx.x; i < ns; i += kTopkThreads) sm.sel[i] = gs[i];
+  for (uint32_t i = threadIdx.x; i < ns; i += kSelThreads) sm.sel[i] = gs[i];
   if (nc <= static_cast<uint32_t>(kCandCap)) {
     const uint32_t* gk = ws.ckey + row * kCandCap;
     const int32_t* gi = ws.cidx + row * kCandCap;
-    for (uint32_t i = threadIdx.x; i < nc; i += kTopkThreads) {
+    for (uint32_t i = threadIdx.x; i < nc; i += kSelThreads) {
       sm.ckey[i] = gk[i];
       sm.cidx[i] = gi[i];
     }
   }
   if (threadIdx.x == 0) sm.misc[4] = ns;
   __syncthreads();
-  (void)above;
-  const float* srow = scores + row * n_cap;
-  finish_row<kTopkThreads>(sm, srow, V, b1, static_cast<uint32_t>(k) - ns, nc, k, out);
+  finish_row<kSelThreads>(sm, scores + row * n_cap, V, b1, static_cast<uint32_t>(k) - ns, nc, k,
+                          out);
+  for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) gh[i] = 0u;
+  if (threadIdx.x < 4) ctrl[threadIdx.x] = 0u;
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = 0u;
 }
 
 // ----------------------------------------------------------------- host side
@@ -452,24 +517,33 @@ size_t topk_workspace_bytes(int64_t B, int64_t T, int64_t n_cap, int k) {
   return rows <= kTopkSplitMaxRows ? split_ws_bytes(rows) : 0;
 }
 
+uint32_t* topk_hist_ptr(void* ws, int64_t B, int64_t T) {
+  return B * T <= kTopkSplitMaxRows ? split_ws(ws, B * T).hist : nullptr;
+}
+
 int launch_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, int64_t n_cap,
-                int m, int k, int32_t* idx, void* ws, hipStream_t s) {
+                int m, int k, int32_t* idx, void* ws, bool hist_ready, hipStream_t s) {
   const int64_t rows = B * T;
   if (rows <= kTopkSplitMaxRows) {
     SplitWs w = split_ws(ws, rows);
-    const int64_t n_zero = rows * (kHistBins + 4);  // hist and counters are adjacent
-    fill_zero_kernel<<<static_cast<unsigned>((n_zero + 255) / 256 < 1024 ? (n_zero + 255) / 256 : 1024), 256, 0,
-                       s>>>(w.hist, n_zero);
-    dim3 grid(static_cast<unsigned>((n_cap + kSliceEntries - 1) / kSliceEntries),
+    dim3 grid(static_cast<unsigned>((n_cap + kSelEntries - 1) / kSelEntries),
               static_cast<unsigned>(rows));
-    topk_hist_kernel<<<grid, kSliceThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, w);
-    topk_split_kernel<<<grid, kSliceThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, w);
-    topk_finish_kernel<<<static_cast<unsigned>(rows), kTopkThreads, 0, s>>>(scores, pos0, T,
-                                                                            n_cap, m, k, w, idx);
+    if (!hist_ready) topk_hist_kernel<<<grid, kSelThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, w);
+    topk_classify_kernel<<<grid, kSelThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, w);
+    topk_finish_kernel<<<static_cast<unsigned>(rows), kSelThreads, 0, s>>>(scores, pos0, T, n_cap,
+                                                                           m, k, w, idx);
   } else {
-    topk_row_kernel<<<static_cast<unsigned>(rows), kTopkThreads, 0, s>>>(scores, pos0, T, n_cap,
-                                                                         m, k, idx);
+    topk_row_kernel<<<static_cast<unsigned>(rows), kRowThreads, 0, s>>>(scores, pos0, T, n_cap, m,
+                                                                        k, idx);
   }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_clear(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(bytes / 4);
+  if (n == 0) return 0;
+  const int64_t blocks = (n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048;
+  fill_zero_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(static_cast<uint32_t*>(p), n);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

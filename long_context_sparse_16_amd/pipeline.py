@@ -22,7 +22,7 @@ import torch
 
 from . import (csa_attend, csa_compress, csa_index_scores, csa_quantize_fp8_rows, csa_topk,
                csa_topk_workspace_size, csa_attend_workspace_size, hca_attend,
-               hca_attend_workspace_size)
+               hca_attend_workspace_size, workspace)
 
 
 def to_device(a: np.ndarray, device, storage: str) -> torch.Tensor:
@@ -62,9 +62,7 @@ class CSAStep:
         self.out = torch.empty((B, T, cfg.H, d), dtype=torch.float32, device=dev)
         self.lse = torch.empty((B, T, cfg.H), dtype=torch.float32, device=dev)
         if cfg.hca:
-            self.att_ws = torch.empty(
-                max(1, hca_attend_workspace_size(B, T, cfg.H, d, n_cap, cfg.W)),
-                dtype=torch.uint8, device=dev)
+            self.att_ws = workspace(hca_attend_workspace_size(B, T, cfg.H, d, n_cap, cfg.W), dev)
             self.idx = None
             return
         self.qi = to_device(batch["qi"], dev, st)
@@ -80,11 +78,8 @@ class CSAStep:
                 self.quantize_keys(0, cfg.n_ctx_entries)
         self.scores = torch.empty((B, T, n_cap), dtype=torch.float32, device=dev)
         self.idx = torch.empty((B, T, cfg.k), dtype=torch.int32, device=dev)
-        self.topk_ws = torch.empty(max(1, csa_topk_workspace_size(B, T, n_cap, cfg.k)),
-                                   dtype=torch.uint8, device=dev)
-        self.att_ws = torch.empty(
-            max(1, csa_attend_workspace_size(B, T, cfg.H, d, cfg.k, cfg.W)),
-            dtype=torch.uint8, device=dev)
+        self.topk_ws = workspace(csa_topk_workspace_size(B, T, n_cap, cfg.k), dev)
+        self.att_ws = workspace(csa_attend_workspace_size(B, T, cfg.H, d, cfg.k, cfg.W), dev)
 
     # ------------------------------------------------------------ stages
     def quantize_keys(self, first: int, last: int) -> None:
@@ -105,16 +100,20 @@ class CSAStep:
             self.quantize_keys(cfg.n_ctx_entries, cfg.n_cap)
 
     def index(self) -> None:
+        """Indexer scores; also builds the top-k histogram in the top-k
+        workspace, which topk() then consumes."""
         cfg = self.cfg
         if cfg.ki_fp8:
             csa_index_scores(self.qi_codes, self.w, self.ki_codes, self.pos0, cfg.m, self.act,
-                             qi_scale=self.qi_scale, ki_scale=self.ki_scale, scores=self.scores)
+                             qi_scale=self.qi_scale, ki_scale=self.ki_scale, scores=self.scores,
+                             topk_ws=self.topk_ws, k=cfg.k)
         else:
             csa_index_scores(self.qi, self.w, self.kc, self.pos0, cfg.m, self.act,
-                             scores=self.scores)
+                             scores=self.scores, topk_ws=self.topk_ws, k=cfg.k)
 
     def topk(self) -> None:
-        csa_topk(self.scores, self.pos0, self.cfg.m, self.cfg.k, idx=self.idx, ws=self.topk_ws)
+        csa_topk(self.scores, self.pos0, self.cfg.m, self.cfg.k, idx=self.idx, ws=self.topk_ws,
+                 hist_ready=True)
 
     def attend(self) -> None:
         cfg = self.cfg

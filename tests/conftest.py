@@ -29,6 +29,6 @@ def ensure_library():
     """Build libcsa.so if it is not there yet (hipcc cross-compiles on CPU)."""
     lib = os.path.join(ROOT, "long_context_sparse_16_amd", "libcsa.so")
     if not os.path.exists(lib):
-        from long_context_sparse_16_amd import build as _b
-        _b.build()
+        import __graft_entry__
+        __graft_entry__._build_module().build()
     return lib

@@ -54,6 +54,15 @@ def test_compress_validation():
     assert lib.csa_compress(FAKE, 0, FAKE, 1, 8, 4, 4, 16, 32, FAKE, 0, 2, 0, NULL) == -2
 
 
+def test_workspace_clear_validation():
+    assert lib.csa_workspace_clear(NULL, 0, NULL) == 0
+    assert lib.csa_workspace_clear(NULL, 64, NULL) == -1
+    assert lib.csa_workspace_clear(ctypes.c_void_p(0x100004), 64, NULL) == -5
+    # index with a too-small top-k workspace
+    assert lib.csa_index_scores(FAKE, 1, NULL, FAKE, FAKE, 1, NULL, FAKE, 32, 1, 64, 128, 32768, 4,
+                                0, FAKE, 1024, FAKE, 16, NULL) == -5
+
+
 def test_quantize_validation():
     assert lib.csa_quantize_fp8_rows(NULL, 1, 4, 128, FAKE, FAKE, NULL) == -1
     assert lib.csa_quantize_fp8_rows(FAKE, 2, 4, 128, FAKE, FAKE, NULL) == -3
@@ -63,7 +72,7 @@ def test_quantize_validation():
 def _index(qi_dtype=1, ki_dtype=1, qs=NULL, ks=NULL, B=1, T=1, H=64, dI=128, n_cap=32, m=4, act=0,
            scores=FAKE, qi=FAKE):
     return lib.csa_index_scores(qi, qi_dtype, qs, FAKE, FAKE, ki_dtype, ks, FAKE, B, T, H, dI,
-                                n_cap, m, act, scores, NULL)
+                                n_cap, m, act, scores, 0, NULL, 0, NULL)
 
 
 def test_index_validation():
@@ -80,13 +89,13 @@ def test_index_validation():
 
 
 def test_topk_validation_and_workspace():
-    assert lib.csa_topk(NULL, FAKE, 1, 1, 64, 4, 8, FAKE, NULL, 0, NULL) == -1
-    assert lib.csa_topk(FAKE, FAKE, 1, 1, 64, 4, 0, FAKE, NULL, 0, NULL) == -4
-    assert lib.csa_topk(FAKE, FAKE, 1, 1, 64, 4, 5000, FAKE, NULL, 0, NULL) == -4
+    assert lib.csa_topk(NULL, FAKE, 1, 1, 64, 4, 8, FAKE, NULL, 0, 0, NULL) == -1
+    assert lib.csa_topk(FAKE, FAKE, 1, 1, 64, 4, 0, FAKE, NULL, 0, 0, NULL) == -4
+    assert lib.csa_topk(FAKE, FAKE, 1, 1, 64, 4, 5000, FAKE, NULL, 0, 0, NULL) == -4
     need = lib.csa_topk_workspace_size(32, 1, 32768, 1024)
     assert need > 0 and need % 256 == 0
-    assert lib.csa_topk(FAKE, FAKE, 32, 1, 32768, 4, 1024, FAKE, NULL, 0, NULL) == -5
-    assert lib.csa_topk(FAKE, FAKE, 32, 1, 32768, 4, 1024, FAKE, FAKE, need - 1, NULL) == -5
+    assert lib.csa_topk(FAKE, FAKE, 32, 1, 32768, 4, 1024, FAKE, NULL, 0, 0, NULL) == -5
+    assert lib.csa_topk(FAKE, FAKE, 32, 1, 32768, 4, 1024, FAKE, FAKE, need - 1, 0, NULL) == -5
     assert "workspace" in _last()
     # many rows use one workgroup per row and need no workspace
     assert lib.csa_topk_workspace_size(1, 8192, 67584, 1024) == 0

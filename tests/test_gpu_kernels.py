@@ -299,3 +299,53 @@ def test_hca_parity(storage, m):
     err, rel = _attend_case(storage, B, T, H, d, N, 0, W, R, raw, seed=800 + m, hca_m=m)
     assert err <= (1e-4 if storage == "f32" else 2e-2), err
     assert rel <= (1e-5 if storage == "f32" else 1e-2), rel
+
+
+def test_workspaces_are_reusable_across_calls():
+    """A workspace is left all-zero by every call: reusing one workspace for
+    several top-k / attention calls on different data gives the same
+    results as fresh workspaces, and the workspace is zero afterwards."""
+    say("workspace reuse")
+    rng = np.random.default_rng(900)
+    B, T, n_cap, k = 3, 2, 9000, 256
+    ws = csa.workspace(csa.csa_topk_workspace_size(B, T, n_cap, k), DEV)
+    pos0 = to_dev(np.array([n_cap - 2, 5000, 3000], np.int64))
+    for trial in range(3):
+        s = (rng.standard_normal((B, T, n_cap)) * (trial + 1)).astype(np.float32)
+        if trial == 1:
+            s[0] = 0.0  # candidate overflow path on one sequence
+        got = csa.csa_topk(to_dev(s), pos0, 1, k, ws=ws)
+        ref = csa.csa_topk(to_dev(s), pos0, 1, k)
+        assert torch.equal(got, ref), trial
+    # the histogram and counters (the part read before being written) are zero
+    hist_bytes = B * T * (4096 + 4) * 4
+    assert int(ws[:hist_bytes].count_nonzero().item()) == 0
+    # fused indexer histogram + top-k with a reused workspace
+    H_I, d_I = 64, 128
+    qi = to_dev(bf16_codes(rng.standard_normal((B, T, H_I, d_I))))
+    ki = to_dev(bf16_codes(rng.standard_normal((B, n_cap, d_I))))
+    w = to_dev(rng.random((B, T, H_I)).astype(np.float32))
+    pos4 = to_dev(np.array([4 * n_cap - 5, 4 * 5000, 4 * 3000], np.int64))
+    for trial in range(3):
+        sc = csa.csa_index_scores(qi, w, ki, pos4, 4, topk_ws=ws, k=k)
+        fused = csa.csa_topk(sc, pos4, 4, k, ws=ws, hist_ready=True)
+        plain = csa.csa_topk(sc, pos4, 4, k)
+        assert torch.equal(fused, plain), trial
+    torch.cuda.synchronize()
+    assert int(ws[:hist_bytes].count_nonzero().item()) == 0
+    # attention with split partials and a reused workspace
+    H, d, W, R = 64, 128, 128, 200
+    Bq, Tq, N, ka = 2, 1, 3000, 700
+    aws = csa.workspace(csa.csa_attend_workspace_size(Bq, Tq, H, d, ka, W), DEV)
+    for trial in range(3):
+        q = to_dev(bf16_codes(rng.standard_normal((Bq, Tq, H, d))))
+        kc = to_dev(bf16_codes(rng.standard_normal((Bq, N, d))))
+        vc = to_dev(bf16_codes(rng.standard_normal((Bq, N, d))))
+        kr = to_dev(bf16_codes(rng.standard_normal((Bq, R, d))))
+        vr = to_dev(bf16_codes(rng.standard_normal((Bq, R, d))))
+        idx = np.sort(rng.choice(N, size=(Bq, Tq, ka)), axis=-1).astype(np.int32)
+        raw = to_dev(np.array([5000, 5100], np.int64))
+        p0 = to_dev(np.array([5000 + R - 1, 5100 + R - 1], np.int64))
+        a, al = csa.csa_attend(q, kc, vc, to_dev(idx), kr, vr, raw, p0, W, 0.088, ws=aws)
+        b_, bl = csa.csa_attend(q, kc, vc, to_dev(idx), kr, vr, raw, p0, W, 0.088)
+        assert torch.equal(a, b_) and torch.equal(al, bl), trial

@@ -186,3 +186,42 @@ def test_chunked_prefill_256k_bf16_sampled():
     err, rel, overlap = _stage_parity(step, cfg, batch, 0, rows, kc, vc)
     say("C3 sampled max-abs", err, "rel-l2", rel, "overlap", overlap)
     assert err <= 2e-2 and rel <= 1e-2 and overlap >= 0.99
+
+
+@pytest.mark.parametrize("name", ["csa_decode_128k_bf16", "hca_decode_1m_bf16"])
+def test_graph_replay_matches_eager(name):
+    """Each stage captured in a HIP graph and replayed several times, with
+    eager work and synchronisations in between, reproduces the eager
+    results bit for bit on every replay."""
+    cfg = WL.BY_NAME[name]
+    if cfg.B > 8:
+        cfg = cfg.replace(B=8)
+    say("graph replay", cfg.name)
+    step = CSAStep(cfg, WL.make_batch(cfg))
+    step.run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (step.scores if not cfg.hca else step.out, step.idx if not cfg.hca
+                               else step.lse, step.out)]
+    stages = ([step.index, step.topk] if not cfg.hca else []) + [step.attend]
+    graphs = []
+    for fn in stages:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs.append(g)
+    for rep in range(4):
+        step.out.zero_()
+        step.lse.zero_()
+        if not cfg.hca:
+            step.scores.zero_()
+            step.idx.zero_()
+        torch.cuda.synchronize()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        got = (step.scores if not cfg.hca else step.out, step.idx if not cfg.hca else step.lse,
+               step.out)
+        for a, b in zip(ref, got):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), rep
+        step.run()          # eager work between replays
+        torch.cuda.synchronize()
