@@ -246,6 +246,189 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   }
 }
 
+// ------------------------------------------------------------------ prefill
+//
+// Many query tokens per sequence (chunked prefill): the key matrix is
+// shared by every token, so it is the B operand streamed once per group of
+// 8 tokens, while the tokens' queries (8 x 64 heads x 128 dims) stay in
+// registers as A fragments (2 tokens per wave).  Each 64-entry key tile is
+// loaded cooperatively into double-buffered LDS (the next tile's loads are
+// in flight during the current tile's 128 MFMAs per wave); B fragments are
+// read from LDS with a padded row stride (no bank conflicts).  The epilogue
+// applies ReLU and the head weights, sums the 64 heads of each token (in
+// lane plus two lane shuffles) and writes 64 consecutive fp32 scores per
+// token per tile.  Entries past a token's visible count are not written.
+constexpr int kPfTok = 8;        // query tokens per workgroup
+constexpr int kPfTile = 64;      // entries per LDS tile
+#ifndef CSA_PF_TOK_PER_WAVE
+#define CSA_PF_TOK_PER_WAVE 1
+#endif
+constexpr int kPfTokPerWave = CSA_PF_TOK_PER_WAVE;  // 1: 8 waves x 1 token
+
+// TPW query tokens per wave, 8 / TPW waves per workgroup.
+template <int DTYPE, bool RELU, int TPW>
+__global__ __launch_bounds__(64 * kPfTok / TPW) void indexer_prefill_kernel(
+    const uint8_t* __restrict__ qi, const float* __restrict__ qi_scale,
+    const float* __restrict__ w, const uint8_t* __restrict__ ki,
+    const float* __restrict__ ki_scale, const int64_t* __restrict__ pos0, int64_t T,
+    int H_I, int64_t n_cap, int m, float* __restrict__ scores) {
+  constexpr int DI = 128;
+  using Tr = IdxTraits<DTYPE, DI>;
+  constexpr int kVec = Tr::kLaneBytes / 16;
+  constexpr int RB = DI * Tr::kElemBytes;             // key row bytes
+  constexpr int kStride = RB + 16;                    // padded LDS row
+  constexpr int kThreads = 64 * kPfTok / TPW;
+  constexpr int kLoads = kPfTile * RB / 16 / kThreads;  // 16-byte loads per thread per tile
+  __shared__ __attribute__((aligned(16))) uint8_t bt[2][kPfTile * kStride];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int64_t b = blockIdx.y;
+  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * kPfTok;
+  const int64_t tok_last = min(tok0 + kPfTok, T) - 1;
+  const int64_t p0 = pos0[b];
+  const int64_t V_max = visible_entries(p0 + tok_last, m, n_cap);
+  if (V_max <= 0) return;
+
+  // A fragments and head weights of this wave's tokens
+  u32x4 a[TPW][4][kVec];
+  float wq[TPW][4][4];
+  int64_t Vt[TPW];
+  int64_t srow_off[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int64_t tok = tok0 + wave * TPW + tt;
+    const bool tok_ok = tok < T;
+    const int64_t row = b * T + (tok_ok ? tok : 0);
+    Vt[tt] = tok_ok ? visible_entries(p0 + tok, m, n_cap) : 0;
+    srow_off[tt] = row * n_cap;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      const int h = ht * 16 + col;
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) a[tt][ht][v] = u32x4{0u, 0u, 0u, 0u};
+      if (tok_ok && h < H_I) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(
+            qi + (row * H_I + h) * RB + g * Tr::kLaneBytes);
+#pragma unroll
+        for (int v = 0; v < kVec; ++v) a[tt][ht][v] = src[v];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = ht * 16 + g * 4 + i;
+        float wv = 0.f;
+        if (tok_ok && hh < H_I) {
+          wv = w[row * H_I + hh];
+          if (DTYPE == 2) wv *= qi_scale[row * H_I + hh];
+        }
+        wq[tt][ht][i] = wv;
+      }
+    }
+  }
+
+  const uint8_t* kib = ki + b * n_cap * RB;
+  const int ntiles = static_cast<int>((V_max + kPfTile - 1) / kPfTile);
+  u32x4 breg[kLoads];
+  auto load_tile = [&](int tile) {
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+      const int id = tid + kThreads * r;
+      const int ent = id / (RB / 16);
+      const int pc = id - ent * (RB / 16);
+      int64_t e = static_cast<int64_t>(tile) * kPfTile + ent;
+      e = e < V_max ? e : V_max - 1;
+      breg[r] = *reinterpret_cast<const u32x4*>(kib + e * RB + pc * 16);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+      const int id = tid + kThreads * r;
+      const int ent = id / (RB / 16);
+      const int pc = id - ent * (RB / 16);
+      *reinterpret_cast<u32x4*>(&bt[buf][ent * kStride + pc * 16]) = breg[r];
+    }
+  };
+
+  load_tile(0);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    store_tile(buf);
+    __syncthreads();
+    load_tile(tile + 1 < ntiles ? tile + 1 : tile);
+    f32x4 acc[TPW][4][4];  // [token][head tile][column tile]
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[tt][ht][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint8_t* bb = &bt[buf][0];
+#pragma unroll
+    for (int st = 0; st < Tr::kSteps; ++st) {
+      u32x4 bf[4][kVec / Tr::kSteps > 0 ? kVec / Tr::kSteps : 1];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const uint8_t* src = bb + (ct * 16 + col) * kStride + g * Tr::kLaneBytes;
+#pragma unroll
+        for (int v = 0; v < kVec / Tr::kSteps; ++v)
+          bf[ct][v] = *reinterpret_cast<const u32x4*>(src + (st * (kVec / Tr::kSteps) + v) * 16);
+      }
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            if (DTYPE == 1) {
+              acc[tt][ht][ct] = mma_bf16(__builtin_bit_cast(bf16x8, a[tt][ht][st]),
+                                         __builtin_bit_cast(bf16x8, bf[ct][0]), acc[tt][ht][ct]);
+            } else {
+              i32x8 av, bv;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                av[i] = static_cast<int>(a[tt][ht][0][i]);
+                av[4 + i] = static_cast<int>(a[tt][ht][1][i]);
+                bv[i] = static_cast<int>(bf[ct][0][i]);
+                bv[4 + i] = static_cast<int>(bf[ct][1][i]);
+              }
+              acc[tt][ht][ct] = mma_fp8(av, bv, acc[tt][ht][ct]);
+            }
+          }
+    }
+    // epilogue: per token and column tile, sum_h w_h phi(acc)
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      float v[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        float x = 0.f;
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float y = RELU ? fmaxf(acc[tt][ht][ct][i], 0.f) : acc[tt][ht][ct][i];
+            x = fmaf(wq[tt][ht][i], y, x);
+          }
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+        v[ct] = x;
+      }
+      // lane group g writes column tile g: 64 consecutive scores per token
+      const float mine = g == 0 ? v[0] : g == 1 ? v[1] : g == 2 ? v[2] : v[3];
+      const int64_t e = static_cast<int64_t>(tile) * kPfTile + g * 16 + col;
+      if (e < Vt[tt]) {
+        float out = mine;
+        if (DTYPE == 2) out *= ki_scale[b * n_cap + e];
+        scores[srow_off[tt] + e] = out;
+      }
+    }
+  }
+}
+
 template <int DTYPE, int DI>
 static void launch_idx_t(const void* qi, const float* qs, const float* w, const void* ki,
                          const float* ks, const int64_t* pos0, int64_t B, int64_t T, int H_I,
@@ -258,6 +441,17 @@ static void launch_idx_t(const void* qi, const float* qs, const float* w, const 
             static_cast<unsigned>(B * T));
   auto q8 = static_cast<const uint8_t*>(qi);
   auto k8 = static_cast<const uint8_t*>(ki);
+  if ((DTYPE == 1 || DTYPE == 2) && DI == 128 && T >= kPfTok && hist == nullptr) {
+    constexpr int DT = DTYPE == 2 ? 2 : 1;
+    dim3 pgrid(static_cast<unsigned>((T + kPfTok - 1) / kPfTok), static_cast<unsigned>(B));
+    if (relu)
+      indexer_prefill_kernel<DT, true, kPfTokPerWave><<<pgrid, 64 * kPfTok / kPfTokPerWave, 0, s>>>(
+          q8, qs, w, k8, ks, pos0, T, H_I, n_cap, m, scores);
+    else
+      indexer_prefill_kernel<DT, false, kPfTokPerWave><<<pgrid, 64 * kPfTok / kPfTokPerWave, 0, s>>>(
+          q8, qs, w, k8, ks, pos0, T, H_I, n_cap, m, scores);
+    return;
+  }
 #define CSA_IDX_GO(R, HST)                                                                 \
   indexer_kernel<DTYPE, DI, R, HST><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, pos0, T, H_I,  \
                                                          n_cap, m, tiles_per_wg, scores,   \

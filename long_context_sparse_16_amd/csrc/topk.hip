@@ -40,7 +40,8 @@ constexpr int kMaxK = 4096;
 constexpr int kBitmapMaxEntries = 262144;       // bitmap output up to this V
 constexpr int kSelThreads = 256;
 constexpr int kSelEntries = 4096;               // entries per select workgroup
-constexpr int kRowThreads = 512;
+constexpr int kRowThreads = 1024;
+constexpr int64_t kRowDirectMaxEntries = 65536;  // few-row cut-over to the row kernel
 
 struct FinishShared {
   uint32_t hist[2048];                    // digit passes 2.. (<= 2048 bins)
@@ -267,9 +268,16 @@ __device__ void finish_row(FinishShared& sm, const float* srow, int64_t V, uint3
 
 // ------------------------------------------------------------- row path
 
+// The row is read twice (histogram, then classification); each pass takes
+// the row in batches of kRowBatch independent loads per thread that are all
+// in flight before any is used.
+constexpr int kRowBatch = 16;
+
+// hist_io (nullable): the rows' first-digit histograms built by the
+// indexer; used instead of the first pass and returned to zero.
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ pos0, int64_t T,
-    int64_t n_cap, int m, int k, int32_t* __restrict__ idx) {
+    int64_t n_cap, int m, int k, int32_t* __restrict__ idx, uint32_t* __restrict__ hist_io) {
   __shared__ FinishShared sm;
   const int64_t row = blockIdx.x;
   const int64_t b = row / T;
@@ -282,17 +290,35 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
   }
   const float* srow = scores + row * n_cap;
   uint32_t* h1 = sm.bitmap;  // first-digit histogram (the bitmap is used later)
-  for (int i = threadIdx.x; i < kHistBins; i += kRowThreads) h1[i] = 0u;
+  uint32_t* gh = hist_io ? hist_io + row * kHistBins : nullptr;
+  for (int i = threadIdx.x; i < kHistBins; i += kRowThreads) h1[i] = gh ? gh[i] : 0u;
   if (threadIdx.x < 8) sm.misc[threadIdx.x] = 0u;
   __syncthreads();
-  for (int64_t j = threadIdx.x; j < V; j += kRowThreads)
-    atomicAdd(&h1[score_key(srow[j]) >> kTopkDigit1Shift], 1u);
-  __syncthreads();
+  // visit(f): f(key, j) for every visible entry, batched loads
+  auto visit_row = [&](auto f) {
+    for (int64_t base = threadIdx.x; base < V; base += static_cast<int64_t>(kRowThreads) * kRowBatch) {
+      float v[kRowBatch];
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        const int64_t j = base + static_cast<int64_t>(u) * kRowThreads;
+        v[u] = srow[j < V ? j : V - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        const int64_t j = base + static_cast<int64_t>(u) * kRowThreads;
+        if (j < V) f(score_key(v[u]), j);
+      }
+    }
+  };
+  if (!gh) {
+    visit_row([&](uint32_t key, int64_t) { atomicAdd(&h1[key >> kTopkDigit1Shift], 1u); });
+    __syncthreads();
+  } else {
+    for (int i = threadIdx.x; i < kHistBins; i += kRowThreads) gh[i] = 0u;
+  }
   block_find_top<kRowThreads>(h1, kHistBins, static_cast<uint32_t>(k), sm.scan, sm.misc);
   const uint32_t b1 = sm.misc[0];
-  const uint32_t above = sm.misc[1];
-  for (int64_t j = threadIdx.x; j < V; j += kRowThreads) {
-    const uint32_t key = score_key(srow[j]);
+  visit_row([&](uint32_t key, int64_t j) {
     const uint32_t bk = key >> kTopkDigit1Shift;
     if (bk > b1) {
       sm.sel[atomicAdd(&sm.misc[4], 1u)] = static_cast<int32_t>(j);
@@ -303,7 +329,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
         sm.cidx[p] = static_cast<int32_t>(j);
       }
     }
-  }
+  });
+  const uint32_t above = sm.misc[1];
   __syncthreads();
   const uint32_t nc = sm.misc[5];
   finish_row<kRowThreads>(sm, srow, V, b1, static_cast<uint32_t>(k) - above, nc, k, out);
@@ -524,7 +551,13 @@ uint32_t* topk_hist_ptr(void* ws, int64_t B, int64_t T) {
 int launch_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, int64_t n_cap,
                 int m, int k, int32_t* idx, void* ws, bool hist_ready, hipStream_t s) {
   const int64_t rows = B * T;
-  if (rows <= kTopkSplitMaxRows) {
+  if (rows <= kTopkSplitMaxRows && n_cap <= kRowDirectMaxEntries) {
+    // few rows short enough for one workgroup each: one pass over the row
+    // using the indexer's histogram when it built one
+    uint32_t* h = hist_ready ? split_ws(ws, rows).hist : nullptr;
+    topk_row_kernel<<<static_cast<unsigned>(rows), kRowThreads, 0, s>>>(scores, pos0, T, n_cap, m,
+                                                                        k, idx, h);
+  } else if (rows <= kTopkSplitMaxRows) {
     SplitWs w = split_ws(ws, rows);
     dim3 grid(static_cast<unsigned>((n_cap + kSelEntries - 1) / kSelEntries),
               static_cast<unsigned>(rows));
@@ -534,7 +567,7 @@ int launch_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, 
                                                                            m, k, w, idx);
   } else {
     topk_row_kernel<<<static_cast<unsigned>(rows), kRowThreads, 0, s>>>(scores, pos0, T, n_cap, m,
-                                                                        k, idx);
+                                                                        k, idx, nullptr);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

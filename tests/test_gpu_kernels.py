@@ -165,12 +165,16 @@ def _topk_case(scores, V, k):
     return got
 
 
-@pytest.mark.parametrize("path", ["split", "row"])
+@pytest.mark.parametrize("path", ["split", "few_rows", "row"])
 def test_topk_random_and_ties(path):
+    """split: few rows longer than one workgroup handles (classify + finish
+    kernels); few_rows: few short rows, one workgroup each; row: many rows."""
     say("topk", path)
     rng = np.random.default_rng(500)
     k = 100
     if path == "split":
+        B, T, n_cap = 2, 4, 70000
+    elif path == "few_rows":
         B, T, n_cap = 5, 4, 9000
     else:
         B, T, n_cap = 1, 300, 3000
@@ -180,7 +184,7 @@ def test_topk_random_and_ties(path):
     s[:, 2, ::7] = rng.standard_normal(s[:, 2, ::7].shape)
     V = np.zeros((B, T), np.int64)
     for b in range(B):
-        start = n_cap - T - 3 * b if path == "split" else 40
+        start = n_cap - T - 3 * b if path != "row" else 40
         V[b] = start + np.arange(T)
     _topk_case(s, np.minimum(V, n_cap), k)
 
@@ -197,6 +201,12 @@ def test_topk_edge_rows():
     s = np.zeros((2, 1, 20000), np.float32)
     got = _topk_case(s, np.full((2, 1), 20000, np.int64), 1024)
     assert np.array_equal(got[0, 0], np.arange(1024))
+    # equal scores on rows longer than one workgroup handles: the candidate
+    # lists overflow and the finish kernel re-reads the row
+    s = np.zeros((2, 1, 70000), np.float32)
+    s[1, 0, 12345] = -1.0
+    got = _topk_case(s, np.full((2, 1), 70000, np.int64), 2048)
+    assert np.array_equal(got[0, 0], np.arange(2048))
     s = np.zeros((1, 300, 20000), np.float32)
     s[0, :, 5000] = 1.0
     got = _topk_case(s, np.arange(19700, 20000)[None], 16)
@@ -349,3 +359,40 @@ def test_workspaces_are_reusable_across_calls():
         a, al = csa.csa_attend(q, kc, vc, to_dev(idx), kr, vr, raw, p0, W, 0.088, ws=aws)
         b_, bl = csa.csa_attend(q, kc, vc, to_dev(idx), kr, vr, raw, p0, W, 0.088)
         assert torch.equal(a, b_) and torch.equal(al, bl), trial
+
+
+@pytest.mark.parametrize("kind,H_I", [("bf16", 64), ("bf16", 40), ("fp8", 64)])
+@pytest.mark.parametrize("act", ["relu", "identity"])
+def test_indexer_prefill_parity(kind, H_I, act):
+    """Many query tokens per sequence (the multi-token MFMA tile path): a
+    ragged token count, visibility growing across the chunk and, for one
+    sequence, entries cut by the cache capacity."""
+    say("indexer prefill", kind, H_I, act)
+    rng = np.random.default_rng(1000 + H_I)
+    B, T, m, n_cap, d_I = 2, 21, 4, 3000, 128
+    pos0 = np.array([4 * 2990, 4 * 1000 - 7], np.int64)
+    qi = bf16_codes(rng.standard_normal((B, T, H_I, d_I)))
+    ki = bf16_codes(rng.standard_normal((B, n_cap, d_I)))
+    w = rng.random((B, T, H_I)).astype(np.float32)
+    qi_d, ki_d = to_dev(qi), to_dev(ki)
+    qs = ks = None
+    qv, kv = decode(qi), decode(ki)
+    if kind == "fp8":
+        qi_d, qs = csa.csa_quantize_fp8_rows(qi_d)
+        ki_d, ks = csa.csa_quantize_fp8_rows(ki_d)
+        qv = oracle.e4m3_decode(from_dev(qi_d)) * from_dev(qs)[..., None]
+        kv = oracle.e4m3_decode(from_dev(ki_d)) * from_dev(ks)[..., None]
+    scores = torch.full((B, T, n_cap), float("nan"), device=DEV)
+    csa.csa_index_scores(qi_d, to_dev(w), ki_d, to_dev(pos0), m, act, qi_scale=qs, ki_scale=ks,
+                         scores=scores)
+    got = from_dev(scores)
+    worst = 0.0
+    for b in range(B):
+        pos = pos0[b] + np.arange(T)
+        V = np.minimum(oracle.visible_count(pos, m), n_cap)
+        ref = oracle.indexer_scores(qv[b], w[b], kv[b][:n_cap], np.minimum(pos, 4 * n_cap - 1), m,
+                                    act)
+        for i in range(T):
+            worst = max(worst, score_close(got[b, i, :V[i]], ref[i, :V[i]]))
+            assert np.all(np.isnan(got[b, i, V[i]:])), "wrote past the visible entries"
+    assert worst <= 1.0, worst
