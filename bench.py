@@ -33,19 +33,82 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="csa_decode_128k_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--eager", action="store_true", help="launch stages directly, no HIP graphs")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay one HIP graph per step instead of launching each stage "
+                         "directly (slower here: each graph replay adds ~13 us)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (for HBM counter scaling)")
     return ap.parse_args()
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode_128k_traffic.md")
+INDEXER_SOURCES = [os.path.join(ROOT, "long_context_sparse_16_amd", "csrc", f)
+                   for f in ("indexer.hip", "common.h", "kernels.h")]
+
+
+def source_digest(paths) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(cfg):
+    """HBM bytes per indexer launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by the same
+    counter's reading for a plain copy of known size), or None when the
+    summary is for another workload or for a different indexer source."""
+    t = {}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if line.startswith("- ") and ": " in line:
+                    key, val = line[2:].strip().split(": ", 1)
+                    t[key] = val
+    except OSError:
+        return None
+    if t.get("workload") != cfg.name or t.get("source_sha256") != source_digest(INDEXER_SOURCES):
+        return None
+    return float(t["traffic_bytes_per_launch"])
+
+
+def copy_calibration():
+    """A plain device copy of 256 MiB, five times (rocprofv3 counters of
+    this copy scale FETCH_SIZE / WRITE_SIZE to bytes)."""
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+
+
+def visible_sum(cfg) -> int:
+    """Sum over the step's queries of the causally visible entries V(t)."""
+    return sum(min(cfg.n_cap, (cfg.pos0 + i + 1) // cfg.m) for i in range(cfg.T))
+
+
 def indexer_bytes(cfg, V: int) -> int:
-    """Algorithmic HBM bytes of one indexer launch: every visible key once,
-    one fp32 score written per entry, the queries and head weights."""
+    """Algorithmic HBM bytes of one indexer launch: every visible key (and
+    its fp8 scale) read once per sequence, one fp32 score written per
+    (query, visible entry), the queries and head weights read once."""
     key_bytes = cfg.d_I * (1 if cfg.ki_fp8 else 2 if cfg.storage == "bf16" else 4)
-    per_entry = key_bytes + 4 + (4 if cfg.ki_fp8 else 0)
+    key_bytes += 4 if cfg.ki_fp8 else 0
     q_bytes = cfg.T * cfg.H_I * (cfg.d_I * (1 if cfg.ki_fp8 else 2) + 4 + (4 if cfg.ki_fp8 else 0))
-    return cfg.B * (V * per_entry + q_bytes)
+    return cfg.B * (V * key_bytes + 4 * visible_sum(cfg) + q_bytes)
+
+
+def indexer_flops(cfg) -> int:
+    """Algorithmic flops of one indexer launch: a d_I-long dot product per
+    (query, indexer head, visible entry)."""
+    return 2 * cfg.B * cfg.H_I * cfg.d_I * visible_sum(cfg)
 
 
 def hca_bytes(cfg, V: int) -> int:
@@ -103,6 +166,9 @@ def main():
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the hot path has no multi-GPU mode)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import numpy as np
     import torch
 
@@ -120,46 +186,79 @@ def main():
         step.run()
     torch.cuda.synchronize()
 
-    # one HIP graph per stage: replays carry almost no host launch cost, and
-    # events between replays on the same stream time each stage
-    stages = ([step.compress] if cfg.n_new_tokens else []) + \
-        ([step.index, step.topk] if not cfg.hca else []) + [step.attend]
-    names = (["compress"] if cfg.n_new_tokens else []) + \
-        (["index", "topk"] if not cfg.hca else []) + ["attend"]
-    run_stage = stages
-    if not args.eager:
-        graphs = []
-        for fn in stages:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                fn()
-            graphs.append(g)
-        run_stage = [g.replay for g in graphs]
-        for _ in range(args.warmup):
-            for r in run_stage:
-                r()
-        torch.cuda.synchronize()
+    # The timed step launches each stage directly on the current stream
+    # (--graph: one HIP graph per step instead).  Each stage is also timed on
+    # its own with events over back-to-back calls; the dominant kernel's
+    # duration for the roofline comes from those.
     stream = torch.cuda.current_stream()
+    if not args.graph:
+        run_step = step.run
+    else:
+        g_step = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step):
+            step.run()
+        run_step = g_step.replay
+        for _ in range(args.warmup):
+            run_step()
+    torch.cuda.synchronize()
 
     K = args.steps
-    n_ev = len(run_stage) + 1
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(K)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev[0].record(stream)
     for s in range(K):
-        e = ev[s]
-        e[0].record(stream)
-        for j, r in enumerate(run_stage):
-            r()
-            e[j + 1].record(stream)
+        run_step()
+        ev[s + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_event_ms = ev[0].elapsed_time(ev[K]) / K
 
-    def stage(a, b):
-        return float(np.mean([ev[s][a].elapsed_time(ev[s][b]) for s in range(K)]))
+    # per-stage timing: R back-to-back calls of one stage (--graph: one graph
+    # holding them).
+    # The indexer also accumulates the top-k histogram into the top-k
+    # workspace, which only the following top-k call consumes: the index
+    # stage is timed alone and the workspace cleared afterwards, and top-k
+    # is timed as (index + top-k) minus index.
+    import long_context_sparse_16_amd as csa_lib
 
-    st = {nm: stage(j, j + 1) for j, nm in enumerate(names)}
-    st["step_events"] = stage(0, n_ev - 1)
+    def timed(fn, R=20, reps=3):
+        """Per-call time of fn: one graph holding R calls back to back,
+        replayed `reps` times between events (default: R*reps direct calls)."""
+        if not args.graph:
+            def rep():
+                for _ in range(R):
+                    fn()
+        else:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(R):
+                    fn()
+            rep = g.replay
+        rep()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            rep()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (R * reps)
+
+    st = {}
+    if cfg.n_new_tokens:
+        st["compress"] = timed(step.compress)
+    if not cfg.hca:
+        st["index"] = timed(step.index)
+        csa_lib.csa_workspace_clear(step.topk_ws)
+
+        def index_topk():
+            step.index()
+            step.topk()
+        st["topk"] = timed(index_topk) - st["index"]
+    st["attend"] = timed(step.attend)
+    st["step_events"] = step_event_ms
+
     queries = cfg.B * cfg.T
     V = int(min(cfg.n_cap, (cfg.pos0 + cfg.T) // cfg.m))
     ms_per_step = wall * 1e3 / K
@@ -168,13 +267,21 @@ def main():
         kb = hca_bytes(cfg, V)
         roof = {"kernel": "attend_kernel (HCA)", "bound": "hbm", "achieved": kb / (st["attend"] * 1e6),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None}
+    elif cfg.T >= 8:
+        # prefill: the indexer is one MFMA score GEMM per sequence
+        fl = indexer_flops(cfg)
+        dt = "fp8" if cfg.ki_fp8 else cfg.storage
+        roof = {"kernel": "indexer_prefill_kernel", "bound": "mfma",
+                "achieved": fl / (st["index"] * 1e9), "peak": MFMA_PEAK_TFLOPS[dt],
+                "unit": "TFLOP/s", "traffic": None, "algorithmic_flops": fl}
     else:
         ib = indexer_bytes(cfg, V)
         roof = {"kernel": "indexer_kernel", "bound": "hbm", "achieved": ib / (st["index"] * 1e6),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None}
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": measured_traffic(cfg),
+                "algorithmic_bytes": ib}
     roof["frac"] = roof["achieved"] / roof["peak"]
     line = {
-        "metric": "CSA decode queries/s (+ indexer entries scored/s) at 128K ctx",
+        "metric": "CSA decode queries/s + indexer entries scored/s at 128K/1M ctx; % HBM/MFMA peak",
         "value": value,
         "unit": "queries/s",
         "n_gpus": 1,
@@ -189,9 +296,9 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.B, "context_tokens": cfg.pos0,
                    "compressed_entries": V, "m": cfg.m, "indexer": f"{cfg.H_I}x{cfg.d_I}",
                    "top_k": cfg.k, "heads": cfg.H, "head_dim": cfg.d, "window": cfg.W},
-        "entries_scored_per_s": (cfg.B * cfg.T * V * K / wall) if not cfg.hca else None,
+        "entries_scored_per_s": (cfg.B * visible_sum(cfg) * K / wall) if not cfg.hca else None,
         "stage_ms": st,
-        "launch": "eager" if args.eager else "hip_graph_per_stage",
+        "launch": "hip_graph_per_step" if args.graph else "direct",
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

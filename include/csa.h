@@ -221,8 +221,9 @@ int csa_index_topk(const void* qi, int qi_dtype, const float* qi_scale,
  *         on entry do not matter; size 0 and ws may be NULL when each query
  *         fits one workgroup)
  * Supported: dtypes F32, BF16; d in {64, 128}; 1 <= H <= 64;
- * 0 <= W <= 4096; 0 <= k <= 65536; k + W >= 1.  A query whose key set is
- * empty gets out = 0 and lse = -inf.
+ * 0 <= W <= 4096; 0 <= k <= 65536; k + W >= 1; scale finite and > 0
+ * (else CSA_ERR_SHAPE).  A query whose key set is empty gets out = 0 and
+ * lse = -inf.
  */
 size_t csa_attend_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d,
                                  int k, int W);

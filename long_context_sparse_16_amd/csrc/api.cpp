@@ -96,7 +96,7 @@ int check_topk_args(const float* scores, const int64_t* pos0, int64_t B, int64_t
 int check_attend_args(const void* q, int q_dtype, const void* kc, const void* vc, int kv_dtype,
                       const void* kr, const void* vr, const int64_t* raw_pos0, int64_t R,
                       const int64_t* pos0, int64_t B, int64_t T, int64_t H, int64_t d,
-                      int64_t n_cap, int W, const float* out, const char* fn) {
+                      int64_t n_cap, int W, float scale, const float* out, const char* fn) {
   CSA_REQUIRE(q && kc && vc && pos0 && out, CSA_ERR_NULL,
               "%s: q, kc, vc, pos0 and out must be non-NULL", fn);
   CSA_REQUIRE(W == 0 || (kr && vr && raw_pos0), CSA_ERR_NULL,
@@ -113,6 +113,8 @@ int check_attend_args(const void* q, int q_dtype, const void* kc, const void* vc
   CSA_REQUIRE(n_cap >= 1 && n_cap <= kMaxIndex, CSA_ERR_SHAPE, "%s: n_cap must be in [1, 2^31)",
               fn);
   CSA_REQUIRE(W >= 0 && W <= 4096, CSA_ERR_UNSUPPORTED, "%s: W must be in [0, 4096]", fn);
+  CSA_REQUIRE(scale > 0.f && scale <= 3.4e38f, CSA_ERR_SHAPE, "%s: scale must be finite and > 0",
+              fn);
   CSA_REQUIRE(R >= 0 && (W == 0 || R >= 1), CSA_ERR_SHAPE, "%s: R must be >= 1 when W > 0", fn);
   CSA_REQUIRE(aligned16(q) && aligned16(kc) && aligned16(vc) && aligned16(out) &&
                   (W == 0 || (aligned16(kr) && aligned16(vr))),
@@ -279,7 +281,7 @@ int csa_index_topk(const void* qi, int qi_dtype, const float* qi_scale, const fl
 
 size_t csa_attend_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d, int k, int W) {
   if (B < 1 || T < 1 || H < 1 || d < 1 || k < 0 || W < 0) return 0;
-  return round_up(csa::attend_workspace_bytes(B * T, H, d, static_cast<int64_t>(k) + W));
+  return round_up(csa::attend_workspace_bytes(B * T, H, d, static_cast<int64_t>(k) + W, false));
 }
 
 int csa_attend(const void* q, int q_dtype, const void* kc, const void* vc, int kv_dtype,
@@ -289,7 +291,7 @@ int csa_attend(const void* q, int q_dtype, const void* kc, const void* vc, int k
                void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "csa_attend";
   int rc = check_attend_args(q, q_dtype, kc, vc, kv_dtype, kr, vr, raw_pos0, R, pos0, B, T, H, d,
-                             n_cap, W, out, fn);
+                             n_cap, W, scale, out, fn);
   if (rc) return rc;
   CSA_REQUIRE(k >= 0 && k <= 65536, CSA_ERR_UNSUPPORTED, "%s: k must be in [0, 65536]", fn);
   CSA_REQUIRE(k == 0 || idx, CSA_ERR_NULL, "%s: idx must be non-NULL when k > 0", fn);
@@ -308,7 +310,7 @@ int csa_attend(const void* q, int q_dtype, const void* kc, const void* vc, int k
 size_t hca_attend_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d, int64_t n_cap,
                                  int W) {
   if (B < 1 || T < 1 || H < 1 || d < 1 || n_cap < 1 || W < 0) return 0;
-  return round_up(csa::attend_workspace_bytes(B * T, H, d, n_cap + W));
+  return round_up(csa::attend_workspace_bytes(B * T, H, d, n_cap + W, true));
 }
 
 int hca_attend(const void* q, int q_dtype, const void* kc, const void* vc, int kv_dtype, int m,
@@ -318,7 +320,7 @@ int hca_attend(const void* q, int q_dtype, const void* kc, const void* vc, int k
                void* stream) {
   const char* fn = "hca_attend";
   int rc = check_attend_args(q, q_dtype, kc, vc, kv_dtype, kr, vr, raw_pos0, R, pos0, B, T, H, d,
-                             n_cap, W, out, fn);
+                             n_cap, W, scale, out, fn);
   if (rc) return rc;
   CSA_REQUIRE(m >= 1, CSA_ERR_SHAPE, "%s: m must be >= 1", fn);
   const size_t need = hca_attend_workspace_size(B, T, H, d, n_cap, W);

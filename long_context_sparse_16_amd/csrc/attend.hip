@@ -16,26 +16,42 @@
 // MFMA orientation: S^T = K . Q^T puts keys on rows and heads on columns,
 // so each lane ends up holding the probabilities of its own head for 4 keys
 // per tile -- exactly the B operand layout of O^T = V^T . P^T (the key order
-// inside the reduction is free as long as V^T uses the same one).  V is
-// therefore staged transposed ([dim][key]) in LDS.
+// inside the reduction is free as long as V^T uses the same one).  K and V
+// are both staged row-major ([key][dim]) in LDS; the bf16 V^T operand is
+// read with the LDS transpose read (4 keys x 4 dims per 4 lanes), and the
+// fp32 one (one key per lane group) needs no transpose.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace csa {
 
 constexpr int kAttChunk = 64;  // keys per LDS chunk
-constexpr int kMergeMaxSplits = 64;  // partials merged per row
+// CSA: a split's slice of the top-k list is staged in LDS, so a split spans
+// at most this many chunks.
+constexpr int kAttMaxSplitChunks = 32;
+constexpr int kMergeMaxSplits = 64;  // most partials per row (bounds the workspace)
 constexpr float kLog2e = 1.4426950408889634f;
+// The running softmax reference only moves up when a chunk's maximum exceeds
+// it by more than this (log2 domain), so probabilities stay <= 2^8 and the
+// accumulators are rescaled only on the rare large jumps; the final
+// normalisation makes the result independent of the reference.
+constexpr float kAttMaxSlack = 8.0f;
 
 template <int DTYPE, int D>
 struct AttTraits;
 
+// LDS row strides (bytes): K rows are read 16 rows x 16 bytes at a time
+// (stride = 4 banks mod 64); bf16 V rows are read 8 rows x 32 bytes per half
+// wave by the transpose read (stride = 8 banks mod 64), fp32 V rows 4 rows x
+// 64 bytes (stride = 4 banks mod 64).
 template <int D>
 struct AttTraits<0, D> {  // fp32 storage, v_mfma_f32_16x16x4_f32
   static constexpr int kElem = 4;
   static constexpr int kRowBytes = D * 4;
   static constexpr int kKSteps = D / 4;       // QK steps (1 element per lane)
-  static constexpr int kVtStride = kAttChunk * 4 + 16;  // bytes per dim row
+  static constexpr int kVsStride = kRowBytes + 16;
 };
 
 template <int D>
@@ -43,7 +59,7 @@ struct AttTraits<1, D> {  // bf16 storage, v_mfma_f32_16x16x32_bf16
   static constexpr int kElem = 2;
   static constexpr int kRowBytes = D * 2;
   static constexpr int kKSteps = D / 32;
-  static constexpr int kVtStride = kAttChunk * 2 + 8;
+  static constexpr int kVsStride = kRowBytes + 32;
 };
 
 struct AttParams {
@@ -73,9 +89,16 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
   constexpr int kPieces = RB / 16;             // 16-byte pieces per row
   constexpr int kPerThread = kAttChunk * kPieces / 256;
   constexpr int kKsStride = RB + 16;
-  __shared__ __attribute__((aligned(16))) uint8_t ks[kAttChunk * kKsStride];
-  __shared__ __attribute__((aligned(16))) uint8_t vt[D * Tr::kVtStride];
-  __shared__ int valid[kAttChunk];
+  constexpr int kVsStride = Tr::kVsStride;
+  // Two LDS buffers: chunk i+1 is staged into one while chunk i is computed
+  // from the other, with one barrier per chunk.
+  __shared__ __attribute__((aligned(16))) uint8_t ks[2][kAttChunk * kKsStride];
+  __shared__ __attribute__((aligned(16))) uint8_t vs[2][kAttChunk * kVsStride];
+  __shared__ int valid[2][kAttChunk];
+  // 1 + (split-relative) index of the last chunk staged into the buffer that
+  // had absent keys, so no flag ever has to be cleared
+  __shared__ int s_partial[2];
+  __shared__ int32_t s_ent[HCA ? 1 : kAttMaxSplitChunks * kAttChunk];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -85,8 +108,10 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
   const int64_t row = blockIdx.y;
   const int split = blockIdx.x;
   const int64_t b = row / p.T;
+  // both position loads are unconditional, so they are in flight together
+  // (raw_pos0 may be NULL when W == 0; its value is then unused)
   const int64_t t = p.pos0[b] + (row - b * p.T);
-  const int64_t rp0 = p.W > 0 ? p.raw_pos0[b] : 0;
+  const int64_t rp0 = (p.W > 0 ? p.raw_pos0 : p.pos0)[b];
   const int64_t n_ent = HCA ? visible_entries(t, p.m, p.n_cap) : static_cast<int64_t>(p.k);
   const int64_t n_slots = n_ent + p.W;
   const int64_t c_begin = static_cast<int64_t>(split) * p.chunks_per_split;
@@ -96,90 +121,111 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
   const int head = wave * 16 + col;
 
   // Q^T fragments: this lane's head, one contiguous quarter of the row.
+  // Lanes past the last head load it again (unconditional loads); their
+  // columns are never written out.
   constexpr int kQVec = RB / 4 / 16;
   u32x4 qf[kQVec];
-#pragma unroll
-  for (int v = 0; v < kQVec; ++v) qf[v] = u32x4{0u, 0u, 0u, 0u};
-  if (has_heads && head < p.H) {
-    const u32x4* src =
-        reinterpret_cast<const u32x4*>(p.q + (row * p.H + head) * RB + g * (RB / 4));
+  {
+    const int64_t hq = head < p.H ? head : p.H - 1;
+    const u32x4* src = reinterpret_cast<const u32x4*>(p.q + (row * p.H + hq) * RB + g * (RB / 4));
 #pragma unroll
     for (int v = 0; v < kQVec; ++v) qf[v] = src[v];
   }
 
-  // Every thread gathers kPerThread 16-byte pieces of K and of V per chunk.
-  // Absent slots (padding, positions outside the raw buffer) read row 0 of
-  // the sequence's cache instead, so every load is issued unconditionally;
-  // they are masked out of the softmax and their values get weight 0.
+  // CSA: the split's slice of the top-k list is copied to LDS once, so the
+  // gathers never wait on index loads.
+  const int64_t s_begin = c_begin * kAttChunk;
+  const int64_t idx_row = row * p.k;
+  if (!HCA) {
+    const int64_t n_list = min(c_end * kAttChunk, n_ent) - s_begin;
+    for (int64_t i = tid; i < n_list; i += 256) s_ent[i] = p.idx[idx_row + s_begin + i];
+  }
+  if (tid == 0) s_partial[0] = s_partial[1] = 0;
+
+  // Every thread gathers kPerThread 16-byte pieces of K and of V per chunk
+  // (piece r: key (tid + 256 r) / kPieces, same column pc), into one of two
+  // register slots: while chunk i is computed, the loads of chunks i+2 and
+  // i+3 are in flight.  Absent slots (padding, positions outside the raw
+  // buffer) read row 0 of the sequence's cache instead, and chunks past the
+  // split's end re-read its last chunk, so every load is issued
+  // unconditionally (which keeps the compiler's wait counts partial); absent
+  // keys are masked out of the softmax.
   const uint8_t* kc_b = p.kc + b * p.n_cap * RB;
   const uint8_t* vc_b = p.vc + b * p.n_cap * RB;
-  const int64_t idx_row = row * p.k;
-  int32_t ent[kPerThread];  // the chunk's entry index per piece (CSA)
-  auto fetch_idx = [&](int64_t chunk) {
+  const int pc = tid % kPieces;
+  const int key0 = tid / kPieces;
+  struct Slot {
+    u32x4 k[kPerThread], v[kPerThread];
+    bool ok[kPerThread];
+  };
+  Slot ring0, ring1;
+  auto pick = [&](auto slot) __attribute__((always_inline)) -> Slot& {
+    if constexpr (decltype(slot)::value == 0) return ring0;
+    else return ring1;
+  };
+  auto gather = [&](auto slot, int64_t chunk) __attribute__((always_inline)) {
+    Slot& S = pick(slot);
+    const int64_t s0 = chunk * kAttChunk;
+    int64_t koff[kPerThread], voff[kPerThread];  // byte offsets from kc_b / vc_b
+    if (s0 + kAttChunk <= n_ent) {
+      // uniform fast path: every slot of the chunk is a compressed entry
 #pragma unroll
-    for (int r = 0; r < kPerThread; ++r) {
-      const int64_t s = chunk * kAttChunk + (tid + 256 * r) / kPieces;
-      if (HCA) {
-        ent[r] = static_cast<int32_t>(s);
-      } else {
-        const int64_t sc = s < n_ent ? s : n_ent - 1;
-        ent[r] = n_ent > 0 ? p.idx[idx_row + sc] : -1;
+      for (int r = 0; r < kPerThread; ++r) {
+        const int key = key0 + r * (256 / kPieces);
+        int64_t e;
+        if (HCA) {
+          e = s0 + key;
+          S.ok[r] = true;
+        } else {
+          const int32_t ei = s_ent[s0 + key - s_begin];
+          S.ok[r] = ei >= 0 && ei < p.n_cap;
+          e = S.ok[r] ? ei : 0;
+        }
+        koff[r] = voff[r] = e * RB + pc * 16;
+      }
+    } else {
+      // window slots, the split's tail, padding
+      const int64_t raw_k = p.kr - kc_b, raw_v = p.vr - vc_b;
+#pragma unroll
+      for (int r = 0; r < kPerThread; ++r) {
+        const int64_t s = s0 + key0 + r * (256 / kPieces);
+        int64_t ko = pc * 16, vo = pc * 16;
+        bool ok = false;
+        if (s < n_ent) {
+          const int64_t e = HCA ? s : static_cast<int64_t>(s_ent[s - s_begin]);
+          ok = e >= 0 && e < p.n_cap;
+          if (ok) ko = vo = e * RB + pc * 16;
+        } else {
+          const int64_t pos = t - p.W + 1 + (s - n_ent);
+          const int64_t rr = pos - rp0;
+          ok = s < n_slots && pos >= 0 && rr >= 0 && rr < p.R;
+          if (ok) {
+            ko = raw_k + (b * p.R + rr) * RB + pc * 16;
+            vo = raw_v + (b * p.R + rr) * RB + pc * 16;
+          }
+        }
+        S.ok[r] = ok;
+        koff[r] = ko;
+        voff[r] = vo;
       }
     }
-  };
-  u32x4 kreg[kPerThread], vreg[kPerThread];
-  bool vld[kPerThread];
-  auto gather = [&](int64_t chunk) {
 #pragma unroll
     for (int r = 0; r < kPerThread; ++r) {
-      const int id = tid + 256 * r;
-      const int key = id / kPieces;
-      const int pc = id - key * kPieces;
-      const int64_t s = chunk * kAttChunk + key;
-      const uint8_t* krow = kc_b;
-      const uint8_t* vrow = vc_b;
-      bool ok = false;
-      if (s < n_ent) {
-        const int64_t e = ent[r];
-        ok = e >= 0 && e < p.n_cap;
-        if (ok) {
-          krow = kc_b + e * RB;
-          vrow = vc_b + e * RB;
-        }
-      } else {
-        const int64_t pos = t - p.W + 1 + (s - n_ent);
-        const int64_t rr = pos - rp0;
-        ok = s < n_slots && pos >= 0 && rr >= 0 && rr < p.R;
-        if (ok) {
-          krow = p.kr + (b * p.R + rr) * RB;
-          vrow = p.vr + (b * p.R + rr) * RB;
-        }
-      }
-      vld[r] = ok;
-      kreg[r] = *reinterpret_cast<const u32x4*>(krow + pc * 16);
-      vreg[r] = *reinterpret_cast<const u32x4*>(vrow + pc * 16);
+      S.k[r] = *reinterpret_cast<const u32x4*>(kc_b + koff[r]);
+      S.v[r] = *reinterpret_cast<const u32x4*>(vc_b + voff[r]);
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](auto slot, auto buf, int i) __attribute__((always_inline)) {
+    const Slot& S = pick(slot);
+    constexpr int bf = decltype(buf)::value;
 #pragma unroll
     for (int r = 0; r < kPerThread; ++r) {
-      const int id = tid + 256 * r;
-      const int key = id / kPieces;
-      const int pc = id - key * kPieces;
-      *reinterpret_cast<u32x4*>(ks + key * kKsStride + pc * 16) = kreg[r];
-      if (pc == 0) valid[key] = vld[r] ? 1 : 0;
-      if (DTYPE == 1) {
-        // 8 bf16 values: dims pc*8 .. pc*8+7 of this key
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t word = vreg[r][e >> 1];
-          const uint16_t h = static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xffffu));
-          *reinterpret_cast<uint16_t*>(vt + (pc * 8 + e) * Tr::kVtStride + key * 2) = h;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *reinterpret_cast<uint32_t*>(vt + (pc * 4 + e) * Tr::kVtStride + key * 4) = vreg[r][e];
+      const int key = key0 + r * (256 / kPieces);
+      *reinterpret_cast<u32x4*>(&ks[bf][key * kKsStride + pc * 16]) = S.k[r];
+      *reinterpret_cast<u32x4*>(&vs[bf][key * kVsStride + pc * 16]) = S.v[r];
+      if (pc == 0) {
+        valid[bf][key] = S.ok[r] ? 1 : 0;
+        if (!S.ok[r]) s_partial[bf] = i + 1;
       }
     }
   };
@@ -188,30 +234,23 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
   f32x4 o[kDT];
 #pragma unroll
   for (int i = 0; i < kDT; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max (log2 domain), uniform per head
+  float m_run = -INFINITY;  // softmax reference (log2 domain), uniform per head
   float l_run = 0.f;        // this lane's partial sum of exp
 
-  if (c_begin < c_end) {
-    fetch_idx(c_begin);
-    gather(c_begin);
-    if (c_begin + 1 < c_end) fetch_idx(c_begin + 1);
-  }
-  for (int64_t c = c_begin; c < c_end; ++c) {
-    __syncthreads();
-    stage();
-    __syncthreads();
-    if (c + 1 < c_end) {
-      gather(c + 1);
-      if (c + 2 < c_end) fetch_idx(c + 2);
-    }
-    if (!has_heads) continue;
-
+  // Chunk i from LDS buffer `buf`: scores, online softmax update,
+  // O^T += V^T . P^T.
+  auto compute = [&](auto buf, int i) __attribute__((always_inline)) {
+    constexpr int bf = decltype(buf)::value;
+    if (!has_heads) return;
+    const bool masked = s_partial[bf] == i + 1;
+    const uint8_t* kb = ks[bf];
+    const uint8_t* vb = vs[bf];
     // S^T tiles: 4 tiles of 16 keys x 16 heads
     f32x4 s[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint8_t* arow = ks + (kt * 16 + col) * kKsStride + g * (RB / 4);
+      const uint8_t* arow = kb + (kt * 16 + col) * kKsStride + g * (RB / 4);
       if (DTYPE == 1) {
 #pragma unroll
         for (int st = 0; st < Tr::kKSteps; ++st) {
@@ -226,39 +265,56 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
         }
       }
     }
-    // scale, mask, running max
+    // scale (log2 domain), mask, chunk maximum.  The scaled score is
+    // rounded once and the maximum taken over those values, so the largest
+    // key gets exactly exp2(0) = 1 (no contraction into the exponent's FMA).
+    {
+#pragma clang fp contract(off)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[kt][i] *= p.scale_log2;
+    }
+    if (masked) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!valid[bf][kt * 16 + g * 4 + i]) s[kt][i] = -INFINITY;
+    }
     float mloc = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = valid[kt * 16 + g * 4 + i] ? s[kt][i] * p.scale_log2 : -INFINITY;
-        s[kt][i] = x;
-        mloc = fmaxf(mloc, x);
-      }
-    }
+      for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, s[kt][i]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    if (m_new == -INFINITY) continue;  // nothing valid so far (uniform per head)
-    const float alpha = exp2f(m_run - m_new);
+    const float m_new = mloc > m_run + kAttMaxSlack ? mloc : m_run;
+    if (m_new == -INFINITY) return;  // nothing valid so far (uniform per head)
+    if (__any(m_new != m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first update
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < kDT; ++i) o[i] *= alpha;
+    }
     m_run = m_new;
     float lsum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float e = exp2f(s[kt][i] - m_new);
+        const float e = __builtin_amdgcn_exp2f(s[kt][i] - m_new);
         s[kt][i] = e;
         lsum += e;
       }
     }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int i = 0; i < kDT; ++i) o[i] *= alpha;
+    l_run += lsum;
 
     // O^T += V^T . P^T
     if (DTYPE == 1) {
+      // lane (dim col, group g) needs V[32kk + 4g + i][dim] (lo) and
+      // V[32kk + 16 + 4g + i][dim] (hi), i = 0..3
+      const uint8_t* vbase = vb + (4 * g + (col >> 2)) * kVsStride + (col & 3) * 8;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         bf16x8 pb;
@@ -269,9 +325,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
         }
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) {
-          const uint8_t* vrow = vt + (dt * 16 + col) * Tr::kVtStride;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + (32 * kk + 4 * g) * 2);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + (32 * kk + 16 + 4 * g) * 2);
+          const u32x2 lo = lds_read_tr16(vbase + 32 * kk * kVsStride + dt * 32);
+          const u32x2 hi = lds_read_tr16(vbase + (32 * kk + 16) * kVsStride + dt * 32);
           const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
           o[dt] = mma_bf16(__builtin_bit_cast(bf16x8, a), pb, o[dt]);
         }
@@ -281,15 +336,53 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
       for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          const float* vrow = reinterpret_cast<const float*>(vb + (kt * 16 + 4 * g + i) * kVsStride);
 #pragma unroll
-          for (int dt = 0; dt < kDT; ++dt) {
-            const float a = *reinterpret_cast<const float*>(
-                vt + (dt * 16 + col) * Tr::kVtStride + (kt * 16 + 4 * g + i) * 4);
-            o[dt] = mma_f32(a, s[kt][i], o[dt]);
-          }
+          for (int dt = 0; dt < kDT; ++dt) o[dt] = mma_f32(vrow[dt * 16 + col], s[kt][i], o[dt]);
         }
       }
     }
+  };
+
+  // Chunk i (split-relative) lives in register slot i % 2 and LDS buffer
+  // i % 2.  Step i stages chunk i+1, refills its register slot with chunk
+  // i+3, computes chunk i and ends with the barrier that publishes chunk i+1
+  // and releases buffer i % 2.  The loop is unrolled by two so every slot
+  // and buffer index is static and the order of loads in flight is the same
+  // on every path.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  const int n_chunks = c_end > c_begin ? static_cast<int>(c_end - c_begin) : 0;
+  auto clamp_chunk = [&](int i) __attribute__((always_inline)) {
+    return c_begin + min(i, n_chunks - 1);
+  };
+  if (n_chunks > 0) {
+    // HCA gathers need nothing from LDS: their first loads go out before the
+    // barrier that publishes s_ent / s_partial.
+    if (HCA) {
+      gather(I0{}, clamp_chunk(0));
+      gather(I1{}, clamp_chunk(1));
+    }
+    __syncthreads();
+    if (!HCA) {
+      gather(I0{}, clamp_chunk(0));
+      gather(I1{}, clamp_chunk(1));
+    }
+    stage(I0{}, I0{}, 0);
+    gather(I0{}, clamp_chunk(2));
+    __syncthreads();
+    int i = 0;
+    for (; i + 1 < n_chunks; i += 2) {
+      stage(I1{}, I1{}, i + 1);
+      gather(I1{}, clamp_chunk(i + 3));
+      compute(I0{}, i);
+      __syncthreads();
+      stage(I0{}, I0{}, i + 2);
+      gather(I0{}, clamp_chunk(i + 4));
+      compute(I1{}, i + 1);
+      __syncthreads();
+    }
+    if (i < n_chunks) compute(I0{}, i);
   }
 
   float l_tot = l_run;
@@ -319,53 +412,67 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
   }
 }
 
-// Merge the split partials of one (query row, head): one thread per output
-// dim.  All split maxima and sums are fetched at once into LDS, the merge
-// weights follow from them, and each thread then issues its partial-output
-// loads for every split before using any (fixed split order, so the result
-// does not depend on scheduling).
+// Merge the split partials of one query row: each thread owns 4 output dims
+// of one head.  Splits are taken in batches of kMergeBatch: every load of a
+// batch (maxima, sums, partial outputs; indices clamped so none is
+// conditional) is issued before any is used, and the batch is folded into a
+// running (max, sum, O) in split order, so the result does not depend on
+// scheduling.
+constexpr int kMergeBatch = 16;
+constexpr int kMergeThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(D) void attend_merge_kernel(AttParams p) {
-  __shared__ float s_w[kMergeMaxSplits];
-  __shared__ float s_inv[2];
+__global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(AttParams p) {
+  constexpr int kTPH = D / 4;  // threads per head
+  constexpr int kHPB = kMergeThreads / kTPH;
   const int64_t row = blockIdx.y;
-  const int64_t h = blockIdx.x;
-  const int dd = threadIdx.x;
+  const int64_t h = static_cast<int64_t>(blockIdx.x) * kHPB + threadIdx.x / kTPH;
+  const int d4 = threadIdx.x % kTPH;
+  if (h >= p.H) return;
   const int64_t base = row * p.splits * p.H + h;  // partial (row, split 0, head h)
-  if (dd < 64) {
-    // one wave: per-split weights exp2(m_s - M) and the merged normaliser
-    const bool on = dd < p.splits;
-    const float pm = on ? p.pm[base + dd * p.H] : -INFINITY;
-    const float pl = on ? p.pl[base + dd * p.H] : 0.f;
-    const float M = wave_max(pm);
-    const float wgt = (M == -INFINITY || pm == -INFINITY) ? 0.f : exp2f(pm - M);
-    const float L = wave_sum(pl * wgt);
-    if (on) s_w[dd] = wgt;
-    if (dd == 0) {
-      s_inv[0] = L > 0.f ? 1.0f / L : 0.f;
-      s_inv[1] = L > 0.f ? (M + log2f(L)) / kLog2e : -INFINITY;
+  float M = -INFINITY, L = 0.f;
+  f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < p.splits; s0 += kMergeBatch) {
+    float pm[kMergeBatch], pl[kMergeBatch];
+    f32x4 po[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int64_t sp = min(s0 + j, p.splits - 1);
+      pm[j] = p.pm[base + sp * p.H];
+      pl[j] = p.pl[base + sp * p.H];
+      po[j] = *reinterpret_cast<const f32x4*>(p.po + (base + sp * p.H) * D + 4 * d4);
     }
+    float mb = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j)
+      if (s0 + j < p.splits) mb = fmaxf(mb, pm[j]);
+    const float m_new = fmaxf(M, mb);
+    if (m_new == -INFINITY) continue;  // every split so far is empty
+    const float f = exp2f(M - m_new);  // 0 while M is -inf
+    L *= f;
+    O *= f;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const float w = s0 + j < p.splits ? exp2f(pm[j] - m_new) : 0.f;  // 0 for empty splits
+      L = fmaf(pl[j], w, L);
+      O += po[j] * w;
+    }
+    M = m_new;
   }
-  __syncthreads();
-  float po[kMergeMaxSplits];
-#pragma unroll
-  for (int s = 0; s < kMergeMaxSplits; ++s)
-    po[s] = s < p.splits ? p.po[(base + s * p.H) * D + dd] : 0.f;
-  float O = 0.f;
-#pragma unroll
-  for (int s = 0; s < kMergeMaxSplits; ++s)
-    if (s < p.splits) O = fmaf(po[s], s_w[s], O);
-  p.out[(row * p.H + h) * D + dd] = O * s_inv[0];
-  if (p.lse && dd == 0) p.lse[row * p.H + h] = s_inv[1];
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  *reinterpret_cast<f32x4*>(p.out + (row * p.H + h) * D + 4 * d4) = O * inv;
+  if (p.lse && d4 == 0) p.lse[row * p.H + h] = L > 0.f ? (M + log2f(L)) / kLog2e : -INFINITY;
 }
 
 // ----------------------------------------------------------------- host side
 
-AttSplit attend_split(int64_t rows, int64_t n_slots_max) {
+AttSplit attend_split(int64_t rows, int64_t n_slots_max, bool hca) {
   // A split's partial result (H x D fp32) is as large as 64 gathered K/V
   // rows, so splits are kept at >= 4 chunks (256 keys) unless the batch is
   // too small to occupy the GPU otherwise; enough splits are made to give
-  // roughly 256 workgroups.
+  // roughly 256 workgroups.  CSA splits span at most kAttMaxSplitChunks
+  // chunks (k <= 65536 and W <= 4096 keep that within the merge's
+  // kMergeMaxSplits).
   AttSplit s;
   int64_t chunks = (n_slots_max + kAttChunk - 1) / kAttChunk;
   if (chunks < 1) chunks = 1;
@@ -374,9 +481,10 @@ AttSplit attend_split(int64_t rows, int64_t n_slots_max) {
   if (target > chunks) target = chunks;
   int64_t cps = (chunks + target - 1) / target;
   if (cps < min_cps) cps = min_cps;
-  // the merge handles at most kMergeMaxSplits partials per row
+  // at most kMergeMaxSplits partials per row
   if (cps < (chunks + kMergeMaxSplits - 1) / kMergeMaxSplits)
     cps = (chunks + kMergeMaxSplits - 1) / kMergeMaxSplits;
+  if (!hca && cps > kAttMaxSplitChunks) cps = kAttMaxSplitChunks;
   if (cps > chunks) cps = chunks;
   s.chunks_per_split = static_cast<int>(cps);
   s.splits = static_cast<int>((chunks + cps - 1) / cps);
@@ -385,8 +493,8 @@ AttSplit attend_split(int64_t rows, int64_t n_slots_max) {
 
 // Workspace: the split partials (O, max, sum); nothing in it is read before
 // being written in the same call.
-size_t attend_workspace_bytes(int64_t rows, int64_t H, int64_t D, int64_t n_slots_max) {
-  const AttSplit s = attend_split(rows, n_slots_max);
+size_t attend_workspace_bytes(int64_t rows, int64_t H, int64_t D, int64_t n_slots_max, bool hca) {
+  const AttSplit s = attend_split(rows, n_slots_max, hca);
   if (s.splits == 1) return 0;
   return static_cast<size_t>(rows) * s.splits * H * (D + 2) * sizeof(float);
 }
@@ -399,7 +507,9 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
   const bool hca = hca_m > 0;
   const int64_t rows = B * T;
   const int64_t n_slots_max = (hca ? n_cap : k) + W;
-  const AttSplit sp = attend_split(rows, n_slots_max);
+  const AttSplit sp = attend_split(rows, n_slots_max, hca);
+  if (sp.splits > kMergeMaxSplits || (!hca && sp.chunks_per_split > kAttMaxSplitChunks))
+    return -2;
   AttParams p;
   p.q = static_cast<const uint8_t*>(q);
   p.kc = static_cast<const uint8_t*>(kc);
@@ -436,8 +546,10 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
     else                                                                            \
       attend_kernel<DT, DD, false><<<grid, 256, 0, stream>>>(p);                    \
     if (sp.splits > 1)                                                              \
-      attend_merge_kernel<DD><<<dim3(static_cast<unsigned>(H), static_cast<unsigned>(rows)), \
-                                DD, 0, stream>>>(p);                                \
+      attend_merge_kernel<DD><<<dim3(static_cast<unsigned>((H + kMergeThreads / (DD / 4) - 1) / \
+                                                           (kMergeThreads / (DD / 4))),      \
+                                     static_cast<unsigned>(rows)),                           \
+                                kMergeThreads, 0, stream>>>(p);                              \
     return hipGetLastError() == hipSuccess ? 0 : -1;                                \
   }
   CSA_ATT_CASE(0, 64)

@@ -14,6 +14,20 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// ------------------------------------------------------ LDS transpose read
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 (gfx950).  Within each group of 16 lanes, with M[L]
+// the four 16-bit values at lane L's address, lane j receives element e =
+// M[4e + j/4][j % 4]: four lanes per row of 4 x 4 values come back
+// transposed.  `p` must point into LDS and be 8-byte aligned.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(const_cast<uint8_t*>(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // ---------------------------------------------------------------- bfloat16
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {

@@ -44,8 +44,8 @@ struct AttSplit {
   int splits;
   int chunks_per_split;
 };
-AttSplit attend_split(int64_t rows, int64_t n_slots_max);
-size_t attend_workspace_bytes(int64_t rows, int64_t H, int64_t D, int64_t n_slots_max);
+AttSplit attend_split(int64_t rows, int64_t n_slots_max, bool hca);
+size_t attend_workspace_bytes(int64_t rows, int64_t H, int64_t D, int64_t n_slots_max, bool hca);
 // hca_m > 0 selects HCA (all visible entries, idx ignored).
 int launch_attend(const void* q, int dtype, const void* kc, const void* vc, const int32_t* idx,
                   int k, int hca_m, const void* kr, const void* vr, const int64_t* raw_pos0,

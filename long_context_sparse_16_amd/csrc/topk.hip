@@ -321,7 +321,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
   visit_row([&](uint32_t key, int64_t j) {
     const uint32_t bk = key >> kTopkDigit1Shift;
     if (bk > b1) {
-      sm.sel[atomicAdd(&sm.misc[4], 1u)] = static_cast<int32_t>(j);
+      const uint32_t p = atomicAdd(&sm.misc[4], 1u);
+      if (p < kMaxK) sm.sel[p] = static_cast<int32_t>(j);
     } else if (bk == b1) {
       const uint32_t p = atomicAdd(&sm.misc[5], 1u);
       if (p < kCandCap) {
@@ -512,7 +513,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(
   const uint32_t b1 = cv[2];
   if (threadIdx.x < 8) sm.misc[threadIdx.x] = 0u;
   const int32_t* gs = ws.sure + row * kMaxK;
-  for (uint32_t i = threadIdx.x; i < ns; i += kSelThreads) sm.sel[i] = gs[i];
+  for (uint32_t i = threadIdx.x; i < ns; i += kSelThreads) sm.sel[i] = gs[i];  // ns <= k
   if (nc <= static_cast<uint32_t>(kCandCap)) {
     const uint32_t* gk = ws.ckey + row * kCandCap;
     const int32_t* gi = ws.cidx + row * kCandCap;

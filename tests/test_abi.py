@@ -104,9 +104,9 @@ def test_topk_validation_and_workspace():
 
 
 def _attend(q=FAKE, dt=1, kvdt=1, idx=FAKE, k=1024, kr=FAKE, W=128, H=64, d=128, B=1, T=1,
-            ws=NULL, wsb=0, R=128):
+            ws=NULL, wsb=0, R=128, scale=0.1):
     return lib.csa_attend(q, dt, FAKE, FAKE, kvdt, idx, k, kr, FAKE, FAKE, R, FAKE, B, T, H, d,
-                          4096, W, 0.1, FAKE, NULL, ws, wsb, NULL)
+                          4096, W, scale, FAKE, NULL, ws, wsb, NULL)
 
 
 def test_attend_validation():
@@ -120,6 +120,10 @@ def test_attend_validation():
     assert _attend(W=5000) == -4
     assert _attend(idx=NULL) == -1
     assert _attend(k=0, W=0, kr=NULL) == -2              # empty key set
+    assert _attend(scale=0.0) == -2                      # scale must be finite and > 0
+    assert _attend(scale=-0.1) == -2
+    assert _attend(scale=float("inf")) == -2
+    assert _attend(scale=float("nan")) == -2
     need = lib.csa_attend_workspace_size(1, 1, 64, 128, 1024, 128)
     assert need > 0
     assert _attend() == -5
