@@ -37,9 +37,10 @@
  *   buffers; positions with V(t) > n_cap are a caller error.
  * - Scores must be finite; -0.0 is ranked equal to +0.0.
  * - Workspaces (`ws`): device memory owned by the caller, sized by the
- *   matching *_workspace_size() query.  Top-k workspaces follow an
- *   all-zero protocol: zero before first use (a zero-filled allocation, or
- *   csa_workspace_clear), and every call returns them to all-zero, so they
+ *   matching *_workspace_size() query.  Top-k workspaces must be zero
+ *   before first use (a zero-filled allocation, or csa_workspace_clear);
+ *   every call leaves them ready for the next (the parts read before being
+ *   written -- histograms and counters -- are returned to zero), so they
  *   are reused call after call without clearing.  Attention workspaces
  *   hold per-call partial results and may contain anything on entry.
  *   Calls that share a workspace must be ordered (same stream); concurrent
@@ -137,8 +138,9 @@ int csa_quantize_fp8_rows(const void* x, int x_dtype, int64_t rows, int64_t d,
  * accumulates into topk_ws the first-digit histogram of the top-k
  * selection with this k (saves csa_topk one pass over the scores); the
  * next call must then be csa_topk(..., topk_ws, ..., hist_ready = 1) with
- * the same B, T, n_cap, m, k, which consumes it.  topk_ws must be in its
- * all-zero state and at least csa_topk_workspace_size() bytes.  With
+ * the same B, T, n_cap, m, k, which consumes it.  topk_ws must follow the
+ * top-k workspace protocol above and be at least csa_topk_workspace_size()
+ * bytes.  With
  * topk_ws == NULL, k is ignored.
  *
  *   qi        [B][T][H_I][d_I]      qi_dtype
@@ -167,8 +169,8 @@ int csa_index_scores(const void* qi, int qi_dtype, const float* qi_scale,
  *
  *   scores [B][T][n_cap] fp32 (only j < V(t) is read)
  *   idx    [B][T][k] int32
- *   ws     device workspace of csa_topk_workspace_size() bytes (all-zero
- *          protocol above; the size is 0, and ws may be NULL, when B*T is
+ *   ws     device workspace of csa_topk_workspace_size() bytes (top-k
+ *          workspace protocol above; the size is 0, and ws may be NULL, when B*T is
  *          large enough for one workgroup per query row).
  *   hist_ready  1 if the directly preceding csa_index_scores was given
  *          this ws (and k) and so already built the first-digit
@@ -184,8 +186,8 @@ int csa_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T,
  * csa_index_topk -- csa_index_scores followed by csa_topk on the same
  * stream, with the top-k histogram fused into the indexer.  scores may be
  * NULL, in which case the score matrix lives in the workspace
- * (csa_index_topk_workspace_size accounts for it).  Same all-zero
- * workspace protocol.
+ * (csa_index_topk_workspace_size accounts for it).  Same top-k workspace
+ * protocol.
  */
 size_t csa_index_topk_workspace_size(int64_t B, int64_t T, int64_t n_cap,
                                      int k, int scores_in_workspace);

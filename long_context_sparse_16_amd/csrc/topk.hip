@@ -20,15 +20,16 @@
 //      ascending order by a prefix sum of per-word popcounts.
 //
 // Drivers:
-//   * split path (few long rows, decode): many workgroups per row classify
-//     a 4096-entry slice each and append sure entries / candidates to
-//     per-row lists with one atomic per wave; a second kernel resolves each
-//     row in one workgroup and returns the row's workspace to all-zero.
-//     (A kernel boundary is the cheap way to make the lists visible: a
-//     last-workgroup hand-off would need device-scope fences, which write
-//     back and invalidate a whole XCD's L2.)
-//   * row path (many rows, prefill): one workgroup per row reads its score
-//     row twice (histogram, then classification) and resolves in LDS.
+//   * split path (few long rows, decode): one workgroup per 4096-entry
+//     slice finds the bucket from the row's histogram and writes the
+//     slice's sure entries and candidates to its own workspace region; a
+//     second kernel, one workgroup per row, gathers them, resolves the row
+//     and returns the row's histogram to zero.  (A kernel boundary is the
+//     cheap way to make the lists visible: a last-workgroup hand-off would
+//     need device-scope fences, which write back and invalidate a whole
+//     XCD's L2.)
+//   * row path (many rows, prefill; short rows): one workgroup per row;
+//     rows of up to 32768 entries are held in registers and read once.
 #include "common.h"
 #include "kernels.h"
 
@@ -41,14 +42,16 @@ constexpr int kBitmapMaxEntries = 262144;       // bitmap output up to this V
 constexpr int kSelThreads = 256;
 constexpr int kSelEntries = 4096;               // entries per select workgroup
 constexpr int kRowThreads = 1024;
-constexpr int64_t kRowDirectMaxEntries = 65536;  // few-row cut-over to the row kernel
+constexpr int64_t kRowSplitMinEntries = 8192;  // few rows longer than this take the split path
 
 struct FinishShared {
   uint32_t hist[2048];                    // digit passes 2.. (<= 2048 bins)
   uint32_t ckey[kCandCap];
   int32_t cidx[kCandCap];
   int32_t sel[kMaxK];
-  uint32_t bitmap[kBitmapMaxEntries / 32];  // also the 4096-bin first digit
+  // row bitmap, one pad word after every 32 (see bm_slot); also holds the
+  // 4096-bin first-digit histogram in the row kernel
+  uint32_t bitmap[kBitmapMaxEntries / 32 + kBitmapMaxEntries / 1024];
   uint32_t scan[32];
   uint32_t misc[8];  // [0] bin [1] above [4] selected [5] candidates [7] flag
 };
@@ -122,10 +125,16 @@ __device__ void digit_pass(FinishShared& sm, Visit visit, int shift, int nb, uin
   block_find_top<NT>(sm.hist, nb, r, sm.scan, sm.misc);
 }
 
-// Resolve the exact selection among items that all share the first digit,
-// needing r of them; winners are appended to sm.sel at sm.misc[4].
+// The exact selection among items that all share the first digit, needing
+// r of them: an item (key, j) wins iff (key & 0xfffff) > low20, or it equals
+// low20 and j <= jmax.  Returns {low20, jmax}.
+struct Cut {
+  uint32_t low20;
+  int32_t jmax;
+};
+
 template <int NT, typename Visit>
-__device__ void resolve_candidates(FinishShared& sm, Visit visit_all, uint32_t r) {
+__device__ Cut resolve_cut(FinishShared& sm, Visit visit_all, uint32_t r) {
   digit_pass<NT>(sm, visit_all, 10, 1024, r);  // key bits 19..10
   const uint32_t b2 = sm.misc[0];
   const uint32_t r2 = r - sm.misc[1];
@@ -173,9 +182,20 @@ __device__ void resolve_candidates(FinishShared& sm, Visit visit_all, uint32_t r
     __syncthreads();
     jmax = static_cast<int32_t>(0x7fffffffu - ((c1 << 20) | (c2 << 10) | c3));
   }
+  return Cut{low20, jmax};
+}
+
+__device__ __forceinline__ bool cut_wins(Cut c, uint32_t key, int32_t j) {
+  const uint32_t lo = key & 0xfffffu;
+  return lo > c.low20 || (lo == c.low20 && j <= c.jmax);
+}
+
+// resolve_cut, then append the winners to sm.sel at sm.misc[4].
+template <int NT, typename Visit>
+__device__ void resolve_candidates(FinishShared& sm, Visit visit_all, uint32_t r) {
+  const Cut c = resolve_cut<NT>(sm, visit_all, r);
   visit_all([&](uint32_t key, int32_t j) {
-    const uint32_t lo = key & 0xfffffu;
-    if (lo > low20 || (lo == low20 && j <= jmax)) {
+    if (cut_wins(c, key, j)) {
       const uint32_t p = atomicAdd(&sm.misc[4], 1u);
       if (p < kMaxK) sm.sel[p] = j;
     }
@@ -183,30 +203,36 @@ __device__ void resolve_candidates(FinishShared& sm, Visit visit_all, uint32_t r
   __syncthreads();
 }
 
+// LDS slot of bitmap word w: one pad word after every 32, so that threads
+// reading 32 consecutive words each hit distinct banks.
+__device__ __forceinline__ int bm_slot(int w) { return w + (w >> 5); }
+
 // Emit sm.sel[0..k) in ascending order to out[0..k).  Rows up to
-// kBitmapMaxEntries long use a bitmap over the row and a prefix sum of
-// popcounts; longer rows sort with a bitonic network.
+// kBitmapMaxEntries long use a bitmap over the row: each thread owns a run
+// of consecutive words, counts their bits, takes its output position from
+// a block prefix sum and writes its entries in order.  Longer rows sort
+// with a bitonic network.
 template <int NT>
 __device__ void emit_sorted(FinishShared& sm, int k, int64_t V, int32_t* out) {
   const int tid = threadIdx.x;
   if (V <= kBitmapMaxEntries) {
     const int nw = static_cast<int>((V + 31) >> 5);
-    for (int i = tid; i < nw; i += NT) sm.bitmap[i] = 0u;
+    for (int i = tid; i < bm_slot(nw); i += NT) sm.bitmap[i] = 0u;
     __syncthreads();
     for (int i = tid; i < k; i += NT) {
       const int32_t j = sm.sel[i];
-      if (j >= 0 && j < V) atomicOr(&sm.bitmap[j >> 5], 1u << (j & 31));
+      if (j >= 0 && j < V) atomicOr(&sm.bitmap[bm_slot(j >> 5)], 1u << (j & 31));
     }
     __syncthreads();
     const int per = (nw + NT - 1) / NT;
     const int w0 = tid * per;
     const int w1 = min(nw, w0 + per);
     uint32_t cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += __popc(sm.bitmap[w]);
+    for (int w = w0; w < w1; ++w) cnt += __popc(sm.bitmap[bm_slot(w)]);
     uint32_t pos = block_excl_scan<NT>(cnt, sm.scan);
     if (tid == NT - 1) sm.misc[6] = pos + cnt;  // number of marked entries
     for (int w = w0; w < w1; ++w) {
-      uint32_t bits = sm.bitmap[w];
+      uint32_t bits = sm.bitmap[bm_slot(w)];
       while (bits) {
         const int bit = __ffs(bits) - 1;
         if (pos < static_cast<uint32_t>(k)) out[pos] = w * 32 + bit;
@@ -268,17 +294,25 @@ __device__ void finish_row(FinishShared& sm, const float* srow, int64_t V, uint3
 
 // ------------------------------------------------------------- row path
 
-// The row is read twice (histogram, then classification); each pass takes
-// the row in batches of kRowBatch independent loads per thread that are all
-// in flight before any is used.
+// Rows of up to kRowThreads * REGS entries are held in registers (REGS > 0):
+// the histogram loads go out first, then the row's, so the histogram is
+// usable before the row has arrived, and the row is read once.  Longer rows
+// (REGS == 0) are read in batches of kRowBatch independent loads per thread
+// (twice when the histogram is built here).  Classification counts each
+// thread's sure entries and candidates, takes list positions from one
+// block prefix sum of the packed counts and writes without atomics.
 constexpr int kRowBatch = 16;
+constexpr int kRowRegs = 32;  // register-resident rows: V <= 32768 (1024 threads x 32)
 
 // hist_io (nullable): the rows' first-digit histograms built by the
-// indexer; used instead of the first pass and returned to zero.
+// indexer; used instead of a histogram pass and returned to zero.
+template <int REGS>
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ pos0, int64_t T,
     int64_t n_cap, int m, int k, int32_t* __restrict__ idx, uint32_t* __restrict__ hist_io) {
   __shared__ FinishShared sm;
+  constexpr int kHistPer = kHistBins / kRowThreads;
+  const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int64_t b = row / T;
   const int64_t t = pos0[b] + (row - b * T);
@@ -291,47 +325,109 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
   const float* srow = scores + row * n_cap;
   uint32_t* h1 = sm.bitmap;  // first-digit histogram (the bitmap is used later)
   uint32_t* gh = hist_io ? hist_io + row * kHistBins : nullptr;
-  for (int i = threadIdx.x; i < kHistBins; i += kRowThreads) h1[i] = gh ? gh[i] : 0u;
-  if (threadIdx.x < 8) sm.misc[threadIdx.x] = 0u;
+  uint32_t hv[kHistPer];
+#pragma unroll
+  for (int q = 0; q < kHistPer; ++q) hv[q] = gh ? gh[tid + q * kRowThreads] : 0u;
+  float rv[REGS > 0 ? REGS : 1];
+  if (REGS > 0) {
+#pragma unroll
+    for (int u = 0; u < REGS; ++u) {
+      const int64_t j = tid + static_cast<int64_t>(u) * kRowThreads;
+      rv[u] = srow[j < V ? j : V - 1];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kHistPer; ++q) h1[tid + q * kRowThreads] = hv[q];
+  if (tid < 8) sm.misc[tid] = 0u;
   __syncthreads();
-  // visit(f): f(key, j) for every visible entry, batched loads
-  auto visit_row = [&](auto f) {
-    for (int64_t base = threadIdx.x; base < V; base += static_cast<int64_t>(kRowThreads) * kRowBatch) {
+  if (!gh) {
+    if (REGS > 0) {
+#pragma unroll
+      for (int u = 0; u < REGS; ++u) {
+        const int64_t j = tid + static_cast<int64_t>(u) * kRowThreads;
+        if (j < V) atomicAdd(&h1[score_key(rv[u]) >> kTopkDigit1Shift], 1u);
+      }
+    } else {
+      for (int64_t base = 0; base < V; base += static_cast<int64_t>(kRowThreads) * kRowBatch) {
+        float v[kRowBatch];
+#pragma unroll
+        for (int u = 0; u < kRowBatch; ++u) {
+          const int64_t j = base + tid + static_cast<int64_t>(u) * kRowThreads;
+          v[u] = srow[j < V ? j : V - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < kRowBatch; ++u) {
+          const int64_t j = base + tid + static_cast<int64_t>(u) * kRowThreads;
+          if (j < V) atomicAdd(&h1[score_key(v[u]) >> kTopkDigit1Shift], 1u);
+        }
+      }
+    }
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int q = 0; q < kHistPer; ++q) gh[tid + q * kRowThreads] = 0u;
+  }
+  block_find_top<kRowThreads>(h1, kHistBins, static_cast<uint32_t>(k), sm.scan, sm.misc);
+  const uint32_t b1 = sm.misc[0];
+  const uint32_t above = sm.misc[1];
+  if (REGS > 0) {
+    // count, one packed prefix sum, then write at the thread's positions.
+    // Packing: sure entries in the low 12 bits (fewer than k <= 4096 in the
+    // whole row), candidates above them (at most V <= 32768).
+    uint32_t ns = 0, nc = 0;
+#pragma unroll
+    for (int u = 0; u < REGS; ++u) {
+      const int64_t j = tid + static_cast<int64_t>(u) * kRowThreads;
+      const uint32_t bk = score_key(rv[u]) >> kTopkDigit1Shift;
+      ns += (j < V && bk > b1) ? 1u : 0u;
+      nc += (j < V && bk == b1) ? 1u : 0u;
+    }
+    const uint32_t packed = block_excl_scan<kRowThreads>(ns | (nc << 12), sm.scan);
+    uint32_t ps = packed & 0xfffu, pcand = packed >> 12;
+    if (tid == kRowThreads - 1) sm.misc[5] = pcand + nc;  // total candidates
+#pragma unroll
+    for (int u = 0; u < REGS; ++u) {
+      const int64_t j = tid + static_cast<int64_t>(u) * kRowThreads;
+      const uint32_t key = score_key(rv[u]);
+      const uint32_t bk = key >> kTopkDigit1Shift;
+      if (j < V && bk > b1) {
+        if (ps < static_cast<uint32_t>(kMaxK)) sm.sel[ps] = static_cast<int32_t>(j);
+        ++ps;
+      } else if (j < V && bk == b1) {
+        if (pcand < static_cast<uint32_t>(kCandCap)) {
+          sm.ckey[pcand] = key;
+          sm.cidx[pcand] = static_cast<int32_t>(j);
+        }
+        ++pcand;
+      }
+    }
+    if (tid == kRowThreads - 1) sm.misc[4] = ps;  // sure entries (== above)
+  } else {
+    for (int64_t base = 0; base < V; base += static_cast<int64_t>(kRowThreads) * kRowBatch) {
       float v[kRowBatch];
 #pragma unroll
       for (int u = 0; u < kRowBatch; ++u) {
-        const int64_t j = base + static_cast<int64_t>(u) * kRowThreads;
+        const int64_t j = base + tid + static_cast<int64_t>(u) * kRowThreads;
         v[u] = srow[j < V ? j : V - 1];
       }
 #pragma unroll
       for (int u = 0; u < kRowBatch; ++u) {
-        const int64_t j = base + static_cast<int64_t>(u) * kRowThreads;
-        if (j < V) f(score_key(v[u]), j);
+        const int64_t j = base + tid + static_cast<int64_t>(u) * kRowThreads;
+        const uint32_t key = score_key(v[u]);
+        const uint32_t bk = key >> kTopkDigit1Shift;
+        if (j < V && bk > b1) {
+          const uint32_t p = atomicAdd(&sm.misc[4], 1u);
+          if (p < kMaxK) sm.sel[p] = static_cast<int32_t>(j);
+        } else if (j < V && bk == b1) {
+          const uint32_t p = atomicAdd(&sm.misc[5], 1u);
+          if (p < kCandCap) {
+            sm.ckey[p] = key;
+            sm.cidx[p] = static_cast<int32_t>(j);
+          }
+        }
       }
     }
-  };
-  if (!gh) {
-    visit_row([&](uint32_t key, int64_t) { atomicAdd(&h1[key >> kTopkDigit1Shift], 1u); });
-    __syncthreads();
-  } else {
-    for (int i = threadIdx.x; i < kHistBins; i += kRowThreads) gh[i] = 0u;
   }
-  block_find_top<kRowThreads>(h1, kHistBins, static_cast<uint32_t>(k), sm.scan, sm.misc);
-  const uint32_t b1 = sm.misc[0];
-  visit_row([&](uint32_t key, int64_t j) {
-    const uint32_t bk = key >> kTopkDigit1Shift;
-    if (bk > b1) {
-      const uint32_t p = atomicAdd(&sm.misc[4], 1u);
-      if (p < kMaxK) sm.sel[p] = static_cast<int32_t>(j);
-    } else if (bk == b1) {
-      const uint32_t p = atomicAdd(&sm.misc[5], 1u);
-      if (p < kCandCap) {
-        sm.ckey[p] = key;
-        sm.cidx[p] = static_cast<int32_t>(j);
-      }
-    }
-  });
-  const uint32_t above = sm.misc[1];
   __syncthreads();
   const uint32_t nc = sm.misc[5];
   finish_row<kRowThreads>(sm, srow, V, b1, static_cast<uint32_t>(k) - above, nc, k, out);
@@ -339,37 +435,51 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
 
 // ------------------------------------------------------------ split path
 //
-// Workspace per row, all-zero between calls: hist[4096] u32, ctrl[4] u32
-// (sure count, candidate count, first-digit bucket, count above it); then
-// the per-row lists
-// sure[kMaxK] i32, ckey[kCandCap] u32, cidx[kCandCap] i32, whose contents
-// never matter on entry.
+// Workspace per row: hist[4096] u32 (zero between calls; the indexer or
+// topk_hist_kernel accumulates into it and the finishing kernel clears it),
+// ctrl[4] u32 (first-digit bucket, count above it; cleared after use), then
+// per 4096-entry slice: cnt[2] u32 (sure entries, candidates) and the
+// slice's lists sure[4096] i32, ckey[4096] u32, cidx[4096] i32, which are
+// written before they are read in the same call.
 
 struct SplitWs {
-  uint32_t* hist;
-  uint32_t* ctrl;
-  int32_t* sure;
-  uint32_t* ckey;
-  int32_t* cidx;
+  uint32_t* hist;   // [rows][kHistBins]
+  uint32_t* ctrl;   // [rows][4]
+  uint32_t* cnt;    // [rows][n_sl][2]
+  int32_t* sure;    // [rows][n_sl][kSelEntries]
+  uint32_t* ckey;   // [rows][n_sl][kSelEntries]
+  int32_t* cidx;    // [rows][n_sl][kSelEntries]
+  int64_t n_sl;     // slices per row
 };
 
-inline size_t split_ws_bytes(int64_t rows) {
+// Rows of the split path hold at most this many slices (the finishing
+// kernel keeps a 4-word record per slice in its bitmap area).
+constexpr int64_t kMaxSlices = 2048;
+static_assert(4 * kMaxSlices <= kBitmapMaxEntries / 32, "slice table must fit the bitmap area");
+
+inline int64_t n_slices(int64_t n_cap) { return (n_cap + kSelEntries - 1) / kSelEntries; }
+
+inline size_t split_ws_bytes(int64_t rows, int64_t n_cap) {
+  const int64_t ns = n_slices(n_cap);
   return static_cast<size_t>(rows) *
-         (sizeof(uint32_t) * (kHistBins + 4) + sizeof(int32_t) * kMaxK +
-          (sizeof(uint32_t) + sizeof(int32_t)) * kCandCap);
+         (sizeof(uint32_t) * (kHistBins + 4) +
+          static_cast<size_t>(ns) * (sizeof(uint32_t) * 2 + sizeof(int32_t) * kSelEntries * 3));
 }
 
-inline SplitWs split_ws(void* base, int64_t rows) {
+inline SplitWs split_ws(void* base, int64_t rows, int64_t n_cap) {
   SplitWs w;
+  w.n_sl = n_slices(n_cap);
   char* p = static_cast<char*>(base);
   w.hist = reinterpret_cast<uint32_t*>(p);
   p += sizeof(uint32_t) * kHistBins * rows;
   w.ctrl = reinterpret_cast<uint32_t*>(p);
   p += sizeof(uint32_t) * 4 * rows;
+  w.cnt = reinterpret_cast<uint32_t*>(p);
+  p += sizeof(uint32_t) * 2 * w.n_sl * rows;
   w.sure = reinterpret_cast<int32_t*>(p);
-  p += sizeof(int32_t) * kMaxK * rows;
+  p += sizeof(int32_t) * kSelEntries * w.n_sl * rows;
   w.ckey = reinterpret_cast<uint32_t*>(p);
-  p += sizeof(uint32_t) * kCandCap * rows;
+  p += sizeof(uint32_t) * kSelEntries * w.n_sl * rows;
   w.cidx = reinterpret_cast<int32_t*>(p);
   return w;
 }
@@ -399,103 +509,167 @@ __global__ __launch_bounds__(kSelThreads) void topk_hist_kernel(
   }
 }
 
-// Append the lanes whose flag is set to an LDS list with one LDS atomic per
-// wave; positions within the wave follow lane order.
-__device__ __forceinline__ void wave_append_lds(bool flag, uint32_t* counter, int32_t* list_idx,
-                                                uint32_t* list_key, int32_t j, uint32_t key) {
-  const unsigned long long mask = __ballot(flag);
-  if (mask == 0ull) return;
-  const int lane = threadIdx.x & 63;
-  const int leader = __ffsll(static_cast<long long>(mask)) - 1;
-  uint32_t base = 0;
-  if (lane == leader) base = atomicAdd(counter, static_cast<uint32_t>(__popcll(mask)));
-  base = __shfl(base, leader);
-  if (flag) {
-    const uint32_t p = base + static_cast<uint32_t>(__popcll(mask & ((1ull << lane) - 1ull)));
-    list_idx[p] = j;
-    if (list_key) list_key[p] = key;
-  }
+// Classify one 4096-entry slice of a row: entries above the bucket of the
+// k-th largest key are "sure", entries in that bucket candidates.  The
+// slice's scores and the row's histogram are loaded together; each thread
+// keeps 16 consecutive bins (thread 0 the highest) and one block prefix sum
+// of their totals gives the bucket.  Pass `it` of wave w covers the 64
+// consecutive entries j0 + 256 it + 64 w + lane, so the slice's lists come
+// out in ascending entry order from per-(pass, wave) ballot counts, one
+// prefix sum over those 64 counts and each lane's rank in its ballot.  The
+// lists go to the slice's own workspace region (no atomics) with their
+// lengths in cnt; slice 0 also records the bucket.
+constexpr int kSelPer = kSelEntries / kSelThreads;   // 16 passes
+constexpr int kHistPerSel = kHistBins / kSelThreads;  // 16 bins per thread
+constexpr int kSelWaves = kSelThreads / 64;
+
+__device__ __forceinline__ uint32_t lanes_below(unsigned long long mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
 }
 
-// Classify one 4096-entry slice of a row: entries above the bucket of the
-// k-th largest key go to the row's "sure" list, entries in that bucket to
-// its candidate list.  Each workgroup collects its slice's entries in LDS
-// and reserves its range of the row's lists with one global atomic per
-// list.  The bucket and the count above it are also recorded for the
-// finishing kernel.
 __global__ __launch_bounds__(kSelThreads) void topk_classify_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ pos0, int64_t T,
     int64_t n_cap, int m, int k, SplitWs ws) {
-  __shared__ uint32_t hist[kHistBins];
   __shared__ uint32_t scan[32];
-  __shared__ uint32_t res[8];
-  __shared__ int32_t l_sure[kSelEntries];
-  __shared__ int32_t l_cidx[kSelEntries];
-  __shared__ uint32_t l_ckey[kSelEntries];
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t tab[kSelPer * kSelWaves];  // (pass, wave) counts, sure | cand << 16
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int64_t row = blockIdx.y;
   const int64_t b = row / T;
   const int64_t t = pos0[b] + (row - b * T);
   const int64_t V = visible_entries(t, m, n_cap);
   const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kSelEntries;
   if (V <= k || j0 >= V) return;
-  const uint32_t* gh = ws.hist + row * kHistBins;
-  uint32_t* ctrl = ws.ctrl + row * 4;
-  for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) hist[i] = gh[i];
-  if (threadIdx.x < 8) res[threadIdx.x] = 0u;
-  __syncthreads();
-  block_find_top<kSelThreads>(hist, kHistBins, static_cast<uint32_t>(k), scan, res);
-  const uint32_t b1 = res[0];
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    ctrl[2] = b1;
-    ctrl[3] = res[1];
-  }
-  const float* srow = scores + row * n_cap;
   const int64_t j1 = min(V, j0 + kSelEntries);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // all of this thread's scores are loaded before any is classified
-  constexpr int kIters = kSelEntries / kSelThreads;
-  float sv[kIters];
+  const float* srow = scores + row * n_cap;
+  // bins [kHistBins - 16 (tid + 1), kHistBins - 16 tid), 64-byte aligned
+  const uint32_t* gh = ws.hist + row * kHistBins + (kHistBins - kHistPerSel * (tid + 1));
+  u32x4 hq[kHistPerSel / 4];
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    int64_t j = j0 + it * kSelThreads + wave * 64 + lane;
+  for (int q = 0; q < kHistPerSel / 4; ++q) hq[q] = reinterpret_cast<const u32x4*>(gh)[q];
+  float sv[kSelPer];
+#pragma unroll
+  for (int it = 0; it < kSelPer; ++it) {
+    const int64_t j = j0 + it * kSelThreads + tid;
     sv[it] = srow[j < j1 ? j : j1 - 1];
   }
+  uint32_t local = 0;
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int64_t j = j0 + it * kSelThreads + wave * 64 + lane;
-    const bool valid = j < j1;
+  for (int q = 0; q < kHistPerSel / 4; ++q) local += hq[q][0] + hq[q][1] + hq[q][2] + hq[q][3];
+  const uint32_t excl = block_excl_scan<kSelThreads>(local, scan);
+  const uint32_t r = static_cast<uint32_t>(k);
+  if (excl < r && r <= excl + local) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (int q = kHistPerSel - 1; q >= 0; --q) {  // highest bin first
+      const uint32_t c = hq[q >> 2][q & 3];
+      if (acc < r && r <= acc + c) {
+        res[0] = static_cast<uint32_t>(kHistBins - kHistPerSel * (tid + 1) + q);
+        res[1] = acc;
+      }
+      acc += c;
+    }
+  }
+  __syncthreads();
+  const uint32_t b1 = res[0];
+  // per (pass, wave) counts; at most 64 of each, packed
+#pragma unroll
+  for (int it = 0; it < kSelPer; ++it) {
+    const int64_t j = j0 + it * kSelThreads + tid;
+    const uint32_t bk = score_key(sv[it]) >> kTopkDigit1Shift;
+    const unsigned long long ms = __ballot(j < j1 && bk > b1);
+    const unsigned long long mc = __ballot(j < j1 && bk == b1);
+    if (lane == 0)
+      tab[it * kSelWaves + wv] =
+          static_cast<uint32_t>(__popcll(ms)) | (static_cast<uint32_t>(__popcll(mc)) << 16);
+  }
+  __syncthreads();
+  static_assert(kSelPer * kSelWaves == 64, "one wave scans the (pass, wave) table");
+  if (wv == 0) {
+    // exclusive prefix over the 64 entries in (pass, wave) order; totals fit
+    // 16 bits each (<= 4096 per slice)
+    const uint32_t c = tab[lane];
+    uint32_t x = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    tab[lane] = x - c;
+    if (lane == 63) {
+      const int64_t slot = row * ws.n_sl + blockIdx.x;
+      ws.cnt[slot * 2] = x & 0xffffu;
+      ws.cnt[slot * 2 + 1] = x >> 16;
+      if (blockIdx.x == 0) {
+        ws.ctrl[row * 4] = b1;
+        ws.ctrl[row * 4 + 1] = res[1];
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t slot = row * ws.n_sl + blockIdx.x;
+  int32_t* gs = ws.sure + slot * kSelEntries;
+  uint32_t* gk = ws.ckey + slot * kSelEntries;
+  int32_t* gi = ws.cidx + slot * kSelEntries;
+#pragma unroll
+  for (int it = 0; it < kSelPer; ++it) {
+    const int64_t j = j0 + it * kSelThreads + tid;
     const uint32_t key = score_key(sv[it]);
     const uint32_t bk = key >> kTopkDigit1Shift;
-    wave_append_lds(valid && bk > b1, &res[4], l_sure, nullptr, static_cast<int32_t>(j), key);
-    wave_append_lds(valid && bk == b1, &res[5], l_cidx, l_ckey, static_cast<int32_t>(j), key);
-  }
-  __syncthreads();
-  const uint32_t ns = res[4], nc = res[5];
-  if (threadIdx.x == 0) {
-    res[6] = ns ? atomicAdd(&ctrl[0], ns) : 0u;
-    res[7] = nc ? atomicAdd(&ctrl[1], nc) : 0u;
-  }
-  __syncthreads();
-  const uint32_t sb = res[6], cb = res[7];
-  int32_t* gs = ws.sure + row * kMaxK;
-  for (uint32_t i = threadIdx.x; i < ns; i += kSelThreads)
-    if (sb + i < static_cast<uint32_t>(kMaxK)) gs[sb + i] = l_sure[i];
-  int32_t* gi = ws.cidx + row * kCandCap;
-  uint32_t* gk = ws.ckey + row * kCandCap;
-  for (uint32_t i = threadIdx.x; i < nc; i += kSelThreads) {
-    if (cb + i < static_cast<uint32_t>(kCandCap)) {
-      gi[cb + i] = l_cidx[i];
-      gk[cb + i] = l_ckey[i];
+    const bool is_s = j < j1 && bk > b1;
+    const bool is_c = j < j1 && bk == b1;
+    const unsigned long long ms = __ballot(is_s);
+    const unsigned long long mc = __ballot(is_c);
+    const uint32_t base = tab[it * kSelWaves + wv];
+    if (is_s) gs[(base & 0xffffu) + lanes_below(ms)] = static_cast<int32_t>(j);
+    if (is_c) {
+      const uint32_t pc = (base >> 16) + lanes_below(mc);
+      gk[pc] = key;
+      gi[pc] = static_cast<int32_t>(j);
     }
   }
 }
 
-// Resolve one row from its sure list and candidates, then return the row's
-// histogram and counters to zero for the next call.
-__global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(
+// Index of the last slice whose list offset (table word `field` of each
+// 4-word record) is <= p; offsets are non-decreasing over the slices.
+__device__ __forceinline__ int slice_of(const uint32_t* table, int n_sl, int field, uint32_t p) {
+  int lo = 0, hi = n_sl - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (table[mid * 4 + field] <= p) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Number of entries of the sorted list a[0..n) that are < x.
+__device__ __forceinline__ uint32_t count_below(const int32_t* a, uint32_t n, int32_t x) {
+  uint32_t lo = 0, hi = n;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Resolve one row from its slices' lists and return its histogram and
+// counters to zero.  The slices' counts are prefix-summed into a table (in
+// the bitmap area); the sure entries and the candidates are gathered in
+// entry order, each output position looking up its slice.  When the
+// candidates fit in LDS, the cut among them is found, the winners are
+// compacted in order behind the sure entries, and the two sorted lists are
+// merged into the output by binary search; otherwise the row is finished as
+// in the row path (candidates re-read from the scores, bitmap emit).
+constexpr int kFinThreads = 1024;
+
+__global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ pos0, int64_t T,
     int64_t n_cap, int m, int k, SplitWs ws, int32_t* __restrict__ idx) {
   __shared__ FinishShared sm;
+  const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int64_t b = row / T;
   const int64_t t = pos0[b] + (row - b * T);
@@ -505,29 +679,90 @@ __global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(
     write_iota(out, V, k);
     return;
   }
-  uint32_t* gh = ws.hist + row * kHistBins;
-  uint32_t* ctrl = ws.ctrl + row * 4;
-  const u32x4 cv = *reinterpret_cast<const u32x4*>(ctrl);  // sure, candidates, bucket, above
-  const uint32_t ns = min(cv[0], static_cast<uint32_t>(k));
-  const uint32_t nc = cv[1];
-  const uint32_t b1 = cv[2];
-  if (threadIdx.x < 8) sm.misc[threadIdx.x] = 0u;
-  const int32_t* gs = ws.sure + row * kMaxK;
-  for (uint32_t i = threadIdx.x; i < ns; i += kSelThreads) sm.sel[i] = gs[i];  // ns <= k
-  if (nc <= static_cast<uint32_t>(kCandCap)) {
-    const uint32_t* gk = ws.ckey + row * kCandCap;
-    const int32_t* gi = ws.cidx + row * kCandCap;
-    for (uint32_t i = threadIdx.x; i < nc; i += kSelThreads) {
-      sm.ckey[i] = gk[i];
-      sm.cidx[i] = gi[i];
+  const int n_sl = static_cast<int>((V + kSelEntries - 1) / kSelEntries);
+  const int64_t slot0 = row * ws.n_sl;
+  const uint32_t b1 = ws.ctrl[row * 4];
+  // per thread: slices [tid * per, tid * per + per)
+  constexpr int kPer = static_cast<int>(kMaxSlices / kFinThreads);
+  uint32_t cs[kPer], cc[kPer];
+  uint32_t ls = 0, lc = 0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int sl = tid * kPer + q;
+    const bool on = sl < n_sl;
+    cs[q] = on ? ws.cnt[(slot0 + sl) * 2] : 0u;
+    cc[q] = on ? ws.cnt[(slot0 + sl) * 2 + 1] : 0u;
+    ls += cs[q];
+    lc += cc[q];
+  }
+  uint32_t os = block_excl_scan<kFinThreads>(ls, sm.scan);
+  uint32_t oc = block_excl_scan<kFinThreads>(lc, sm.scan);
+  uint32_t* table = sm.bitmap;  // [slice][4]: sure offset, count, candidate offset, count
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int sl = tid * kPer + q;
+    if (sl < n_sl) {
+      table[sl * 4] = os;
+      table[sl * 4 + 1] = cs[q];
+      table[sl * 4 + 2] = oc;
+      table[sl * 4 + 3] = cc[q];
+    }
+    os += cs[q];
+    oc += cc[q];
+  }
+  if (tid == kFinThreads - 1) {
+    sm.misc[4] = min(os, static_cast<uint32_t>(k));  // sure entries (fewer than k)
+    sm.misc[5] = oc;                                   // candidates
+  }
+  if (tid < 4) sm.misc[tid] = 0u;
+  __syncthreads();
+  const uint32_t ns = sm.misc[4], nc = sm.misc[5];
+  const bool fits = nc <= static_cast<uint32_t>(kCandCap);
+  for (uint32_t p = tid; p < ns; p += kFinThreads) {
+    const int sl = slice_of(table, n_sl, 0, p);
+    sm.sel[p] = ws.sure[(slot0 + sl) * kSelEntries + (p - table[sl * 4])];
+  }
+  if (fits) {
+    for (uint32_t p = tid; p < nc; p += kFinThreads) {
+      const int sl = slice_of(table, n_sl, 2, p);
+      const int64_t q = (slot0 + sl) * kSelEntries + (p - table[sl * 4 + 2]);
+      sm.ckey[p] = ws.ckey[q];
+      sm.cidx[p] = ws.cidx[q];
     }
   }
-  if (threadIdx.x == 0) sm.misc[4] = ns;
   __syncthreads();
-  finish_row<kSelThreads>(sm, scores + row * n_cap, V, b1, static_cast<uint32_t>(k) - ns, nc, k,
-                          out);
-  for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) gh[i] = 0u;
-  if (threadIdx.x < 4) ctrl[threadIdx.x] = 0u;
+  const float* srow = scores + row * n_cap;
+  const uint32_t r = static_cast<uint32_t>(k) - ns;  // winners needed among the candidates
+  if (!fits) {
+    finish_row<kFinThreads>(sm, srow, V, b1, r, nc, k, out);
+  } else {
+    if (r > 0) {
+      auto visit = [&](auto f) {
+        for (uint32_t i = tid; i < nc; i += kFinThreads) f(sm.ckey[i], sm.cidx[i]);
+      };
+      const Cut c = resolve_cut<kFinThreads>(sm, visit, r);
+      // compact the winners, in entry order, into sel[ns .. k)
+      const uint32_t per = (nc + kFinThreads - 1) / kFinThreads;
+      const uint32_t i0 = tid * per, i1 = min(nc, i0 + per);
+      uint32_t wcount = 0;
+      for (uint32_t i = i0; i < i1; ++i) wcount += cut_wins(c, sm.ckey[i], sm.cidx[i]) ? 1u : 0u;
+      uint32_t wpos = ns + block_excl_scan<kFinThreads>(wcount, sm.scan);
+      for (uint32_t i = i0; i < i1; ++i)
+        if (cut_wins(c, sm.ckey[i], sm.cidx[i]) && wpos < static_cast<uint32_t>(kMaxK))
+          sm.sel[wpos++] = sm.cidx[i];
+      __syncthreads();
+    }
+    // merge the sorted lists sel[0, ns) and sel[ns, k)
+    const int32_t* wl = sm.sel + ns;
+    for (uint32_t i = tid; i < static_cast<uint32_t>(k); i += kFinThreads) {
+      const int32_t j = sm.sel[i];
+      const uint32_t pos = i < ns ? i + count_below(wl, r, j) : (i - ns) + count_below(sm.sel, ns, j);
+      out[pos] = j;
+    }
+  }
+  uint32_t* gh = ws.hist + row * kHistBins;
+  for (int i = tid; i < kHistBins; i += kFinThreads) gh[i] = 0u;
+  if (tid < 4) ws.ctrl[row * 4 + tid] = 0u;
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
@@ -539,36 +774,44 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p
 // ----------------------------------------------------------------- host side
 
 size_t topk_workspace_bytes(int64_t B, int64_t T, int64_t n_cap, int k) {
-  (void)n_cap;
   (void)k;
   const int64_t rows = B * T;
-  return rows <= kTopkSplitMaxRows ? split_ws_bytes(rows) : 0;
+  return rows <= kTopkSplitMaxRows ? split_ws_bytes(rows, n_cap) : 0;
 }
 
 uint32_t* topk_hist_ptr(void* ws, int64_t B, int64_t T) {
-  return B * T <= kTopkSplitMaxRows ? split_ws(ws, B * T).hist : nullptr;
+  // the histogram leads the workspace whatever n_cap is
+  return B * T <= kTopkSplitMaxRows ? static_cast<uint32_t*>(ws) : nullptr;
+}
+
+// One workgroup per row; rows that fit are held in registers.
+static void launch_row_kernel(const float* scores, const int64_t* pos0, int64_t T, int64_t n_cap,
+                              int m, int k, int32_t* idx, uint32_t* hist, int64_t rows,
+                              hipStream_t s) {
+  const unsigned g = static_cast<unsigned>(rows);
+  if (n_cap <= static_cast<int64_t>(kRowThreads) * kRowRegs)
+    topk_row_kernel<kRowRegs><<<g, kRowThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, idx, hist);
+  else
+    topk_row_kernel<0><<<g, kRowThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, idx, hist);
 }
 
 int launch_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, int64_t n_cap,
                 int m, int k, int32_t* idx, void* ws, bool hist_ready, hipStream_t s) {
   const int64_t rows = B * T;
-  if (rows <= kTopkSplitMaxRows && n_cap <= kRowDirectMaxEntries) {
-    // few rows short enough for one workgroup each: one pass over the row
-    // using the indexer's histogram when it built one
-    uint32_t* h = hist_ready ? split_ws(ws, rows).hist : nullptr;
-    topk_row_kernel<<<static_cast<unsigned>(rows), kRowThreads, 0, s>>>(scores, pos0, T, n_cap, m,
-                                                                        k, idx, h);
-  } else if (rows <= kTopkSplitMaxRows) {
-    SplitWs w = split_ws(ws, rows);
-    dim3 grid(static_cast<unsigned>((n_cap + kSelEntries - 1) / kSelEntries),
-              static_cast<unsigned>(rows));
+  if (rows <= kTopkSplitMaxRows && n_cap > kRowSplitMinEntries &&
+      n_slices(n_cap) <= kMaxSlices) {
+    // few long rows: many workgroups per row classify slices, one per row
+    // finishes
+    SplitWs w = split_ws(ws, rows, n_cap);
+    dim3 grid(static_cast<unsigned>(w.n_sl), static_cast<unsigned>(rows));
     if (!hist_ready) topk_hist_kernel<<<grid, kSelThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, w);
     topk_classify_kernel<<<grid, kSelThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, w);
-    topk_finish_kernel<<<static_cast<unsigned>(rows), kSelThreads, 0, s>>>(scores, pos0, T, n_cap,
+    topk_finish_kernel<<<static_cast<unsigned>(rows), kFinThreads, 0, s>>>(scores, pos0, T, n_cap,
                                                                            m, k, w, idx);
   } else {
-    topk_row_kernel<<<static_cast<unsigned>(rows), kRowThreads, 0, s>>>(scores, pos0, T, n_cap, m,
-                                                                        k, idx, nullptr);
+    // one workgroup per row, using the indexer's histogram when it built one
+    uint32_t* h = rows <= kTopkSplitMaxRows && hist_ready ? static_cast<uint32_t*>(ws) : nullptr;
+    launch_row_kernel(scores, pos0, T, n_cap, m, k, idx, h, rows, s);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -312,9 +312,10 @@ def test_hca_parity(storage, m):
 
 
 def test_workspaces_are_reusable_across_calls():
-    """A workspace is left all-zero by every call: reusing one workspace for
-    several top-k / attention calls on different data gives the same
-    results as fresh workspaces, and the workspace is zero afterwards."""
+    """Every call leaves a workspace ready for the next: reusing one
+    workspace for several top-k / attention calls on different data gives
+    the same results as fresh workspaces, and the parts read before being
+    written (histograms, counters) are zero afterwards."""
     say("workspace reuse")
     rng = np.random.default_rng(900)
     B, T, n_cap, k = 3, 2, 9000, 256
