@@ -287,8 +287,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, s[kt][i]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = max_xor32(max_xor16(mloc));
     const float m_new = mloc > m_run + kAttMaxSlack ? mloc : m_run;
     if (m_new == -INFINITY) return;  // nothing valid so far (uniform per head)
     if (__any(m_new != m_run)) {
@@ -386,8 +385,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
   }
 
   float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  l_tot = sum_xor32(sum_xor16(l_tot));
   const bool writer = has_heads && head < p.H;
   if (p.splits == 1) {
     if (!writer) return;

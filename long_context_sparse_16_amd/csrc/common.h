@@ -28,6 +28,30 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// ------------------------------------------------- lane-group reductions
+
+// Combine each lane's value with that of lane ^ 16 (resp. lane ^ 32) using
+// the gfx950 VALU lane swaps instead of an LDS permute: with both operands
+// set to x, the swap leaves every lane's own value in one result and its
+// partner's in the other, so their sum (or max) is the same in both lanes
+// of a pair.
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
 // ---------------------------------------------------------------- bfloat16
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
@@ -72,6 +96,14 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u << 1) == 0u) return 0x80000000u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Smallest float whose score_key is >= key (inverse of score_key on the
+// first key of a bucket).  Valid for keys of finite floats: 0x00800000
+// (-FLT_MAX) .. 0xff800000 (+inf); 0x80000000 gives +0.0, which compares
+// equal to -0.0 as the keys do.
+__device__ __forceinline__ float key_floor_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
 // ---------------------------------------------------------- wave reductions

@@ -17,6 +17,8 @@
 // takes elements [g*d_I/4, (g+1)*d_I/4)), so one entry row is read by four
 // lanes as 16-byte vector loads.  The same k assignment is used for the A
 // operand, which is all the MFMA needs (see common.h).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -195,8 +197,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
           v = fmaf(wq[ht][i], x, v);
         }
       }
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
+      v = sum_xor32(sum_xor16(v));
       if (lane < 16) s_scores[(grp * kGroup + tt) * kIdxTile + col] = v;
     }
   };
@@ -250,24 +251,34 @@ __global__ __launch_bounds__(256) void indexer_kernel(
 //
 // Many query tokens per sequence (chunked prefill): the key matrix is
 // shared by every token, so it is the B operand streamed once per group of
-// 8 tokens, while the tokens' queries (8 x 64 heads x 128 dims) stay in
-// registers as A fragments (2 tokens per wave).  Each 64-entry key tile is
-// loaded cooperatively into double-buffered LDS (the next tile's loads are
-// in flight during the current tile's 128 MFMAs per wave); B fragments are
-// read from LDS with a padded row stride (no bank conflicts).  The epilogue
-// applies ReLU and the head weights, sums the 64 heads of each token (in
-// lane plus two lane shuffles) and writes 64 consecutive fp32 scores per
-// token per tile.  Entries past a token's visible count are not written.
-constexpr int kPfTok = 8;        // query tokens per workgroup
-constexpr int kPfTile = 64;      // entries per LDS tile
-#ifndef CSA_PF_TOK_PER_WAVE
-#define CSA_PF_TOK_PER_WAVE 1
+// 8 tokens, while each wave keeps one token's queries (64 heads x 128 dims)
+// in registers as A fragments.  Each 64-entry key tile is loaded
+// cooperatively into double-buffered LDS (the next tile's loads are in
+// flight during the current tile's 64 MFMAs per wave); B fragments are read
+// from LDS with a padded row stride (no bank conflicts).
+//
+// The epilogue of a 16-entry column tile (ReLU, head weights, the 64-head
+// sum in lane plus two lane swaps) runs while the next column tile's MFMAs
+// are in flight: two accumulator sets alternate, so the matrix cores and
+// the vector ALUs of a wave overlap even though the per-tile barrier keeps
+// the waves in step.  Scores go out through a buffer descriptor whose range is
+// the token's visible entries, so stores past V(t) are dropped by the range
+// check rather than branched around.
+constexpr int kPfTok = 8;        // query tokens per workgroup (one per wave)
+#ifndef CSA_PF_TILE
+#define CSA_PF_TILE 128
 #endif
-constexpr int kPfTokPerWave = CSA_PF_TOK_PER_WAVE;  // 1: 8 waves x 1 token
+constexpr int kPfTile = CSA_PF_TILE;  // entries per LDS tile
+constexpr int kPfCt = kPfTile / 16;   // column tiles per LDS tile
+constexpr int kPfThreads = 64 * kPfTok;
+// Score rows of the prefill path are addressed with 32-bit byte offsets.
+constexpr int64_t kPfMaxEntries = int64_t(1) << 28;
 
-// TPW query tokens per wave, 8 / TPW waves per workgroup.
-template <int DTYPE, bool RELU, int TPW>
-__global__ __launch_bounds__(64 * kPfTok / TPW) void indexer_prefill_kernel(
+// Raw buffer descriptor word 3 for gfx9-family targets (32-bit data format).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+template <int DTYPE, bool RELU>
+__global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
     const uint8_t* __restrict__ qi, const float* __restrict__ qi_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ ki,
     const float* __restrict__ ki_scale, const int64_t* __restrict__ pos0, int64_t T,
@@ -277,8 +288,7 @@ __global__ __launch_bounds__(64 * kPfTok / TPW) void indexer_prefill_kernel(
   constexpr int kVec = Tr::kLaneBytes / 16;
   constexpr int RB = DI * Tr::kElemBytes;             // key row bytes
   constexpr int kStride = RB + 16;                    // padded LDS row
-  constexpr int kThreads = 64 * kPfTok / TPW;
-  constexpr int kLoads = kPfTile * RB / 16 / kThreads;  // 16-byte loads per thread per tile
+  constexpr int kLoads = kPfTile * RB / 16 / kPfThreads;  // 16-byte loads per thread per tile
   __shared__ __attribute__((aligned(16))) uint8_t bt[2][kPfTile * kStride];
 
   const int tid = threadIdx.x;
@@ -293,49 +303,45 @@ __global__ __launch_bounds__(64 * kPfTok / TPW) void indexer_prefill_kernel(
   const int64_t V_max = visible_entries(p0 + tok_last, m, n_cap);
   if (V_max <= 0) return;
 
-  // A fragments and head weights of this wave's tokens
-  u32x4 a[TPW][4][kVec];
-  float wq[TPW][4][4];
-  int64_t Vt[TPW];
-  int64_t srow_off[TPW];
+  // this wave's token: A fragments, head weights, score-row descriptor
+  const int64_t tok = tok0 + wave;
+  const bool tok_ok = tok < T;
+  const int64_t row = b * T + (tok_ok ? tok : 0);
+  const int64_t Vt = tok_ok ? visible_entries(p0 + tok, m, n_cap) : 0;
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      scores + row * n_cap, 0, static_cast<int>(Vt * 4), kBufferRsrcWord3);
+  u32x4 a[4][kVec];
+  float wq[4][4];
 #pragma unroll
-  for (int tt = 0; tt < TPW; ++tt) {
-    const int64_t tok = tok0 + wave * TPW + tt;
-    const bool tok_ok = tok < T;
-    const int64_t row = b * T + (tok_ok ? tok : 0);
-    Vt[tt] = tok_ok ? visible_entries(p0 + tok, m, n_cap) : 0;
-    srow_off[tt] = row * n_cap;
+  for (int ht = 0; ht < 4; ++ht) {
+    const int h = ht * 16 + col;
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      const int h = ht * 16 + col;
+    for (int v = 0; v < kVec; ++v) a[ht][v] = u32x4{0u, 0u, 0u, 0u};
+    if (tok_ok && h < H_I) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(
+          qi + (row * H_I + h) * RB + g * Tr::kLaneBytes);
 #pragma unroll
-      for (int v = 0; v < kVec; ++v) a[tt][ht][v] = u32x4{0u, 0u, 0u, 0u};
-      if (tok_ok && h < H_I) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(
-            qi + (row * H_I + h) * RB + g * Tr::kLaneBytes);
+      for (int v = 0; v < kVec; ++v) a[ht][v] = src[v];
+    }
 #pragma unroll
-        for (int v = 0; v < kVec; ++v) a[tt][ht][v] = src[v];
+    for (int i = 0; i < 4; ++i) {
+      const int hh = ht * 16 + g * 4 + i;
+      float wv = 0.f;
+      if (tok_ok && hh < H_I) {
+        wv = w[row * H_I + hh];
+        if (DTYPE == 2) wv *= qi_scale[row * H_I + hh];
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hh = ht * 16 + g * 4 + i;
-        float wv = 0.f;
-        if (tok_ok && hh < H_I) {
-          wv = w[row * H_I + hh];
-          if (DTYPE == 2) wv *= qi_scale[row * H_I + hh];
-        }
-        wq[tt][ht][i] = wv;
-      }
+      wq[ht][i] = wv;
     }
   }
 
   const uint8_t* kib = ki + b * n_cap * RB;
   const int ntiles = static_cast<int>((V_max + kPfTile - 1) / kPfTile);
   u32x4 breg[kLoads];
-  auto load_tile = [&](int tile) {
+  auto load_tile = [&](int tile) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < kLoads; ++r) {
-      const int id = tid + kThreads * r;
+      const int id = tid + kPfThreads * r;
       const int ent = id / (RB / 16);
       const int pc = id - ent * (RB / 16);
       int64_t e = static_cast<int64_t>(tile) * kPfTile + ent;
@@ -343,90 +349,101 @@ __global__ __launch_bounds__(64 * kPfTok / TPW) void indexer_prefill_kernel(
       breg[r] = *reinterpret_cast<const u32x4*>(kib + e * RB + pc * 16);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](auto buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < kLoads; ++r) {
-      const int id = tid + kThreads * r;
+      const int id = tid + kPfThreads * r;
       const int ent = id / (RB / 16);
       const int pc = id - ent * (RB / 16);
-      *reinterpret_cast<u32x4*>(&bt[buf][ent * kStride + pc * 16]) = breg[r];
+      *reinterpret_cast<u32x4*>(&bt[decltype(buf)::value][ent * kStride + pc * 16]) = breg[r];
     }
   };
-
-  load_tile(0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    store_tile(buf);
-    __syncthreads();
-    load_tile(tile + 1 < ntiles ? tile + 1 : tile);
-    f32x4 acc[TPW][4][4];  // [token][head tile][column tile]
+  // One column tile (16 entries) at a time: its 4 x kSteps MFMAs go into
+  // one of two accumulator sets while the other set's epilogue runs.
+  using Acc = f32x4[4];  // [head tile]
+  auto mfma_ct = [&](auto buf, int ct, Acc& acc) __attribute__((always_inline)) {
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[tt][ht][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint8_t* bb = &bt[buf][0];
+    for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint8_t* src = &bt[decltype(buf)::value][(ct * 16 + col) * kStride + g * Tr::kLaneBytes];
 #pragma unroll
     for (int st = 0; st < Tr::kSteps; ++st) {
-      u32x4 bf[4][kVec / Tr::kSteps > 0 ? kVec / Tr::kSteps : 1];
+      u32x4 bf[kVec / Tr::kSteps > 0 ? kVec / Tr::kSteps : 1];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const uint8_t* src = bb + (ct * 16 + col) * kStride + g * Tr::kLaneBytes;
+      for (int v = 0; v < kVec / Tr::kSteps; ++v)
+        bf[v] = *reinterpret_cast<const u32x4*>(src + (st * (kVec / Tr::kSteps) + v) * 16);
 #pragma unroll
-        for (int v = 0; v < kVec / Tr::kSteps; ++v)
-          bf[ct][v] = *reinterpret_cast<const u32x4*>(src + (st * (kVec / Tr::kSteps) + v) * 16);
-      }
-#pragma unroll
-      for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct) {
-            if (DTYPE == 1) {
-              acc[tt][ht][ct] = mma_bf16(__builtin_bit_cast(bf16x8, a[tt][ht][st]),
-                                         __builtin_bit_cast(bf16x8, bf[ct][0]), acc[tt][ht][ct]);
-            } else {
-              i32x8 av, bv;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                av[i] = static_cast<int>(a[tt][ht][0][i]);
-                av[4 + i] = static_cast<int>(a[tt][ht][1][i]);
-                bv[i] = static_cast<int>(bf[ct][0][i]);
-                bv[4 + i] = static_cast<int>(bf[ct][1][i]);
-              }
-              acc[tt][ht][ct] = mma_fp8(av, bv, acc[tt][ht][ct]);
-            }
-          }
-    }
-    // epilogue: per token and column tile, sum_h w_h phi(acc)
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-      float v[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        float x = 0.f;
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht)
+      for (int ht = 0; ht < 4; ++ht) {
+        if (DTYPE == 1) {
+          acc[ht] = mma_bf16(__builtin_bit_cast(bf16x8, a[ht][st]), __builtin_bit_cast(bf16x8, bf[0]),
+                             acc[ht]);
+        } else {
+          i32x8 av, bv;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float y = RELU ? fmaxf(acc[tt][ht][ct][i], 0.f) : acc[tt][ht][ct][i];
-            x = fmaf(wq[tt][ht][i], y, x);
+            av[i] = static_cast<int>(a[ht][0][i]);
+            av[4 + i] = static_cast<int>(a[ht][1][i]);
+            bv[i] = static_cast<int>(bf[0][i]);
+            bv[4 + i] = static_cast<int>(bf[1][i]);
           }
-        x += __shfl_xor(x, 16);
-        x += __shfl_xor(x, 32);
-        v[ct] = x;
-      }
-      // lane group g writes column tile g: 64 consecutive scores per token
-      const float mine = g == 0 ? v[0] : g == 1 ? v[1] : g == 2 ? v[2] : v[3];
-      const int64_t e = static_cast<int64_t>(tile) * kPfTile + g * 16 + col;
-      if (e < Vt[tt]) {
-        float out = mine;
-        if (DTYPE == 2) out *= ki_scale[b * n_cap + e];
-        scores[srow_off[tt] + e] = out;
+          acc[ht] = mma_fp8(av, bv, acc[ht]);
+        }
       }
     }
+  };
+  // sum_h w_h phi(acc) for one column tile (all 64 heads: in lane, then two
+  // lane swaps, after which every lane group holds the 16 column sums);
+  // lane group ct % 4 stores them (the other lanes' offsets are out of the
+  // descriptor's range, so their stores are dropped)
+  auto epi_ct = [&](int tile, int ct, const Acc& acc) __attribute__((always_inline)) {
+    float x = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float y = RELU ? fmaxf(acc[ht][i], 0.f) : acc[ht][i];
+        x = fmaf(wq[ht][i], y, x);
+      }
+    x = sum_xor32(sum_xor16(x));
+    const int e = tile * kPfTile + ct * 16 + col;
+    if (DTYPE == 2) x *= ki_scale[b * n_cap + (e < V_max ? e : V_max - 1)];
+    const uint32_t off = g == (ct & 3) ? static_cast<uint32_t>(e) * 4u : 0x80000000u;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), srsrc, off, 0, 0);
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  Acc acc0, acc1;
+  // Tile t: stage it, then its column tiles alternate acc0 / acc1; the
+  // epilogue of each column tile runs under the next one's MFMAs (the last
+  // column tile's under the next tile's first).
+  static_assert(kPfCt % 2 == 0, "column tiles alternate two accumulator sets");
+  auto do_tile = [&](auto buf, int t) __attribute__((always_inline)) {
+    store_tile(buf);
+    __syncthreads();
+    load_tile(t + 1 < ntiles ? t + 1 : t);
+    mfma_ct(buf, 0, acc0);
+    if (t > 0) epi_ct(t - 1, kPfCt - 1, acc1);
+#pragma unroll
+    for (int ct = 1; ct < kPfCt; ct += 2) {
+      mfma_ct(buf, ct, acc1);
+      epi_ct(t, ct - 1, acc0);
+      if (ct + 1 < kPfCt) {
+        mfma_ct(buf, ct + 1, acc0);
+        epi_ct(t, ct, acc1);
+      }
+    }
+  };
+  load_tile(0);
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    do_tile(I0{}, t);
+    do_tile(I1{}, t + 1);
   }
+  if (t < ntiles) {
+    do_tile(I0{}, t);
+    ++t;
+  }
+  epi_ct(t - 1, kPfCt - 1, acc1);
 }
 
 template <int DTYPE, int DI>
@@ -441,15 +458,16 @@ static void launch_idx_t(const void* qi, const float* qs, const float* w, const 
             static_cast<unsigned>(B * T));
   auto q8 = static_cast<const uint8_t*>(qi);
   auto k8 = static_cast<const uint8_t*>(ki);
-  if ((DTYPE == 1 || DTYPE == 2) && DI == 128 && T >= kPfTok && hist == nullptr) {
+  if ((DTYPE == 1 || DTYPE == 2) && DI == 128 && T >= kPfTok && hist == nullptr &&
+      n_cap <= kPfMaxEntries) {
     constexpr int DT = DTYPE == 2 ? 2 : 1;
     dim3 pgrid(static_cast<unsigned>((T + kPfTok - 1) / kPfTok), static_cast<unsigned>(B));
     if (relu)
-      indexer_prefill_kernel<DT, true, kPfTokPerWave><<<pgrid, 64 * kPfTok / kPfTokPerWave, 0, s>>>(
-          q8, qs, w, k8, ks, pos0, T, H_I, n_cap, m, scores);
+      indexer_prefill_kernel<DT, true><<<pgrid, kPfThreads, 0, s>>>(q8, qs, w, k8, ks, pos0, T,
+                                                                    H_I, n_cap, m, scores);
     else
-      indexer_prefill_kernel<DT, false, kPfTokPerWave><<<pgrid, 64 * kPfTok / kPfTokPerWave, 0, s>>>(
-          q8, qs, w, k8, ks, pos0, T, H_I, n_cap, m, scores);
+      indexer_prefill_kernel<DT, false><<<pgrid, kPfThreads, 0, s>>>(q8, qs, w, k8, ks, pos0, T,
+                                                                     H_I, n_cap, m, scores);
     return;
   }
 #define CSA_IDX_GO(R, HST)                                                                 \

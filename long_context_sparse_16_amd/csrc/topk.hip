@@ -371,34 +371,43 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
   const uint32_t b1 = sm.misc[0];
   const uint32_t above = sm.misc[1];
   if (REGS > 0) {
-    // count, one packed prefix sum, then write at the thread's positions.
-    // Packing: sure entries in the low 12 bits (fewer than k <= 4096 in the
-    // whole row), candidates above them (at most V <= 32768).
+#pragma unroll
+    for (int u = 0; u < REGS; ++u)
+      if (tid + static_cast<int64_t>(u) * kRowThreads >= V) rv[u] = -INFINITY;
+    // The bucket test runs on the floats: bucket(v) > b1 iff v >= hi and
+    // bucket(v) == b1 iff lo <= v < hi, with lo / hi the smallest floats of
+    // buckets b1 and b1 + 1 (finite scores keep b1 in 8 .. 0xff7, so both
+    // are proper floats).  Slots past V hold -inf, below every bucket of a
+    // finite score.  Count, one packed prefix sum, then write at the
+    // thread's positions; only hits compute their key.  Packing: sure
+    // entries in the low 12 bits (fewer than k <= 4096 in the whole row),
+    // candidates above them (at most V <= 32768).
+    const float lo = key_floor_float(b1 << kTopkDigit1Shift);
+    const float hi = key_floor_float((b1 + 1u) << kTopkDigit1Shift);
     uint32_t ns = 0, nc = 0;
 #pragma unroll
     for (int u = 0; u < REGS; ++u) {
-      const int64_t j = tid + static_cast<int64_t>(u) * kRowThreads;
-      const uint32_t bk = score_key(rv[u]) >> kTopkDigit1Shift;
-      ns += (j < V && bk > b1) ? 1u : 0u;
-      nc += (j < V && bk == b1) ? 1u : 0u;
+      ns += rv[u] >= hi ? 1u : 0u;
+      nc += rv[u] >= lo ? 1u : 0u;
     }
+    nc -= ns;
     const uint32_t packed = block_excl_scan<kRowThreads>(ns | (nc << 12), sm.scan);
     uint32_t ps = packed & 0xfffu, pcand = packed >> 12;
     if (tid == kRowThreads - 1) sm.misc[5] = pcand + nc;  // total candidates
 #pragma unroll
     for (int u = 0; u < REGS; ++u) {
-      const int64_t j = tid + static_cast<int64_t>(u) * kRowThreads;
-      const uint32_t key = score_key(rv[u]);
-      const uint32_t bk = key >> kTopkDigit1Shift;
-      if (j < V && bk > b1) {
-        if (ps < static_cast<uint32_t>(kMaxK)) sm.sel[ps] = static_cast<int32_t>(j);
-        ++ps;
-      } else if (j < V && bk == b1) {
-        if (pcand < static_cast<uint32_t>(kCandCap)) {
-          sm.ckey[pcand] = key;
-          sm.cidx[pcand] = static_cast<int32_t>(j);
+      if (rv[u] >= lo) {
+        const int32_t j = tid + u * kRowThreads;
+        if (rv[u] >= hi) {
+          if (ps < static_cast<uint32_t>(kMaxK)) sm.sel[ps] = j;
+          ++ps;
+        } else {
+          if (pcand < static_cast<uint32_t>(kCandCap)) {
+            sm.ckey[pcand] = score_key(rv[u]);
+            sm.cidx[pcand] = j;
+          }
+          ++pcand;
         }
-        ++pcand;
       }
     }
     if (tid == kRowThreads - 1) sm.misc[4] = ps;  // sure entries (== above)
