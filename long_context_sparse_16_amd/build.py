@@ -22,6 +22,13 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libcsa.so")
 
 SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "topk.hip", "attend.hip"]
+# Per-source additions.  The indexer's epilogue is pure VALU work next to
+# the MFMAs: with IEEE mode off (its inputs never hold NaN) a ReLU is one
+# v_max_f32 instead of a canonicalize plus max, and the VGPR form of MFMA
+# keeps the accumulators out of AGPRs, saving one copy per value.
+SOURCE_FLAGS = {
+    "indexer.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 HEADERS = ["common.h", "kernels.h"]
 
 ARCH = "gfx950"
@@ -47,7 +54,7 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

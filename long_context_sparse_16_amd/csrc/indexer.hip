@@ -17,6 +17,7 @@
 // takes elements [g*d_I/4, (g+1)*d_I/4)), so one entry row is read by four
 // lanes as 16-byte vector loads.  The same k assignment is used for the A
 // operand, which is all the MFMA needs (see common.h).
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -70,15 +71,27 @@ struct IdxTraits<2, DI> {  // fp8 e4m3, v_mfma_f32_16x16x128_f8f6f4
   }
 };
 
+// Raw buffer descriptor word 3 for gfx9-family targets (32-bit data format).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 constexpr int kIdxWaves = 4;
-constexpr int kIdxTile = 16;  // entries per MFMA column tile
-constexpr int kIdxMaxTilesPerWg = 128;  // 2048 entries per workgroup
+constexpr int kIdxTile = 16;        // entries per MFMA column tile
+constexpr int kIdxGroupLoads = 8;   // 16-byte key loads per lane per group
+
+// Tiles per load group: 8 KiB of keys per wave.
+template <int DTYPE, int DI>
+constexpr int idx_group_tiles() {
+  return kIdxGroupLoads / (IdxTraits<DTYPE, DI>::kLaneBytes / 16) > 0
+             ? kIdxGroupLoads / (IdxTraits<DTYPE, DI>::kLaneBytes / 16)
+             : 1;
+}
 
 // grid: x = entry chunk, y = query row (b * T + i).  block: 4 waves.
-// The chunk's tiles are taken in groups of kGroup tiles (12 KiB of keys per
-// wave); wave w handles groups w, w+4, ...  While one group is multiplied,
-// the next group's loads are already in flight (two register buffers,
-// statically indexed so they stay in VGPRs).
+// The chunk's tiles are taken in groups of kGroup tiles; wave w handles
+// groups w, w+4, ...  While one group is multiplied, the next group's loads
+// are already in flight (two register buffers, statically indexed so they
+// stay in VGPRs).  The host sizes the chunks so that the grid is about one
+// workgroup per compute unit.
 template <int DTYPE, int DI, bool RELU, bool HIST>
 __global__ __launch_bounds__(256) void indexer_kernel(
     const uint8_t* __restrict__ qi, const float* __restrict__ qi_scale,
@@ -89,12 +102,11 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   using Tr = IdxTraits<DTYPE, DI>;
   constexpr int kVec = Tr::kLaneBytes / 16;  // 16-byte loads per lane per row
   constexpr int kRowBytes = DI * Tr::kElemBytes;
-  constexpr int kGroup = 12 / kVec > 0 ? 12 / kVec : 1;  // tiles per group: 12 loads per lane
+  constexpr int kGroup = idx_group_tiles<DTYPE, DI>();
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int col = lane & 15;
   const int g = lane >> 4;
-  __shared__ float s_scores[kIdxMaxTilesPerWg * kIdxTile];
   __shared__ uint32_t s_hist[HIST ? kTopkHistBins : 1];
   const int64_t row = blockIdx.y;
   const int64_t b = row / T;
@@ -156,16 +168,20 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const uint8_t* kwg = kib + e_begin * kRowBytes;          // wave-uniform
   const uint32_t lane_off = static_cast<uint32_t>(col * kRowBytes + g * Tr::kLaneBytes);
 
-  auto load_full = [&](int grp, u32x4 (&dst)[kGroup][kVec]) {
+  // FP8: each lane also fetches the key scale of its column's entry, with
+  // the group's keys
+  const float* ksc = DTYPE == 2 ? ki_scale + b * n_cap + e_begin : nullptr;
+  auto load_full = [&](int grp, u32x4 (&dst)[kGroup][kVec], float (&kd)[kGroup]) {
     const uint8_t* gb = kwg + static_cast<int64_t>(grp) * (kGroupEnt * kRowBytes);
 #pragma unroll
     for (int tt = 0; tt < kGroup; ++tt) {
       const u32x4* src = reinterpret_cast<const u32x4*>(gb + tt * (kIdxTile * kRowBytes) + lane_off);
 #pragma unroll
       for (int v = 0; v < kVec; ++v) dst[tt][v] = src[v];
+      if (DTYPE == 2) kd[tt] = ksc[grp * kGroupEnt + tt * kIdxTile + col];
     }
   };
-  auto load_tail = [&](int grp, u32x4 (&dst)[kGroup][kVec]) {
+  auto load_tail = [&](int grp, u32x4 (&dst)[kGroup][kVec], float (&kd)[kGroup]) {
 #pragma unroll
     for (int tt = 0; tt < kGroup; ++tt) {
       int e = (grp * kGroup + tt) * kIdxTile + col;
@@ -174,10 +190,19 @@ __global__ __launch_bounds__(256) void indexer_kernel(
           kwg + static_cast<uint32_t>(e) * kRowBytes + g * Tr::kLaneBytes);
 #pragma unroll
       for (int v = 0; v < kVec; ++v) dst[tt][v] = src[v];
+      if (DTYPE == 2) kd[tt] = ksc[e];
     }
   };
 
-  auto compute_group = [&](int grp, const u32x4 (&bt)[kGroup][kVec]) {
+  // Scores go straight out, one 16-entry tile at a time from lane group 0,
+  // through a buffer descriptor whose range is this workgroup's entries (so
+  // past-the-end columns are dropped by the range check), and with HIST the
+  // first-digit histogram of the top-k selection is accumulated in LDS on
+  // the way (rows that keep every visible entry need none).
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+      srow + e_begin, 0, n_ent_wg * 4, kBufferRsrcWord3);
+  const bool do_hist = HIST && V > topk_k;
+  auto compute_group = [&](int grp, const u32x4 (&bt)[kGroup][kVec], const float (&kd)[kGroup]) {
 #pragma unroll
     for (int tt = 0; tt < kGroup; ++tt) {
       f32x4 acc[4];
@@ -198,44 +223,40 @@ __global__ __launch_bounds__(256) void indexer_kernel(
         }
       }
       v = sum_xor32(sum_xor16(v));
-      if (lane < 16) s_scores[(grp * kGroup + tt) * kIdxTile + col] = v;
+      if (DTYPE == 2) v *= kd[tt];
+      const int e = (grp * kGroup + tt) * kIdxTile + col;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srsrc,
+                                            g == 0 ? static_cast<uint32_t>(e) * 4u : 0x80000000u,
+                                            0, 0);
+      if (HIST && do_hist && g == 0 && e < n_ent_wg)
+        atomicAdd(&s_hist[score_key(v) >> kTopkDigit1Shift], 1u);
     }
   };
 
+  if (do_hist) {
+    for (int i = threadIdx.x; i < kTopkHistBins; i += 256) s_hist[i] = 0u;
+    __syncthreads();
+  }
   u32x4 buf0[kGroup][kVec], buf1[kGroup][kVec];
+  float ks0[kGroup], ks1[kGroup];
   int grp = wave;
   if (grp < n_full) {
     const int last = n_full - 1 - ((n_full - 1 - wave) & (kIdxWaves - 1));  // this wave's last
-    load_full(grp, buf0);
+    load_full(grp, buf0, ks0);
     while (true) {
-      load_full(grp + kIdxWaves <= last ? grp + kIdxWaves : last, buf1);
-      compute_group(grp, buf0);
+      load_full(grp + kIdxWaves <= last ? grp + kIdxWaves : last, buf1, ks1);
+      compute_group(grp, buf0, ks0);
       grp += kIdxWaves;
       if (grp > last) break;
-      load_full(grp + kIdxWaves <= last ? grp + kIdxWaves : last, buf0);
-      compute_group(grp, buf1);
+      load_full(grp + kIdxWaves <= last ? grp + kIdxWaves : last, buf0, ks0);
+      compute_group(grp, buf1, ks1);
       grp += kIdxWaves;
       if (grp > last) break;
     }
   }
   if (n_full < n_grp && (n_full & (kIdxWaves - 1)) == wave) {
-    load_tail(n_full, buf0);
-    compute_group(n_full, buf0);
-  }
-  // Scores were staged in LDS; write this workgroup's slice out coalesced
-  // (and apply the per-entry key scale of the FP8 path here).  With HIST,
-  // the first-digit histogram of the top-k selection is accumulated on the
-  // way (rows that keep every visible entry need none).
-  const bool do_hist = HIST && V > topk_k;
-  if (do_hist)
-    for (int i = threadIdx.x; i < kTopkHistBins; i += 256) s_hist[i] = 0u;
-  __syncthreads();
-  float* dst = srow + e_begin;
-  for (int i = threadIdx.x; i < n_ent_wg; i += 256) {
-    float v = s_scores[i];
-    if (DTYPE == 2) v *= ki_scale[b * n_cap + e_begin + i];
-    dst[i] = v;
-    if (do_hist) atomicAdd(&s_hist[score_key(v) >> kTopkDigit1Shift], 1u);
+    load_tail(n_full, buf0, ks0);
+    compute_group(n_full, buf0, ks0);
   }
   if (do_hist) {
     __syncthreads();
@@ -273,9 +294,6 @@ constexpr int kPfCt = kPfTile / 16;   // column tiles per LDS tile
 constexpr int kPfThreads = 64 * kPfTok;
 // Score rows of the prefill path are addressed with 32-bit byte offsets.
 constexpr int64_t kPfMaxEntries = int64_t(1) << 28;
-
-// Raw buffer descriptor word 3 for gfx9-family targets (32-bit data format).
-constexpr int kBufferRsrcWord3 = 0x00020000;
 
 template <int DTYPE, bool RELU>
 __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
@@ -446,14 +464,36 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
   epi_ct(t - 1, kPfCt - 1, acc1);
 }
 
+// Compute units of the current device (cached per device).
+static int device_cu_count() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int DTYPE, int DI>
 static void launch_idx_t(const void* qi, const float* qs, const float* w, const void* ki,
                          const float* ks, const int64_t* pos0, int64_t B, int64_t T, int H_I,
                          int64_t n_cap, int m, bool relu, float* scores, uint32_t* hist, int k,
                          hipStream_t s) {
-  // 2048 entries per workgroup (32 tiles per wave) unless the cache is small.
+  // Chunk size: about one workgroup per compute unit over the whole grid
+  // (measured best for this streaming kernel), in whole rounds of load
+  // groups for the 4 waves, and no more than a row.
   const int64_t tiles = (n_cap + kIdxTile - 1) / kIdxTile;
-  const int tiles_per_wg = static_cast<int>(tiles < kIdxMaxTilesPerWg ? tiles : kIdxMaxTilesPerWg);
+  constexpr int64_t kRound = static_cast<int64_t>(idx_group_tiles<DTYPE, DI>()) * kIdxWaves;
+  int64_t tpw = (B * T * tiles + device_cu_count() - 1) / device_cu_count();
+  tpw = (tpw + kRound - 1) / kRound * kRound;
+  if (tpw > tiles) tpw = tiles;
+  // (the workgroup's score range is a 32-bit byte count)
+  if (tpw > (int64_t(1) << 24)) tpw = int64_t(1) << 24;
+  const int tiles_per_wg = static_cast<int>(tpw);
   dim3 grid(static_cast<unsigned>((tiles + tiles_per_wg - 1) / tiles_per_wg),
             static_cast<unsigned>(B * T));
   auto q8 = static_cast<const uint8_t*>(qi);
