@@ -27,7 +27,7 @@ SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "topk.hip", "attend.hip"]
 # v_max_f32 instead of a canonicalize plus max, and the VGPR form of MFMA
 # keeps the accumulators out of AGPRs, saving one copy per value.
 SOURCE_FLAGS = {
-    "indexer.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 HEADERS = ["common.h", "kernels.h"]
 

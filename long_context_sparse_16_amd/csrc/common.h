@@ -88,6 +88,29 @@ __device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
   return static_cast<uint8_t>(sign | mag);
 }
 
+// max(x, 0) for finite x as one integer max on the bit pattern: negative
+// floats (and -0.0) have the sign bit set, so they compare below integer 0
+// and become +0.0; non-negative floats are unchanged.
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// ----------------------------------------------------- range-checked stores
+
+// Raw buffer descriptor over [base, base + nbytes): stores at byte offsets
+// >= nbytes are dropped by the hardware range check.  The caller passes
+// wave-uniform values; they are moved to scalar registers explicitly so the
+// descriptor is never treated as per-lane (a per-lane descriptor makes every
+// store a loop over the distinct descriptors of the wave).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_rsrc(const void* base, int nbytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+  void* up = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(up, 0, __builtin_amdgcn_readfirstlane(nbytes),
+                                           0x00020000);
+}
+
 // ------------------------------------------------------- order-preserving key
 
 // Map a finite float to a uint32 whose unsigned order is the float order;
@@ -139,6 +162,14 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
 // 16x16x128 FP8 (E4M3 x E4M3), fp32 accumulate, unit block scales.
 __device__ __forceinline__ f32x4 mma_fp8(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// A wave-uniform 64-bit value moved to scalar registers (so loop bounds and
+// addresses derived from it stay scalar).
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 __device__ __forceinline__ int64_t visible_entries(int64_t t, int m, int64_t n_cap) {

@@ -71,8 +71,54 @@ struct IdxTraits<2, DI> {  // fp8 e4m3, v_mfma_f32_16x16x128_f8f6f4
   }
 };
 
-// Raw buffer descriptor word 3 for gfx9-family targets (32-bit data format).
-constexpr int kBufferRsrcWord3 = 0x00020000;
+// A fragments (4 tiles of 16 query heads, this lane's quarter of each head
+// row) and per-head weights (times the query scale for fp8) of query row
+// `row`.  issue() starts every load unconditionally from clamped addresses
+// (heads >= H_I read head H_I - 1), so they are in flight together;
+// finish() then zeroes the weights of heads >= H_I, and of every head when
+// !ok, which removes those heads from the score (their A rows need no
+// masking).  Callers put their first key loads between the two.
+template <int DTYPE, int DI>
+struct QueryFrags {
+  using Tr = IdxTraits<DTYPE, DI>;
+  static constexpr int kVec = Tr::kLaneBytes / 16;
+  static constexpr int kRowBytes = DI * Tr::kElemBytes;
+  u32x4 a[4][kVec];
+  float wq[4][4];
+  float ws[4][4];
+
+  __device__ __forceinline__ void issue(const uint8_t* __restrict__ qi,
+                                        const float* __restrict__ qi_scale,
+                                        const float* __restrict__ w, int64_t row, int H_I,
+                                        int col, int g) {
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      const int h = ht * 16 + col;
+      const u32x4* src = reinterpret_cast<const u32x4*>(
+          qi + (row * H_I + (h < H_I ? h : H_I - 1)) * kRowBytes + g * Tr::kLaneBytes);
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) a[ht][v] = src[v];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = ht * 16 + g * 4 + i;
+        const int64_t off = row * H_I + (hh < H_I ? hh : H_I - 1);
+        wq[ht][i] = w[off];
+        ws[ht][i] = DTYPE == 2 ? qi_scale[off] : 1.f;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void finish(int H_I, bool ok, int g) {
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool live = ok && ht * 16 + g * 4 + i < H_I;
+        wq[ht][i] = live ? (DTYPE == 2 ? wq[ht][i] * ws[ht][i] : wq[ht][i]) : 0.f;
+      }
+    }
+  }
+};
 
 constexpr int kIdxWaves = 4;
 constexpr int kIdxTile = 16;        // entries per MFMA column tile
@@ -109,41 +155,22 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const int g = lane >> 4;
   __shared__ uint32_t s_hist[HIST ? kTopkHistBins : 1];
   const int64_t row = blockIdx.y;
-  const int64_t b = row / T;
+  // A operand: 4 head tiles of 16 query heads, kept in registers (issued
+  // first: it does not depend on the row's position).
+  QueryFrags<DTYPE, DI> qf;
+  qf.issue(qi, qi_scale, w, row, H_I, col, g);
+  const auto& a = qf.a;
+  const auto& wq = qf.wq;
+
+  // (rows = B * T is a grid dimension, so 32-bit arithmetic is exact; the
+  // sequence index is wave-uniform, so pos0 comes through the scalar cache)
+  const int64_t b = __builtin_amdgcn_readfirstlane(
+      static_cast<int>(static_cast<uint32_t>(row) / static_cast<uint32_t>(T)));
   const int64_t t = pos0[b] + (row - b * T);
-  const int64_t V = visible_entries(t, m, n_cap);
+  const int64_t V = uniform64(visible_entries(t, m, n_cap));
   const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * tiles_per_wg;
   const int64_t e_begin = tile0 * kIdxTile;
   if (e_begin >= V) return;
-  const int64_t ntiles = min(static_cast<int64_t>(tiles_per_wg), (V - e_begin + kIdxTile - 1) / kIdxTile);
-  const int64_t ngroups = (ntiles + kGroup - 1) / kGroup;
-
-  // A operand: 4 head tiles of 16 query heads, kept in registers.
-  u32x4 a[4][kVec];
-  float wq[4][4];
-  const int n_ht = (H_I + 15) >> 4;
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-    const int h = ht * 16 + col;
-#pragma unroll
-    for (int v = 0; v < kVec; ++v) a[ht][v] = u32x4{0u, 0u, 0u, 0u};
-    if (ht < n_ht && h < H_I) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(
-          qi + (row * H_I + h) * kRowBytes + g * Tr::kLaneBytes);
-#pragma unroll
-      for (int v = 0; v < kVec; ++v) a[ht][v] = src[v];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = ht * 16 + g * 4 + i;
-      float wv = 0.f;
-      if (hh < H_I) {
-        wv = w[row * H_I + hh];
-        if (DTYPE == 2) wv *= qi_scale[row * H_I + hh];
-      }
-      wq[ht][i] = wv;
-    }
-  }
 
   const uint8_t* kib = ki + b * n_cap * kRowBytes;
   float* srow = scores + row * n_cap;
@@ -199,8 +226,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   // past-the-end columns are dropped by the range check), and with HIST the
   // first-digit histogram of the top-k selection is accumulated in LDS on
   // the way (rows that keep every visible entry need none).
-  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
-      srow + e_begin, 0, n_ent_wg * 4, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t srsrc = store_rsrc(srow + e_begin, n_ent_wg * 4);
   const bool do_hist = HIST && V > topk_k;
   auto compute_group = [&](int grp, const u32x4 (&bt)[kGroup][kVec], const float (&kd)[kGroup]) {
 #pragma unroll
@@ -218,7 +244,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       for (int ht = 0; ht < 4; ++ht) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float x = RELU ? fmaxf(acc[ht][i], 0.f) : acc[ht][i];
+          const float x = RELU ? relu(acc[ht][i]) : acc[ht][i];
           v = fmaf(wq[ht][i], x, v);
         }
       }
@@ -239,21 +265,23 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   }
   u32x4 buf0[kGroup][kVec], buf1[kGroup][kVec];
   float ks0[kGroup], ks1[kGroup];
-  int grp = wave;
-  if (grp < n_full) {
-    const int last = n_full - 1 - ((n_full - 1 - wave) & (kIdxWaves - 1));  // this wave's last
-    load_full(grp, buf0, ks0);
-    while (true) {
-      load_full(grp + kIdxWaves <= last ? grp + kIdxWaves : last, buf1, ks1);
-      compute_group(grp, buf0, ks0);
-      grp += kIdxWaves;
-      if (grp > last) break;
-      load_full(grp + kIdxWaves <= last ? grp + kIdxWaves : last, buf0, ks0);
-      compute_group(grp, buf1, ks1);
-      grp += kIdxWaves;
-      if (grp > last) break;
-    }
+  // This wave's full groups are wave, wave + 4, ...: n_my of them, taken in
+  // pairs (one per buffer) with a single trailing group when n_my is odd.
+  // Every loop iteration runs both halves, so the body is straight-line.
+  const int n_my = wave < n_full ? (n_full - 1 - wave) / kIdxWaves + 1 : 0;
+  // (first group through clamped addresses, unconditionally, so the wait
+  // for the query loads below leaves it in flight; same data when full)
+  load_tail(wave, buf0, ks0);
+  qf.finish(H_I, true, g);
+  int j = 0;
+  for (; j + 2 <= n_my; j += 2) {
+    load_full(wave + (j + 1) * kIdxWaves, buf1, ks1);
+    compute_group(wave + j * kIdxWaves, buf0, ks0);
+    // (past the end this re-reads this wave's last group, from cache)
+    load_full(wave + min(j + 2, n_my - 1) * kIdxWaves, buf0, ks0);
+    compute_group(wave + (j + 1) * kIdxWaves, buf1, ks1);
   }
+  if (j < n_my) compute_group(wave + j * kIdxWaves, buf0, ks0);
   if (n_full < n_grp && (n_full & (kIdxWaves - 1)) == wave) {
     load_tail(n_full, buf0, ks0);
     compute_group(n_full, buf0, ks0);
@@ -308,6 +336,7 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
   constexpr int kStride = RB + 16;                    // padded LDS row
   constexpr int kLoads = kPfTile * RB / 16 / kPfThreads;  // 16-byte loads per thread per tile
   __shared__ __attribute__((aligned(16))) uint8_t bt[2][kPfTile * kStride];
+  __shared__ float s_ksc[2][DTYPE == 2 ? kPfTile : 1];  // fp8 key scales of the staged tiles
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -318,44 +347,24 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
   const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * kPfTok;
   const int64_t tok_last = min(tok0 + kPfTok, T) - 1;
   const int64_t p0 = pos0[b];
-  const int64_t V_max = visible_entries(p0 + tok_last, m, n_cap);
+  const int64_t V_max = uniform64(visible_entries(p0 + tok_last, m, n_cap));
   if (V_max <= 0) return;
 
   // this wave's token: A fragments, head weights, score-row descriptor
   const int64_t tok = tok0 + wave;
   const bool tok_ok = tok < T;
   const int64_t row = b * T + (tok_ok ? tok : 0);
-  const int64_t Vt = tok_ok ? visible_entries(p0 + tok, m, n_cap) : 0;
-  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
-      scores + row * n_cap, 0, static_cast<int>(Vt * 4), kBufferRsrcWord3);
-  u32x4 a[4][kVec];
-  float wq[4][4];
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-    const int h = ht * 16 + col;
-#pragma unroll
-    for (int v = 0; v < kVec; ++v) a[ht][v] = u32x4{0u, 0u, 0u, 0u};
-    if (tok_ok && h < H_I) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(
-          qi + (row * H_I + h) * RB + g * Tr::kLaneBytes);
-#pragma unroll
-      for (int v = 0; v < kVec; ++v) a[ht][v] = src[v];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = ht * 16 + g * 4 + i;
-      float wv = 0.f;
-      if (tok_ok && hh < H_I) {
-        wv = w[row * H_I + hh];
-        if (DTYPE == 2) wv *= qi_scale[row * H_I + hh];
-      }
-      wq[ht][i] = wv;
-    }
-  }
+  const int64_t Vt = uniform64(tok_ok ? visible_entries(p0 + tok, m, n_cap) : 0);
+  const __amdgpu_buffer_rsrc_t srsrc = store_rsrc(scores + row * n_cap, static_cast<int>(Vt * 4));
+  QueryFrags<DTYPE, DI> qf;
+  qf.issue(qi, qi_scale, w, row, H_I, col, g);
+  const auto& a = qf.a;
+  const auto& wq = qf.wq;
 
   const uint8_t* kib = ki + b * n_cap * RB;
   const int ntiles = static_cast<int>((V_max + kPfTile - 1) / kPfTile);
   u32x4 breg[kLoads];
+  float kreg = 0.f;  // fp8: one key scale per thread (threads < kPfTile)
   auto load_tile = [&](int tile) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < kLoads; ++r) {
@@ -366,6 +375,10 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
       e = e < V_max ? e : V_max - 1;
       breg[r] = *reinterpret_cast<const u32x4*>(kib + e * RB + pc * 16);
     }
+    if (DTYPE == 2) {
+      int64_t e = static_cast<int64_t>(tile) * kPfTile + (tid & (kPfTile - 1));
+      kreg = ki_scale[b * n_cap + (e < V_max ? e : V_max - 1)];
+    }
   };
   auto store_tile = [&](auto buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -375,6 +388,7 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
       const int pc = id - ent * (RB / 16);
       *reinterpret_cast<u32x4*>(&bt[decltype(buf)::value][ent * kStride + pc * 16]) = breg[r];
     }
+    if (DTYPE == 2 && tid < kPfTile) s_ksc[decltype(buf)::value][tid] = kreg;
   };
   // One column tile (16 entries) at a time: its 4 x kSteps MFMAs go into
   // one of two accumulator sets while the other set's epilogue runs.
@@ -418,12 +432,12 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float y = RELU ? fmaxf(acc[ht][i], 0.f) : acc[ht][i];
+        const float y = RELU ? relu(acc[ht][i]) : acc[ht][i];
         x = fmaf(wq[ht][i], y, x);
       }
     x = sum_xor32(sum_xor16(x));
     const int e = tile * kPfTile + ct * 16 + col;
-    if (DTYPE == 2) x *= ki_scale[b * n_cap + (e < V_max ? e : V_max - 1)];
+    if (DTYPE == 2) x *= s_ksc[tile & 1][ct * 16 + col];
     const uint32_t off = g == (ct & 3) ? static_cast<uint32_t>(e) * 4u : 0x80000000u;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), srsrc, off, 0, 0);
   };
@@ -452,6 +466,7 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
     }
   };
   load_tile(0);
+  qf.finish(H_I, tok_ok, g);
   int t = 0;
   for (; t + 1 < ntiles; t += 2) {
     do_tile(I0{}, t);
