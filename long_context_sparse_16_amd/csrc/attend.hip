@@ -107,12 +107,13 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
   const int g = lane >> 4;
   const int64_t row = blockIdx.y;
   const int split = blockIdx.x;
-  const int64_t b = row / p.T;
+  const int64_t b = seq_of_row(row, p.T);
   // both position loads are unconditional, so they are in flight together
   // (raw_pos0 may be NULL when W == 0; its value is then unused)
   const int64_t t = p.pos0[b] + (row - b * p.T);
   const int64_t rp0 = (p.W > 0 ? p.raw_pos0 : p.pos0)[b];
-  const int64_t n_ent = HCA ? visible_entries(t, p.m, p.n_cap) : static_cast<int64_t>(p.k);
+  const int64_t n_ent =
+      HCA ? uniform64(visible_entries(t, p.m, p.n_cap)) : static_cast<int64_t>(p.k);
   const int64_t n_slots = n_ent + p.W;
   const int64_t c_begin = static_cast<int64_t>(split) * p.chunks_per_split;
   const int64_t c_end = min(c_begin + p.chunks_per_split, (n_slots + kAttChunk - 1) / kAttChunk);

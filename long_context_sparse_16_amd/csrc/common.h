@@ -164,6 +164,15 @@ __device__ __forceinline__ f32x4 mma_fp8(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// Sequence index of query row `row` (row = b * T + i).  The row count is a
+// grid dimension, so 32-bit arithmetic is exact; the result is moved to a
+// scalar register (wave-uniform), so per-sequence loads go through the
+// scalar cache and values derived from it stay scalar.
+__device__ __forceinline__ int64_t seq_of_row(int64_t row, int64_t T) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<int>(static_cast<uint32_t>(row) / static_cast<uint32_t>(T)));
+}
+
 // A wave-uniform 64-bit value moved to scalar registers (so loop bounds and
 // addresses derived from it stay scalar).
 __device__ __forceinline__ int64_t uniform64(int64_t x) {

@@ -162,10 +162,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const auto& a = qf.a;
   const auto& wq = qf.wq;
 
-  // (rows = B * T is a grid dimension, so 32-bit arithmetic is exact; the
-  // sequence index is wave-uniform, so pos0 comes through the scalar cache)
-  const int64_t b = __builtin_amdgcn_readfirstlane(
-      static_cast<int>(static_cast<uint32_t>(row) / static_cast<uint32_t>(T)));
+  const int64_t b = seq_of_row(row, T);
   const int64_t t = pos0[b] + (row - b * T);
   const int64_t V = uniform64(visible_entries(t, m, n_cap));
   const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * tiles_per_wg;

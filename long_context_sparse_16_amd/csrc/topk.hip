@@ -25,9 +25,10 @@
 //     slice's sure entries and candidates to its own workspace region; a
 //     second kernel, one workgroup per row, gathers them, resolves the row
 //     and returns the row's histogram to zero.  (A kernel boundary is the
-//     cheap way to make the lists visible: a last-workgroup hand-off would
-//     need device-scope fences, which write back and invalidate a whole
-//     XCD's L2.)
+//     cheap way to make the lists visible: a last-workgroup hand-off needs
+//     device-scope fences, which write back and invalidate a whole XCD's
+//     L2; measured on the 32 x 32768 decode rows, such a fused kernel took
+//     three times as long as the two launches.)
 //   * row path (many rows, prefill; short rows): one workgroup per row;
 //     rows of up to 32768 entries are held in registers and read once.
 #include "common.h"
@@ -53,7 +54,7 @@ struct FinishShared {
   // 4096-bin first-digit histogram in the row kernel
   uint32_t bitmap[kBitmapMaxEntries / 32 + kBitmapMaxEntries / 1024];
   uint32_t scan[32];
-  uint32_t misc[8];  // [0] bin [1] above [4] selected [5] candidates [7] flag
+  uint32_t misc[8];  // [0] bin [1] above [4] selected [5] candidates [6] flag [7] count
 };
 
 // ------------------------------------------------------------ block helpers
@@ -314,9 +315,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
   constexpr int kHistPer = kHistBins / kRowThreads;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
-  const int64_t b = row / T;
+  const int64_t b = seq_of_row(row, T);
   const int64_t t = pos0[b] + (row - b * T);
-  const int64_t V = visible_entries(t, m, n_cap);
+  const int64_t V = uniform64(visible_entries(t, m, n_cap));
   int32_t* out = idx + row * k;
   if (V <= k) {
     write_iota(out, V, k);
@@ -447,17 +448,18 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
 // Workspace per row: hist[4096] u32 (zero between calls; the indexer or
 // topk_hist_kernel accumulates into it and the finishing kernel clears it),
 // ctrl[4] u32 (first-digit bucket, count above it; cleared after use), then
-// per 4096-entry slice: cnt[2] u32 (sure entries, candidates) and the
-// slice's lists sure[4096] i32, ckey[4096] u32, cidx[4096] i32, which are
-// written before they are read in the same call.
+// per 4096-entry slice: cnt[2] u32 (listed entries, candidates among them)
+// and the slice's list lidx[4096] i32, lkey[4096] u32: every entry whose
+// first digit is >= the row's bucket (the sure entries and the
+// candidates), in entry order, with its key.  cnt and the lists are written
+// before they are read in the same call.
 
 struct SplitWs {
   uint32_t* hist;   // [rows][kHistBins]
   uint32_t* ctrl;   // [rows][4]
   uint32_t* cnt;    // [rows][n_sl][2]
-  int32_t* sure;    // [rows][n_sl][kSelEntries]
-  uint32_t* ckey;   // [rows][n_sl][kSelEntries]
-  int32_t* cidx;    // [rows][n_sl][kSelEntries]
+  int32_t* lidx;    // [rows][n_sl][kSelEntries]
+  uint32_t* lkey;   // [rows][n_sl][kSelEntries]
   int64_t n_sl;     // slices per row
 };
 
@@ -472,7 +474,7 @@ inline size_t split_ws_bytes(int64_t rows, int64_t n_cap) {
   const int64_t ns = n_slices(n_cap);
   return static_cast<size_t>(rows) *
          (sizeof(uint32_t) * (kHistBins + 4) +
-          static_cast<size_t>(ns) * (sizeof(uint32_t) * 2 + sizeof(int32_t) * kSelEntries * 3));
+          static_cast<size_t>(ns) * (sizeof(uint32_t) * 2 + sizeof(int32_t) * kSelEntries * 2));
 }
 
 inline SplitWs split_ws(void* base, int64_t rows, int64_t n_cap) {
@@ -485,11 +487,9 @@ inline SplitWs split_ws(void* base, int64_t rows, int64_t n_cap) {
   p += sizeof(uint32_t) * 4 * rows;
   w.cnt = reinterpret_cast<uint32_t*>(p);
   p += sizeof(uint32_t) * 2 * w.n_sl * rows;
-  w.sure = reinterpret_cast<int32_t*>(p);
+  w.lidx = reinterpret_cast<int32_t*>(p);
   p += sizeof(int32_t) * kSelEntries * w.n_sl * rows;
-  w.ckey = reinterpret_cast<uint32_t*>(p);
-  p += sizeof(uint32_t) * kSelEntries * w.n_sl * rows;
-  w.cidx = reinterpret_cast<int32_t*>(p);
+  w.lkey = reinterpret_cast<uint32_t*>(p);
   return w;
 }
 
@@ -499,9 +499,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_hist_kernel(
     int64_t n_cap, int m, int k, SplitWs ws) {
   __shared__ uint32_t hist[kHistBins];
   const int64_t row = blockIdx.y;
-  const int64_t b = row / T;
+  const int64_t b = seq_of_row(row, T);
   const int64_t t = pos0[b] + (row - b * T);
-  const int64_t V = visible_entries(t, m, n_cap);
+  const int64_t V = uniform64(visible_entries(t, m, n_cap));
   const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kSelEntries;
   if (V <= k || j0 >= V) return;
   const int64_t j1 = min(V, j0 + kSelEntries);
@@ -526,8 +526,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_hist_kernel(
 // consecutive entries j0 + 256 it + 64 w + lane, so the slice's lists come
 // out in ascending entry order from per-(pass, wave) ballot counts, one
 // prefix sum over those 64 counts and each lane's rank in its ballot.  The
-// lists go to the slice's own workspace region (no atomics) with their
-// lengths in cnt; slice 0 also records the bucket.
+// list (sure entries and candidates together, with their keys) goes to the
+// slice's own workspace region (no atomics) with its length and candidate
+// count in cnt; slice 0 also records the bucket.
 constexpr int kSelPer = kSelEntries / kSelThreads;   // 16 passes
 constexpr int kHistPerSel = kHistBins / kSelThreads;  // 16 bins per thread
 constexpr int kSelWaves = kSelThreads / 64;
@@ -537,22 +538,21 @@ __device__ __forceinline__ uint32_t lanes_below(unsigned long long mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
 }
 
-__global__ __launch_bounds__(kSelThreads) void topk_classify_kernel(
-    const float* __restrict__ scores, const int64_t* __restrict__ pos0, int64_t T,
-    int64_t n_cap, int m, int k, SplitWs ws) {
-  __shared__ uint32_t scan[32];
-  __shared__ uint32_t res[2];
-  __shared__ uint32_t tab[kSelPer * kSelWaves];  // (pass, wave) counts, sure | cand << 16
+struct ClassifyShared {
+  uint32_t scan[32];
+  uint32_t res[2];
+  uint32_t tab[kSelPer * kSelWaves];  // (pass, wave) counts, sure | cand << 16
+};
+
+// Classify slice blockIdx.x of row `row` (entries [j0, j1), j0 < V, V > k):
+// writes the slice's lists and counts and returns the bucket b1.
+__device__ uint32_t classify_slice(ClassifyShared& cs, const float* __restrict__ srow,
+                                   int64_t row, int64_t j0, int64_t j1, int k, SplitWs ws) {
+  uint32_t* scan = cs.scan;
+  uint32_t* res = cs.res;
+  uint32_t* tab = cs.tab;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int64_t row = blockIdx.y;
-  const int64_t b = row / T;
-  const int64_t t = pos0[b] + (row - b * T);
-  const int64_t V = visible_entries(t, m, n_cap);
-  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kSelEntries;
-  if (V <= k || j0 >= V) return;
-  const int64_t j1 = min(V, j0 + kSelEntries);
-  const float* srow = scores + row * n_cap;
   // bins [kHistBins - 16 (tid + 1), kHistBins - 16 tid), 64-byte aligned
   const uint32_t* gh = ws.hist + row * kHistBins + (kHistBins - kHistPerSel * (tid + 1));
   u32x4 hq[kHistPerSel / 4];
@@ -583,16 +583,17 @@ __global__ __launch_bounds__(kSelThreads) void topk_classify_kernel(
   }
   __syncthreads();
   const uint32_t b1 = res[0];
-  // per (pass, wave) counts; at most 64 of each, packed
+  // per (pass, wave) counts of listed entries (bucket >= b1) and of
+  // candidates among them (bucket == b1); at most 64 of each, packed
 #pragma unroll
   for (int it = 0; it < kSelPer; ++it) {
     const int64_t j = j0 + it * kSelThreads + tid;
     const uint32_t bk = score_key(sv[it]) >> kTopkDigit1Shift;
-    const unsigned long long ms = __ballot(j < j1 && bk > b1);
+    const unsigned long long ml = __ballot(j < j1 && bk >= b1);
     const unsigned long long mc = __ballot(j < j1 && bk == b1);
     if (lane == 0)
       tab[it * kSelWaves + wv] =
-          static_cast<uint32_t>(__popcll(ms)) | (static_cast<uint32_t>(__popcll(mc)) << 16);
+          static_cast<uint32_t>(__popcll(ml)) | (static_cast<uint32_t>(__popcll(mc)) << 16);
   }
   __syncthreads();
   static_assert(kSelPer * kSelWaves == 64, "one wave scans the (pass, wave) table");
@@ -619,159 +620,203 @@ __global__ __launch_bounds__(kSelThreads) void topk_classify_kernel(
   }
   __syncthreads();
   const int64_t slot = row * ws.n_sl + blockIdx.x;
-  int32_t* gs = ws.sure + slot * kSelEntries;
-  uint32_t* gk = ws.ckey + slot * kSelEntries;
-  int32_t* gi = ws.cidx + slot * kSelEntries;
+  int32_t* gi = ws.lidx + slot * kSelEntries;
+  uint32_t* gk = ws.lkey + slot * kSelEntries;
 #pragma unroll
   for (int it = 0; it < kSelPer; ++it) {
     const int64_t j = j0 + it * kSelThreads + tid;
     const uint32_t key = score_key(sv[it]);
-    const uint32_t bk = key >> kTopkDigit1Shift;
-    const bool is_s = j < j1 && bk > b1;
-    const bool is_c = j < j1 && bk == b1;
-    const unsigned long long ms = __ballot(is_s);
-    const unsigned long long mc = __ballot(is_c);
-    const uint32_t base = tab[it * kSelWaves + wv];
-    if (is_s) gs[(base & 0xffffu) + lanes_below(ms)] = static_cast<int32_t>(j);
-    if (is_c) {
-      const uint32_t pc = (base >> 16) + lanes_below(mc);
-      gk[pc] = key;
-      gi[pc] = static_cast<int32_t>(j);
+    const bool listed = j < j1 && (key >> kTopkDigit1Shift) >= b1;
+    const unsigned long long ml = __ballot(listed);
+    if (listed) {
+      const uint32_t pl = (tab[it * kSelWaves + wv] & 0xffffu) + lanes_below(ml);
+      gi[pl] = static_cast<int32_t>(j);
+      gk[pl] = key;
     }
   }
+  return b1;
 }
 
-// Index of the last slice whose list offset (table word `field` of each
-// 4-word record) is <= p; offsets are non-decreasing over the slices.
-__device__ __forceinline__ int slice_of(const uint32_t* table, int n_sl, int field, uint32_t p) {
-  int lo = 0, hi = n_sl - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (table[mid * 4 + field] <= p) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
-// Number of entries of the sorted list a[0..n) that are < x.
-__device__ __forceinline__ uint32_t count_below(const int32_t* a, uint32_t n, int32_t x) {
-  uint32_t lo = 0, hi = n;
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi) >> 1;
-    if (a[mid] < x) lo = mid + 1;
-    else hi = mid;
-  }
-  return lo;
+__global__ __launch_bounds__(kSelThreads) void topk_classify_kernel(
+    const float* __restrict__ scores, const int64_t* __restrict__ pos0, int64_t T,
+    int64_t n_cap, int m, int k, SplitWs ws) {
+  __shared__ ClassifyShared cs;
+  const int64_t row = blockIdx.y;
+  const int64_t b = seq_of_row(row, T);
+  const int64_t t = pos0[b] + (row - b * T);
+  const int64_t V = uniform64(visible_entries(t, m, n_cap));
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kSelEntries;
+  if (V <= k || j0 >= V) return;
+  classify_slice(cs, scores + row * n_cap, row, j0, min(V, j0 + kSelEntries), k, ws);
 }
 
 // Resolve one row from its slices' lists and return its histogram and
-// counters to zero.  The slices' counts are prefix-summed into a table (in
-// the bitmap area); the sure entries and the candidates are gathered in
-// entry order, each output position looking up its slice.  When the
-// candidates fit in LDS, the cut among them is found, the winners are
-// compacted in order behind the sure entries, and the two sorted lists are
-// merged into the output by binary search; otherwise the row is finished as
-// in the row path (candidates re-read from the scores, bitmap emit).
+// counters to zero.  The slice counts and a prefix of every slice's list
+// (P entries each, P a power of two sized so that all of them take kPre
+// loads per thread) are loaded together; the counts' prefix sum places the
+// prefetched entries, and any entries past P are fetched afterwards.  The
+// LDS list is then the row's sure entries and candidates in entry order:
+// the cut among the candidates is found and one order-preserving
+// compaction (sure entries and winning candidates) writes the output.  A
+// list longer than the LDS buffer is finished as in the row path
+// (candidates re-read from the scores, bitmap emit).
 constexpr int kFinThreads = 1024;
+constexpr int kFinPre = 4;  // prefetched list entries per thread
+
+template <int NT>
+__device__ void finish_from_lists(FinishShared& sm, const float* __restrict__ srow, int64_t row,
+                                  int64_t V, uint32_t b1, int k, SplitWs ws,
+                                  int32_t* __restrict__ out) {
+  const int tid = threadIdx.x;
+  const int n_sl = static_cast<int>((V + kSelEntries - 1) / kSelEntries);
+  const int64_t slot0 = row * ws.n_sl;
+  // per thread: counts of slices [tid * kPer, tid * kPer + kPer)
+  constexpr int kPer = static_cast<int>(kMaxSlices / NT);
+  uint32_t cl[kPer], cc[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int sl = tid * kPer + q;
+    const int64_t sc = slot0 + (sl < n_sl ? sl : n_sl - 1);
+    cl[q] = ws.cnt[sc * 2];
+    cc[q] = ws.cnt[sc * 2 + 1];
+  }
+  // speculative prefix of every list: slot q = tid + NT i is entry q % P of
+  // slice q / P (addresses clamped to the row's slices; unused past a count)
+  int lp = 0;  // log2 P
+  while (lp < 12 && (n_sl << (lp + 1)) <= NT * kFinPre) ++lp;
+  int32_t pi[kFinPre];
+  uint32_t pk[kFinPre];
+#pragma unroll
+  for (int i = 0; i < kFinPre; ++i) {
+    const int q = tid + NT * i;
+    const int sl = q >> lp;
+    const int64_t at = (slot0 + (sl < n_sl ? sl : n_sl - 1)) * kSelEntries + (q & ((1 << lp) - 1));
+    pi[i] = ws.lidx[at];
+    pk[i] = ws.lkey[at];
+  }
+  uint32_t ll = 0, lc = 0, lmax = 0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    if (tid * kPer + q < n_sl) {
+      ll += cl[q];
+      lc += cc[q];
+      lmax = max(lmax, cl[q]);
+    }
+  }
+  uint32_t ol = block_excl_scan<NT>(ll, sm.scan);
+  const uint32_t oc = block_excl_scan<NT>(lc, sm.scan);
+  uint32_t* table = sm.bitmap;  // [slice][2]: list offset, list length
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int sl = tid * kPer + q;
+    if (sl < n_sl) {
+      table[sl * 2] = ol;
+      table[sl * 2 + 1] = cl[q];
+      ol += cl[q];
+    }
+  }
+  if (tid == NT - 1) {
+    sm.misc[4] = ol;       // listed entries
+    sm.misc[5] = oc + lc;  // candidates among them
+  }
+  if (tid < 4) sm.misc[tid] = 0u;
+  if (tid == 0) sm.misc[6] = sm.misc[7] = 0u;
+  __syncthreads();
+  if (lmax > (1u << lp)) sm.misc[6] = 1u;  // some list is longer than its prefix
+  const uint32_t n_list = sm.misc[4], nc = sm.misc[5];
+  const uint32_t ns = n_list - nc;                   // sure entries (fewer than k)
+  const uint32_t r = static_cast<uint32_t>(k) - ns;  // winners needed among the candidates
+  const bool fits = n_list <= static_cast<uint32_t>(kCandCap);
+  if (fits) {
+#pragma unroll
+    for (int i = 0; i < kFinPre; ++i) {
+      const int q = tid + NT * i;
+      const int sl = q >> lp;
+      const uint32_t pos = static_cast<uint32_t>(q & ((1 << lp) - 1));
+      if (sl < n_sl && pos < table[sl * 2 + 1]) {
+        const uint32_t at = table[sl * 2] + pos;
+        sm.cidx[at] = pi[i];
+        sm.ckey[at] = pk[i];
+      }
+    }
+  }
+  __syncthreads();
+  if (fits && sm.misc[6] != 0u) {
+    for (int sl = 0; sl < n_sl; ++sl) {
+      const uint32_t o = table[sl * 2], c = table[sl * 2 + 1];
+      for (uint32_t pos = (1u << lp) + tid; pos < c; pos += NT) {
+        const int64_t at = (slot0 + sl) * kSelEntries + pos;
+        sm.cidx[o + pos] = ws.lidx[at];
+        sm.ckey[o + pos] = ws.lkey[at];
+      }
+    }
+    __syncthreads();
+  }
+  if (!fits) {
+    // the sure entries into sel (any order: the bitmap emit sorts), then
+    // the row path's resolution from the scores
+    for (int sl = 0; sl < n_sl; ++sl) {
+      const uint32_t c = table[sl * 2 + 1];
+      for (uint32_t pos = tid; pos < c; pos += NT) {
+        const int64_t at = (slot0 + sl) * kSelEntries + pos;
+        if ((ws.lkey[at] >> kTopkDigit1Shift) > b1) {
+          const uint32_t p = atomicAdd(&sm.misc[7], 1u);
+          if (p < static_cast<uint32_t>(kMaxK)) sm.sel[p] = ws.lidx[at];
+        }
+      }
+    }
+    __syncthreads();
+    if (tid == 0) sm.misc[4] = ns;
+    __syncthreads();
+    // (the candidates are not in LDS: a count above kCandCap makes
+    // finish_row read them from the scores)
+    finish_row<NT>(sm, srow, V, b1, r, static_cast<uint32_t>(kCandCap) + 1u, k, out);
+  } else {
+    Cut c{0u, 0x7fffffff};  // r == nc: every candidate wins
+    if (r < nc) {
+      auto visit = [&](auto f) {
+        for (uint32_t i = tid; i < n_list; i += NT) {
+          const uint32_t key = sm.ckey[i];
+          if ((key >> kTopkDigit1Shift) == b1) f(key, sm.cidx[i]);
+        }
+      };
+      c = resolve_cut<NT>(sm, visit, r);
+    }
+    // sure entries and winning candidates, in entry order
+    auto keep = [&](uint32_t i) {
+      const uint32_t key = sm.ckey[i];
+      return (key >> kTopkDigit1Shift) > b1 || r >= nc || cut_wins(c, key, sm.cidx[i]);
+    };
+    const uint32_t per = (n_list + NT - 1) / NT;
+    const uint32_t i0 = min(n_list, tid * per), i1 = min(n_list, i0 + per);
+    uint32_t cnt = 0;
+    for (uint32_t i = i0; i < i1; ++i) cnt += keep(i) ? 1u : 0u;
+    uint32_t pos = block_excl_scan<NT>(cnt, sm.scan);
+    for (uint32_t i = i0; i < i1; ++i)
+      if (keep(i)) {
+        if (pos < static_cast<uint32_t>(k)) out[pos] = sm.cidx[i];
+        ++pos;
+      }
+  }
+  uint32_t* gh = ws.hist + row * kHistBins;
+  for (int i = tid; i < kHistBins; i += NT) gh[i] = 0u;
+  if (tid < 4) ws.ctrl[row * 4 + tid] = 0u;
+}
 
 __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ pos0, int64_t T,
     int64_t n_cap, int m, int k, SplitWs ws, int32_t* __restrict__ idx) {
   __shared__ FinishShared sm;
-  const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
-  const int64_t b = row / T;
+  const int64_t b = seq_of_row(row, T);
   const int64_t t = pos0[b] + (row - b * T);
-  const int64_t V = visible_entries(t, m, n_cap);
+  const int64_t V = uniform64(visible_entries(t, m, n_cap));
   int32_t* out = idx + row * k;
   if (V <= k) {
     write_iota(out, V, k);
     return;
   }
-  const int n_sl = static_cast<int>((V + kSelEntries - 1) / kSelEntries);
-  const int64_t slot0 = row * ws.n_sl;
-  const uint32_t b1 = ws.ctrl[row * 4];
-  // per thread: slices [tid * per, tid * per + per)
-  constexpr int kPer = static_cast<int>(kMaxSlices / kFinThreads);
-  uint32_t cs[kPer], cc[kPer];
-  uint32_t ls = 0, lc = 0;
-#pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    const int sl = tid * kPer + q;
-    const bool on = sl < n_sl;
-    cs[q] = on ? ws.cnt[(slot0 + sl) * 2] : 0u;
-    cc[q] = on ? ws.cnt[(slot0 + sl) * 2 + 1] : 0u;
-    ls += cs[q];
-    lc += cc[q];
-  }
-  uint32_t os = block_excl_scan<kFinThreads>(ls, sm.scan);
-  uint32_t oc = block_excl_scan<kFinThreads>(lc, sm.scan);
-  uint32_t* table = sm.bitmap;  // [slice][4]: sure offset, count, candidate offset, count
-#pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    const int sl = tid * kPer + q;
-    if (sl < n_sl) {
-      table[sl * 4] = os;
-      table[sl * 4 + 1] = cs[q];
-      table[sl * 4 + 2] = oc;
-      table[sl * 4 + 3] = cc[q];
-    }
-    os += cs[q];
-    oc += cc[q];
-  }
-  if (tid == kFinThreads - 1) {
-    sm.misc[4] = min(os, static_cast<uint32_t>(k));  // sure entries (fewer than k)
-    sm.misc[5] = oc;                                   // candidates
-  }
-  if (tid < 4) sm.misc[tid] = 0u;
-  __syncthreads();
-  const uint32_t ns = sm.misc[4], nc = sm.misc[5];
-  const bool fits = nc <= static_cast<uint32_t>(kCandCap);
-  for (uint32_t p = tid; p < ns; p += kFinThreads) {
-    const int sl = slice_of(table, n_sl, 0, p);
-    sm.sel[p] = ws.sure[(slot0 + sl) * kSelEntries + (p - table[sl * 4])];
-  }
-  if (fits) {
-    for (uint32_t p = tid; p < nc; p += kFinThreads) {
-      const int sl = slice_of(table, n_sl, 2, p);
-      const int64_t q = (slot0 + sl) * kSelEntries + (p - table[sl * 4 + 2]);
-      sm.ckey[p] = ws.ckey[q];
-      sm.cidx[p] = ws.cidx[q];
-    }
-  }
-  __syncthreads();
-  const float* srow = scores + row * n_cap;
-  const uint32_t r = static_cast<uint32_t>(k) - ns;  // winners needed among the candidates
-  if (!fits) {
-    finish_row<kFinThreads>(sm, srow, V, b1, r, nc, k, out);
-  } else {
-    if (r > 0) {
-      auto visit = [&](auto f) {
-        for (uint32_t i = tid; i < nc; i += kFinThreads) f(sm.ckey[i], sm.cidx[i]);
-      };
-      const Cut c = resolve_cut<kFinThreads>(sm, visit, r);
-      // compact the winners, in entry order, into sel[ns .. k)
-      const uint32_t per = (nc + kFinThreads - 1) / kFinThreads;
-      const uint32_t i0 = tid * per, i1 = min(nc, i0 + per);
-      uint32_t wcount = 0;
-      for (uint32_t i = i0; i < i1; ++i) wcount += cut_wins(c, sm.ckey[i], sm.cidx[i]) ? 1u : 0u;
-      uint32_t wpos = ns + block_excl_scan<kFinThreads>(wcount, sm.scan);
-      for (uint32_t i = i0; i < i1; ++i)
-        if (cut_wins(c, sm.ckey[i], sm.cidx[i]) && wpos < static_cast<uint32_t>(kMaxK))
-          sm.sel[wpos++] = sm.cidx[i];
-      __syncthreads();
-    }
-    // merge the sorted lists sel[0, ns) and sel[ns, k)
-    const int32_t* wl = sm.sel + ns;
-    for (uint32_t i = tid; i < static_cast<uint32_t>(k); i += kFinThreads) {
-      const int32_t j = sm.sel[i];
-      const uint32_t pos = i < ns ? i + count_below(wl, r, j) : (i - ns) + count_below(sm.sel, ns, j);
-      out[pos] = j;
-    }
-  }
-  uint32_t* gh = ws.hist + row * kHistBins;
-  for (int i = tid; i < kHistBins; i += kFinThreads) gh[i] = 0u;
-  if (tid < 4) ws.ctrl[row * 4 + tid] = 0u;
+  finish_from_lists<kFinThreads>(sm, scores + row * n_cap, row, V, ws.ctrl[row * 4], k, ws, out);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {

@@ -213,6 +213,18 @@ def test_topk_edge_rows():
     assert np.array_equal(got[0, 0], np.r_[np.arange(15), 5000])
 
 
+def test_topk_split_lists_past_prefetch():
+    """Split path: the finishing kernel prefetches a prefix of every slice's
+    list; here one slice holds almost all the selected entries, so its list
+    is fetched mostly in the second step."""
+    say("topk concentrated slice")
+    rng = np.random.default_rng(503)
+    s = (rng.standard_normal((2, 1, 70000)) * 30 + 140).astype(np.float32)
+    s[0, 0, 4096:8192] += 400.0            # slice 1 holds the top 4096
+    s[1, 0, 60000:60000 + 3000] = 1000.0   # 3000 equal maxima in slices 14-15
+    _topk_case(s, np.full((2, 1), 70000, np.int64), 2048)
+
+
 def test_topk_long_rows_decode_shape():
     say("topk long rows")
     rng = np.random.default_rng(502)
