@@ -652,48 +652,66 @@ __global__ __launch_bounds__(kSelThreads) void topk_classify_kernel(
 
 // Resolve one row from its slices' lists and return its histogram and
 // counters to zero.  The slice counts and a prefix of every slice's list
-// (P entries each, P a power of two sized so that all of them take kPre
-// loads per thread) are loaded together; the counts' prefix sum places the
-// prefetched entries, and any entries past P are fetched afterwards.  The
+// (P entries each, P a power of two sized so that all of them take kFinPre
+// loads per thread) are loaded together, before the row's position is
+// known; the counts' prefix sum places the prefetched entries, and any
+// entries past P are fetched afterwards.  The
 // LDS list is then the row's sure entries and candidates in entry order:
 // the cut among the candidates is found and one order-preserving
 // compaction (sure entries and winning candidates) writes the output.  A
 // list longer than the LDS buffer is finished as in the row path
 // (candidates re-read from the scores, bitmap emit).
 constexpr int kFinThreads = 1024;
-constexpr int kFinPre = 4;  // prefetched list entries per thread
+constexpr int kFinPre = 8;  // prefetched list entries per thread
+constexpr int kFinBatch = 8;  // loads in flight per thread for list entries past the prefix
 
-template <int NT>
-__device__ void finish_from_lists(FinishShared& sm, const float* __restrict__ srow, int64_t row,
-                                  int64_t V, uint32_t b1, int k, SplitWs ws,
-                                  int32_t* __restrict__ out) {
+__global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
+    const float* __restrict__ scores, const int64_t* __restrict__ pos0, int64_t T,
+    int64_t n_cap, int m, int k, SplitWs ws, int32_t* __restrict__ idx) {
+  constexpr int NT = kFinThreads;
+  __shared__ FinishShared sm;
   const int tid = threadIdx.x;
-  const int n_sl = static_cast<int>((V + kSelEntries - 1) / kSelEntries);
+  const int64_t row = blockIdx.x;
   const int64_t slot0 = row * ws.n_sl;
-  // per thread: counts of slices [tid * kPer, tid * kPer + kPer)
-  constexpr int kPer = static_cast<int>(kMaxSlices / NT);
+  const int n_alloc = static_cast<int>(ws.n_sl);  // slices per row in the workspace
+  // Everything that does not depend on the row's length is loaded first:
+  // the slice counts, a prefix of every slice's list (slot q = tid + NT i
+  // is entry q % P of slice q / P; addresses clamped to the workspace's
+  // slices, entries past a count unused), the bucket and the position.
+  constexpr int kPer = static_cast<int>(kMaxSlices / NT);  // slices per thread
   uint32_t cl[kPer], cc[kPer];
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
     const int sl = tid * kPer + q;
-    const int64_t sc = slot0 + (sl < n_sl ? sl : n_sl - 1);
+    const int64_t sc = slot0 + (sl < n_alloc ? sl : n_alloc - 1);
     cl[q] = ws.cnt[sc * 2];
     cc[q] = ws.cnt[sc * 2 + 1];
   }
-  // speculative prefix of every list: slot q = tid + NT i is entry q % P of
-  // slice q / P (addresses clamped to the row's slices; unused past a count)
-  int lp = 0;  // log2 P
-  while (lp < 12 && (n_sl << (lp + 1)) <= NT * kFinPre) ++lp;
+  int lp = 0;  // log2 P (P <= 512: lists are a few hundred entries long)
+  while (lp < 9 && (n_alloc << (lp + 1)) <= NT * kFinPre) ++lp;
   int32_t pi[kFinPre];
   uint32_t pk[kFinPre];
 #pragma unroll
   for (int i = 0; i < kFinPre; ++i) {
     const int q = tid + NT * i;
     const int sl = q >> lp;
-    const int64_t at = (slot0 + (sl < n_sl ? sl : n_sl - 1)) * kSelEntries + (q & ((1 << lp) - 1));
+    const int64_t at =
+        (slot0 + (sl < n_alloc ? sl : n_alloc - 1)) * kSelEntries + (q & ((1 << lp) - 1));
     pi[i] = ws.lidx[at];
     pk[i] = ws.lkey[at];
   }
+  const uint32_t b1 = ws.ctrl[row * 4];
+  const int64_t b = seq_of_row(row, T);
+  const int64_t t = pos0[b] + (row - b * T);
+  const int64_t V = uniform64(visible_entries(t, m, n_cap));
+  int32_t* out = idx + row * k;
+  if (V <= k) {
+    write_iota(out, V, k);
+    return;
+  }
+  const float* srow = scores + row * n_cap;
+  const int n_sl = static_cast<int>((V + kSelEntries - 1) / kSelEntries);
+
   uint32_t ll = 0, lc = 0, lmax = 0;
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
@@ -742,12 +760,37 @@ __device__ void finish_from_lists(FinishShared& sm, const float* __restrict__ sr
   }
   __syncthreads();
   if (fits && sm.misc[6] != 0u) {
-    for (int sl = 0; sl < n_sl; ++sl) {
-      const uint32_t o = table[sl * 2], c = table[sl * 2 + 1];
-      for (uint32_t pos = (1u << lp) + tid; pos < c; pos += NT) {
-        const int64_t at = (slot0 + sl) * kSelEntries + pos;
-        sm.cidx[o + pos] = ws.lidx[at];
-        sm.ckey[o + pos] = ws.lkey[at];
+    // entries past the prefixes: 2^lt threads per slice, kFinBatch loads
+    // in flight per thread
+    int lt = 0;
+    while ((n_sl << (lt + 1)) <= NT) ++lt;
+    const uint32_t step = 1u << lt;
+    for (int base = 0; base < (n_sl << lt); base += NT) {
+      const int q = base + tid;
+      const int sl = q >> lt;
+      if (sl < n_sl) {
+        const uint32_t o = table[sl * 2], c = table[sl * 2 + 1];
+        const int64_t g0 = (slot0 + sl) * kSelEntries;
+        for (uint32_t p0 = (1u << lp) + static_cast<uint32_t>(q & (step - 1)); p0 < c;
+             p0 += step * kFinBatch) {
+          int32_t vi[kFinBatch];
+          uint32_t vk[kFinBatch];
+#pragma unroll
+          for (int u = 0; u < kFinBatch; ++u) {
+            const uint32_t pos = p0 + u * step;
+            const int64_t at = g0 + (pos < c ? pos : c - 1);
+            vi[u] = ws.lidx[at];
+            vk[u] = ws.lkey[at];
+          }
+#pragma unroll
+          for (int u = 0; u < kFinBatch; ++u) {
+            const uint32_t pos = p0 + u * step;
+            if (pos < c) {
+              sm.cidx[o + pos] = vi[u];
+              sm.ckey[o + pos] = vk[u];
+            }
+          }
+        }
       }
     }
     __syncthreads();
@@ -801,22 +844,6 @@ __device__ void finish_from_lists(FinishShared& sm, const float* __restrict__ sr
   uint32_t* gh = ws.hist + row * kHistBins;
   for (int i = tid; i < kHistBins; i += NT) gh[i] = 0u;
   if (tid < 4) ws.ctrl[row * 4 + tid] = 0u;
-}
-
-__global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
-    const float* __restrict__ scores, const int64_t* __restrict__ pos0, int64_t T,
-    int64_t n_cap, int m, int k, SplitWs ws, int32_t* __restrict__ idx) {
-  __shared__ FinishShared sm;
-  const int64_t row = blockIdx.x;
-  const int64_t b = seq_of_row(row, T);
-  const int64_t t = pos0[b] + (row - b * T);
-  const int64_t V = uniform64(visible_entries(t, m, n_cap));
-  int32_t* out = idx + row * k;
-  if (V <= k) {
-    write_iota(out, V, k);
-    return;
-  }
-  finish_from_lists<kFinThreads>(sm, scores + row * n_cap, row, V, ws.ctrl[row * 4], k, ws, out);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
