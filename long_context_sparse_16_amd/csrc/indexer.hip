@@ -362,20 +362,22 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
   const int ntiles = static_cast<int>((V_max + kPfTile - 1) / kPfTile);
   u32x4 breg[kLoads];
   float kreg = 0.f;  // fp8: one key scale per thread (threads < kPfTile)
+  // A tile is addressed from a wave-uniform base with 32-bit per-lane
+  // offsets: piece r of this thread is byte ent * RB + pc * 16 of the tile,
+  // and entries past V_max are clamped to the last visible one (one min).
   auto load_tile = [&](int tile) __attribute__((always_inline)) {
+    const int64_t e0 = static_cast<int64_t>(tile) * kPfTile;  // uniform
+    const uint8_t* tb = kib + e0 * RB;
+    const int last = static_cast<int>(min<int64_t>(kPfTile, V_max - e0)) - 1;  // >= 0
 #pragma unroll
     for (int r = 0; r < kLoads; ++r) {
       const int id = tid + kPfThreads * r;
       const int ent = id / (RB / 16);
       const int pc = id - ent * (RB / 16);
-      int64_t e = static_cast<int64_t>(tile) * kPfTile + ent;
-      e = e < V_max ? e : V_max - 1;
-      breg[r] = *reinterpret_cast<const u32x4*>(kib + e * RB + pc * 16);
+      const uint32_t off = static_cast<uint32_t>(min(ent, last) * RB + pc * 16);
+      breg[r] = *reinterpret_cast<const u32x4*>(tb + off);
     }
-    if (DTYPE == 2) {
-      int64_t e = static_cast<int64_t>(tile) * kPfTile + (tid & (kPfTile - 1));
-      kreg = ki_scale[b * n_cap + (e < V_max ? e : V_max - 1)];
-    }
+    if (DTYPE == 2) kreg = ki_scale[b * n_cap + e0 + min(tid & (kPfTile - 1), last)];
   };
   auto store_tile = [&](auto buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -420,9 +422,13 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
     }
   };
   // sum_h w_h phi(acc) for one column tile (all 64 heads: in lane, then two
-  // lane swaps, after which every lane group holds the 16 column sums);
-  // lane group ct % 4 stores them (the other lanes' offsets are out of the
-  // descriptor's range, so their stores are dropped)
+  // lane swaps, after which every lane group holds the 16 column sums)
+  // store offsets: lane group ct % 4 writes column ct's 16 sums; the other
+  // lanes' offsets start at 2^31, past the descriptor's range (the entry
+  // part added to them stays below 2^30), so their stores are dropped
+  uint32_t lane_off[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) lane_off[c] = g == c ? static_cast<uint32_t>(col) * 4u : 0x80000000u;
   auto epi_ct = [&](int tile, int ct, const Acc& acc) __attribute__((always_inline)) {
     float x = 0.f;
 #pragma unroll
@@ -433,9 +439,8 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
         x = fmaf(wq[ht][i], y, x);
       }
     x = sum_xor32(sum_xor16(x));
-    const int e = tile * kPfTile + ct * 16 + col;
     if (DTYPE == 2) x *= s_ksc[tile & 1][ct * 16 + col];
-    const uint32_t off = g == (ct & 3) ? static_cast<uint32_t>(e) * 4u : 0x80000000u;
+    const uint32_t off = lane_off[ct & 3] + static_cast<uint32_t>(tile * kPfTile + ct * 16) * 4u;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), srsrc, off, 0, 0);
   };
 
