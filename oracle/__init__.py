@@ -33,6 +33,11 @@ from .codecs import (
     e4m3_decode,
     e4m3_encode,
     quantize_fp8_rows,
+    e2m1_decode,
+    e2m1_encode,
+    e8m0_decode,
+    quantize_mxfp4_rows,
+    mxfp4_decode_rows,
 )
 from .csa import (
     visible_count,
@@ -50,6 +55,11 @@ __all__ = [
     "e4m3_decode",
     "e4m3_encode",
     "quantize_fp8_rows",
+    "e2m1_decode",
+    "e2m1_encode",
+    "e8m0_decode",
+    "quantize_mxfp4_rows",
+    "mxfp4_decode_rows",
     "visible_count",
     "compress",
     "indexer_scores",
