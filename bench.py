@@ -23,7 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 10100.0, "f32": 157.3}
 
 
 def parse():
@@ -97,12 +97,21 @@ def visible_sum(cfg) -> int:
 
 def indexer_bytes(cfg, V: int) -> int:
     """Algorithmic HBM bytes of one indexer launch: every visible key (and
-    its fp8 scale) read once per sequence, one fp32 score written per
-    (query, visible entry), the queries and head weights read once."""
-    key_bytes = cfg.d_I * (1 if cfg.ki_fp8 else 2 if cfg.storage == "bf16" else 4)
-    key_bytes += 4 if cfg.ki_fp8 else 0
-    q_bytes = cfg.T * cfg.H_I * (cfg.d_I * (1 if cfg.ki_fp8 else 2) + 4 + (4 if cfg.ki_fp8 else 0))
-    return cfg.B * (V * key_bytes + 4 * visible_sum(cfg) + q_bytes)
+    its fp8 scale or MXFP4 block scales) read once per sequence, one fp32
+    score written per (query, visible entry), the queries (with their
+    scales) and head weights read once."""
+    if cfg.ki_mxfp4:
+        row = cfg.d_I // 2 + cfg.d_I // 32          # E2M1 codes + E8M0 scales
+    elif cfg.ki_fp8:
+        row = cfg.d_I + 4                           # E4M3 codes + fp32 scale
+    else:
+        row = cfg.d_I * (2 if cfg.storage == "bf16" else 4)
+    q_bytes = cfg.T * cfg.H_I * (row + 4)
+    return cfg.B * (V * row + 4 * visible_sum(cfg) + q_bytes)
+
+
+def index_dtype(cfg) -> str:
+    return "mxfp4" if cfg.ki_mxfp4 else "fp8" if cfg.ki_fp8 else cfg.storage
 
 
 def indexer_flops(cfg) -> int:
@@ -145,6 +154,9 @@ def cpu_baseline(cfg, budget_s: float):
                 qcode, qsc = oracle.quantize_fp8_rows(qi.astype(np.float32))
                 ki = oracle.e4m3_decode(kcode) * ksc[:, None]
                 qi = oracle.e4m3_decode(qcode) * qsc[..., None]
+            if cfg.ki_mxfp4:
+                ki = oracle.mxfp4_decode_rows(*oracle.quantize_mxfp4_rows(kc.astype(np.float32)))
+                qi = oracle.mxfp4_decode_rows(*oracle.quantize_mxfp4_rows(qi.astype(np.float32)))
             S = oracle.indexer_scores(qi, s["w"], ki, pos, cfg.m)
             V = oracle.visible_count(pos, cfg.m)
             idx = np.stack([oracle.topk_select(S[i], int(V[i]), cfg.k) for i in range(cfg.T)])
@@ -270,7 +282,7 @@ def main():
     elif cfg.T >= 8:
         # prefill: the indexer is one MFMA score GEMM per sequence
         fl = indexer_flops(cfg)
-        dt = "fp8" if cfg.ki_fp8 else cfg.storage
+        dt = index_dtype(cfg)
         roof = {"kernel": "indexer_prefill_kernel", "bound": "mfma",
                 "achieved": fl / (st["index"] * 1e9), "peak": MFMA_PEAK_TFLOPS[dt],
                 "unit": "TFLOP/s", "traffic": None, "algorithmic_flops": fl}
@@ -291,7 +303,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if cfg.ki_fp8 else cfg.storage,
+        "dtype": index_dtype(cfg),
         "data": "synthetic (seeded N(0,1) K/V/q, U(0,1) head weights, planted entries)",
         "config": {"workload": cfg.name, "batch": cfg.B, "context_tokens": cfg.pos0,
                    "compressed_entries": V, "m": cfg.m, "indexer": f"{cfg.H_I}x{cfg.d_I}",

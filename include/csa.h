@@ -60,6 +60,11 @@ extern "C" {
 #define CSA_F32 0      /* IEEE binary32 */
 #define CSA_BF16 1     /* bfloat16, stored as 16-bit words */
 #define CSA_FP8_E4M3 2 /* OCP FP8 E4M3FN byte codes (max 448, no inf) */
+/* OCP MX FP4: E2M1 codes two per byte (element 2i in the low nibble, 2i+1
+ * in the high nibble; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) with one E8M0
+ * scale byte (2^(byte - 127)) per block of 32 consecutive elements.  A row
+ * of d elements is d/2 code bytes plus d/32 scale bytes, in two arrays. */
+#define CSA_MXFP4 3
 
 /* indexer nonlinearity */
 #define CSA_ACT_RELU 0
@@ -125,13 +130,33 @@ int csa_quantize_fp8_rows(const void* x, int x_dtype, int64_t rows, int64_t d,
                           uint8_t* codes, float* scales, void* stream);
 
 /*
+ * csa_quantize_mxfp4_rows -- MXFP4 storage of indexer keys and queries, the
+ * pages' own precision for the indexer's query-key path (takeshell.com
+ * section 5; dataforcee.us "Muon Optimizer and FP4 QAT": MXFP4 QAT of the
+ * Lightning Indexer's QK path, FP4 E2M1 dequantizing losslessly to FP8).
+ * The scale rule is the OCP MX v1.0 one.  For each block of 32 consecutive
+ * elements of each row r of x [rows][d]:
+ *   amax = max |x|;  s = floor(log2(amax)) - 2, clamped to [-127, 127]
+ *   scales[r, blk] = s + 127   (0 for an all-zero block)
+ *   code = E2M1(x * 2^-s): nearest, ties to the even code, saturating at
+ *          +-6; the sign bit is the sign of x
+ * codes [rows][d/2] (two codes per byte, low nibble first), scales
+ * [rows][d/32].  Dequantized value = e2m1(code) * 2^(scale - 127).  x_dtype
+ * F32 or BF16; d a multiple of 32 in [32, 4096].  rows == 0 is a no-op.
+ */
+int csa_quantize_mxfp4_rows(const void* x, int x_dtype, int64_t rows, int64_t d,
+                            uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
  * csa_index_scores -- the Lightning Indexer (takeshell.com 2.1: indexer
  * queries per query token, scored against the compressed entries; 64 heads
  * x 128 dims for V4-Pro).  For query (b, i) at position t and j < V(t):
  *   scores[b,i,j] = sum_h w[b,i,h] * phi( qi[b,i,h,:] . ki[b,j,:] )
  * phi = ReLU (act = CSA_ACT_RELU) or identity (CSA_ACT_IDENTITY).  With
  * FP8 inputs the operands are decode(code) * scale, i.e.
- *   scores = ki_scale[b,j] * sum_h (w * qi_scale[b,i,h]) * phi(q~ . k~).
+ *   scores = ki_scale[b,j] * sum_h (w * qi_scale[b,i,h]) * phi(q~ . k~);
+ * with MXFP4 inputs they are the dequantized MXFP4 rows (each 32-element
+ * block times its own scale, inside the dot product).
  * Entries j >= V(t) of a score row are not written.
  *
  * Optional fusion with csa_topk: when topk_ws is non-NULL, the call also
@@ -143,19 +168,21 @@ int csa_quantize_fp8_rows(const void* x, int x_dtype, int64_t rows, int64_t d,
  * bytes.  With
  * topk_ws == NULL, k is ignored.
  *
- *   qi        [B][T][H_I][d_I]      qi_dtype
- *   qi_scale  [B][T][H_I] fp32      FP8 only (else ignored, may be NULL)
+ *   qi        [B][T][H_I][d_I]      qi_dtype (MXFP4: [B][T][H_I][d_I/2] bytes)
+ *   qi_scale  FP8: [B][T][H_I] fp32; MXFP4: [B][T][H_I][d_I/32] E8M0
+ *             bytes; other dtypes: ignored, may be NULL
  *   w         [B][T][H_I] fp32
- *   ki        [B][n_cap][d_I]       ki_dtype (== qi_dtype)
- *   ki_scale  [B][n_cap] fp32       FP8 only (else ignored, may be NULL)
+ *   ki        [B][n_cap][d_I]       ki_dtype (== qi_dtype; MXFP4: d_I/2 bytes)
+ *   ki_scale  FP8: [B][n_cap] fp32; MXFP4: [B][n_cap][d_I/32] E8M0 bytes,
+ *             4-byte aligned; other dtypes: ignored, may be NULL
  *   pos0      [B] int64 (device)
  *   scores    [B][T][n_cap] fp32
- * Supported: dtypes F32, BF16 (d_I % 32 == 0, d_I <= 256) and FP8_E4M3
- * (d_I == 128); 1 <= H_I <= 64; m >= 1; T >= 1, B >= 1.
+ * Supported: dtypes F32, BF16 (d_I % 32 == 0, d_I <= 256), FP8_E4M3 and
+ * MXFP4 (d_I == 128); 1 <= H_I <= 64; m >= 1; T >= 1, B >= 1.
  */
-int csa_index_scores(const void* qi, int qi_dtype, const float* qi_scale,
+int csa_index_scores(const void* qi, int qi_dtype, const void* qi_scale,
                      const float* w, const void* ki, int ki_dtype,
-                     const float* ki_scale, const int64_t* pos0,
+                     const void* ki_scale, const int64_t* pos0,
                      int64_t B, int64_t T, int64_t H_I, int64_t d_I,
                      int64_t n_cap, int m, int act, float* scores, int k,
                      void* topk_ws, size_t topk_ws_bytes, void* stream);
@@ -191,9 +218,9 @@ int csa_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T,
  */
 size_t csa_index_topk_workspace_size(int64_t B, int64_t T, int64_t n_cap,
                                      int k, int scores_in_workspace);
-int csa_index_topk(const void* qi, int qi_dtype, const float* qi_scale,
+int csa_index_topk(const void* qi, int qi_dtype, const void* qi_scale,
                    const float* w, const void* ki, int ki_dtype,
-                   const float* ki_scale, const int64_t* pos0,
+                   const void* ki_scale, const int64_t* pos0,
                    int64_t B, int64_t T, int64_t H_I, int64_t d_I,
                    int64_t n_cap, int m, int act, int k, float* scores,
                    int32_t* idx, void* ws, size_t ws_bytes, void* stream);

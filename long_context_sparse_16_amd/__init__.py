@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsa.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "csa.h")
 
-CSA_F32, CSA_BF16, CSA_FP8_E4M3 = 0, 1, 2
+CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_MXFP4 = 0, 1, 2, 3
 CSA_ACT_RELU, CSA_ACT_IDENTITY = 0, 1
 
 
@@ -50,6 +50,7 @@ _SIGNATURES = {
     "csa_workspace_clear": (_i, [_vp, _sz, _vp]),
     "csa_compress": (_i, [_vp, _i, _vp, _i64, _i64, _i64, _i, _i64, _i64, _vp, _i, _i64, _i64, _vp]),
     "csa_quantize_fp8_rows": (_i, [_vp, _i, _i64, _i64, _vp, _vp, _vp]),
+    "csa_quantize_mxfp4_rows": (_i, [_vp, _i, _i64, _i64, _vp, _vp, _vp]),
     "csa_index_scores": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                               _i, _i, _vp, _i, _vp, _sz, _vp]),
     "csa_topk_workspace_size": (_sz, [_i64, _i64, _i64, _i]),
@@ -106,6 +107,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return CSA_BF16
     if t.dtype in (torch.uint8, torch.float8_e4m3fn):
         return CSA_FP8_E4M3
+    if t.dtype == torch.float4_e2m1fn_x2:
+        return CSA_MXFP4
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -184,13 +187,42 @@ def csa_quantize_fp8_rows(x: torch.Tensor, codes: torch.Tensor = None, scales: t
     return codes, scales
 
 
+def csa_quantize_mxfp4_rows(x: torch.Tensor, codes: torch.Tensor = None,
+                            scales: torch.Tensor = None, stream=None):
+    """Quantize the rows (last axis, a multiple of 32) of x to MXFP4.
+    Returns (codes, scales): codes torch.float4_e2m1fn_x2 [..., d/2] (two
+    E2M1 codes per byte, low nibble first), scales torch.float8_e8m0fnu
+    [..., d/32] (one per 32-element block)."""
+    dev = _dev(x)
+    _contig("x", x)
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    if codes is None:
+        codes = torch.empty(x.shape[:-1] + (d // 2,), dtype=torch.uint8,
+                            device=dev).view(torch.float4_e2m1fn_x2)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1] + (d // 32,), dtype=torch.uint8,
+                             device=dev).view(torch.float8_e8m0fnu)
+    _contig("codes", codes)
+    _contig("scales", scales)
+    if codes.numel() * 2 != x.numel() or scales.numel() * 32 != x.numel():
+        raise ValueError("codes / scales have the wrong size")
+    _check("csa_quantize_mxfp4_rows", _lib.csa_quantize_mxfp4_rows(
+        _ptr(x), _dtype_code(x), rows, d, _ptr(codes), _ptr(scales), _stream(stream, dev)))
+    return codes, scales
+
+
 # ------------------------------------------------------------------ indexer
 
 def _index_shapes(qi, w, ki, pos0):
+    """Shapes of the indexer operands; for MXFP4 (float4_e2m1fn_x2) the last
+    axis holds d_I / 2 bytes."""
     if qi.dim() != 4:
         raise ValueError("qi must be [B, T, H_I, d_I]")
     B, T, H_I, d_I = qi.shape
-    if ki.dim() != 3 or ki.shape[0] != B or ki.shape[2] != d_I:
+    if qi.dtype == torch.float4_e2m1fn_x2:
+        d_I *= 2
+    if ki.dim() != 3 or ki.shape[0] != B or ki.shape[2] != qi.shape[3]:
         raise ValueError("ki must be [B, n_cap, d_I]")
     if w.shape != (B, T, H_I) or w.dtype != torch.float32:
         raise ValueError("w must be float32 [B, T, H_I]")
@@ -367,7 +399,8 @@ def hca_attend(q, kc, vc, m: int, kr, vr, raw_pos0, pos0, W: int, scale: float, 
 __all__ = [
     "CSAError", "LIB_PATH", "abi_version", "last_error", "header_functions", "workspace",
     "csa_workspace_clear",
-    "csa_compress", "csa_quantize_fp8_rows", "csa_index_scores", "csa_topk",
+    "csa_compress", "csa_quantize_fp8_rows", "csa_quantize_mxfp4_rows", "csa_index_scores",
+    "csa_topk",
     "csa_topk_workspace_size", "csa_index_topk", "csa_index_topk_workspace_size",
     "csa_attend", "csa_attend_workspace_size", "hca_attend", "hca_attend_workspace_size",
 ]

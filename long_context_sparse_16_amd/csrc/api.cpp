@@ -47,18 +47,25 @@ size_t round_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
     if (!(cond)) return fail(code, __VA_ARGS__); \
   } while (0)
 
-int check_index_args(const void* qi, int qi_dtype, const float* qi_scale, const float* w,
-                     const void* ki, int ki_dtype, const float* ki_scale, const int64_t* pos0,
+int check_index_args(const void* qi, int qi_dtype, const void* qi_scale, const float* w,
+                     const void* ki, int ki_dtype, const void* ki_scale, const int64_t* pos0,
                      int64_t B, int64_t T, int64_t H_I, int64_t d_I, int64_t n_cap, int m, int act,
                      const float* scores, const char* fn) {
   CSA_REQUIRE(qi && w && ki && pos0 && scores, CSA_ERR_NULL,
               "%s: qi, w, ki, pos0 and scores must be non-NULL", fn);
   CSA_REQUIRE(qi_dtype == ki_dtype, CSA_ERR_DTYPE, "%s: qi_dtype (%d) must equal ki_dtype (%d)", fn,
               qi_dtype, ki_dtype);
-  CSA_REQUIRE(qi_dtype == CSA_F32 || qi_dtype == CSA_BF16 || qi_dtype == CSA_FP8_E4M3,
+  CSA_REQUIRE(qi_dtype == CSA_F32 || qi_dtype == CSA_BF16 || qi_dtype == CSA_FP8_E4M3 ||
+                  qi_dtype == CSA_MXFP4,
               CSA_ERR_DTYPE, "%s: unknown dtype %d", fn, qi_dtype);
   if (qi_dtype == CSA_FP8_E4M3)
     CSA_REQUIRE(qi_scale && ki_scale, CSA_ERR_NULL, "%s: FP8 inputs need qi_scale and ki_scale", fn);
+  if (qi_dtype == CSA_MXFP4) {
+    CSA_REQUIRE(qi_scale && ki_scale, CSA_ERR_NULL,
+                "%s: MXFP4 inputs need qi_scale and ki_scale (E8M0 block scales)", fn);
+    CSA_REQUIRE((reinterpret_cast<uintptr_t>(ki_scale) & 3) == 0, CSA_ERR_SHAPE,
+                "%s: MXFP4 ki_scale must be 4-byte aligned", fn);
+  }
   CSA_REQUIRE(act == CSA_ACT_RELU || act == CSA_ACT_IDENTITY, CSA_ERR_SHAPE, "%s: unknown act %d",
               fn, act);
   CSA_REQUIRE(B >= 1 && T >= 1, CSA_ERR_SHAPE, "%s: B and T must be >= 1", fn);
@@ -74,7 +81,7 @@ int check_index_args(const void* qi, int qi_dtype, const float* qi_scale, const 
     CSA_REQUIRE(d_I == 64 || d_I == 128 || d_I == 256, CSA_ERR_UNSUPPORTED,
                 "%s: bf16 needs d_I in {64, 128, 256}", fn);
   else
-    CSA_REQUIRE(d_I == 128, CSA_ERR_UNSUPPORTED, "%s: fp8 needs d_I == 128", fn);
+    CSA_REQUIRE(d_I == 128, CSA_ERR_UNSUPPORTED, "%s: fp8 and mxfp4 need d_I == 128", fn);
   CSA_REQUIRE(aligned16(qi) && aligned16(ki), CSA_ERR_SHAPE, "%s: qi and ki must be 16-byte aligned",
               fn);
   return CSA_OK;
@@ -141,7 +148,7 @@ const char* csa_status_string(int status) {
 
 const char* csa_last_error(void) { return g_last_error; }
 
-int csa_abi_version(void) { return 1; }
+int csa_abi_version(void) { return 2; }
 
 int csa_workspace_clear(void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "csa_workspace_clear";
@@ -196,8 +203,24 @@ int csa_quantize_fp8_rows(const void* x, int x_dtype, int64_t rows, int64_t d, u
                     fn);
 }
 
-int csa_index_scores(const void* qi, int qi_dtype, const float* qi_scale, const float* w,
-                     const void* ki, int ki_dtype, const float* ki_scale, const int64_t* pos0,
+int csa_quantize_mxfp4_rows(const void* x, int x_dtype, int64_t rows, int64_t d, uint8_t* codes,
+                            uint8_t* scales, void* stream) {
+  const char* fn = "csa_quantize_mxfp4_rows";
+  CSA_REQUIRE(x && codes && scales, CSA_ERR_NULL, "%s: x, codes and scales must be non-NULL", fn);
+  CSA_REQUIRE(x_dtype == CSA_F32 || x_dtype == CSA_BF16, CSA_ERR_DTYPE,
+              "%s: dtype must be F32 or BF16, got %d", fn, x_dtype);
+  CSA_REQUIRE(rows >= 0, CSA_ERR_SHAPE, "%s: rows must be >= 0", fn);
+  CSA_REQUIRE(d >= 32 && d <= 4096 && d % 32 == 0, CSA_ERR_UNSUPPORTED,
+              "%s: d must be a multiple of 32 in [32, 4096]", fn);
+  CSA_REQUIRE(rows / 4 < 0x7fffffffLL, CSA_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  if (rows == 0) return ok();
+  return hip_result(csa::launch_quantize_mxfp4_rows(x, x_dtype, rows, d, codes, scales,
+                                                    static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int csa_index_scores(const void* qi, int qi_dtype, const void* qi_scale, const float* w,
+                     const void* ki, int ki_dtype, const void* ki_scale, const int64_t* pos0,
                      int64_t B, int64_t T, int64_t H_I, int64_t d_I, int64_t n_cap, int m, int act,
                      float* scores, int k, void* topk_ws, size_t topk_ws_bytes, void* stream) {
   const char* fn = "csa_index_scores";
@@ -247,8 +270,8 @@ size_t csa_index_topk_workspace_size(int64_t B, int64_t T, int64_t n_cap, int k,
   return s;
 }
 
-int csa_index_topk(const void* qi, int qi_dtype, const float* qi_scale, const float* w,
-                   const void* ki, int ki_dtype, const float* ki_scale, const int64_t* pos0,
+int csa_index_topk(const void* qi, int qi_dtype, const void* qi_scale, const float* w,
+                   const void* ki, int ki_dtype, const void* ki_scale, const int64_t* pos0,
                    int64_t B, int64_t T, int64_t H_I, int64_t d_I, int64_t n_cap, int m, int act,
                    int k, float* scores, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "csa_index_topk";

@@ -181,6 +181,19 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
   return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// MXFP4 x MXFP4: each lane's 16 bytes are the 32 E2M1 codes of one
+// 32-element block of its row (A) or column (B), and byte 0 of sa / sb is
+// that block's E8M0 scale.
+__device__ __forceinline__ f32x4 mma_fp4(u32x4 a, u32x4 b, f32x4 c, uint32_t sa, uint32_t sb) {
+  const i32x8 av = {static_cast<int>(a[0]), static_cast<int>(a[1]), static_cast<int>(a[2]),
+                    static_cast<int>(a[3]), 0, 0, 0, 0};
+  const i32x8 bv = {static_cast<int>(b[0]), static_cast<int>(b[1]), static_cast<int>(b[2]),
+                    static_cast<int>(b[3]), 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0,
+                                                          static_cast<int>(sa), 0,
+                                                          static_cast<int>(sb));
+}
+
 __device__ __forceinline__ int64_t visible_entries(int64_t t, int m, int64_t n_cap) {
   int64_t v = (t + 1) / m;
   if (v < 0) v = 0;

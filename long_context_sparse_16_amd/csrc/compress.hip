@@ -93,6 +93,64 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const T* __restrict_
   if (lane == 0) scales[r] = scale;
 }
 
+// MXFP4 row quantizer (OCP MX: E2M1 elements, one E8M0 scale per block of
+// 32): one wave per row, lane l taking elements 2l and 2l+1 of each group of
+// 128 (one output byte; a block is 16 lanes).  Block scale exponent
+// s = floor(log2 amax) - 2 (clamped to [-127, 127]; code 0 for a zero
+// block); element code = E2M1 rounding of x * 2^-s (exact), nearest with
+// ties to even and saturation at 6, as a sum of threshold tests; the sign
+// bit is the sign of x.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float v) {
+  const float a = fabsf(v);
+  const uint32_t mag = (a > 0.25f ? 1u : 0u) + (a >= 0.75f ? 1u : 0u) + (a > 1.25f ? 1u : 0u) +
+                       (a >= 1.75f ? 1u : 0u) + (a > 2.5f ? 1u : 0u) + (a >= 3.5f ? 1u : 0u) +
+                       (a > 5.0f ? 1u : 0u);
+  return mag | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_mxfp4_rows_kernel(const T* __restrict__ x,
+                                                                  uint8_t* __restrict__ codes,
+                                                                  uint8_t* __restrict__ scales,
+                                                                  int64_t rows, int d) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const T* xr = x + r * d;
+  for (int c0 = 0; c0 < d; c0 += 128) {
+    const int c = c0 + 2 * lane;
+    const bool live = c < d;  // d % 32 == 0: whole 16-lane blocks are live or not
+    const float x0 = live ? load_elem<T>(xr, c) : 0.f;
+    const float x1 = live ? load_elem<T>(xr, c + 1) : 0.f;
+    float a = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
+    int s = -127;
+    if (a > 0.f) {
+      s = __builtin_amdgcn_frexp_expf(a) - 1 - 2;  // a = f * 2^e, f in [0.5, 1)
+      s = s < -127 ? -127 : (s > 127 ? 127 : s);
+    }
+    const uint32_t q = f32_to_e2m1(ldexpf(x0, -s)) | (f32_to_e2m1(ldexpf(x1, -s)) << 4);
+    if (live) {
+      codes[r * (d / 2) + c / 2] = static_cast<uint8_t>(q);
+      if ((lane & 15) == 0) scales[r * (d / 32) + c / 32] = static_cast<uint8_t>(a > 0.f ? s + 127 : 0);
+    }
+  }
+}
+
+int launch_quantize_mxfp4_rows(const void* x, int dtype, int64_t rows, int64_t d, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+  if (dtype == 0) {
+    quantize_mxfp4_rows_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), codes,
+                                                           scales, rows, static_cast<int>(d));
+  } else {
+    quantize_mxfp4_rows_kernel<uint16_t><<<grid, 256, 0, s>>>(
+        static_cast<const uint16_t*>(x), codes, scales, rows, static_cast<int>(d));
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_quantize_fp8_rows(const void* x, int dtype, int64_t rows, int64_t d,
                              uint8_t* codes, float* scales, hipStream_t s) {
   dim3 grid(static_cast<unsigned>((rows + 3) / 4));

@@ -33,6 +33,7 @@ struct IdxTraits;
 template <int DI>
 struct IdxTraits<0, DI> {  // fp32, v_mfma_f32_16x16x4_f32
   static constexpr int kElemBytes = 4;
+  static constexpr int kRowBytes = DI * 4;
   static constexpr int kLaneBytes = DI * 4 / 4;
   static constexpr int kSteps = DI / 4;
   using Frag = float;
@@ -46,6 +47,7 @@ struct IdxTraits<0, DI> {  // fp32, v_mfma_f32_16x16x4_f32
 template <int DI>
 struct IdxTraits<1, DI> {  // bf16, v_mfma_f32_16x16x32_bf16
   static constexpr int kElemBytes = 2;
+  static constexpr int kRowBytes = DI * 2;
   static constexpr int kLaneBytes = DI * 2 / 4;
   static constexpr int kSteps = DI / 32;
   __device__ static f32x4 mma(const u32x4* a, const u32x4* b, int s, f32x4 c) {
@@ -56,6 +58,7 @@ struct IdxTraits<1, DI> {  // bf16, v_mfma_f32_16x16x32_bf16
 template <int DI>
 struct IdxTraits<2, DI> {  // fp8 e4m3, v_mfma_f32_16x16x128_f8f6f4
   static constexpr int kElemBytes = 1;
+  static constexpr int kRowBytes = DI;
   static constexpr int kLaneBytes = DI / 4;
   static constexpr int kSteps = DI / 128;
   __device__ static f32x4 mma(const u32x4* a, const u32x4* b, int s, f32x4 c) {
@@ -71,6 +74,17 @@ struct IdxTraits<2, DI> {  // fp8 e4m3, v_mfma_f32_16x16x128_f8f6f4
   }
 };
 
+// MXFP4 (OCP MX: E2M1 codes two per byte, one E8M0 scale per 32 elements),
+// v_mfma_scale_f32_16x16x128_f8f6f4: a lane's 16 bytes are exactly one
+// 32-element block, so the block scales ride along as one byte per lane
+// (see mma_fp4); the kernel passes them.
+template <int DI>
+struct IdxTraits<3, DI> {
+  static constexpr int kRowBytes = DI / 2;
+  static constexpr int kLaneBytes = DI / 8;
+  static constexpr int kSteps = DI / 128;
+};
+
 // A fragments (4 tiles of 16 query heads, this lane's quarter of each head
 // row) and per-head weights (times the query scale for fp8) of query row
 // `row`.  issue() starts every load unconditionally from clamped addresses
@@ -82,10 +96,11 @@ template <int DTYPE, int DI>
 struct QueryFrags {
   using Tr = IdxTraits<DTYPE, DI>;
   static constexpr int kVec = Tr::kLaneBytes / 16;
-  static constexpr int kRowBytes = DI * Tr::kElemBytes;
+  static constexpr int kRowBytes = Tr::kRowBytes;
   u32x4 a[4][kVec];
   float wq[4][4];
   float ws[4][4];
+  uint32_t sa[4];  // MXFP4: E8M0 scale of this lane's block of each head tile's row
 
   __device__ __forceinline__ void issue(const uint8_t* __restrict__ qi,
                                         const float* __restrict__ qi_scale,
@@ -94,10 +109,12 @@ struct QueryFrags {
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
       const int h = ht * 16 + col;
-      const u32x4* src = reinterpret_cast<const u32x4*>(
-          qi + (row * H_I + (h < H_I ? h : H_I - 1)) * kRowBytes + g * Tr::kLaneBytes);
+      const int64_t hrow = row * H_I + (h < H_I ? h : H_I - 1);
+      const u32x4* src =
+          reinterpret_cast<const u32x4*>(qi + hrow * kRowBytes + g * Tr::kLaneBytes);
 #pragma unroll
       for (int v = 0; v < kVec; ++v) a[ht][v] = src[v];
+      if (DTYPE == 3) sa[ht] = reinterpret_cast<const uint8_t*>(qi_scale)[hrow * (DI / 32) + g];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int hh = ht * 16 + g * 4 + i;
@@ -147,7 +164,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     uint32_t* __restrict__ hist, int topk_k) {
   using Tr = IdxTraits<DTYPE, DI>;
   constexpr int kVec = Tr::kLaneBytes / 16;  // 16-byte loads per lane per row
-  constexpr int kRowBytes = DI * Tr::kElemBytes;
+  constexpr int kRowBytes = Tr::kRowBytes;
   constexpr int kGroup = idx_group_tiles<DTYPE, DI>();
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -192,20 +209,29 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const uint8_t* kwg = kib + e_begin * kRowBytes;          // wave-uniform
   const uint32_t lane_off = static_cast<uint32_t>(col * kRowBytes + g * Tr::kLaneBytes);
 
-  // FP8: each lane also fetches the key scale of its column's entry, with
-  // the group's keys
+  // FP8: each lane also fetches the fp32 scale of its column's entry with
+  // the group's keys; MXFP4: the entry's four E8M0 block scales as one
+  // word, whose byte g the MFMA step shifts into place.  (KScale holds
+  // either.)
+  using KScale = std::conditional_t<DTYPE == 3, uint32_t, float>;
   const float* ksc = DTYPE == 2 ? ki_scale + b * n_cap + e_begin : nullptr;
-  auto load_full = [&](int grp, u32x4 (&dst)[kGroup][kVec], float (&kd)[kGroup]) {
+  const uint32_t* ksw =
+      DTYPE == 3 ? reinterpret_cast<const uint32_t*>(ki_scale) + b * n_cap + e_begin : nullptr;
+  auto load_scale = [&](int e, KScale& kd) __attribute__((always_inline)) {
+    if constexpr (DTYPE == 2) kd = ksc[e];
+    if constexpr (DTYPE == 3) kd = ksw[e];
+  };
+  auto load_full = [&](int grp, u32x4 (&dst)[kGroup][kVec], KScale (&kd)[kGroup]) {
     const uint8_t* gb = kwg + static_cast<int64_t>(grp) * (kGroupEnt * kRowBytes);
 #pragma unroll
     for (int tt = 0; tt < kGroup; ++tt) {
       const u32x4* src = reinterpret_cast<const u32x4*>(gb + tt * (kIdxTile * kRowBytes) + lane_off);
 #pragma unroll
       for (int v = 0; v < kVec; ++v) dst[tt][v] = src[v];
-      if (DTYPE == 2) kd[tt] = ksc[grp * kGroupEnt + tt * kIdxTile + col];
+      load_scale(grp * kGroupEnt + tt * kIdxTile + col, kd[tt]);
     }
   };
-  auto load_tail = [&](int grp, u32x4 (&dst)[kGroup][kVec], float (&kd)[kGroup]) {
+  auto load_tail = [&](int grp, u32x4 (&dst)[kGroup][kVec], KScale (&kd)[kGroup]) {
 #pragma unroll
     for (int tt = 0; tt < kGroup; ++tt) {
       int e = (grp * kGroup + tt) * kIdxTile + col;
@@ -214,7 +240,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
           kwg + static_cast<uint32_t>(e) * kRowBytes + g * Tr::kLaneBytes);
 #pragma unroll
       for (int v = 0; v < kVec; ++v) dst[tt][v] = src[v];
-      if (DTYPE == 2) kd[tt] = ksc[e];
+      load_scale(e, kd[tt]);
     }
   };
 
@@ -225,16 +251,23 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   // the way (rows that keep every visible entry need none).
   const __amdgpu_buffer_rsrc_t srsrc = store_rsrc(srow + e_begin, n_ent_wg * 4);
   const bool do_hist = HIST && V > topk_k;
-  auto compute_group = [&](int grp, const u32x4 (&bt)[kGroup][kVec], const float (&kd)[kGroup]) {
+  auto compute_group = [&](int grp, const u32x4 (&bt)[kGroup][kVec], const KScale (&kd)[kGroup]) {
 #pragma unroll
     for (int tt = 0; tt < kGroup; ++tt) {
       f32x4 acc[4];
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (DTYPE == 3) {
+        static_assert(DI == 128, "MXFP4 indexer: one 128-element MFMA step");
 #pragma unroll
-      for (int st = 0; st < Tr::kSteps; ++st) {
+        for (int ht = 0; ht < 4; ++ht)
+          acc[ht] = mma_fp4(a[ht][0], bt[tt][0], acc[ht], qf.sa[ht], kd[tt] >> (8 * g));
+      } else {
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) acc[ht] = Tr::mma(a[ht], bt[tt], st, acc[ht]);
+        for (int st = 0; st < Tr::kSteps; ++st) {
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht) acc[ht] = Tr::mma(a[ht], bt[tt], st, acc[ht]);
+        }
       }
       float v = 0.f;
 #pragma unroll
@@ -246,7 +279,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
         }
       }
       v = sum_xor32(sum_xor16(v));
-      if (DTYPE == 2) v *= kd[tt];
+      if constexpr (DTYPE == 2) v *= kd[tt];
       const int e = (grp * kGroup + tt) * kIdxTile + col;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srsrc,
                                             g == 0 ? static_cast<uint32_t>(e) * 4u : 0x80000000u,
@@ -261,7 +294,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     __syncthreads();
   }
   u32x4 buf0[kGroup][kVec], buf1[kGroup][kVec];
-  float ks0[kGroup], ks1[kGroup];
+  KScale ks0[kGroup], ks1[kGroup];
   // This wave's full groups are wave, wave + 4, ...: n_my of them, taken in
   // pairs (one per buffer) with a single trailing group when n_my is odd.
   // Every loop iteration runs both halves, so the body is straight-line.
@@ -539,12 +572,15 @@ static void launch_idx_t(const void* qi, const float* qs, const float* w, const 
 #undef CSA_IDX_GO
 }
 
-int launch_index_scores(const void* qi, int dtype, const float* qs, const float* w,
-                        const void* ki, const float* ks, const int64_t* pos0, int64_t B,
+int launch_index_scores(const void* qi, int dtype, const void* qs_v, const float* w,
+                        const void* ki, const void* ks_v, const int64_t* pos0, int64_t B,
                         int64_t T, int64_t H_I, int64_t d_I, int64_t n_cap, int m, int act,
                         float* scores, uint32_t* hist, int k, hipStream_t s) {
   const bool relu = act == 0;
   const int H = static_cast<int>(H_I);
+  // (fp32 scales for FP8; for MXFP4 the kernel reads them as E8M0 bytes)
+  const float* qs = static_cast<const float*>(qs_v);
+  const float* ks = static_cast<const float*>(ks_v);
 #define CSA_IDX_CASE(DT, DI)                                                                  \
   if (dtype == DT && d_I == DI) {                                                             \
     launch_idx_t<DT, DI>(qi, qs, w, ki, ks, pos0, B, T, H, n_cap, m, relu, scores, hist, k, s); \
@@ -556,6 +592,7 @@ int launch_index_scores(const void* qi, int dtype, const float* qs, const float*
   CSA_IDX_CASE(1, 128)
   CSA_IDX_CASE(1, 256)
   CSA_IDX_CASE(2, 128)
+  CSA_IDX_CASE(3, 128)
 #undef CSA_IDX_CASE
   return -2;
 }

@@ -15,6 +15,8 @@ int launch_compress(const void* x, int dtype, const float* z, int64_t B, int64_t
 
 int launch_quantize_fp8_rows(const void* x, int dtype, int64_t rows, int64_t d, uint8_t* codes,
                              float* scales, hipStream_t s);
+int launch_quantize_mxfp4_rows(const void* x, int dtype, int64_t rows, int64_t d, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s);
 
 // Top-k first digit: the 12 most significant bits of the order-preserving
 // score key (4096 bins).
@@ -22,9 +24,10 @@ constexpr int kTopkDigit1Shift = 20;
 constexpr int kTopkHistBins = 1 << (32 - kTopkDigit1Shift);
 
 // hist (nullable): per-row first-digit histogram accumulated for csa_topk
-// (rows with V <= k are skipped).  It must be zero on entry.
-int launch_index_scores(const void* qi, int dtype, const float* qs, const float* w,
-                        const void* ki, const float* ks, const int64_t* pos0, int64_t B,
+// (rows with V <= k are skipped).  It must be zero on entry.  qs / ks are
+// fp32 row scales (dtype 2, FP8) or E8M0 block-scale bytes (dtype 3, MXFP4).
+int launch_index_scores(const void* qi, int dtype, const void* qs, const float* w,
+                        const void* ki, const void* ks, const int64_t* pos0, int64_t B,
                         int64_t T, int64_t H_I, int64_t d_I, int64_t n_cap, int m, int act,
                         float* scores, uint32_t* hist, int k, hipStream_t s);
 

@@ -20,7 +20,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (csa_attend, csa_compress, csa_index_scores, csa_quantize_fp8_rows, csa_topk,
+from . import (csa_attend, csa_compress, csa_index_scores, csa_quantize_fp8_rows,
+               csa_quantize_mxfp4_rows, csa_topk,
                csa_topk_workspace_size, csa_attend_workspace_size, hca_attend,
                hca_attend_workspace_size, workspace)
 
@@ -76,6 +77,14 @@ class CSAStep:
             self.ki_scale = torch.ones((B, n_cap), dtype=torch.float32, device=dev)
             if cfg.n_ctx_entries:
                 self.quantize_keys(0, cfg.n_ctx_entries)
+        if cfg.ki_mxfp4:
+            self.qi_codes, self.qi_scale = csa_quantize_mxfp4_rows(self.qi)
+            # byte storage (torch cannot copy between FP4 / E8M0 tensors);
+            # the indexer gets FP4 / E8M0 views of it
+            self.ki_codes = torch.empty((B, n_cap, cfg.d_I // 2), dtype=torch.uint8, device=dev)
+            self.ki_scale = torch.zeros((B, n_cap, cfg.d_I // 32), dtype=torch.uint8, device=dev)
+            if cfg.n_ctx_entries:
+                self.quantize_keys(0, cfg.n_ctx_entries)
         self.scores = torch.empty((B, T, n_cap), dtype=torch.float32, device=dev)
         self.idx = torch.empty((B, T, cfg.k), dtype=torch.int32, device=dev)
         self.topk_ws = workspace(csa_topk_workspace_size(B, T, n_cap, cfg.k), dev)
@@ -83,7 +92,13 @@ class CSAStep:
 
     # ------------------------------------------------------------ stages
     def quantize_keys(self, first: int, last: int) -> None:
-        """FP8 copy (codes + per-entry scale) of compressed keys [first, last)."""
+        """FP8 (codes + per-entry scale) or MXFP4 (codes + block scales) copy
+        of compressed keys [first, last)."""
+        if self.cfg.ki_mxfp4:
+            codes, scales = csa_quantize_mxfp4_rows(self.kc[:, first:last].contiguous())
+            self.ki_codes[:, first:last] = codes.view(torch.uint8)
+            self.ki_scale[:, first:last] = scales.view(torch.uint8)
+            return
         codes, scales = csa_quantize_fp8_rows(self.kc[:, first:last].contiguous())
         self.ki_codes[:, first:last] = codes
         self.ki_scale[:, first:last] = scales
@@ -96,7 +111,7 @@ class CSAStep:
         x_v = self.vr[:, cfg.raw_before:cfg.raw_before + cfg.n_new_tokens]
         csa_compress(x_k, self.z, self.kc, cfg.m, cfg.n_ctx_entries)
         csa_compress(x_v, self.z, self.vc, cfg.m, cfg.n_ctx_entries)
-        if cfg.ki_fp8:
+        if cfg.ki_fp8 or cfg.ki_mxfp4:
             self.quantize_keys(cfg.n_ctx_entries, cfg.n_cap)
 
     def index(self) -> None:
@@ -107,6 +122,11 @@ class CSAStep:
             csa_index_scores(self.qi_codes, self.w, self.ki_codes, self.pos0, cfg.m, self.act,
                              qi_scale=self.qi_scale, ki_scale=self.ki_scale, scores=self.scores,
                              topk_ws=self.topk_ws, k=cfg.k)
+        elif cfg.ki_mxfp4:
+            csa_index_scores(self.qi_codes, self.w, self.ki_codes.view(torch.float4_e2m1fn_x2),
+                             self.pos0, cfg.m, self.act, qi_scale=self.qi_scale,
+                             ki_scale=self.ki_scale.view(torch.float8_e8m0fnu),
+                             scores=self.scores, topk_ws=self.topk_ws, k=cfg.k)
         else:
             csa_index_scores(self.qi, self.w, self.kc, self.pos0, cfg.m, self.act,
                              scores=self.scores, topk_ws=self.topk_ws, k=cfg.k)

@@ -40,6 +40,8 @@ def to_dev(arr: np.ndarray) -> torch.Tensor:
 def from_dev(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype in (torch.float4_e2m1fn_x2, torch.float8_e8m0fnu, torch.float8_e4m3fn):
+        return t.view(torch.uint8).cpu().numpy()
     return t.cpu().numpy()
 
 

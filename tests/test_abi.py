@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported():
 def test_status_strings_and_version():
     assert lib.csa_status_string(0) == b"CSA_OK"
     assert lib.csa_status_string(-5) == b"CSA_ERR_WORKSPACE"
-    assert lib.csa_abi_version() == 1
+    assert lib.csa_abi_version() == 2
 
 
 def _last():
@@ -67,6 +67,10 @@ def test_quantize_validation():
     assert lib.csa_quantize_fp8_rows(NULL, 1, 4, 128, FAKE, FAKE, NULL) == -1
     assert lib.csa_quantize_fp8_rows(FAKE, 2, 4, 128, FAKE, FAKE, NULL) == -3
     assert lib.csa_quantize_fp8_rows(FAKE, 1, 4, 2048, FAKE, FAKE, NULL) == -4
+    assert lib.csa_quantize_mxfp4_rows(NULL, 1, 4, 128, FAKE, FAKE, NULL) == -1
+    assert lib.csa_quantize_mxfp4_rows(FAKE, 3, 4, 128, FAKE, FAKE, NULL) == -3
+    assert lib.csa_quantize_mxfp4_rows(FAKE, 1, 4, 100, FAKE, FAKE, NULL) == -4   # not % 32
+    assert lib.csa_quantize_mxfp4_rows(FAKE, 1, -1, 128, FAKE, FAKE, NULL) == -2
 
 
 def _index(qi_dtype=1, ki_dtype=1, qs=NULL, ks=NULL, B=1, T=1, H=64, dI=128, n_cap=32, m=4, act=0,
@@ -80,6 +84,10 @@ def test_index_validation():
     assert _index(qi_dtype=1, ki_dtype=0) == -3
     assert _index(qi_dtype=2, ki_dtype=2) == -1          # fp8 needs scales
     assert _index(qi_dtype=2, ki_dtype=2, qs=FAKE, ks=FAKE, dI=64) == -4
+    assert _index(qi_dtype=3, ki_dtype=3) == -1          # mxfp4 needs block scales
+    assert _index(qi_dtype=3, ki_dtype=3, qs=FAKE, ks=FAKE, dI=256) == -4
+    assert _index(qi_dtype=3, ki_dtype=3, qs=FAKE, ks=ctypes.c_void_p(0x100002)) == -2
+    assert _index(qi_dtype=4, ki_dtype=4) == -3
     assert _index(H=65) == -4
     assert _index(dI=96) == -4
     assert _index(m=0) == -2

@@ -54,6 +54,35 @@ def test_quantize_fp8_rows_bitexact(storage):
     assert np.array_equal(from_dev(codes), ref_codes)
 
 
+# ----------------------------------------------------------- MXFP4 quantizer
+
+@pytest.mark.parametrize("storage,d", [("f32", 128), ("bf16", 128), ("f32", 96), ("bf16", 256)])
+def test_quantize_mxfp4_rows_bitexact(storage, d):
+    say("quantize mxfp4", storage, d)
+    rng = np.random.default_rng(110 + d)
+    x = rng.standard_normal((613, d)).astype(np.float32) * np.exp(rng.uniform(-30, 30, (613, 1)))
+    x = x.astype(np.float32)
+    x[0] = 0.0                                   # zero blocks -> scale code 0
+    x[1, :32] = -0.0
+    # exact E2M1 midpoints times the block scale (ties to even) with the
+    # block maximum fixing the scale at 2^0 and at 2^-5
+    vals = oracle.e2m1_decode(np.arange(8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    for r, sc in ((2, 1.0), (3, 2.0 ** -5)):
+        x[r] = 0.0
+        x[r, 0] = 6.0 * sc
+        x[r, 1:8] = mids * sc
+        x[r, 8:15] = -mids * sc
+        x[r, 15] = 7.9 * sc                      # saturates to 6
+    x[4, :32] = np.float32(2.0 ** -149)          # smallest subnormal block
+    xs = _store(x, storage)
+    codes, scales = csa.csa_quantize_mxfp4_rows(to_dev(xs))
+    torch.cuda.synchronize()
+    ref_codes, ref_scales = oracle.quantize_mxfp4_rows(decode(xs).astype(np.float32))
+    assert np.array_equal(from_dev(scales), ref_scales)
+    assert np.array_equal(from_dev(codes), ref_codes)
+
+
 # ---------------------------------------------------------------- compressor
 
 @pytest.mark.parametrize("storage", ["f32", "bf16"])
@@ -112,7 +141,8 @@ def test_compress_one_hot_and_chunked_append(storage):
 # ------------------------------------------------------------------- indexer
 
 @pytest.mark.parametrize("kind,H_I,d_I", [("f32", 4, 64), ("f32", 64, 128), ("bf16", 64, 128),
-                                         ("bf16", 20, 64), ("fp8", 64, 128), ("fp8", 7, 128)])
+                                         ("bf16", 20, 64), ("fp8", 64, 128), ("fp8", 7, 128),
+                                         ("mxfp4", 64, 128), ("mxfp4", 7, 128)])
 @pytest.mark.parametrize("act", ["relu", "identity"])
 def test_indexer_parity(kind, H_I, d_I, act):
     say("indexer", kind, H_I, d_I, act)
@@ -134,6 +164,14 @@ def test_indexer_parity(kind, H_I, d_I, act):
         assert np.array_equal(from_dev(qi_d), qc) and np.array_equal(from_dev(ki_d), kcode)
         qv = oracle.e4m3_decode(qc) * qsc[..., None]
         kv = oracle.e4m3_decode(kcode) * ksc[..., None]
+    if kind == "mxfp4":
+        qi_d, qs = csa.csa_quantize_mxfp4_rows(qi_d)
+        ki_d, ks = csa.csa_quantize_mxfp4_rows(ki_d)
+        qc = oracle.quantize_mxfp4_rows(qv.astype(np.float32))
+        kq = oracle.quantize_mxfp4_rows(kv.astype(np.float32))
+        assert np.array_equal(from_dev(qi_d), qc[0]) and np.array_equal(from_dev(qs), qc[1])
+        assert np.array_equal(from_dev(ki_d), kq[0]) and np.array_equal(from_dev(ks), kq[1])
+        qv, kv = oracle.mxfp4_decode_rows(*qc), oracle.mxfp4_decode_rows(*kq)
     scores = torch.full((B, T, n_cap), float("nan"), device=DEV)
     csa.csa_index_scores(qi_d, to_dev(w), ki_d, to_dev(pos0), m, act, qi_scale=qs, ki_scale=ks,
                          scores=scores)
@@ -374,7 +412,7 @@ def test_workspaces_are_reusable_across_calls():
         assert torch.equal(a, b_) and torch.equal(al, bl), trial
 
 
-@pytest.mark.parametrize("kind,H_I", [("bf16", 64), ("bf16", 40), ("fp8", 64)])
+@pytest.mark.parametrize("kind,H_I", [("bf16", 64), ("bf16", 40), ("fp8", 64), ("mxfp4", 64)])
 @pytest.mark.parametrize("act", ["relu", "identity"])
 def test_indexer_prefill_parity(kind, H_I, act):
     """Many query tokens per sequence (the multi-token MFMA tile path): a
@@ -395,6 +433,11 @@ def test_indexer_prefill_parity(kind, H_I, act):
         ki_d, ks = csa.csa_quantize_fp8_rows(ki_d)
         qv = oracle.e4m3_decode(from_dev(qi_d)) * from_dev(qs)[..., None]
         kv = oracle.e4m3_decode(from_dev(ki_d)) * from_dev(ks)[..., None]
+    if kind == "mxfp4":   # (many tokens take the decode kernel for MXFP4)
+        qi_d, qs = csa.csa_quantize_mxfp4_rows(qi_d)
+        ki_d, ks = csa.csa_quantize_mxfp4_rows(ki_d)
+        qv = oracle.mxfp4_decode_rows(from_dev(qi_d), from_dev(qs))
+        kv = oracle.mxfp4_decode_rows(from_dev(ki_d), from_dev(ks))
     scores = torch.full((B, T, n_cap), float("nan"), device=DEV)
     csa.csa_index_scores(qi_d, to_dev(w), ki_d, to_dev(pos0), m, act, qi_scale=qs, ki_scale=ks,
                          scores=scores)

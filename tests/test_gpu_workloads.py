@@ -117,6 +117,14 @@ def _decode_workload(cfg, sample):
             qc, qs = oracle.quantize_fp8_rows(decode(batch["qi"][b]).astype(np.float32))
             assert np.array_equal(from_dev(step.qi_codes[b]), qc)
             qi = oracle.e4m3_decode(qc) * qs[..., None]
+        if cfg.ki_mxfp4:
+            kq = oracle.quantize_mxfp4_rows(kc.astype(np.float32))
+            assert np.array_equal(from_dev(step.ki_codes[b]), kq[0])
+            assert np.array_equal(from_dev(step.ki_scale[b]), kq[1])
+            ki = oracle.mxfp4_decode_rows(*kq)
+            qq = oracle.quantize_mxfp4_rows(decode(batch["qi"][b]).astype(np.float32))
+            assert np.array_equal(from_dev(step.qi_codes[b]), qq[0])
+            qi = oracle.mxfp4_decode_rows(*qq)
         err, rel, overlap = _stage_parity(step, cfg, batch, b, np.arange(cfg.T), kc, vc, ki, qi)
         say(cfg.name, "seq", b, "max-abs", err, "rel-l2", rel, "overlap", overlap)
         assert err <= 2e-2 and rel <= 1e-2
@@ -137,6 +145,10 @@ def test_decode_128k_bf16_full():
 
 def test_decode_1m_fp8_full():
     _decode_workload(WL.DECODE_1M_FP8, sample=[0, 3])
+
+
+def test_decode_1m_mxfp4_full():
+    _decode_workload(WL.DECODE_1M_MXFP4, sample=[1])
 
 
 def test_hca_decode_1m_bf16_full():

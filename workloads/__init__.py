@@ -49,6 +49,7 @@ class Workload:
     k: int = 0                 # top-k (0: HCA)
     storage: str = "bf16"      # "f32" or "bf16" (K/V, q, q_I)
     ki_fp8: bool = False       # indexer keys / queries stored as e4m3 + scale
+    ki_mxfp4: bool = False     # indexer keys / queries stored as MXFP4
     planted: int = 0           # planted high-affinity entries per sequence
     planted_spread: bool = False  # evenly spaced (else seeded distinct random)
     description: str = ""
@@ -81,7 +82,8 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads.  Decode queries sit at position t = context length
+# The five workloads, then the MXFP4 variant of the 1M decode.  Decode
+# queries sit at position t = context length
 # (the new token is the last raw token of the window); the chunked prefill's
 # queries are the 8192 appended tokens.
 TINY_PREFILL_F32 = Workload(
@@ -118,8 +120,13 @@ DECODE_1M_FP8 = Workload(
     description="CSA decode at 1M, fp8 e4m3 indexer keys/queries with fp32 "
                 "row scales: batch 4 x 262144 entries, top-k 1024, 64 planted")
 
+DECODE_1M_MXFP4 = DECODE_1M_FP8.replace(
+    name="csa_decode_1m_mxfp4", number=5, ki_fp8=False, ki_mxfp4=True,
+    description="CSA decode at 1M, MXFP4 indexer keys/queries (E2M1 + E8M0 "
+                "per 32): batch 4 x 262144 entries, top-k 1024, 64 planted")
+
 WORKLOADS = [TINY_PREFILL_F32, DECODE_128K_BF16, PREFILL_256K_BF16,
-             HCA_DECODE_1M_BF16, DECODE_1M_FP8]
+             HCA_DECODE_1M_BF16, DECODE_1M_FP8, DECODE_1M_MXFP4]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
 
