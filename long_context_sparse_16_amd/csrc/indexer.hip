@@ -141,11 +141,13 @@ constexpr int kIdxWaves = 4;
 constexpr int kIdxTile = 16;        // entries per MFMA column tile
 constexpr int kIdxGroupLoads = 8;   // 16-byte key loads per lane per group
 
-// Tiles per load group: 8 KiB of keys per wave.
+// Tiles per load group: 8 KiB of keys per wave (MXFP4: 4 KiB, measured
+// best there, where the per-entry epilogue is the larger share of the work).
 template <int DTYPE, int DI>
 constexpr int idx_group_tiles() {
-  return kIdxGroupLoads / (IdxTraits<DTYPE, DI>::kLaneBytes / 16) > 0
-             ? kIdxGroupLoads / (IdxTraits<DTYPE, DI>::kLaneBytes / 16)
+  constexpr int loads = DTYPE == 3 ? kIdxGroupLoads / 2 : kIdxGroupLoads;
+  return loads / (IdxTraits<DTYPE, DI>::kLaneBytes / 16) > 0
+             ? loads / (IdxTraits<DTYPE, DI>::kLaneBytes / 16)
              : 1;
 }
 
@@ -170,7 +172,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int col = lane & 15;
   const int g = lane >> 4;
-  __shared__ uint32_t s_hist[HIST ? kTopkHistBins : 1];
+  // first-digit histogram, then one dummy word per lane (see below)
+  __shared__ uint32_t s_hist[HIST ? kTopkHistBins + 64 : 1];
   const int64_t row = blockIdx.y;
   // A operand: 4 head tiles of 16 query heads, kept in registers (issued
   // first: it does not depend on the row's position).
@@ -252,6 +255,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const __amdgpu_buffer_rsrc_t srsrc = store_rsrc(srow + e_begin, n_ent_wg * 4);
   const bool do_hist = HIST && V > topk_k;
   auto compute_group = [&](int grp, const u32x4 (&bt)[kGroup][kVec], const KScale (&kd)[kGroup]) {
+    float vv[kGroup];  // the tiles' 16 scores (every lane group holds all of them)
 #pragma unroll
     for (int tt = 0; tt < kGroup; ++tt) {
       f32x4 acc[4];
@@ -280,12 +284,33 @@ __global__ __launch_bounds__(256) void indexer_kernel(
       }
       v = sum_xor32(sum_xor16(v));
       if constexpr (DTYPE == 2) v *= kd[tt];
-      const int e = (grp * kGroup + tt) * kIdxTile + col;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srsrc,
-                                            g == 0 ? static_cast<uint32_t>(e) * 4u : 0x80000000u,
+      vv[tt] = v;
+    }
+    // Write-out and histogram, up to four tiles per instruction: lane group
+    // g takes tile 4r + g.  Lanes without a tile in the round, and
+    // past-the-end columns, store to an offset past the descriptor's range
+    // (dropped) and count into a word of their own past the bins, so every
+    // lane executes both without a branch.  The bin is the top of the
+    // order-preserving key: flip all bits of a negative score, set the sign
+    // bit of a positive one; adding +0.0 first makes -0.0 count as +0.0.
+#pragma unroll
+    for (int r = 0; r < (kGroup + 3) / 4; ++r) {
+      float my = vv[4 * r];
+#pragma unroll
+      for (int t = 1; t < 4; ++t)
+        if (4 * r + t < kGroup) my = g == t ? vv[4 * r + t] : my;
+      const bool live = 4 * r + g < kGroup;
+      const int e = (grp * kGroup + 4 * r + g) * kIdxTile + col;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(my), srsrc,
+                                            live ? static_cast<uint32_t>(e) * 4u : 0x80000000u,
                                             0, 0);
-      if (HIST && do_hist && g == 0 && e < n_ent_wg)
-        atomicAdd(&s_hist[score_key(v) >> kTopkDigit1Shift], 1u);
+      if (HIST && do_hist) {
+        const uint32_t u = __float_as_uint(my + 0.0f);
+        const uint32_t bin = (u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u)) >>
+                             kTopkDigit1Shift;
+        const bool mine = live & (e < n_ent_wg);
+        atomicAdd(&s_hist[mine ? bin : static_cast<uint32_t>(kTopkHistBins + lane)], 1u);
+      }
     }
   };
 
