@@ -138,15 +138,37 @@ def cpu_baseline(cfg, budget_s: float):
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     done, t_total = 0, 0.0
+    layer_cfgs = WL.layer_workloads(cfg) if cfg.layers else [cfg]
     for b in range(cfg.B):
-        s = WL.make_sequence(cfg, b)
-        t0 = time.perf_counter()
+        for lc in layer_cfgs:
+            s = WL.make_sequence(lc, b)
+            t0 = time.perf_counter()
+            _oracle_sequence(lc, s)
+            t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    q = done * cfg.T
+    return {"value": q / t_total, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {cfg.B} sequences ({q} queries) of {cfg.name}, fp64 NumPy, "
+                      f"{t_total:.1f} s"}
+
+
+def _oracle_sequence(cfg, s):
+    """The oracle's whole step for one sequence's inputs ``s``."""
+    import numpy as np
+    import oracle
+    if True:
         dec = oracle.bf16_decode if s["kc"].dtype == np.uint16 else (lambda a: a.astype(np.float64))
         pos = cfg.pos0 + np.arange(cfg.T)
         kc, vc = dec(s["kc"]), dec(s["vc"])
         if cfg.hca:
             oracle.hca_attend(dec(s["q"]), kc, vc, dec(s["kr"]), dec(s["vr"]), cfg.raw_pos0, pos,
                               cfg.m, cfg.W, cfg.scale)
+        elif cfg.swa:
+            idx = np.zeros((cfg.T, 0), np.int64)
+            oracle.attend(dec(s["q"]), kc, vc, idx, dec(s["kr"]), dec(s["vr"]), cfg.raw_pos0, pos,
+                          cfg.W, cfg.scale)
         else:
             qi, ki = dec(s["qi"]), kc
             if cfg.ki_fp8:
@@ -162,14 +184,6 @@ def cpu_baseline(cfg, budget_s: float):
             idx = np.stack([oracle.topk_select(S[i], int(V[i]), cfg.k) for i in range(cfg.T)])
             oracle.attend(dec(s["q"]), kc, vc, idx, dec(s["kr"]), dec(s["vr"]), cfg.raw_pos0, pos,
                           cfg.W, cfg.scale)
-        t_total += time.perf_counter() - t0
-        done += 1
-        if t_total >= budget_s:
-            break
-    q = done * cfg.T
-    return {"value": q / t_total, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {cfg.B} sequences ({q} queries) of {cfg.name}, fp64 NumPy, "
-                      f"{t_total:.1f} s"}
 
 
 def main():
@@ -191,11 +205,22 @@ def main():
     from long_context_sparse_16_amd.pipeline import CSAStep
 
     cfg = WL.BY_NAME[args.workload]
-    batch = WL.make_batch(cfg)
-    step = CSAStep(cfg, batch)
-    del batch
+    if cfg.layers:
+        # hybrid stack: every layer runs in the step; the stage timings and
+        # the roofline are those of its first CSA layer
+        from long_context_sparse_16_amd.pipeline import HybridStep
+        layer_cfgs = WL.layer_workloads(cfg)
+        hstep = HybridStep(layer_cfgs, [WL.make_batch(c) for c in layer_cfgs])
+        run_once = hstep.run
+        first_csa = next(i for i, c in enumerate(layer_cfgs) if c.k > 0)
+        step, rcfg = hstep.layers[first_csa], layer_cfgs[first_csa]
+    else:
+        batch = WL.make_batch(cfg)
+        step = CSAStep(cfg, batch)
+        del batch
+        run_once, rcfg = step.run, cfg
     for _ in range(args.warmup):
-        step.run()
+        run_once()
     torch.cuda.synchronize()
 
     # The timed step launches each stage directly on the current stream
@@ -204,11 +229,11 @@ def main():
     # duration for the roofline comes from those.
     stream = torch.cuda.current_stream()
     if not args.graph:
-        run_step = step.run
+        run_step = run_once
     else:
         g_step = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_step):
-            step.run()
+            run_once()
         run_step = g_step.replay
         for _ in range(args.warmup):
             run_step()
@@ -258,9 +283,13 @@ def main():
         return a.elapsed_time(b) / (R * reps)
 
     st = {}
+    if cfg.layers:
+        for i, lay in enumerate(hstep.layers):
+            st[f"layer{i}_{cfg.layers[i]}"] = timed(lay.run)
+    cfg_all, cfg = cfg, rcfg  # stage timings and roofline: the (first CSA) layer
     if cfg.n_new_tokens:
         st["compress"] = timed(step.compress)
-    if not cfg.hca:
+    if cfg.k > 0:
         st["index"] = timed(step.index)
         csa_lib.csa_workspace_clear(step.topk_ws)
 
@@ -270,8 +299,10 @@ def main():
         st["topk"] = timed(index_topk) - st["index"]
     st["attend"] = timed(step.attend)
     st["step_events"] = step_event_ms
+    cfg = cfg_all
 
     queries = cfg.B * cfg.T
+    n_indexed = (sum(1 for k in cfg.layers if k == "csa") if cfg.layers else 1) if cfg.k > 0 else 0
     V = int(min(cfg.n_cap, (cfg.pos0 + cfg.T) // cfg.m))
     ms_per_step = wall * 1e3 / K
     value = queries * K / wall
@@ -307,8 +338,9 @@ def main():
         "data": "synthetic (seeded N(0,1) K/V/q, U(0,1) head weights, planted entries)",
         "config": {"workload": cfg.name, "batch": cfg.B, "context_tokens": cfg.pos0,
                    "compressed_entries": V, "m": cfg.m, "indexer": f"{cfg.H_I}x{cfg.d_I}",
-                   "top_k": cfg.k, "heads": cfg.H, "head_dim": cfg.d, "window": cfg.W},
-        "entries_scored_per_s": (cfg.B * visible_sum(cfg) * K / wall) if not cfg.hca else None,
+                   "top_k": cfg.k, "heads": cfg.H, "head_dim": cfg.d, "window": cfg.W,
+                   **({"layers": list(cfg.layers)} if cfg.layers else {})},
+        "entries_scored_per_s": (n_indexed * cfg.B * visible_sum(cfg) * K / wall) if n_indexed else None,
         "stage_ms": st,
         "launch": "hip_graph_per_step" if args.graph else "direct",
         "roofline": roof,

@@ -66,6 +66,10 @@ class CSAStep:
             self.att_ws = workspace(hca_attend_workspace_size(B, T, cfg.H, d, n_cap, cfg.W), dev)
             self.idx = None
             return
+        if cfg.swa:
+            self.att_ws = workspace(csa_attend_workspace_size(B, T, cfg.H, d, 0, cfg.W), dev)
+            self.idx = None
+            return
         self.qi = to_device(batch["qi"], dev, st)
         self.w = to_device(batch["w"], dev, "f32")
         self.qi_scale = None
@@ -140,15 +144,33 @@ class CSAStep:
         if cfg.hca:
             hca_attend(self.q, self.kc, self.vc, cfg.m, self.kr, self.vr, self.raw_pos0,
                        self.pos0, cfg.W, cfg.scale, out=self.out, lse=self.lse, ws=self.att_ws)
+        elif cfg.swa:
+            csa_attend(self.q, self.kc, self.vc, None, self.kr, self.vr, self.raw_pos0,
+                       self.pos0, cfg.W, cfg.scale, out=self.out, lse=self.lse, ws=self.att_ws)
         else:
             csa_attend(self.q, self.kc, self.vc, self.idx, self.kr, self.vr, self.raw_pos0,
                        self.pos0, cfg.W, cfg.scale, out=self.out, lse=self.lse, ws=self.att_ws)
 
     def run(self) -> None:
         """The whole step: compress (if the step completes blocks), then
-        indexer + top-k + attention (CSA) or dense attention (HCA)."""
+        indexer + top-k + attention (CSA), dense attention (HCA) or
+        window-only attention (sliding-window layers)."""
         self.compress()
-        if not self.cfg.hca:
+        if self.cfg.k > 0:
             self.index()
             self.topk()
         self.attend()
+
+
+class HybridStep:
+    """One decode token through a stack of attention layers, each with its
+    own caches and workspaces (layer kinds and shapes from
+    ``workloads.layer_workloads``): the layers run one after another on the
+    stream, as they would in the model."""
+
+    def __init__(self, layer_cfgs, batches, device="cuda:0"):
+        self.layers = [CSAStep(c, b, device) for c, b in zip(layer_cfgs, batches)]
+
+    def run(self) -> None:
+        for layer in self.layers:
+            layer.run()

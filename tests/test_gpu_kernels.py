@@ -351,6 +351,16 @@ def test_attend_window_edges(storage):
     assert np.array_equal(from_dev(out)[0, 0], np.tile(decode(v)[0, 0], (H, 1)).astype(np.float32))
 
 
+@pytest.mark.parametrize("storage", ["f32", "bf16"])
+def test_attend_window_only(storage):
+    """Sliding-window-only attention (the hybrid stack's first layers):
+    k = 0, no compressed entry is read."""
+    say("attend window only", storage)
+    err, rel = _attend_case(storage, 2, 3, 64, 128, 1, 0, 128, 300, [1000, 5000], seed=720)
+    assert err <= (1e-4 if storage == "f32" else 2e-2), err
+    assert rel <= (1e-5 if storage == "f32" else 1e-2), rel
+
+
 @pytest.mark.parametrize("storage,m", [("bf16", 128), ("bf16", 4), ("f32", 4)])
 def test_hca_parity(storage, m):
     say("hca", storage, m)

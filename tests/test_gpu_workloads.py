@@ -151,6 +151,40 @@ def test_decode_1m_mxfp4_full():
     _decode_workload(WL.DECODE_1M_MXFP4, sample=[1])
 
 
+def test_hybrid_stack_layers():
+    """A hybrid decode stack at a 16K context (2 sliding-window layers, then
+    CSA / HCA alternating, own caches each): every layer of every sequence
+    against the oracle."""
+    from long_context_sparse_16_amd.pipeline import HybridStep
+    cfg = WL.HYBRID_DECODE_128K_BF16.replace(B=2, pos0=16384, n_ctx_entries=4096, planted=4)
+    say("workload", cfg.name, "16K")
+    lcfgs = WL.layer_workloads(cfg)
+    batches = [WL.make_batch(c) for c in lcfgs]
+    hs = HybridStep(lcfgs, batches)
+    hs.run()
+    torch.cuda.synchronize()
+    for layer, c, batch in zip(hs.layers, lcfgs, batches):
+        out = from_dev(layer.out)
+        for b in range(cfg.B):
+            kc, vc = decode(batch["kc"][b]), decode(batch["vc"][b])
+            pos = c.pos0 + np.arange(c.T)
+            if c.k > 0:
+                err, rel, overlap = _stage_parity(layer, c, batch, b, np.arange(c.T), kc, vc)
+                assert overlap >= 0.99, (c.name, overlap)
+            else:
+                if c.hca:
+                    ref, _ = oracle.hca_attend(decode(batch["q"][b]), kc, vc, decode(batch["kr"][b]),
+                                               decode(batch["vr"][b]), c.raw_pos0, pos, c.m, c.W,
+                                               c.scale)
+                else:
+                    ref, _ = oracle.attend(decode(batch["q"][b]), kc, vc, np.zeros((c.T, 0), np.int64),
+                                           decode(batch["kr"][b]), decode(batch["vr"][b]),
+                                           c.raw_pos0, pos, c.W, c.scale)
+                err, rel = float(np.max(np.abs(out[b] - ref))), rel_l2(out[b], ref)
+            say(c.name, "seq", b, "max-abs", err, "rel-l2", rel)
+            assert err <= 2e-2 and rel <= 1e-2, (c.name, b)
+
+
 def test_hca_decode_1m_bf16_full():
     cfg = WL.HCA_DECODE_1M_BF16
     say("workload", cfg.name)

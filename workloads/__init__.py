@@ -50,6 +50,8 @@ class Workload:
     storage: str = "bf16"      # "f32" or "bf16" (K/V, q, q_I)
     ki_fp8: bool = False       # indexer keys / queries stored as e4m3 + scale
     ki_mxfp4: bool = False     # indexer keys / queries stored as MXFP4
+    swa: bool = False          # sliding-window-only attention (no compressed entries read)
+    layers: tuple = ()         # hybrid stack: per-layer kinds "swa" / "csa" / "hca"
     planted: int = 0           # planted high-affinity entries per sequence
     planted_spread: bool = False  # evenly spaced (else seeded distinct random)
     description: str = ""
@@ -60,7 +62,7 @@ class Workload:
 
     @property
     def hca(self) -> bool:
-        return self.k == 0
+        return self.k == 0 and not self.swa
 
     @property
     def n_cap(self) -> int:
@@ -125,8 +127,19 @@ DECODE_1M_MXFP4 = DECODE_1M_FP8.replace(
     description="CSA decode at 1M, MXFP4 indexer keys/queries (E2M1 + E8M0 "
                 "per 32): batch 4 x 262144 entries, top-k 1024, 64 planted")
 
+# A hybrid stack of attention layers for one decode token ("DeepSeek V4
+# technical review", takeshell.com, 2.3 "Hybrid Architecture Design": the
+# first 2 layers are pure sliding-window attention, then CSA and HCA
+# alternate).  Every layer has its own caches; the layer count (8) is this
+# build's choice (the pages give none).
+HYBRID_DECODE_128K_BF16 = DECODE_128K_BF16.replace(
+    name="hybrid_decode_128k_bf16", number=6,
+    layers=("swa", "swa", "csa", "hca", "csa", "hca", "csa", "hca"),
+    description="hybrid decode stack, bf16: 2 sliding-window layers then CSA / HCA "
+                "alternating (8 layers, own caches each), batch 32 x 131072 tokens")
+
 WORKLOADS = [TINY_PREFILL_F32, DECODE_128K_BF16, PREFILL_256K_BF16,
-             HCA_DECODE_1M_BF16, DECODE_1M_FP8, DECODE_1M_MXFP4]
+             HCA_DECODE_1M_BF16, DECODE_1M_FP8, DECODE_1M_MXFP4, HYBRID_DECODE_128K_BF16]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
 
@@ -200,7 +213,7 @@ def make_sequence(cfg: Workload, b: int) -> dict:
     vr = _normal(rng, (cfg.R, d))
     z = _normal(rng, (cfg.n_new_tokens, d))
     q = _normal(rng, (cfg.T, cfg.H, d))
-    if not cfg.hca:
+    if cfg.k > 0:
         qi = _normal(rng, (cfg.T, cfg.H_I, cfg.d_I))
         w = rng.random((cfg.T, cfg.H_I), dtype=np.float32)
         out["qi"] = _store(cfg, qi)
@@ -226,6 +239,26 @@ def make_batch(cfg: Workload, sequences=None) -> dict:
     seqs = range(cfg.B) if sequences is None else sequences
     per = [make_sequence(cfg, b) for b in seqs]
     return {key: np.stack([p[key] for p in per]) for key in per[0]}
+
+
+def layer_workloads(cfg: Workload) -> list:
+    """The per-layer workloads of a hybrid stack: each has its own seed
+    (number 100 * cfg.number + layer).  CSA layers keep cfg's indexer and
+    top-k; HCA layers compress at m' = 128 (entries = context / 128);
+    sliding-window layers read only the window (one placeholder entry)."""
+    out = []
+    for i, kind in enumerate(cfg.layers):
+        base = cfg.replace(name=f"{cfg.name}/{i}:{kind}", number=100 * cfg.number + i, layers=())
+        if kind == "csa":
+            out.append(base)
+        elif kind == "hca":
+            out.append(base.replace(m=128, n_ctx_entries=cfg.pos0 // 128, H_I=0, d_I=0, k=0,
+                                    planted=0))
+        elif kind == "swa":
+            out.append(base.replace(n_ctx_entries=1, H_I=0, d_I=0, k=0, planted=0, swa=True))
+        else:
+            raise ValueError(kind)
+    return out
 
 
 def tiny(cfg: Workload, **kw) -> Workload:
