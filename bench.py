@@ -158,32 +158,37 @@ def _oracle_sequence(cfg, s):
     """The oracle's whole step for one sequence's inputs ``s``."""
     import numpy as np
     import oracle
-    if True:
-        dec = oracle.bf16_decode if s["kc"].dtype == np.uint16 else (lambda a: a.astype(np.float64))
-        pos = cfg.pos0 + np.arange(cfg.T)
-        kc, vc = dec(s["kc"]), dec(s["vc"])
-        if cfg.hca:
-            oracle.hca_attend(dec(s["q"]), kc, vc, dec(s["kr"]), dec(s["vr"]), cfg.raw_pos0, pos,
-                              cfg.m, cfg.W, cfg.scale)
-        elif cfg.swa:
-            idx = np.zeros((cfg.T, 0), np.int64)
-            oracle.attend(dec(s["q"]), kc, vc, idx, dec(s["kr"]), dec(s["vr"]), cfg.raw_pos0, pos,
-                          cfg.W, cfg.scale)
-        else:
-            qi, ki = dec(s["qi"]), kc
-            if cfg.ki_fp8:
-                kcode, ksc = oracle.quantize_fp8_rows(kc.astype(np.float32))
-                qcode, qsc = oracle.quantize_fp8_rows(qi.astype(np.float32))
-                ki = oracle.e4m3_decode(kcode) * ksc[:, None]
-                qi = oracle.e4m3_decode(qcode) * qsc[..., None]
-            if cfg.ki_mxfp4:
-                ki = oracle.mxfp4_decode_rows(*oracle.quantize_mxfp4_rows(kc.astype(np.float32)))
-                qi = oracle.mxfp4_decode_rows(*oracle.quantize_mxfp4_rows(qi.astype(np.float32)))
-            S = oracle.indexer_scores(qi, s["w"], ki, pos, cfg.m)
-            V = oracle.visible_count(pos, cfg.m)
-            idx = np.stack([oracle.topk_select(S[i], int(V[i]), cfg.k) for i in range(cfg.T)])
-            oracle.attend(dec(s["q"]), kc, vc, idx, dec(s["kr"]), dec(s["vr"]), cfg.raw_pos0, pos,
-                          cfg.W, cfg.scale)
+    dec = oracle.bf16_decode if s["kc"].dtype == np.uint16 else (lambda a: a.astype(np.float64))
+    pos = cfg.pos0 + np.arange(cfg.T)
+    kc, vc = dec(s["kc"]), dec(s["vc"])
+    if cfg.block_end:
+        # the block completed by the query token: its last m raw rows
+        r0 = cfg.R - cfg.m
+        z = s["z"][r0:]
+        kc = np.vstack([kc, oracle.compress(dec(s["kr"][r0:]), z, cfg.m)])
+        vc = np.vstack([vc, oracle.compress(dec(s["vr"][r0:]), z, cfg.m)])
+    if cfg.hca:
+        oracle.hca_attend(dec(s["q"]), kc, vc, dec(s["kr"]), dec(s["vr"]), cfg.raw_pos0, pos,
+                          cfg.m, cfg.W, cfg.scale)
+    elif cfg.swa:
+        idx = np.zeros((cfg.T, 0), np.int64)
+        oracle.attend(dec(s["q"]), kc, vc, idx, dec(s["kr"]), dec(s["vr"]), cfg.raw_pos0, pos,
+                      cfg.W, cfg.scale)
+    else:
+        qi, ki = dec(s["qi"]), kc
+        if cfg.ki_fp8:
+            kcode, ksc = oracle.quantize_fp8_rows(kc.astype(np.float32))
+            qcode, qsc = oracle.quantize_fp8_rows(qi.astype(np.float32))
+            ki = oracle.e4m3_decode(kcode) * ksc[:, None]
+            qi = oracle.e4m3_decode(qcode) * qsc[..., None]
+        if cfg.ki_mxfp4:
+            ki = oracle.mxfp4_decode_rows(*oracle.quantize_mxfp4_rows(kc.astype(np.float32)))
+            qi = oracle.mxfp4_decode_rows(*oracle.quantize_mxfp4_rows(qi.astype(np.float32)))
+        S = oracle.indexer_scores(qi, s["w"], ki, pos, cfg.m)
+        V = oracle.visible_count(pos, cfg.m)
+        idx = np.stack([oracle.topk_select(S[i], int(V[i]), cfg.k) for i in range(cfg.T)])
+        oracle.attend(dec(s["q"]), kc, vc, idx, dec(s["kr"]), dec(s["vr"]), cfg.raw_pos0, pos,
+                      cfg.W, cfg.scale)
 
 
 def main():
@@ -298,6 +303,12 @@ def main():
             step.topk()
         st["topk"] = timed(index_topk) - st["index"]
     st["attend"] = timed(step.attend)
+    if cfg.block_end:
+        # the fused selection (block compression inside the indexer launch,
+        # then top-k) against the same step with separate compress launches
+        st["select_fused"] = timed(step.select)
+        st["compress_unfused"] = timed(step.compress)
+        st["step_unfused"] = timed(step.run_unfused)
     st["step_events"] = step_event_ms
     cfg = cfg_all
 

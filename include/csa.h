@@ -226,6 +226,41 @@ int csa_index_topk(const void* qi, int qi_dtype, const void* qi_scale,
                    int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa_decode_index_topk -- the selection half of a decode step, one new
+ * query token per sequence, with the block compression folded into the
+ * indexer launch (takeshell.com 2.1: every m tokens become one entry by
+ * weighted aggregation, then the indexer scores the query against every
+ * visible entry and keeps the top-k).  For sequence b the query sits at
+ * t = pos0[b].  When t completes a block ((t + 1) % m == 0 and
+ * (t + 1) / m <= n_cap), entry j = (t + 1) / m - 1 of kc and vc is first
+ * written as in csa_compress from the raw rows of positions t-m+1 .. t
+ * (bit-identical to csa_compress on those rows), and is then scored with
+ * the rest; otherwise kc and vc are not written.  The indexer keys are the
+ * compressed keys kc themselves.  Results are those of csa_compress (K and
+ * V) followed by csa_index_topk, in one indexer launch plus the top-k.
+ *
+ *   qi     [B][H_I][d] bf16;  w [B][H_I] fp32
+ *   kc,vc  [B][n_cap][d] bf16 (read; entry j written as above)
+ *   kr,vr  [B][R][d] bf16; row r holds position raw_pos0[b] + r.  A block
+ *          whose raw rows are not all inside the buffer is not written
+ *          (a caller error).
+ *   zk,zv  [B][R][d] fp32 compressor logits of the raw rows (may be equal)
+ *   raw_pos0, pos0 [B] int64 (device)
+ *   scores [B][n_cap] fp32 or NULL (then kept in the workspace), idx
+ *          [B][k] int32, ws: as csa_index_topk with T = 1.
+ * Supported: d in {64, 128, 256}; 1 <= H_I <= 64; 1 <= m <= 4 (CSA's
+ * compression ratio; larger m: csa_compress then csa_index_topk); R >= m;
+ * 1 <= k <= 4096.
+ */
+int csa_decode_index_topk(const void* qi, const float* w, void* kc, void* vc,
+                          const void* kr, const void* vr, const float* zk,
+                          const float* zv, const int64_t* raw_pos0, int64_t R,
+                          const int64_t* pos0, int64_t B, int64_t H_I,
+                          int64_t d, int64_t n_cap, int m, int act, int k,
+                          float* scores, int32_t* idx, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
  * csa_attend -- core attention over the selected compressed entries plus
  * the sliding window, in one softmax (octagono.org "Hybrid Attention":
  * attend only to the selected entries, with a 128-token window for local

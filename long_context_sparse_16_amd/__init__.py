@@ -58,6 +58,8 @@ _SIGNATURES = {
     "csa_index_topk_workspace_size": (_sz, [_i64, _i64, _i64, _i, _i]),
     "csa_index_topk": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i,
                             _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "csa_decode_index_topk": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64,
+                                   _i64, _i64, _i64, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "csa_attend_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i, _i]),
     "csa_attend": (_i, [_vp, _i, _vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _i64, _vp, _i64, _i64, _i64,
                         _i64, _i64, _i, _f, _vp, _vp, _vp, _sz, _vp]),
@@ -317,6 +319,46 @@ def csa_index_topk(qi, w, ki, pos0, m: int, k: int, act="relu", qi_scale=None, k
     return scores, idx
 
 
+def csa_decode_index_topk(qi, w, kc, vc, kr, vr, zk, zv, raw_pos0, pos0, m: int, k: int,
+                          act="relu", scores=None, idx=None, ws=None, keep_scores=True,
+                          stream=None):
+    """Decode step selection with the block compression fused into the
+    indexer: when a query's position t completes a block, entry
+    (t + 1) / m - 1 of kc / vc is formed from the raw rows first (as
+    csa_compress would), then indexer scores and top-k as csa_index_topk
+    with ki = kc.  qi [B, 1, H_I, d] bf16, w [B, 1, H_I], kr / vr [B, R, d]
+    bf16, zk / zv [B, R, d] fp32.  Returns (scores or None, idx)."""
+    dev = _dev(qi, w, kc, pos0)
+    B, T, H_I, d, n_cap = _index_shapes(qi, w, kc, pos0)
+    if T != 1:
+        raise ValueError("one query token per sequence (qi [B, 1, H_I, d])")
+    for name, t in (("qi", qi), ("kc", kc), ("vc", vc), ("kr", kr), ("vr", vr)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+    if vc.shape != kc.shape:
+        raise ValueError("vc must have kc's shape")
+    if kr.dim() != 3 or kr.shape[0] != B or kr.shape[2] != d or vr.shape != kr.shape:
+        raise ValueError("kr, vr must be [B, R, d]")
+    for name, t in (("zk", zk), ("zv", zv)):
+        if t.shape != kr.shape or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 [B, R, d]")
+    if raw_pos0.shape != (B,) or raw_pos0.dtype != torch.int64:
+        raise ValueError("raw_pos0 must be int64 [B]")
+    for name, t in (("vc", vc), ("kr", kr), ("vr", vr), ("zk", zk), ("zv", zv),
+                    ("raw_pos0", raw_pos0)):
+        _contig(name, t)
+    if scores is None and keep_scores:
+        scores = torch.empty((B, 1, n_cap), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+    ws, nbytes = _workspace(ws, csa_index_topk_workspace_size(B, 1, n_cap, k, scores is None), dev)
+    _check("csa_decode_index_topk", _lib.csa_decode_index_topk(
+        _ptr(qi), _ptr(w), _ptr(kc), _ptr(vc), _ptr(kr), _ptr(vr), _ptr(zk), _ptr(zv),
+        _ptr(raw_pos0), kr.shape[1], _ptr(pos0), B, H_I, d, n_cap, int(m), _act_code(act), int(k),
+        _ptr(scores), _ptr(idx), _ptr(ws), nbytes, _stream(stream, dev)))
+    return scores, idx
+
+
 # ---------------------------------------------------------------- attention
 
 def _attend_shapes(q, kc, vc, kr, vr, raw_pos0, pos0, W):
@@ -402,5 +444,6 @@ __all__ = [
     "csa_compress", "csa_quantize_fp8_rows", "csa_quantize_mxfp4_rows", "csa_index_scores",
     "csa_topk",
     "csa_topk_workspace_size", "csa_index_topk", "csa_index_topk_workspace_size",
+    "csa_decode_index_topk",
     "csa_attend", "csa_attend_workspace_size", "hca_attend", "hca_attend_workspace_size",
 ]

@@ -237,7 +237,7 @@ int csa_index_scores(const void* qi, int qi_dtype, const void* qi_scale, const f
     hist = need ? csa::topk_hist_ptr(topk_ws, B, T) : nullptr;
   }
   return hip_result(csa::launch_index_scores(qi, qi_dtype, qi_scale, w, ki, ki_scale, pos0, B, T,
-                                             H_I, d_I, n_cap, m, act, scores, hist, k,
+                                             H_I, d_I, n_cap, m, act, scores, hist, k, nullptr,
                                              static_cast<hipStream_t>(stream)),
                     fn);
 }
@@ -295,7 +295,57 @@ int csa_index_topk(const void* qi, int qi_dtype, const void* qi_scale, const flo
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint32_t* hist = csa::topk_hist_ptr(topk_ws, B, T);
   rc = hip_result(csa::launch_index_scores(qi, qi_dtype, qi_scale, w, ki, ki_scale, pos0, B, T,
-                                           H_I, d_I, n_cap, m, act, sc, hist, k, s),
+                                           H_I, d_I, n_cap, m, act, sc, hist, k, nullptr, s),
+                  fn);
+  if (rc) return rc;
+  return hip_result(csa::launch_topk(sc, pos0, B, T, n_cap, m, k, idx, topk_ws, hist != nullptr, s),
+                    fn);
+}
+
+int csa_decode_index_topk(const void* qi, const float* w, void* kc, void* vc, const void* kr,
+                          const void* vr, const float* zk, const float* zv,
+                          const int64_t* raw_pos0, int64_t R, const int64_t* pos0, int64_t B,
+                          int64_t H_I, int64_t d, int64_t n_cap, int m, int act, int k,
+                          float* scores, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "csa_decode_index_topk";
+  CSA_REQUIRE(kc && vc && kr && vr && zk && zv && raw_pos0, CSA_ERR_NULL,
+              "%s: kc, vc, kr, vr, zk, zv and raw_pos0 must be non-NULL", fn);
+  CSA_REQUIRE(R >= m && m >= 1, CSA_ERR_SHAPE, "%s: the raw buffer must hold a block (R >= m >= 1)",
+              fn);
+  CSA_REQUIRE(m <= csa::kFusedMaxM, CSA_ERR_UNSUPPORTED, "%s: m must be <= %d", fn,
+              csa::kFusedMaxM);
+  CSA_REQUIRE(aligned16(vc), CSA_ERR_SHAPE, "%s: vc must be 16-byte aligned", fn);
+  const int64_t T = 1;
+  const bool scores_in_ws = scores == nullptr;
+  const size_t need = csa_index_topk_workspace_size(B, T, n_cap, k, scores_in_ws ? 1 : 0);
+  CSA_REQUIRE(need == 0 || (ws && ws_bytes >= need), CSA_ERR_WORKSPACE,
+              "%s: workspace of %zu bytes needed, got %zu", fn, need, ws ? ws_bytes : 0);
+  CSA_REQUIRE(ws == nullptr || aligned16(ws), CSA_ERR_WORKSPACE, "%s: ws must be 16-byte aligned",
+              fn);
+  float* sc = scores;
+  char* topk_ws = static_cast<char*>(ws);
+  if (scores_in_ws && ws) {
+    sc = static_cast<float*>(ws);
+    topk_ws += round_up(static_cast<size_t>(B * T) * n_cap * sizeof(float));
+  }
+  int rc = check_index_args(qi, CSA_BF16, nullptr, w, kc, CSA_BF16, nullptr, pos0, B, T, H_I, d,
+                            n_cap, m, act, sc, fn);
+  if (rc) return rc;
+  rc = check_topk_args(sc, pos0, B, T, n_cap, m, k, idx, fn);
+  if (rc) return rc;
+  csa::FusedCompress fc;
+  fc.kr = static_cast<const uint16_t*>(kr);
+  fc.vr = static_cast<const uint16_t*>(vr);
+  fc.zk = zk;
+  fc.zv = zv;
+  fc.raw_pos0 = raw_pos0;
+  fc.kc = static_cast<uint16_t*>(kc);
+  fc.vc = static_cast<uint16_t*>(vc);
+  fc.R = R;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* hist = csa::topk_hist_ptr(topk_ws, B, T);
+  rc = hip_result(csa::launch_index_scores(qi, CSA_BF16, nullptr, w, kc, nullptr, pos0, B, T, H_I,
+                                           d, n_cap, m, act, sc, hist, k, &fc, s),
                   fn);
   if (rc) return rc;
   return hip_result(csa::launch_topk(sc, pos0, B, T, n_cap, m, k, idx, topk_ws, hist != nullptr, s),

@@ -194,6 +194,99 @@ __device__ __forceinline__ f32x4 mma_fp4(u32x4 a, u32x4 b, f32x4 c, uint32_t sa,
                                                           static_cast<int>(sb));
 }
 
+// ------------------------------------------------------------- compressor
+
+template <typename T>
+__device__ __forceinline__ float load_elem(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_elem<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+constexpr int kCompressBatch = 8;
+
+// The m tokens of one channel of a block with m <= NB, loaded together
+// (indices clamped to the last token; the repeats are never used).
+template <int NB, typename T>
+__device__ __forceinline__ void compress_load(const T* x, const float* z, int64_t stride, int m,
+                                              float (&zz)[NB], float (&xx)[NB]) {
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int64_t o = static_cast<int64_t>(min(j, m - 1)) * stride;
+    zz[j] = z[o];
+    xx[j] = load_elem<T>(x, o);
+  }
+}
+
+// The entry value from loaded tokens (m <= NB): softmax over the m logits
+// weights the m values, accumulated in token order.  The result does not
+// depend on NB.
+template <int NB>
+__device__ __forceinline__ float compress_loaded(const float (&zz)[NB], const float (&xx)[NB],
+                                                 int m) {
+  float zmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) zmax = fmaxf(zmax, zz[j]);  // repeats change nothing
+  float num = 0.f, den = 0.f;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    if (j < m) {
+      const float a = expf(zz[j] - zmax);
+      den += a;
+      num = fmaf(a, xx[j], num);
+    }
+  }
+  return num / den;
+}
+
+// One channel of one compressed entry: the softmax over the block's m
+// tokens of their logits z weights the tokens' values x ("DeepSeek V4
+// technical review", takeshell.com, section 2.1: each block of m tokens is
+// aggregated into one entry).  x and z step by `stride` elements per
+// token.  The compressor kernel and the decode indexer's fused block
+// compression compute entries with these functions, so the two give the
+// same bits.  Longer blocks are read in batches of kCompressBatch tokens
+// (every load of a batch in flight at once), in the same arithmetic order.
+template <typename T>
+__device__ __forceinline__ float compress_channel(const T* x, const float* z, int64_t stride,
+                                                  int m) {
+  constexpr int kB = kCompressBatch;
+  if (m <= kB) {
+    float zz[kB], xx[kB];
+    compress_load<kB>(x, z, stride, m, zz, xx);
+    return compress_loaded<kB>(zz, xx, m);
+  }
+  float zmax = -INFINITY;
+  for (int i0 = 0; i0 < m; i0 += kB) {
+    float zz[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) zz[j] = z[static_cast<int64_t>(min(i0 + j, m - 1)) * stride];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) zmax = fmaxf(zmax, zz[j]);
+  }
+  float num = 0.f, den = 0.f;
+  for (int i0 = 0; i0 < m; i0 += kB) {
+    float zz[kB], xx[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const int64_t o = static_cast<int64_t>(min(i0 + j, m - 1)) * stride;
+      zz[j] = z[o];
+      xx[j] = load_elem<T>(x, o);
+    }
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      if (i0 + j < m) {
+        const float a = expf(zz[j] - zmax);
+        den += a;
+        num = fmaf(a, xx[j], num);
+      }
+    }
+  }
+  return num / den;
+}
+
 __device__ __forceinline__ int64_t visible_entries(int64_t t, int m, int64_t n_cap) {
   int64_t v = (t + 1) / m;
   if (v < 0) v = 0;

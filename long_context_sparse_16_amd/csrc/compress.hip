@@ -15,15 +15,6 @@
 namespace csa {
 
 template <typename T>
-__device__ __forceinline__ float load_elem(const T* p, int64_t i);
-template <>
-__device__ __forceinline__ float load_elem<float>(const float* p, int64_t i) { return p[i]; }
-template <>
-__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int64_t i) {
-  return bf16_to_f32(p[i]);
-}
-
-template <typename T>
 __device__ __forceinline__ void store_elem(T* p, int64_t i, float v);
 template <>
 __device__ __forceinline__ void store_elem<float>(float* p, int64_t i, float v) { p[i] = v; }
@@ -44,15 +35,7 @@ __global__ __launch_bounds__(256) void compress_kernel(
   const int64_t c = e - j * d;
   const T* xb = x + b * x_sb + (j * m) * d + c;
   const float* zb = z + b * z_sb + (j * m) * d + c;
-  float zmax = -INFINITY;
-  for (int i = 0; i < m; ++i) zmax = fmaxf(zmax, zb[static_cast<int64_t>(i) * d]);
-  float num = 0.f, den = 0.f;
-  for (int i = 0; i < m; ++i) {
-    const float a = expf(zb[static_cast<int64_t>(i) * d] - zmax);
-    den += a;
-    num = fmaf(a, load_elem<T>(xb, static_cast<int64_t>(i) * d), num);
-  }
-  store_elem<T>(cache, b * n_cap * d + (first_entry + j) * d + c, num / den);
+  store_elem<T>(cache, b * n_cap * d + (first_entry + j) * d + c, compress_channel(xb, zb, d, m));
 }
 
 int launch_compress(const void* x, int dtype, const float* z, int64_t B, int64_t n_tok,

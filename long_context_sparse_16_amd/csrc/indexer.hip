@@ -157,13 +157,13 @@ constexpr int idx_group_tiles() {
 // are already in flight (two register buffers, statically indexed so they
 // stay in VGPRs).  The host sizes the chunks so that the grid is about one
 // workgroup per compute unit.
-template <int DTYPE, int DI, bool RELU, bool HIST>
+template <int DTYPE, int DI, bool RELU, bool HIST, bool FUSED>
 __global__ __launch_bounds__(256) void indexer_kernel(
     const uint8_t* __restrict__ qi, const float* __restrict__ qi_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ ki,
     const float* __restrict__ ki_scale, const int64_t* __restrict__ pos0, int64_t T,
     int H_I, int64_t n_cap, int m, int tiles_per_wg, float* __restrict__ scores,
-    uint32_t* __restrict__ hist, int topk_k) {
+    uint32_t* __restrict__ hist, int topk_k, FusedCompress fc) {
   using Tr = IdxTraits<DTYPE, DI>;
   constexpr int kVec = Tr::kLaneBytes / 16;  // 16-byte loads per lane per row
   constexpr int kRowBytes = Tr::kRowBytes;
@@ -211,6 +211,43 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const int n_grp = (n_ent_wg + kGroupEnt - 1) / kGroupEnt;
   const uint8_t* kwg = kib + e_begin * kRowBytes;          // wave-uniform
   const uint32_t lane_off = static_cast<uint32_t>(col * kRowBytes + g * Tr::kLaneBytes);
+
+  // Fused block compression (bf16, one query per sequence): the workgroup
+  // whose entries include the block completed by the new token (entry
+  // V - 1, its last) forms that entry, K and V, from the raw rows.  The
+  // wave that scores the last group (the one holding entry V - 1) issues
+  // the raw loads first, and just before scoring that group computes the
+  // entry, stores it to kc / vc and puts the key into the loaded group
+  // through its own LDS slot, so nothing waits for the global stores and
+  // no other wave is involved.  A block whose raw rows are not all in the
+  // raw buffer is left unwritten (and entry V - 1 is scored as stored).
+  bool comp_ok = false;
+  int64_t comp_src = 0;
+  const int comp_grp = n_grp - 1;
+  const int comp_wave = comp_grp & (kIdxWaves - 1);
+  if constexpr (DTYPE == 1 && FUSED) {
+    if (fc.kr != nullptr && T == 1 && (t + 1) % m == 0 && (t + 1) / m <= n_cap &&
+        V - 1 >= e_begin && V - 1 < e_begin + n_ent_wg) {
+      const int64_t r0 = t - m + 1 - fc.raw_pos0[b];
+      comp_ok = r0 >= 0 && r0 + m <= fc.R;
+      comp_src = (b * fc.R + r0) * DI;
+    }
+  }
+  // The block's tokens (m <= kFusedMaxM) are preloaded into registers.
+  constexpr int kCh = (DI + 63) / 64;  // channels per lane of the fused compression
+  constexpr int kPre = kFusedMaxM;
+  float ckz[kCh][kPre], ckx[kCh][kPre], cvz[kCh][kPre], cvx[kCh][kPre];
+  __shared__ __attribute__((aligned(16))) uint16_t s_newk[DTYPE == 1 && FUSED ? DI : 1];
+  if constexpr (DTYPE == 1 && FUSED) {
+    if (comp_ok && wave == comp_wave) {
+#pragma unroll
+      for (int i = 0; i < kCh; ++i) {
+        const int64_t o = comp_src + min(lane + 64 * i, DI - 1);
+        compress_load<kPre>(fc.kr + o, fc.zk + o, DI, m, ckz[i], ckx[i]);
+        compress_load<kPre>(fc.vr + o, fc.zv + o, DI, m, cvz[i], cvx[i]);
+      }
+    }
+  }
 
   // FP8: each lane also fetches the fp32 scale of its column's entry with
   // the group's keys; MXFP4: the entry's four E8M0 block scales as one
@@ -314,6 +351,43 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     }
   };
 
+  // compute_group, with the fused compression's new key put into the
+  // group that holds entry V - 1 (the lanes of that column, and the
+  // clamped past-the-end ones of a tail group, hold its row)
+  auto compute_last = [&](int grp, u32x4 (&bt)[kGroup][kVec], const KScale (&kd)[kGroup])
+      __attribute__((always_inline)) {
+    if constexpr (DTYPE == 1 && FUSED) {
+      if (comp_ok && grp == comp_grp) {
+        const int64_t dst = (b * n_cap + V - 1) * DI;
+#pragma unroll
+        for (int i = 0; i < kCh; ++i) {
+          const int c = lane + 64 * i;
+          const float kv = compress_loaded<kPre>(ckz[i], ckx[i], m);
+          const float vv = compress_loaded<kPre>(cvz[i], cvx[i], m);
+          if (c < DI) {
+            const uint16_t kb = f32_to_bf16(kv);
+            s_newk[c] = kb;
+            fc.kc[dst + c] = kb;
+            fc.vc[dst + c] = f32_to_bf16(vv);
+          }
+        }
+        // this wave's LDS writes are done before its reads below
+        __builtin_amdgcn_wave_barrier();
+        const int e_last = n_ent_wg - 1 - grp * kGroupEnt;  // entry V - 1 within the group
+        const u32x4* nk = reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const uint8_t*>(s_newk) + g * Tr::kLaneBytes);
+#pragma unroll
+        for (int tt = 0; tt < kGroup; ++tt) {
+          if (tt * kIdxTile + col >= e_last) {
+#pragma unroll
+            for (int v = 0; v < kVec; ++v) bt[tt][v] = nk[v];
+          }
+        }
+      }
+    }
+    compute_group(grp, bt, kd);
+  };
+
   if (do_hist) {
     for (int i = threadIdx.x; i < kTopkHistBins; i += 256) s_hist[i] = 0u;
     __syncthreads();
@@ -334,12 +408,12 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     compute_group(wave + j * kIdxWaves, buf0, ks0);
     // (past the end this re-reads this wave's last group, from cache)
     load_full(wave + min(j + 2, n_my - 1) * kIdxWaves, buf0, ks0);
-    compute_group(wave + (j + 1) * kIdxWaves, buf1, ks1);
+    compute_last(wave + (j + 1) * kIdxWaves, buf1, ks1);
   }
-  if (j < n_my) compute_group(wave + j * kIdxWaves, buf0, ks0);
+  if (j < n_my) compute_last(wave + j * kIdxWaves, buf0, ks0);
   if (n_full < n_grp && (n_full & (kIdxWaves - 1)) == wave) {
     load_tail(n_full, buf0, ks0);
-    compute_group(n_full, buf0, ks0);
+    compute_last(n_full, buf0, ks0);
   }
   if (do_hist) {
     __syncthreads();
@@ -557,7 +631,7 @@ template <int DTYPE, int DI>
 static void launch_idx_t(const void* qi, const float* qs, const float* w, const void* ki,
                          const float* ks, const int64_t* pos0, int64_t B, int64_t T, int H_I,
                          int64_t n_cap, int m, bool relu, float* scores, uint32_t* hist, int k,
-                         hipStream_t s) {
+                         const FusedCompress& fc, hipStream_t s) {
   // Chunk size: about one workgroup per compute unit over the whole grid
   // (measured best for this streaming kernel), in whole rounds of load
   // groups for the 4 waves, and no more than a row.
@@ -574,7 +648,7 @@ static void launch_idx_t(const void* qi, const float* qs, const float* w, const 
   auto q8 = static_cast<const uint8_t*>(qi);
   auto k8 = static_cast<const uint8_t*>(ki);
   if ((DTYPE == 1 || DTYPE == 2) && DI == 128 && T >= kPfTok && hist == nullptr &&
-      n_cap <= kPfMaxEntries) {
+      n_cap <= kPfMaxEntries && fc.kr == nullptr) {
     constexpr int DT = DTYPE == 2 ? 2 : 1;
     dim3 pgrid(static_cast<unsigned>((T + kPfTok - 1) / kPfTok), static_cast<unsigned>(B));
     if (relu)
@@ -585,10 +659,17 @@ static void launch_idx_t(const void* qi, const float* qs, const float* w, const 
                                                                      H_I, n_cap, m, scores);
     return;
   }
-#define CSA_IDX_GO(R, HST)                                                                 \
-  indexer_kernel<DTYPE, DI, R, HST><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, pos0, T, H_I,  \
-                                                         n_cap, m, tiles_per_wg, scores,   \
-                                                         hist, k)
+  // (the fused block compression has kernels of its own, so the plain
+  // decode kernels keep their register allocation)
+#define CSA_IDX_GO(R, HST)                                                                   \
+  do {                                                                                       \
+    if (DTYPE == 1 && fc.kr != nullptr)                                                      \
+      indexer_kernel<DTYPE, DI, R, HST, DTYPE == 1><<<grid, 256, 0, s>>>(                    \
+          q8, qs, w, k8, ks, pos0, T, H_I, n_cap, m, tiles_per_wg, scores, hist, k, fc);     \
+    else                                                                                     \
+      indexer_kernel<DTYPE, DI, R, HST, false><<<grid, 256, 0, s>>>(                         \
+          q8, qs, w, k8, ks, pos0, T, H_I, n_cap, m, tiles_per_wg, scores, hist, k, fc);     \
+  } while (0)
   if (relu) {
     if (hist) CSA_IDX_GO(true, true); else CSA_IDX_GO(true, false);
   } else {
@@ -600,15 +681,19 @@ static void launch_idx_t(const void* qi, const float* qs, const float* w, const 
 int launch_index_scores(const void* qi, int dtype, const void* qs_v, const float* w,
                         const void* ki, const void* ks_v, const int64_t* pos0, int64_t B,
                         int64_t T, int64_t H_I, int64_t d_I, int64_t n_cap, int m, int act,
-                        float* scores, uint32_t* hist, int k, hipStream_t s) {
+                        float* scores, uint32_t* hist, int k, const FusedCompress* fc,
+                        hipStream_t s) {
   const bool relu = act == 0;
+  const FusedCompress none{};
+  const FusedCompress& fcr = fc ? *fc : none;
   const int H = static_cast<int>(H_I);
   // (fp32 scales for FP8; for MXFP4 the kernel reads them as E8M0 bytes)
   const float* qs = static_cast<const float*>(qs_v);
   const float* ks = static_cast<const float*>(ks_v);
 #define CSA_IDX_CASE(DT, DI)                                                                  \
   if (dtype == DT && d_I == DI) {                                                             \
-    launch_idx_t<DT, DI>(qi, qs, w, ki, ks, pos0, B, T, H, n_cap, m, relu, scores, hist, k, s); \
+    launch_idx_t<DT, DI>(qi, qs, w, ki, ks, pos0, B, T, H, n_cap, m, relu, scores, hist, k,    \
+                         fcr, s);                                                             \
     return hipGetLastError() == hipSuccess ? 0 : -1;                                          \
   }
   CSA_IDX_CASE(0, 64)

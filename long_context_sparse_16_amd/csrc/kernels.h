@@ -9,6 +9,23 @@
 
 namespace csa {
 
+// Block compression fused into the decode indexer (bf16 caches): when the
+// new token at t completes a block ((t + 1) % m == 0), the block's K and V
+// entries are formed from the raw rows of positions t - m + 1 .. t and
+// written to entry (t + 1) / m - 1 of kc / vc before that entry is scored.
+// kr == nullptr disables it.  Blocks of at most kFusedMaxM tokens.
+constexpr int kFusedMaxM = 4;
+struct FusedCompress {
+  const uint16_t* kr;        // [B][R][d] raw keys; row r holds position raw_pos0[b] + r
+  const uint16_t* vr;        // [B][R][d] raw values
+  const float* zk;           // [B][R][d] compressor logits of the raw keys
+  const float* zv;           // [B][R][d] compressor logits of the raw values
+  const int64_t* raw_pos0;   // [B]
+  uint16_t* kc;              // [B][n_cap][d] compressed keys (the indexer keys)
+  uint16_t* vc;              // [B][n_cap][d] compressed values
+  int64_t R;
+};
+
 int launch_compress(const void* x, int dtype, const float* z, int64_t B, int64_t n_tok, int64_t d,
                     int m, int64_t x_sb, int64_t z_sb, void* cache, int64_t n_cap,
                     int64_t first_entry, hipStream_t s);
@@ -26,10 +43,12 @@ constexpr int kTopkHistBins = 1 << (32 - kTopkDigit1Shift);
 // hist (nullable): per-row first-digit histogram accumulated for csa_topk
 // (rows with V <= k are skipped).  It must be zero on entry.  qs / ks are
 // fp32 row scales (dtype 2, FP8) or E8M0 block-scale bytes (dtype 3, MXFP4).
+// fc (nullable): block compression fused into the launch (bf16, T == 1).
 int launch_index_scores(const void* qi, int dtype, const void* qs, const float* w,
                         const void* ki, const void* ks, const int64_t* pos0, int64_t B,
                         int64_t T, int64_t H_I, int64_t d_I, int64_t n_cap, int m, int act,
-                        float* scores, uint32_t* hist, int k, hipStream_t s);
+                        float* scores, uint32_t* hist, int k, const FusedCompress* fc,
+                        hipStream_t s);
 
 // Rows (B*T) up to this count use the multi-workgroup split top-k, which
 // needs a workspace; more rows use one workgroup per row and none.

@@ -7,6 +7,8 @@ time them individually:
   compress()  new raw tokens -> appended compressed K/V entries
   index()     Lightning Indexer scores
   topk()      per-query top-k entry indices
+  select()    decode at a block boundary: the block compression, indexer
+              and top-k with the compression folded into the indexer launch
   attend()    attention over the selected entries + sliding window
               (HCA: dense attention over every visible entry + window)
 
@@ -20,7 +22,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (csa_attend, csa_compress, csa_index_scores, csa_quantize_fp8_rows,
+from . import (csa_attend, csa_compress, csa_decode_index_topk, csa_index_scores,
+               csa_quantize_fp8_rows,
                csa_quantize_mxfp4_rows, csa_topk,
                csa_topk_workspace_size, csa_attend_workspace_size, hca_attend,
                hca_attend_workspace_size, workspace)
@@ -56,7 +59,11 @@ class CSAStep:
             self.vc[:, :cfg.n_ctx_entries] = to_device(batch["vc"], dev, st)
         self.kr = to_device(batch["kr"], dev, st)
         self.vr = to_device(batch["vr"], dev, st)
-        self.z = to_device(batch["z"], dev, st) if cfg.n_new_tokens else None
+        self.z = to_device(batch["z"], dev, st) if cfg.n_new_tokens or cfg.block_end else None
+        # a block-completing decode step with bf16 indexer keys folds the
+        # compression into the indexer launch
+        self.fused_select = (cfg.block_end and cfg.T == 1 and st == "bf16" and cfg.k > 0
+                             and not (cfg.ki_fp8 or cfg.ki_mxfp4))
         self.q = to_device(batch["q"], dev, st)
         self.pos0 = torch.full((B,), cfg.pos0, dtype=torch.int64, device=dev)
         self.raw_pos0 = torch.full((B,), cfg.raw_pos0, dtype=torch.int64, device=dev)
@@ -109,6 +116,15 @@ class CSAStep:
 
     def compress(self) -> None:
         cfg = self.cfg
+        if cfg.block_end:
+            # the block ends at the query token: the last m raw rows
+            r0 = cfg.R - cfg.m
+            z = self.z[:, r0:].contiguous()
+            csa_compress(self.kr[:, r0:].contiguous(), z, self.kc, cfg.m, cfg.n_ctx_entries)
+            csa_compress(self.vr[:, r0:].contiguous(), z, self.vc, cfg.m, cfg.n_ctx_entries)
+            if cfg.ki_fp8 or cfg.ki_mxfp4:
+                self.quantize_keys(cfg.n_ctx_entries, cfg.n_cap)
+            return
         if not cfg.n_new_tokens:
             return
         x_k = self.kr[:, cfg.raw_before:cfg.raw_before + cfg.n_new_tokens]
@@ -117,6 +133,14 @@ class CSAStep:
         csa_compress(x_v, self.z, self.vc, cfg.m, cfg.n_ctx_entries)
         if cfg.ki_fp8 or cfg.ki_mxfp4:
             self.quantize_keys(cfg.n_ctx_entries, cfg.n_cap)
+
+    def select(self) -> None:
+        """Block compression + indexer + top-k of a block-completing decode
+        step, the compression inside the indexer launch."""
+        cfg = self.cfg
+        csa_decode_index_topk(self.qi, self.w, self.kc, self.vc, self.kr, self.vr, self.z,
+                              self.z, self.raw_pos0, self.pos0, cfg.m, cfg.k, act=self.act,
+                              scores=self.scores, idx=self.idx, ws=self.topk_ws)
 
     def index(self) -> None:
         """Indexer scores; also builds the top-k histogram in the top-k
@@ -155,6 +179,18 @@ class CSAStep:
         """The whole step: compress (if the step completes blocks), then
         indexer + top-k + attention (CSA), dense attention (HCA) or
         window-only attention (sliding-window layers)."""
+        if self.fused_select:
+            self.select()
+            self.attend()
+            return
+        self.compress()
+        if self.cfg.k > 0:
+            self.index()
+            self.topk()
+        self.attend()
+
+    def run_unfused(self) -> None:
+        """The same step with the block compression as separate launches."""
         self.compress()
         if self.cfg.k > 0:
             self.index()

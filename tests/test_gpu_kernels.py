@@ -187,6 +187,97 @@ def test_indexer_parity(kind, H_I, d_I, act):
     assert worst <= 1.0, worst
 
 
+@pytest.mark.parametrize("m,d,H_I", [(4, 128, 64), (4, 64, 20), (1, 128, 64), (3, 256, 33)])
+def test_decode_index_topk_fused_compress(m, d, H_I):
+    """csa_decode_index_topk: the block completed by the query token is
+    compressed inside the indexer launch (bit-identical to csa_compress on
+    the same raw rows), then scored with the older entries; scores and
+    indices equal csa_index_topk's on the updated cache, bit for bit, and
+    the oracle's.  Sequences: a block completing at the full cache (entry
+    in the last workgroup), at a short prefix (first workgroup), a token
+    that completes no block, and a block whose first raw row lies before
+    the raw buffer (left unwritten)."""
+    say("decode index+topk fused compress", m, d, H_I)
+    rng = np.random.default_rng(900 + m + d + H_I)
+    B, n_cap, R, k = 4, 3000, 16, 64
+    t = np.array([m * n_cap - 1, m * 37 - 1, m * 500 + (1 if m > 1 else 0), m * 900 - 1], np.int64)
+    if m == 1:
+        t[2] = 499  # every token completes a block when m == 1: a short prefix instead
+    raw_pos0 = t - R + 1
+    raw_pos0[3] = t[3] - m + 2                       # block starts one row before the buffer
+    V = oracle.visible_count(t, m)
+    kc0 = rng.standard_normal((B, n_cap, d))
+    vc0 = rng.standard_normal((B, n_cap, d))
+    for b in range(B):                               # sentinel where a block may land
+        kc0[b, V[b] - 1] = 7.0
+        vc0[b, V[b] - 1] = -7.0
+    kc0, vc0 = bf16_codes(kc0), bf16_codes(vc0)
+    kr = bf16_codes(rng.standard_normal((B, R, d)))
+    vr = bf16_codes(rng.standard_normal((B, R, d)))
+    zk = (rng.standard_normal((B, R, d)) * 2).astype(np.float32)
+    zv = (rng.standard_normal((B, R, d)) * 2).astype(np.float32)
+    qi = bf16_codes(rng.standard_normal((B, 1, H_I, d)))
+    w = rng.random((B, 1, H_I)).astype(np.float32)
+    kc, vc = to_dev(kc0), to_dev(vc0)
+    pos0_d, raw_d = to_dev(t), to_dev(raw_pos0)
+    sc, idx = csa.csa_decode_index_topk(to_dev(qi), to_dev(w), kc, vc, to_dev(kr), to_dev(vr),
+                                        to_dev(zk), to_dev(zv), raw_d, pos0_d, m, k)
+    torch.cuda.synchronize()
+    kc1, vc1 = from_dev(kc), from_dev(vc)
+    completes = [True, True, m == 1, False]
+    for b in range(B):
+        j = V[b] - 1
+        rest = np.ones(n_cap, bool)
+        rest[j] = False
+        assert np.array_equal(kc1[b, rest], kc0[b, rest]) and np.array_equal(vc1[b, rest], vc0[b, rest])
+        if not completes[b]:
+            assert np.array_equal(kc1[b, j], kc0[b, j]) and np.array_equal(vc1[b, j], vc0[b, j]), b
+            continue
+        r0 = t[b] - m + 1 - raw_pos0[b]
+        for name, x, z, got in (("k", kr, zk, kc1), ("v", vr, zv, vc1)):
+            # csa_compress on the same rows: the same bits
+            one = to_dev(bf16_codes(np.zeros((1, 1, d))))
+            csa.csa_compress(to_dev(x[b:b + 1, r0:r0 + m].copy()), to_dev(z[b:b + 1, r0:r0 + m].copy()),
+                             one, m, 0)
+            assert np.array_equal(got[b, j], from_dev(one)[0, 0]), (name, b)
+            xv = decode(x[b, r0:r0 + m])
+            ref = oracle.compress(xv, z[b, r0:r0 + m], m)[0]
+            assert np.all(np.abs(decode(got[b, j]) - ref) <= compress_bound(ref, xv[None], m)[0])
+    # scores and indices: those of csa_index_topk on the updated cache
+    sc2, idx2 = csa.csa_index_topk(to_dev(qi), to_dev(w), kc, pos0_d, m, k)
+    got_s, got_i = from_dev(sc), from_dev(idx)
+    ref_s2 = from_dev(sc2)
+    for b in range(B):
+        assert np.array_equal(got_s[b, 0, :V[b]], ref_s2[b, 0, :V[b]]), b
+    assert np.array_equal(got_i, from_dev(idx2))
+    kv = decode(kc1)
+    for b in range(B):
+        ref = oracle.indexer_scores(decode(qi[b]), w[b], kv[b], t[b:b + 1], m)
+        assert score_close(got_s[b, 0, :V[b]], ref[0, :V[b]]) <= 1.0
+        want = oracle.topk_select(got_s[b, 0].astype(np.float64), int(V[b]), k)
+        assert np.array_equal(got_i[b, 0], want), b
+
+
+def test_decode_index_topk_validation():
+    say("decode index+topk validation")
+    B, n_cap, R, d, m = 2, 256, 8, 128, 4
+    z = lambda *s: torch.zeros(s, device=DEV)
+    bf = lambda *s: torch.zeros(s, device=DEV, dtype=torch.bfloat16)
+    pos = torch.full((B,), 100, dtype=torch.int64, device=DEV)
+    args = dict(qi=bf(B, 1, 64, d), w=z(B, 1, 64), kc=bf(B, n_cap, d), vc=bf(B, n_cap, d),
+                kr=bf(B, R, d), vr=bf(B, R, d), zk=z(B, R, d), zv=z(B, R, d), raw_pos0=pos,
+                pos0=pos)
+    with pytest.raises(ValueError):   # two query tokens
+        csa.csa_decode_index_topk(**{**args, "qi": bf(B, 2, 64, d), "w": z(B, 2, 64)}, m=m, k=16)
+    with pytest.raises(ValueError):   # logits of the wrong shape
+        csa.csa_decode_index_topk(**{**args, "zk": z(B, R - 1, d)}, m=m, k=16)
+    with pytest.raises(csa.CSAError):  # raw buffer shorter than a block
+        csa.csa_decode_index_topk(**{**args, "kr": bf(B, 2, d), "vr": bf(B, 2, d),
+                                     "zk": z(B, 2, d), "zv": z(B, 2, d)}, m=m, k=16)
+    with pytest.raises(csa.CSAError):  # blocks longer than the fused path takes
+        csa.csa_decode_index_topk(**args, m=8, k=16)
+
+
 # --------------------------------------------------------------------- top-k
 
 def _topk_case(scores, V, k):

@@ -143,6 +143,37 @@ def test_decode_128k_bf16_full():
     assert torch.equal(i1, step.idx) and torch.equal(o1.view(torch.int32), step.out.view(torch.int32))
 
 
+def test_decode_128k_bf16_block_end_full():
+    """A decode step whose token completes a block, with the compression
+    fused into the indexer launch: the new entry, scores, indices and
+    outputs equal the unfused step (separate csa_compress launches) bit for
+    bit; the new entry matches the oracle's compressor, and the whole path
+    the oracle on sampled sequences."""
+    cfg = WL.DECODE_128K_BF16_BLOCK_END
+    step = _decode_workload(cfg, sample=[])
+    assert step.fused_select
+    batch = WL.make_batch(cfg)
+    ref = CSAStep(cfg, batch)
+    ref.run_unfused()
+    torch.cuda.synchronize()
+    for name in ("kc", "vc", "scores", "idx", "out"):
+        a, b = getattr(step, name), getattr(ref, name)
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b), name
+    j, m, R = cfg.n_ctx_entries, cfg.m, cfg.R
+    kc_all, vc_all = from_dev(step.kc), from_dev(step.vc)
+    for b in range(cfg.B):
+        for x, got in ((batch["kr"][b], kc_all[b, j]), (batch["vr"][b], vc_all[b, j])):
+            xv = decode(x[R - m:])
+            want = oracle.compress(xv, batch["z"][b][R - m:], m)[0]
+            assert np.all(np.abs(decode(got) - want) <= compress_bound(want, xv[None], m)[0]), b
+    for b in (0, 17, 31):
+        kc, vc = decode(kc_all[b]), decode(vc_all[b])
+        err, rel, overlap = _stage_parity(step, cfg, batch, b, np.arange(cfg.T), kc, vc)
+        say(cfg.name, "seq", b, "max-abs", err, "rel-l2", rel, "overlap", overlap)
+        assert err <= 2e-2 and rel <= 1e-2 and overlap >= 0.99
+
+
 def test_decode_1m_fp8_full():
     _decode_workload(WL.DECODE_1M_FP8, sample=[0, 3])
 

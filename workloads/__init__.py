@@ -52,6 +52,8 @@ class Workload:
     ki_mxfp4: bool = False     # indexer keys / queries stored as MXFP4
     swa: bool = False          # sliding-window-only attention (no compressed entries read)
     layers: tuple = ()         # hybrid stack: per-layer kinds "swa" / "csa" / "hca"
+    block_end: bool = False    # decode token completes a block: the step compresses
+                               # it into entry n_ctx_entries (logits for every raw row)
     planted: int = 0           # planted high-affinity entries per sequence
     planted_spread: bool = False  # evenly spaced (else seeded distinct random)
     description: str = ""
@@ -66,7 +68,7 @@ class Workload:
 
     @property
     def n_cap(self) -> int:
-        return self.n_ctx_entries + self.n_new_tokens // self.m
+        return self.n_ctx_entries + self.n_new_tokens // self.m + (1 if self.block_end else 0)
 
     @property
     def raw_pos0(self) -> int:
@@ -138,8 +140,19 @@ HYBRID_DECODE_128K_BF16 = DECODE_128K_BF16.replace(
     description="hybrid decode stack, bf16: 2 sliding-window layers then CSA / HCA "
                 "alternating (8 layers, own caches each), batch 32 x 131072 tokens")
 
+# The 128K decode at a step whose token completes a block: t = 131071, so
+# (t + 1) % 4 == 0 and block 32767 (positions 131068 .. 131071, the last 4
+# raw rows) is compressed inside the step and is visible to its own query.
+DECODE_128K_BF16_BLOCK_END = DECODE_128K_BF16.replace(
+    name="csa_decode_128k_bf16_block_end", number=7, pos0=131071, n_ctx_entries=32767,
+    block_end=True,
+    description="CSA decode, bf16, at a block boundary: the step compresses the block "
+                "its token completes (entry 32767) and scores it with the 32767 older "
+                "entries; otherwise as csa_decode_128k_bf16")
+
 WORKLOADS = [TINY_PREFILL_F32, DECODE_128K_BF16, PREFILL_256K_BF16,
-             HCA_DECODE_1M_BF16, DECODE_1M_FP8, DECODE_1M_MXFP4, HYBRID_DECODE_128K_BF16]
+             HCA_DECODE_1M_BF16, DECODE_1M_FP8, DECODE_1M_MXFP4, HYBRID_DECODE_128K_BF16,
+             DECODE_128K_BF16_BLOCK_END]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
 
@@ -198,6 +211,7 @@ def make_sequence(cfg: Workload, b: int) -> dict:
     kr, vr     [R, d]               raw K/V at positions raw_pos0 .. pos0+T-1
     z          [n_new_tokens, d]    compressor logits (float32) for the raw
                                     tokens pos0 .. pos0+n_new_tokens-1
+                                    (block_end: [R, d], one row per raw row)
     qi         [T, H_I, d_I]        indexer queries (absent for HCA)
     w          [T, H_I]             indexer head weights, float32
     q          [T, H, d]            attention queries
@@ -211,7 +225,7 @@ def make_sequence(cfg: Workload, b: int) -> dict:
     vc = _normal(rng, (cfg.n_ctx_entries, d))
     kr = _normal(rng, (cfg.R, d))
     vr = _normal(rng, (cfg.R, d))
-    z = _normal(rng, (cfg.n_new_tokens, d))
+    z = _normal(rng, (cfg.R if cfg.block_end else cfg.n_new_tokens, d))
     q = _normal(rng, (cfg.T, cfg.H, d))
     if cfg.k > 0:
         qi = _normal(rng, (cfg.T, cfg.H_I, cfg.d_I))
