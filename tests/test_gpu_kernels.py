@@ -254,7 +254,7 @@ def test_decode_index_topk_fused_compress(m, d, H_I):
     for b in range(B):
         ref = oracle.indexer_scores(decode(qi[b]), w[b], kv[b], t[b:b + 1], m)
         assert score_close(got_s[b, 0, :V[b]], ref[0, :V[b]]) <= 1.0
-        want = oracle.topk_select(got_s[b, 0].astype(np.float64), int(V[b]), k)
+        want = oracle.topk_select(got_s[b, 0, :V[b]].astype(np.float64), int(V[b]), k)
         assert np.array_equal(got_i[b, 0], want), b
 
 
