@@ -49,6 +49,7 @@ from .csa import (
     hca_attend,
     csa_forward,
 )
+from .backward import attend_backward, hca_attend_backward, compress_backward
 
 __all__ = [
     "bf16_decode",
@@ -68,4 +69,7 @@ __all__ = [
     "hca_indices",
     "hca_attend",
     "csa_forward",
+    "attend_backward",
+    "hca_attend_backward",
+    "compress_backward",
 ]
