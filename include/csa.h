@@ -314,6 +314,75 @@ int hca_attend(const void* q, int q_dtype, const void* kc, const void* vc,
                int W, float scale, float* out, float* lse, void* ws,
                size_t ws_bytes, void* stream);
 
+/*
+ * Backward pass (fp32 gradients).  The pages describe a model trained end
+ * to end -- a learned token-level compressor (octagono.org "Hybrid
+ * Attention: CSA and HCA"), an indexer QK path trained quantization-aware
+ * (dataforcee.us "Muon Optimizer and FP4 QAT") -- without a formula for
+ * the backward pass; these calls compute the derivatives of csa_attend /
+ * hca_attend / csa_compress.  No gradient flows through the top-k
+ * selection.  All reductions are deterministic (no float atomics): two
+ * runs give identical bits.
+ *
+ * csa_attend_backward -- for csa_attend's inputs, its outputs out / lse and
+ * the upstream gradient dout (d loss / d out), writes
+ *   dq    [B][T][H][d] fp32
+ *   dkc, dvc [B][n_cap][d] fp32: every entry; the sum over all query rows
+ *         and heads that attended it (0 for entries nobody selected)
+ *   dkr, dvr [B][R][d] fp32: every raw row, the same over the windows
+ * (with one query row t, head h over its key list, p = exp(scale q.K - lse),
+ * dp = V dout, D = dout . out, ds = p (dp - D): dq = scale ds K,
+ * dK += scale ds q, dV += p dout).  idx rows must be strictly ascending
+ * then -1 padded (as csa_topk emits them).  ws: device workspace of
+ * csa_attend_backward_workspace_size() bytes (B*T*(k+W)*d*8: the per-row
+ * key/value contributions; contents on entry do not matter).
+ * Supported: q/kv dtypes F32 or BF16 (equal), d in {64, 128}, H <= 64.
+ */
+size_t csa_attend_backward_workspace_size(int64_t B, int64_t T, int64_t d,
+                                          int k, int W);
+int csa_attend_backward(const void* q, int q_dtype, const void* kc,
+                        const void* vc, int kv_dtype, const int32_t* idx,
+                        int k, const void* kr, const void* vr,
+                        const int64_t* raw_pos0, int64_t R,
+                        const int64_t* pos0, int64_t B, int64_t T,
+                        int64_t H, int64_t d, int64_t n_cap, int W,
+                        float scale, const float* out, const float* lse,
+                        const float* dout, float* dq, float* dkc, float* dvc,
+                        float* dkr, float* dvr, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* hca_attend_backward -- the same for hca_attend (every visible entry
+ * attended, compression ratio m); n_cap <= 65536; workspace of
+ * hca_attend_backward_workspace_size() bytes. */
+size_t hca_attend_backward_workspace_size(int64_t B, int64_t T, int64_t d,
+                                          int64_t n_cap, int W);
+int hca_attend_backward(const void* q, int q_dtype, const void* kc,
+                        const void* vc, int kv_dtype, int m, const void* kr,
+                        const void* vr, const int64_t* raw_pos0, int64_t R,
+                        const int64_t* pos0, int64_t B, int64_t T,
+                        int64_t H, int64_t d, int64_t n_cap, int W,
+                        float scale, const float* out, const float* lse,
+                        const float* dout, float* dq, float* dkc, float* dvc,
+                        float* dkr, float* dvr, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/*
+ * csa_compress_backward -- gradients of csa_compress with respect to its
+ * tokens and logits: for block j, channel c, w_i = softmax_i(logits) and
+ * c_j = sum_i w_i x_i,
+ *   dx[jm+i, c]      = w_i dc[j, c]
+ *   dlogits[jm+i, c] = w_i (x[jm+i, c] - c_j) dc[j, c]
+ *   x       [B][n_tok][d] x_dtype (F32 or BF16), batch stride x_sb elements
+ *   logits  [B][n_tok][d] fp32, batch stride z_sb elements
+ *   dc      [B][n_tok/m][d] fp32 (gradient of the n_tok/m compressed rows)
+ *   dx, dlogits [B][n_tok][d] fp32
+ * n_tok % m == 0.
+ */
+int csa_compress_backward(const void* x, int x_dtype, const float* logits,
+                          const float* dc, int64_t B, int64_t n_tok,
+                          int64_t d, int m, int64_t x_sb, int64_t z_sb,
+                          float* dx, float* dlogits, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,6 +64,16 @@ _SIGNATURES = {
     "csa_attend": (_i, [_vp, _i, _vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _i64, _vp, _i64, _i64, _i64,
                         _i64, _i64, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "hca_attend_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64, _i]),
+    "csa_attend_backward_workspace_size": (_sz, [_i64, _i64, _i64, _i, _i]),
+    "csa_attend_backward": (_i, [_vp, _i, _vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _i64, _vp, _i64,
+                                 _i64, _i64, _i64, _i64, _i, _f, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _sz, _vp]),
+    "hca_attend_backward_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i]),
+    "hca_attend_backward": (_i, [_vp, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _i64, _vp, _i64, _i64,
+                                 _i64, _i64, _i64, _i, _f, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _sz, _vp]),
+    "csa_compress_backward": (_i, [_vp, _i, _vp, _vp, _i64, _i64, _i64, _i, _i64, _i64, _vp, _vp,
+                                   _vp]),
     "hca_attend": (_i, [_vp, _i, _vp, _vp, _i, _i, _vp, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64,
                         _i64, _i, _f, _vp, _vp, _vp, _sz, _vp]),
 }
@@ -438,6 +448,79 @@ def hca_attend(q, kc, vc, m: int, kr, vr, raw_pos0, pos0, W: int, scale: float, 
     return out, lse
 
 
+# ------------------------------------------------------------- backward pass
+
+def _bwd_common(q, kc, vc, kr, vr, raw_pos0, pos0, W, out, lse, dout):
+    dev = _dev(q, kc, vc, pos0)
+    B, T, H, d, n_cap, R = _attend_shapes(q, kc, vc, kr, vr, raw_pos0, pos0, W)
+    for name, t, shape in (("out", out, (B, T, H, d)), ("lse", lse, (B, T, H)),
+                           ("dout", dout, (B, T, H, d))):
+        if t.shape != shape or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 {list(shape)}")
+        _contig(name, t)
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    grads = {"dq": f32(B, T, H, d), "dkc": f32(B, n_cap, d), "dvc": f32(B, n_cap, d),
+             "dkr": f32(B, R, d) if R else None, "dvr": f32(B, R, d) if R else None}
+    return dev, B, T, H, d, n_cap, R, grads
+
+
+def csa_attend_backward(q, kc, vc, idx, kr, vr, raw_pos0, pos0, W: int, scale: float, out, lse,
+                        dout, ws=None, stream=None) -> dict:
+    """Gradients of csa_attend: returns dict dq, dkc, dvc, dkr, dvr (fp32);
+    out / lse are the forward's outputs, dout the upstream gradient."""
+    dev, B, T, H, d, n_cap, R, gr = _bwd_common(q, kc, vc, kr, vr, raw_pos0, pos0, W, out, lse,
+                                                dout)
+    if idx.dim() != 3 or idx.shape[:2] != (B, T) or idx.dtype != torch.int32:
+        raise ValueError("idx must be int32 [B, T, k]")
+    _contig("idx", idx)
+    k = idx.shape[2]
+    need = int(_lib.csa_attend_backward_workspace_size(B, T, d, k, int(W)))
+    ws, nbytes = _workspace(ws, need, dev)
+    _check("csa_attend_backward", _lib.csa_attend_backward(
+        _ptr(q), _dtype_code(q), _ptr(kc), _ptr(vc), _dtype_code(kc), _ptr(idx), k, _ptr(kr),
+        _ptr(vr), _ptr(raw_pos0), R, _ptr(pos0), B, T, H, d, n_cap, int(W), float(scale),
+        _ptr(out), _ptr(lse), _ptr(dout), _ptr(gr["dq"]), _ptr(gr["dkc"]), _ptr(gr["dvc"]),
+        _ptr(gr["dkr"]), _ptr(gr["dvr"]), _ptr(ws), nbytes, _stream(stream, dev)))
+    return gr
+
+
+def hca_attend_backward(q, kc, vc, m: int, kr, vr, raw_pos0, pos0, W: int, scale: float, out, lse,
+                        dout, ws=None, stream=None) -> dict:
+    """Gradients of hca_attend (dict as csa_attend_backward)."""
+    dev, B, T, H, d, n_cap, R, gr = _bwd_common(q, kc, vc, kr, vr, raw_pos0, pos0, W, out, lse,
+                                                dout)
+    need = int(_lib.hca_attend_backward_workspace_size(B, T, d, n_cap, int(W)))
+    ws, nbytes = _workspace(ws, need, dev)
+    _check("hca_attend_backward", _lib.hca_attend_backward(
+        _ptr(q), _dtype_code(q), _ptr(kc), _ptr(vc), _dtype_code(kc), int(m), _ptr(kr), _ptr(vr),
+        _ptr(raw_pos0), R, _ptr(pos0), B, T, H, d, n_cap, int(W), float(scale), _ptr(out),
+        _ptr(lse), _ptr(dout), _ptr(gr["dq"]), _ptr(gr["dkc"]), _ptr(gr["dvc"]), _ptr(gr["dkr"]),
+        _ptr(gr["dvr"]), _ptr(ws), nbytes, _stream(stream, dev)))
+    return gr
+
+
+def csa_compress_backward(x: torch.Tensor, logits: torch.Tensor, dc: torch.Tensor, m: int,
+                          stream=None):
+    """Gradients of csa_compress with respect to x and logits, for dc
+    [B, n_tok/m, d] fp32.  Returns (dx, dlogits), fp32 [B, n_tok, d]."""
+    dev = _dev(x, logits, dc)
+    B, n_tok, d = x.shape
+    for name, t in (("x", x), ("logits", logits)):
+        if t.shape != (B, n_tok, d) or t.stride(2) != 1 or (n_tok > 1 and t.stride(1) != d):
+            raise ValueError(f"{name} must be [B, n_tok, d] with contiguous rows")
+    if logits.dtype != torch.float32 or dc.dtype != torch.float32:
+        raise TypeError("logits and dc must be float32")
+    if n_tok % m or dc.shape != (B, n_tok // m, d):
+        raise ValueError("dc must be [B, n_tok / m, d] and n_tok a multiple of m")
+    _contig("dc", dc)
+    dx = torch.empty((B, n_tok, d), dtype=torch.float32, device=dev)
+    dz = torch.empty((B, n_tok, d), dtype=torch.float32, device=dev)
+    _check("csa_compress_backward", _lib.csa_compress_backward(
+        _ptr(x), _dtype_code(x), _ptr(logits), _ptr(dc), B, n_tok, d, int(m), x.stride(0),
+        logits.stride(0), _ptr(dx), _ptr(dz), _stream(stream, dev)))
+    return dx, dz
+
+
 __all__ = [
     "CSAError", "LIB_PATH", "abi_version", "last_error", "header_functions", "workspace",
     "csa_workspace_clear",
@@ -446,4 +529,5 @@ __all__ = [
     "csa_topk_workspace_size", "csa_index_topk", "csa_index_topk_workspace_size",
     "csa_decode_index_topk",
     "csa_attend", "csa_attend_workspace_size", "hca_attend", "hca_attend_workspace_size",
+    "csa_attend_backward", "hca_attend_backward", "csa_compress_backward",
 ]

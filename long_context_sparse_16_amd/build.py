@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libcsa.so")
 
-SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "topk.hip", "attend.hip"]
+SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "topk.hip", "attend.hip", "attend_bwd.hip"]
 # Per-source additions.  The indexer's epilogue is pure VALU work next to
 # the MFMAs: with IEEE mode off (its inputs never hold NaN) a ReLU is one
 # v_max_f32 instead of a canonicalize plus max, and the VGPR form of MFMA

@@ -407,4 +407,105 @@ int hca_attend(const void* q, int q_dtype, const void* kc, const void* vc, int k
                     fn);
 }
 
+
+// ------------------------------------------------------------ backward pass
+
+static int check_bwd_args(const float* out, const float* lse, const float* dout, float* dq,
+                          float* dkc, float* dvc, float* dkr, float* dvr, int W, int64_t H,
+                          int64_t d, const char* fn) {
+  CSA_REQUIRE(out && lse && dout && dq && dkc && dvc, CSA_ERR_NULL,
+              "%s: out, lse, dout, dq, dkc and dvc must be non-NULL", fn);
+  CSA_REQUIRE(W == 0 || (dkr && dvr), CSA_ERR_NULL, "%s: dkr and dvr must be non-NULL when W > 0",
+              fn);
+  CSA_REQUIRE(H >= 1 && H <= 64, CSA_ERR_UNSUPPORTED, "%s: H must be in [1, 64]", fn);
+  CSA_REQUIRE(d == 64 || d == 128, CSA_ERR_UNSUPPORTED, "%s: d must be 64 or 128", fn);
+  CSA_REQUIRE(aligned16(out) && aligned16(dout) && aligned16(dq), CSA_ERR_SHAPE,
+              "%s: out, dout and dq must be 16-byte aligned", fn);
+  return CSA_OK;
+}
+
+size_t csa_attend_backward_workspace_size(int64_t B, int64_t T, int64_t d, int k, int W) {
+  if (B < 1 || T < 1 || d < 1 || k < 0 || W < 0) return 0;
+  return round_up(csa::attend_bwd_workspace_bytes(B * T, d, k, W));
+}
+
+size_t hca_attend_backward_workspace_size(int64_t B, int64_t T, int64_t d, int64_t n_cap, int W) {
+  if (B < 1 || T < 1 || d < 1 || n_cap < 1 || W < 0) return 0;
+  return round_up(csa::attend_bwd_workspace_bytes(B * T, d, n_cap, W));
+}
+
+static int attend_backward_impl(const void* q, int q_dtype, const void* kc, const void* vc,
+                                int kv_dtype, const int32_t* idx, int k, int hca_m,
+                                const void* kr, const void* vr, const int64_t* raw_pos0,
+                                int64_t R, const int64_t* pos0, int64_t B, int64_t T, int64_t H,
+                                int64_t d, int64_t n_cap, int W, float scale, const float* out,
+                                const float* lse, const float* dout, float* dq, float* dkc,
+                                float* dvc, float* dkr, float* dvr, void* ws, size_t ws_bytes,
+                                void* stream, const char* fn) {
+  int rc = check_attend_args(q, q_dtype, kc, vc, kv_dtype, kr, vr, raw_pos0, R, pos0, B, T, H, d,
+                             n_cap, W, scale, out, fn);
+  if (rc) return rc;
+  rc = check_bwd_args(out, lse, dout, dq, dkc, dvc, dkr, dvr, W, H, d, fn);
+  if (rc) return rc;
+  CSA_REQUIRE(B * T <= kMaxIndex, CSA_ERR_UNSUPPORTED, "%s: B*T too large", fn);
+  const size_t need = hca_m > 0 ? hca_attend_backward_workspace_size(B, T, d, n_cap, W)
+                                : csa_attend_backward_workspace_size(B, T, d, k, W);
+  CSA_REQUIRE(ws && ws_bytes >= need, CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, got %zu",
+              fn, need, ws ? ws_bytes : 0);
+  CSA_REQUIRE(aligned16(ws), CSA_ERR_WORKSPACE, "%s: ws must be 16-byte aligned", fn);
+  return hip_result(csa::launch_attend_bwd(q, q_dtype, kc, vc, idx, k, hca_m, kr, vr, raw_pos0, R,
+                                           pos0, B, T, H, d, n_cap, W, scale, out, lse, dout, dq,
+                                           dkc, dvc, dkr, dvr, ws,
+                                           static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int csa_attend_backward(const void* q, int q_dtype, const void* kc, const void* vc, int kv_dtype,
+                        const int32_t* idx, int k, const void* kr, const void* vr,
+                        const int64_t* raw_pos0, int64_t R, const int64_t* pos0, int64_t B,
+                        int64_t T, int64_t H, int64_t d, int64_t n_cap, int W, float scale,
+                        const float* out, const float* lse, const float* dout, float* dq,
+                        float* dkc, float* dvc, float* dkr, float* dvr, void* ws, size_t ws_bytes,
+                        void* stream) {
+  const char* fn = "csa_attend_backward";
+  CSA_REQUIRE(idx, CSA_ERR_NULL, "%s: idx must be non-NULL", fn);
+  CSA_REQUIRE(k >= 1 && k <= 65536, CSA_ERR_UNSUPPORTED, "%s: k must be in [1, 65536]", fn);
+  return attend_backward_impl(q, q_dtype, kc, vc, kv_dtype, idx, k, 0, kr, vr, raw_pos0, R, pos0,
+                              B, T, H, d, n_cap, W, scale, out, lse, dout, dq, dkc, dvc, dkr, dvr,
+                              ws, ws_bytes, stream, fn);
+}
+
+int hca_attend_backward(const void* q, int q_dtype, const void* kc, const void* vc, int kv_dtype,
+                        int m, const void* kr, const void* vr, const int64_t* raw_pos0, int64_t R,
+                        const int64_t* pos0, int64_t B, int64_t T, int64_t H, int64_t d,
+                        int64_t n_cap, int W, float scale, const float* out, const float* lse,
+                        const float* dout, float* dq, float* dkc, float* dvc, float* dkr,
+                        float* dvr, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "hca_attend_backward";
+  CSA_REQUIRE(m >= 1, CSA_ERR_SHAPE, "%s: m must be >= 1", fn);
+  CSA_REQUIRE(n_cap <= 65536, CSA_ERR_UNSUPPORTED, "%s: n_cap must be <= 65536", fn);
+  return attend_backward_impl(q, q_dtype, kc, vc, kv_dtype, nullptr, 0, m, kr, vr, raw_pos0, R,
+                              pos0, B, T, H, d, n_cap, W, scale, out, lse, dout, dq, dkc, dvc, dkr,
+                              dvr, ws, ws_bytes, stream, fn);
+}
+
+int csa_compress_backward(const void* x, int x_dtype, const float* logits, const float* dc,
+                          int64_t B, int64_t n_tok, int64_t d, int m, int64_t x_sb, int64_t z_sb,
+                          float* dx, float* dlogits, void* stream) {
+  const char* fn = "csa_compress_backward";
+  CSA_REQUIRE(x && logits && dc && dx && dlogits, CSA_ERR_NULL,
+              "%s: x, logits, dc, dx and dlogits must be non-NULL", fn);
+  CSA_REQUIRE(x_dtype == CSA_F32 || x_dtype == CSA_BF16, CSA_ERR_DTYPE,
+              "%s: x_dtype must be F32 or BF16", fn);
+  CSA_REQUIRE(B >= 1 && B <= kMaxGridY && d >= 1 && m >= 1, CSA_ERR_SHAPE,
+              "%s: need 1 <= B <= %lld, d >= 1, m >= 1", fn, static_cast<long long>(kMaxGridY));
+  CSA_REQUIRE(n_tok >= 0 && n_tok % m == 0, CSA_ERR_SHAPE, "%s: n_tok must be a multiple of m", fn);
+  CSA_REQUIRE(x_sb >= n_tok * d && z_sb >= n_tok * d, CSA_ERR_SHAPE,
+              "%s: batch strides must be >= n_tok * d", fn);
+  if (n_tok == 0) return CSA_OK;
+  return hip_result(csa::launch_compress_bwd(x, x_dtype, logits, dc, B, n_tok, d, m, x_sb, z_sb,
+                                             dx, dlogits, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // extern "C"

@@ -1,0 +1,457 @@
+// Backward pass of core attention and of the compressor.
+//
+// The pages describe a model trained end to end (a learned token-level
+// compressor, octagono.org "Hybrid Attention: CSA and HCA"; the indexer's
+// QK path trained quantization-aware, dataforcee.us "Muon Optimizer and FP4
+// QAT") but give no formula for the backward pass; these kernels compute the
+// derivatives of the forward definitions.  For one query row t and head h
+// over its key list (logits s = scale K q, p = softmax(s) = exp(s - lse),
+// o = p V, upstream gradient dout):
+//   dp = V dout,  D = dout . o,  ds = p (dp - D)
+//   dq = scale ds K,  dK += scale ds q,  dV += p dout
+// with the key/value gradients summed over heads and over every query that
+// attends the row.  No gradient flows through the top-k selection.
+//
+// Determinism (no float atomics): the row kernel writes each query row's
+// per-slot key/value gradients (already summed over the row's heads) to a
+// staging buffer; the reduction kernels then give every compressed entry
+// and raw row one workgroup that finds the query rows referencing it and
+// sums their contributions in ascending row order.  Every result is
+// bitwise reproducible.
+//
+// Arithmetic: fp32 throughout (bf16 inputs are exact in fp32), on the
+// 16x16x4 fp32 MFMA.
+#include "common.h"
+#include "kernels.h"
+
+namespace csa {
+
+struct BwdParams {
+  const uint8_t* q;
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const int32_t* idx;
+  const uint8_t* kr;
+  const uint8_t* vr;
+  const int64_t* raw_pos0;
+  const int64_t* pos0;
+  const float* out;
+  const float* lse;
+  const float* dout;
+  float* dq;
+  float* gk;  // [rows][n_ent_max + W][D] key-gradient contributions
+  float* gv;  // [rows][n_ent_max + W][D] value-gradient contributions
+  float* dkc;
+  float* dvc;
+  float* dkr;
+  float* dvr;
+  int64_t T, H, n_cap, R;
+  int k, W, m;
+  int n_ent_max;  // entry slots per staging row: k (CSA) or n_cap (HCA)
+  float scale;
+};
+
+constexpr int kBwdChunk = 32;   // keys per chunk
+constexpr float kLog2eBwd = 1.4426950408889634f;
+constexpr int kBwdHeads = 64;   // head slots (4 waves x 16)
+
+template <int DTYPE>
+__device__ __forceinline__ void load_row_f32(const uint8_t* src, int e0, float* dst, int n);
+
+// n consecutive elements of a storage row starting at element e0, as fp32
+// (bf16: 8 per 16-byte load; fp32: 4 per load); n is 8 (bf16) or 4 (fp32).
+template <>
+__device__ __forceinline__ void load_row_f32<1>(const uint8_t* src, int e0, float* dst, int) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(src + e0 * 2);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    dst[2 * i] = __uint_as_float(v[i] << 16);
+    dst[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load_row_f32<0>(const uint8_t* src, int e0, float* dst, int) {
+  const f32x4 v = *reinterpret_cast<const f32x4*>(src + e0 * 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = v[i];
+}
+
+template <int DTYPE, int D, bool HCA>
+__global__ __launch_bounds__(256) void attend_bwd_rows_kernel(BwdParams p) {
+  constexpr int kEb = DTYPE == 1 ? 2 : 4;     // bytes per stored element
+  constexpr int kPer = 16 / kEb;              // elements per 16-byte load
+  constexpr int kPieces = D / kPer;           // 16-byte pieces per row
+  constexpr int kKs = D / 4;                  // fp32 k-steps over the dims
+  constexpr int kDT = D / 16;                 // dim tiles
+  constexpr int kS = D + 4;                   // padded fp32 row stride
+  constexpr int kHs = kBwdHeads + 4;          // padded [key][head] stride
+  __shared__ __attribute__((aligned(16))) float sQ[kBwdHeads][kS];
+  __shared__ __attribute__((aligned(16))) float sdO[kBwdHeads][kS];
+  __shared__ __attribute__((aligned(16))) float sK[kBwdChunk][kS];
+  __shared__ __attribute__((aligned(16))) float sV[kBwdChunk][kS];
+  __shared__ __attribute__((aligned(16))) float sP[kBwdChunk][kHs];
+  __shared__ __attribute__((aligned(16))) float sdS[kBwdChunk][kHs];
+  __shared__ float sD[kBwdHeads];
+  __shared__ int s_valid[kBwdChunk];
+  __shared__ int s_gslot[kBwdChunk];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int64_t row = blockIdx.x;
+  const int64_t b = seq_of_row(row, p.T);
+  const int64_t t = p.pos0[b] + (row - b * p.T);
+  const int64_t rp0 = (p.W > 0 ? p.raw_pos0 : p.pos0)[b];
+  const int64_t n_ent =
+      HCA ? uniform64(visible_entries(t, p.m, p.n_cap)) : static_cast<int64_t>(p.k);
+  const int64_t n_slots = n_ent + p.W;
+  const int64_t H = p.H;
+
+  // q and dout rows (fp32) of all heads; head slots past H hold zeros, so
+  // their probabilities and gradients are zero (lse = +inf below).
+  for (int i = tid; i < kBwdHeads * kPieces; i += 256) {
+    const int h = i / kPieces, pc = i % kPieces;
+    float v[kPer];
+    if (h < H) {
+      load_row_f32<DTYPE>(p.q + ((row * H + h) * D) * kEb, pc * kPer, v, kPer);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) v[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) sQ[h][pc * kPer + e] = v[e];
+  }
+  for (int i = tid; i < kBwdHeads * (D / 4); i += 256) {
+    const int h = i / (D / 4), c4 = i % (D / 4);
+    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (h < H) v = *reinterpret_cast<const f32x4*>(p.dout + (row * H + h) * D + c4 * 4);
+    *reinterpret_cast<f32x4*>(&sdO[h][c4 * 4]) = v;
+  }
+  // D[h] = dout . o: four threads per head, a quarter of the dims each
+  {
+    const int h = tid >> 2, qd = tid & 3;
+    float acc = 0.f;
+    if (h < H) {
+      const float* orow = p.out + (row * H + h) * D + qd * (D / 4);
+      const float* grow = p.dout + (row * H + h) * D + qd * (D / 4);
+      for (int c = 0; c < D / 4; ++c) acc = fmaf(grow[c], orow[c], acc);
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    if (qd == 0) sD[h] = acc;
+  }
+  const int head = wave * 16 + col;
+  const float lse2 = head < H ? p.lse[row * H + head] * kLog2eBwd : INFINITY;
+  const float scale_log2 = p.scale * kLog2eBwd;
+
+  f32x4 dq[kDT];
+#pragma unroll
+  for (int i = 0; i < kDT; ++i) dq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint8_t* kc_b = p.kc + b * p.n_cap * D * kEb;
+  const uint8_t* vc_b = p.vc + b * p.n_cap * D * kEb;
+  const int n_chunks = static_cast<int>((n_slots + kBwdChunk - 1) / kBwdChunk);
+  __syncthreads();
+  const float Dh = sD[head];
+
+  for (int c = 0; c < n_chunks; ++c) {
+    // ---- stage the chunk's key / value rows (fp32) and slot table
+    const int64_t s0 = static_cast<int64_t>(c) * kBwdChunk;
+    if (tid < kBwdChunk) {
+      const int64_t s = s0 + tid;
+      int ok = 0, gs = 0;
+      if (s < n_ent) {
+        const int64_t e = HCA ? s : static_cast<int64_t>(p.idx[row * p.k + s]);
+        ok = e >= 0 && e < p.n_cap;
+        gs = static_cast<int>(s);
+      } else if (s < n_slots) {
+        const int64_t pos = t - p.W + 1 + (s - n_ent);
+        const int64_t rr = pos - rp0;
+        ok = pos >= 0 && rr >= 0 && rr < p.R;
+        gs = p.n_ent_max + static_cast<int>(s - n_ent);
+      }
+      s_valid[tid] = ok;
+      s_gslot[tid] = gs;
+    }
+    for (int i = tid; i < kBwdChunk * kPieces; i += 256) {
+      const int key = i / kPieces, pc = i % kPieces;
+      const int64_t s = s0 + key;
+      const uint8_t* ksrc = kc_b;  // absent keys: row 0 (masked below)
+      const uint8_t* vsrc = vc_b;
+      if (s < n_ent) {
+        const int64_t e = HCA ? s : static_cast<int64_t>(p.idx[row * p.k + s]);
+        if (e >= 0 && e < p.n_cap) {
+          ksrc = kc_b + e * D * kEb;
+          vsrc = vc_b + e * D * kEb;
+        }
+      } else if (s < n_slots) {
+        const int64_t pos = t - p.W + 1 + (s - n_ent);
+        const int64_t rr = pos - rp0;
+        if (pos >= 0 && rr >= 0 && rr < p.R) {
+          ksrc = p.kr + (b * p.R + rr) * D * kEb;
+          vsrc = p.vr + (b * p.R + rr) * D * kEb;
+        }
+      }
+      float kv[kPer], vv[kPer];
+      load_row_f32<DTYPE>(ksrc, pc * kPer, kv, kPer);
+      load_row_f32<DTYPE>(vsrc, pc * kPer, vv, kPer);
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        sK[key][pc * kPer + e] = kv[e];
+        sV[key][pc * kPer + e] = vv[e];
+      }
+    }
+    __syncthreads();
+
+    // ---- phase A (wave = 16 heads, all 32 keys): S^T, dP^T, P, dS, dq
+    f32x4 sT[2], dpT[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x4 as = f32x4{0.f, 0.f, 0.f, 0.f}, ad = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int ks = 0; ks < kKs; ++ks) {
+        const float kq = sK[kt * 16 + col][ks * 4 + g];
+        const float vq = sV[kt * 16 + col][ks * 4 + g];
+        as = mma_f32(kq, sQ[head][ks * 4 + g], as);
+        ad = mma_f32(vq, sdO[head][ks * 4 + g], ad);
+      }
+      sT[kt] = as;
+      dpT[kt] = ad;
+    }
+    float ps[2][4], dss[2][4];
+    {
+#pragma clang fp contract(off)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kt * 16 + g * 4 + i;
+          const float pr = s_valid[key] ? exp2f(sT[kt][i] * scale_log2 - lse2) : 0.f;
+          ps[kt][i] = pr;
+          dss[kt][i] = pr * (dpT[kt][i] - Dh) * p.scale;
+          sP[key][head] = pr;
+          sdS[key][head] = dss[kt][i];
+        }
+    }
+    // dq^T[dim][head] += sum_key K[key][dim] dS[head][key] (scale folded)
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dq[dt] = mma_f32(sK[kt * 16 + g * 4 + i][dt * 16 + col], dss[kt][i], dq[dt]);
+    __syncthreads();
+
+    // ---- phase B (wave = D/4 dims, all keys, all heads): the chunk's key
+    // and value gradient contributions, summed over heads
+    constexpr int kDW = D / 4 / 16;  // dim tiles per wave (>= 1 for D >= 64)
+#pragma unroll
+    for (int dd = 0; dd < kDW; ++dd) {
+      const int dim0 = wave * (D / 4) + dd * 16;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x4 ak = f32x4{0.f, 0.f, 0.f, 0.f}, av = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int ks = 0; ks < kBwdHeads / 4; ++ks) {
+          const int h = ks * 4 + g;
+          ak = mma_f32(sQ[h][dim0 + col], sdS[kt * 16 + col][h], ak);
+          av = mma_f32(sdO[h][dim0 + col], sP[kt * 16 + col][h], av);
+        }
+        // lane (key col, g) holds dims dim0 + 4 g .. + 3 of key kt*16 + col
+        const int key = kt * 16 + col;
+        if (s_valid[key]) {
+          const int64_t gi = (row * (p.n_ent_max + p.W) + s_gslot[key]) * D + dim0 + g * 4;
+          *reinterpret_cast<f32x4*>(p.gk + gi) = ak;
+          *reinterpret_cast<f32x4*>(p.gv + gi) = av;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (head < H) {
+    float* dst = p.dq + (row * H + head) * D;
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt) *reinterpret_cast<f32x4*>(dst + dt * 16 + g * 4) = dq[dt];
+  }
+}
+
+// Key / value gradients of one compressed entry j of sequence b: the sum of
+// the contributions of every query row that attended it, in ascending row
+// order.  CSA: a row attended j iff j is in its (ascending) index list,
+// found by binary search; HCA: every row that sees j.
+template <int D, bool HCA>
+__global__ __launch_bounds__(256) void attend_bwd_entries_kernel(BwdParams p) {
+  __shared__ int s_row[256];
+  __shared__ int s_slot[256];
+  __shared__ int s_cnt[5];
+  const int tid = threadIdx.x;
+  const int64_t j = blockIdx.x;
+  const int64_t b = blockIdx.y;
+  const int64_t pos0 = p.pos0[b];
+  // HCA: the rows whose position sees entry j, t >= (j + 1) m - 1; CSA:
+  // every row is searched (its list says whether it selected j)
+  int64_t i0 = HCA ? (j + 1) * p.m - 1 - pos0 : 0;
+  if (i0 < 0) i0 = 0;
+  const int64_t n_slots_row = p.n_ent_max + p.W;
+  const int dim = tid % D;
+  const bool is_v = tid >= D;  // threads D .. 2D-1 sum values (D = 128); D = 64: both halves
+  float acc_k = 0.f, acc_v = 0.f;
+  for (int64_t base = i0; base < p.T; base += 256) {
+    const int64_t i = base + tid;
+    int slot = -1;
+    if (i < p.T) {
+      const int64_t rowi = b * p.T + i;
+      if (HCA) {
+        slot = static_cast<int>(j);
+      } else {
+        // the list is ascending, then -1 padding: compared as unsigned the
+        // padding sorts last
+        const uint32_t* lst = reinterpret_cast<const uint32_t*>(p.idx + rowi * p.k);
+        const uint32_t key = static_cast<uint32_t>(j);
+        int lo = 0, hi = p.k;  // first position with lst[pos] >= j
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (lst[mid] < key) lo = mid + 1; else hi = mid;
+        }
+        if (lo < p.k && lst[lo] == key) slot = lo;
+      }
+    }
+    // compact the hits in row order (one block prefix over the flags)
+    const unsigned long long bal = __ballot(slot >= 0);
+    const int w = tid >> 6;
+    if ((tid & 63) == 0) s_cnt[w] = __popcll(bal);
+    __syncthreads();
+    if (tid == 0) {
+      int a = 0;
+      for (int x = 0; x < 4; ++x) { const int c = s_cnt[x]; s_cnt[x] = a; a += c; }
+      s_cnt[4] = a;
+    }
+    __syncthreads();
+    if (slot >= 0) {
+      const int r = s_cnt[w] + static_cast<int>(__popcll(bal & ((1ull << (tid & 63)) - 1ull)));
+      s_row[r] = static_cast<int>(i);
+      s_slot[r] = slot;
+    }
+    __syncthreads();
+    const int n_hit = s_cnt[4];
+    for (int r = 0; r < n_hit; ++r) {
+      const int64_t gi = ((b * p.T + s_row[r]) * n_slots_row + s_slot[r]) * D + dim;
+      if (D == 128) {
+        if (is_v) acc_v += p.gv[gi]; else acc_k += p.gk[gi];
+      } else {
+        acc_k += p.gk[gi];
+        acc_v += p.gv[gi];
+      }
+    }
+    __syncthreads();
+  }
+  const int64_t o = (b * p.n_cap + j) * D + dim;
+  if (D == 128) {
+    if (is_v) p.dvc[o] = acc_v; else p.dkc[o] = acc_k;
+  } else if (tid < D) {
+    p.dkc[o] = acc_k;
+    p.dvc[o] = acc_v;
+  }
+}
+
+// Key / value gradients of raw row r of sequence b (position raw_pos0 + r):
+// the rows whose window holds it, t in [pos, pos + W - 1], in row order.
+template <int D>
+__global__ __launch_bounds__(256) void attend_bwd_raw_kernel(BwdParams p) {
+  const int tid = threadIdx.x;
+  const int64_t r = blockIdx.x;
+  const int64_t b = blockIdx.y;
+  const int64_t pos = p.raw_pos0[b] + r;
+  const int64_t pos0 = p.pos0[b];
+  const int64_t n_slots_row = p.n_ent_max + p.W;
+  const int dim = tid % D;
+  const bool is_v = tid >= D;
+  float acc_k = 0.f, acc_v = 0.f;
+  int64_t i0 = pos - pos0, i1 = pos - pos0 + p.W;  // rows [i0, i1)
+  if (i0 < 0) i0 = 0;
+  if (i1 > p.T) i1 = p.T;
+  if (pos >= 0) {
+    for (int64_t i = i0; i < i1; ++i) {
+      const int64_t t = pos0 + i;
+      const int64_t slot = p.n_ent_max + (pos - (t - p.W + 1));
+      const int64_t gi = ((b * p.T + i) * n_slots_row + slot) * D + dim;
+      if (D == 128) {
+        if (is_v) acc_v += p.gv[gi]; else acc_k += p.gk[gi];
+      } else {
+        acc_k += p.gk[gi];
+        acc_v += p.gv[gi];
+      }
+    }
+  }
+  const int64_t o = (b * p.R + r) * D + dim;
+  if (D == 128) {
+    if (is_v) p.dvr[o] = acc_v; else p.dkr[o] = acc_k;
+  } else if (tid < D) {
+    p.dkr[o] = acc_k;
+    p.dvr[o] = acc_v;
+  }
+}
+
+size_t attend_bwd_workspace_bytes(int64_t rows, int64_t D, int64_t n_ent_max, int W) {
+  return static_cast<size_t>(rows) * (n_ent_max + W) * D * sizeof(float) * 2;
+}
+
+int launch_attend_bwd(const void* q, int dtype, const void* kc, const void* vc,
+                      const int32_t* idx, int k, int hca_m, const void* kr, const void* vr,
+                      const int64_t* raw_pos0, int64_t R, const int64_t* pos0, int64_t B,
+                      int64_t T, int64_t H, int64_t D, int64_t n_cap, int W, float scale,
+                      const float* out, const float* lse, const float* dout, float* dq,
+                      float* dkc, float* dvc, float* dkr, float* dvr, void* ws,
+                      hipStream_t stream) {
+  const bool hca = hca_m > 0;
+  BwdParams p;
+  p.q = static_cast<const uint8_t*>(q);
+  p.kc = static_cast<const uint8_t*>(kc);
+  p.vc = static_cast<const uint8_t*>(vc);
+  p.idx = idx;
+  p.kr = static_cast<const uint8_t*>(kr);
+  p.vr = static_cast<const uint8_t*>(vr);
+  p.raw_pos0 = raw_pos0;
+  p.pos0 = pos0;
+  p.out = out;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dkc = dkc;
+  p.dvc = dvc;
+  p.dkr = dkr;
+  p.dvr = dvr;
+  p.T = T;
+  p.H = H;
+  p.n_cap = n_cap;
+  p.R = R;
+  p.k = k;
+  p.W = W;
+  p.m = hca ? hca_m : 1;
+  p.n_ent_max = hca ? static_cast<int>(n_cap) : k;
+  p.scale = scale;
+  const int64_t rows = B * T;
+  float* base = static_cast<float*>(ws);
+  p.gk = base;
+  p.gv = base + rows * (p.n_ent_max + W) * D;
+#define CSA_BWD_CASE(DT, DD)                                                                  \
+  if (dtype == DT && D == DD) {                                                               \
+    if (hca) attend_bwd_rows_kernel<DT, DD, true><<<dim3(rows), 256, 0, stream>>>(p);          \
+    else attend_bwd_rows_kernel<DT, DD, false><<<dim3(rows), 256, 0, stream>>>(p);             \
+    if (hca) attend_bwd_entries_kernel<DD, true><<<dim3(n_cap, B), 256, 0, stream>>>(p);       \
+    else attend_bwd_entries_kernel<DD, false><<<dim3(n_cap, B), 256, 0, stream>>>(p);          \
+    if (R > 0) attend_bwd_raw_kernel<DD><<<dim3(R, B), 256, 0, stream>>>(p);                   \
+    return hipGetLastError() == hipSuccess ? 0 : -1;                                          \
+  }
+  CSA_BWD_CASE(0, 64)
+  CSA_BWD_CASE(0, 128)
+  CSA_BWD_CASE(1, 64)
+  CSA_BWD_CASE(1, 128)
+#undef CSA_BWD_CASE
+  return -2;
+}
+
+}  // namespace csa

@@ -38,6 +38,50 @@ __global__ __launch_bounds__(256) void compress_kernel(
   store_elem<T>(cache, b * n_cap * d + (first_entry + j) * d + c, compress_channel(xb, zb, d, m));
 }
 
+// Gradients of the compressor for one (block, channel) per thread: with
+// w_i = softmax_i(z) and c = sum_i w_i x_i (the forward's arithmetic),
+// dx_i = w_i dc and dz_i = w_i (x_i - c) dc.
+template <typename T>
+__global__ __launch_bounds__(256) void compress_bwd_kernel(
+    const T* __restrict__ x, const float* __restrict__ z, const float* __restrict__ dc,
+    float* __restrict__ dx, float* __restrict__ dz, int64_t n_blocks, int64_t d, int m,
+    int64_t x_sb, int64_t z_sb) {
+  const int64_t b = blockIdx.y;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= n_blocks * d) return;
+  const int64_t j = e / d;
+  const int64_t ch = e - j * d;
+  const T* xb = x + b * x_sb + (j * m) * d + ch;
+  const float* zb = z + b * z_sb + (j * m) * d + ch;
+  const float c = compress_channel(xb, zb, d, m);
+  float zmax = -INFINITY;
+  for (int i = 0; i < m; ++i) zmax = fmaxf(zmax, zb[static_cast<int64_t>(i) * d]);
+  float den = 0.f;
+  for (int i = 0; i < m; ++i) den += expf(zb[static_cast<int64_t>(i) * d] - zmax);
+  const float g = dc[(b * n_blocks + j) * d + ch];
+  const int64_t o = b * n_blocks * m * d + (j * m) * d + ch;
+  for (int i = 0; i < m; ++i) {
+    const int64_t off = static_cast<int64_t>(i) * d;
+    const float w = expf(zb[off] - zmax) / den;
+    dx[o + off] = w * g;
+    dz[o + off] = w * (load_elem<T>(xb, off) - c) * g;
+  }
+}
+
+int launch_compress_bwd(const void* x, int dtype, const float* z, const float* dc, int64_t B,
+                        int64_t n_tok, int64_t d, int m, int64_t x_sb, int64_t z_sb, float* dx,
+                        float* dz, hipStream_t s) {
+  const int64_t nb = n_tok / m;
+  dim3 grid(static_cast<unsigned>((nb * d + 255) / 256), static_cast<unsigned>(B));
+  if (dtype == 0)
+    compress_bwd_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), z, dc, dx, dz,
+                                                    nb, d, m, x_sb, z_sb);
+  else
+    compress_bwd_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), z, dc,
+                                                       dx, dz, nb, d, m, x_sb, z_sb);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_compress(const void* x, int dtype, const float* z, int64_t B, int64_t n_tok,
                     int64_t d, int m, int64_t x_sb, int64_t z_sb, void* cache,
                     int64_t n_cap, int64_t first_entry, hipStream_t s) {

@@ -75,4 +75,18 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
                   int64_t n_cap, int W, float scale, float* out, float* lse, void* ws,
                   hipStream_t stream);
 
+// Backward pass (fp32 gradients).  The workspace holds the per-row key /
+// value gradient contributions: attend_bwd_workspace_bytes() bytes.
+size_t attend_bwd_workspace_bytes(int64_t rows, int64_t D, int64_t n_ent_max, int W);
+int launch_attend_bwd(const void* q, int dtype, const void* kc, const void* vc,
+                      const int32_t* idx, int k, int hca_m, const void* kr, const void* vr,
+                      const int64_t* raw_pos0, int64_t R, const int64_t* pos0, int64_t B,
+                      int64_t T, int64_t H, int64_t D, int64_t n_cap, int W, float scale,
+                      const float* out, const float* lse, const float* dout, float* dq,
+                      float* dkc, float* dvc, float* dkr, float* dvr, void* ws,
+                      hipStream_t stream);
+int launch_compress_bwd(const void* x, int dtype, const float* z, const float* dc, int64_t B,
+                        int64_t n_tok, int64_t d, int m, int64_t x_sb, int64_t z_sb, float* dx,
+                        float* dz, hipStream_t s);
+
 }  // namespace csa

@@ -139,3 +139,30 @@ def test_attend_validation():
     assert lib.hca_attend(FAKE, 1, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, 128, FAKE, 1, 1, 64, 128,
                           8192, 128, 0.1, FAKE, NULL, NULL, 0, NULL) == -2
     assert lib.hca_attend_workspace_size(16, 1, 64, 128, 8192, 128) > 0
+
+
+def _attend_bwd(q=FAKE, dt=1, kvdt=1, idx=FAKE, k=64, H=64, d=128, W=16, ws=FAKE, wsb=1 << 30,
+                dout=FAKE, dkr=FAKE, scale=0.1):
+    return lib.csa_attend_backward(q, dt, FAKE, FAKE, kvdt, idx, k, FAKE, FAKE, FAKE, 32, FAKE, 1,
+                                   4, H, d, 4096, W, scale, FAKE, FAKE, dout, FAKE, FAKE, FAKE, dkr,
+                                   FAKE, ws, wsb, NULL)
+
+
+def test_backward_validation():
+    assert _attend_bwd(idx=NULL) == -1
+    assert _attend_bwd(dout=NULL) == -1
+    assert _attend_bwd(dkr=NULL) == -1                 # window gradients need dkr / dvr
+    assert _attend_bwd(d=96) == -4
+    assert _attend_bwd(H=65) == -4
+    assert _attend_bwd(dt=2, kvdt=2) == -3
+    assert _attend_bwd(ws=NULL) == -5
+    need = lib.csa_attend_backward_workspace_size(1, 4, 128, 64, 16)
+    assert need == 4 * (64 + 16) * 128 * 8
+    assert _attend_bwd(wsb=need - 1) == -5
+    assert lib.hca_attend_backward(FAKE, 1, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, 32, FAKE, 1, 4, 64,
+                                   128, 4096, 16, 0.1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, 1 << 30, NULL) == -2   # m = 0
+    assert lib.csa_compress_backward(NULL, 1, FAKE, FAKE, 1, 8, 4, 4, 32, 32, FAKE, FAKE, NULL) == -1
+    assert lib.csa_compress_backward(FAKE, 2, FAKE, FAKE, 1, 8, 4, 4, 32, 32, FAKE, FAKE, NULL) == -3
+    assert lib.csa_compress_backward(FAKE, 1, FAKE, FAKE, 1, 6, 4, 4, 32, 32, FAKE, FAKE, NULL) == -2
+    assert lib.csa_compress_backward(FAKE, 1, FAKE, FAKE, 1, 8, 4, 4, 16, 32, FAKE, FAKE, NULL) == -2
