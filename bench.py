@@ -120,6 +120,18 @@ def indexer_flops(cfg) -> int:
     return 2 * cfg.B * cfg.H_I * cfg.d_I * visible_sum(cfg)
 
 
+def backward_flops(cfg) -> int:
+    """Algorithmic FLOP of the attention backward: 10 d per (query row, key,
+    head) -- the logits, dP, dq, dK and dV products -- over every query's
+    key list (min(k, V(t)) selected entries plus its window rows)."""
+    tot = 0
+    for i in range(cfg.T):
+        t = cfg.pos0 + i
+        V = min(cfg.n_cap, (t + 1) // cfg.m)
+        tot += min(cfg.k, V) + min(cfg.W, t + 1)
+    return 10 * cfg.d * cfg.H * cfg.B * tot
+
+
 def hca_bytes(cfg, V: int) -> int:
     """Algorithmic HBM bytes of one HCA attention launch: every visible K/V
     entry and window row once, queries in, fp32 outputs out."""
@@ -139,6 +151,22 @@ def cpu_baseline(cfg, budget_s: float):
         threads = len(os.sched_getaffinity(0))
     done, t_total = 0, 0.0
     layer_cfgs = WL.layer_workloads(cfg) if cfg.layers else [cfg]
+    if cfg.T >= 8:
+        # prefill-shaped: a sample of query rows (i = 31 mod 32) of the first
+        # sequence, grown while the budget lasts
+        s = WL.make_sequence(cfg, 0)
+        sample = np.arange(31, cfg.T, 32)
+        n = 4
+        while True:
+            t0 = time.perf_counter()
+            _oracle_sequence(cfg, s, rows=sample[:n])
+            dt = time.perf_counter() - t0
+            if dt * 2 > budget_s or n >= sample.size:
+                break
+            n = min(sample.size, n * 2)
+        return {"value": n / dt, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"{n} query rows (i = 31 mod 32) of sequence 0 of {cfg.name}, fp64 "
+                          f"NumPy, {dt:.1f} s"}
     for b in range(cfg.B):
         for lc in layer_cfgs:
             s = WL.make_sequence(lc, b)
@@ -154,13 +182,21 @@ def cpu_baseline(cfg, budget_s: float):
                       f"{t_total:.1f} s"}
 
 
-def _oracle_sequence(cfg, s):
-    """The oracle's whole step for one sequence's inputs ``s``."""
+def _oracle_sequence(cfg, s, rows=None):
+    """The oracle's whole step for one sequence's inputs ``s`` (query rows
+    ``rows`` only, when given)."""
     import numpy as np
     import oracle
     dec = oracle.bf16_decode if s["kc"].dtype == np.uint16 else (lambda a: a.astype(np.float64))
-    pos = cfg.pos0 + np.arange(cfg.T)
+    rows = np.arange(cfg.T) if rows is None else np.asarray(rows)
+    pos = cfg.pos0 + rows
     kc, vc = dec(s["kc"]), dec(s["vc"])
+    if cfg.n_new_tokens:
+        # the step's own tokens, compressed and appended
+        r0, r1 = cfg.raw_before, cfg.raw_before + cfg.n_new_tokens
+        kc = np.vstack([kc, oracle.compress(dec(s["kr"][r0:r1]), s["z"], cfg.m)])
+        vc = np.vstack([vc, oracle.compress(dec(s["vr"][r0:r1]), s["z"], cfg.m)])
+    q = dec(s["q"])[rows]
     if cfg.block_end:
         # the block completed by the query token: its last m raw rows
         r0 = cfg.R - cfg.m
@@ -168,14 +204,14 @@ def _oracle_sequence(cfg, s):
         kc = np.vstack([kc, oracle.compress(dec(s["kr"][r0:]), z, cfg.m)])
         vc = np.vstack([vc, oracle.compress(dec(s["vr"][r0:]), z, cfg.m)])
     if cfg.hca:
-        oracle.hca_attend(dec(s["q"]), kc, vc, dec(s["kr"]), dec(s["vr"]), cfg.raw_pos0, pos,
+        oracle.hca_attend(q, kc, vc, dec(s["kr"]), dec(s["vr"]), cfg.raw_pos0, pos,
                           cfg.m, cfg.W, cfg.scale)
     elif cfg.swa:
-        idx = np.zeros((cfg.T, 0), np.int64)
-        oracle.attend(dec(s["q"]), kc, vc, idx, dec(s["kr"]), dec(s["vr"]), cfg.raw_pos0, pos,
+        idx = np.zeros((rows.size, 0), np.int64)
+        oracle.attend(q, kc, vc, idx, dec(s["kr"]), dec(s["vr"]), cfg.raw_pos0, pos,
                       cfg.W, cfg.scale)
     else:
-        qi, ki = dec(s["qi"]), kc
+        qi, ki = dec(s["qi"])[rows], kc
         if cfg.ki_fp8:
             kcode, ksc = oracle.quantize_fp8_rows(kc.astype(np.float32))
             qcode, qsc = oracle.quantize_fp8_rows(qi.astype(np.float32))
@@ -184,11 +220,21 @@ def _oracle_sequence(cfg, s):
         if cfg.ki_mxfp4:
             ki = oracle.mxfp4_decode_rows(*oracle.quantize_mxfp4_rows(kc.astype(np.float32)))
             qi = oracle.mxfp4_decode_rows(*oracle.quantize_mxfp4_rows(qi.astype(np.float32)))
-        S = oracle.indexer_scores(qi, s["w"], ki, pos, cfg.m)
+        S = oracle.indexer_scores(qi, s["w"][rows], ki, pos, cfg.m)
         V = oracle.visible_count(pos, cfg.m)
-        idx = np.stack([oracle.topk_select(S[i], int(V[i]), cfg.k) for i in range(cfg.T)])
-        oracle.attend(dec(s["q"]), kc, vc, idx, dec(s["kr"]), dec(s["vr"]), cfg.raw_pos0, pos,
+        idx = np.stack([oracle.topk_select(S[i], int(V[i]), cfg.k) for i in range(rows.size)])
+        oracle.attend(q, kc, vc, idx, dec(s["kr"]), dec(s["vr"]), cfg.raw_pos0, pos,
                       cfg.W, cfg.scale)
+        if cfg.backward:
+            g_rng = np.random.Generator(np.random.PCG64(cfg.seed))
+            dout = g_rng.standard_normal((cfg.T, cfg.H, cfg.d), dtype=np.float32)[rows]
+            g = oracle.attend_backward(q, kc, vc, idx, dec(s["kr"]), dec(s["vr"]), cfg.raw_pos0,
+                                       pos, cfg.W, cfg.scale, dout)
+            if cfg.n_new_tokens:
+                r0, r1 = cfg.raw_before, cfg.raw_before + cfg.n_new_tokens
+                for x, dc in ((s["kr"], g["dkc"]), (s["vr"], g["dvc"])):
+                    oracle.compress_backward(dec(x[r0:r1]), s["z"], cfg.m,
+                                             dc[cfg.n_ctx_entries:cfg.n_cap])
 
 
 def main():
@@ -224,6 +270,16 @@ def main():
         step = CSAStep(cfg, batch)
         del batch
         run_once, rcfg = step.run, cfg
+        if cfg.backward:
+            # the forward once (its outputs, lse and indices feed the
+            # backward), then a seeded upstream gradient N(0, 1)
+            step.run()
+            g_rng = np.random.Generator(np.random.PCG64(cfg.seed))
+            dout = torch.from_numpy(g_rng.standard_normal((cfg.B, cfg.T, cfg.H, cfg.d),
+                                                          dtype=np.float32)).to("cuda:0")
+
+            def run_once():
+                step.backward(dout)
     for _ in range(args.warmup):
         run_once()
     torch.cuda.synchronize()
@@ -292,9 +348,15 @@ def main():
         for i, lay in enumerate(hstep.layers):
             st[f"layer{i}_{cfg.layers[i]}"] = timed(lay.run)
     cfg_all, cfg = cfg, rcfg  # stage timings and roofline: the (first CSA) layer
-    if cfg.n_new_tokens:
+    if cfg.backward:
+        csa_lib_ = __import__("long_context_sparse_16_amd")
+        st["attend_backward"] = timed(lambda: csa_lib_.csa_attend_backward(
+            step.q, step.kc, step.vc, step.idx, step.kr, step.vr, step.raw_pos0, step.pos0,
+            cfg.W, cfg.scale, step.out, step.lse, dout, ws=step.bwd_ws), R=5, reps=2)
+        st["backward_step"] = step_event_ms
+    elif cfg.n_new_tokens:
         st["compress"] = timed(step.compress)
-    if cfg.k > 0:
+    if cfg.k > 0 and not cfg.backward:
         st["index"] = timed(step.index)
         csa_lib.csa_workspace_clear(step.topk_ws)
 
@@ -302,7 +364,8 @@ def main():
             step.index()
             step.topk()
         st["topk"] = timed(index_topk) - st["index"]
-    st["attend"] = timed(step.attend)
+    if not cfg.backward:
+        st["attend"] = timed(step.attend)
     if cfg.block_end:
         # the fused selection (block compression inside the indexer launch,
         # then top-k) against the same step with separate compress launches
@@ -313,11 +376,20 @@ def main():
     cfg = cfg_all
 
     queries = cfg.B * cfg.T
-    n_indexed = (sum(1 for k in cfg.layers if k == "csa") if cfg.layers else 1) if cfg.k > 0 else 0
+    n_indexed = ((sum(1 for k in cfg.layers if k == "csa") if cfg.layers else 1)
+                 if cfg.k > 0 and not cfg.backward else 0)
     V = int(min(cfg.n_cap, (cfg.pos0 + cfg.T) // cfg.m))
     ms_per_step = wall * 1e3 / K
     value = queries * K / wall
-    if cfg.hca:
+    if cfg.backward:
+        # the attention backward's products (S, dP, dq, dK, dV: 10 d FLOP per
+        # query row, key and head) on the fp32 MFMA, against the whole call
+        # (row kernel + the two deterministic reductions)
+        fl = backward_flops(cfg)
+        roof = {"kernel": "attend_bwd (rows + reductions)", "bound": "mfma",
+                "achieved": fl / (st["attend_backward"] * 1e9), "peak": MFMA_PEAK_TFLOPS["f32"],
+                "unit": "TFLOP/s", "traffic": None, "algorithmic_flops": fl}
+    elif cfg.hca:
         kb = hca_bytes(cfg, V)
         roof = {"kernel": "attend_kernel (HCA)", "bound": "hbm", "achieved": kb / (st["attend"] * 1e6),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None}
@@ -345,7 +417,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": index_dtype(cfg),
+        "dtype": "f32" if cfg.backward else index_dtype(cfg),
         "data": "synthetic (seeded N(0,1) K/V/q, U(0,1) head weights, planted entries)",
         "config": {"workload": cfg.name, "batch": cfg.B, "context_tokens": cfg.pos0,
                    "compressed_entries": V, "m": cfg.m, "indexer": f"{cfg.H_I}x{cfg.d_I}",

@@ -334,12 +334,14 @@ int hca_attend(const void* q, int q_dtype, const void* kc, const void* vc,
  * dp = V dout, D = dout . out, ds = p (dp - D): dq = scale ds K,
  * dK += scale ds q, dV += p dout).  idx rows must be strictly ascending
  * then -1 padded (as csa_topk emits them).  ws: device workspace of
- * csa_attend_backward_workspace_size() bytes (B*T*(k+W)*d*8: the per-row
- * key/value contributions; contents on entry do not matter).
- * Supported: q/kv dtypes F32 or BF16 (equal), d in {64, 128}, H <= 64.
+ * csa_attend_backward_workspace_size() bytes (the per-row key/value
+ * contributions, B*T*(k+W)*d*8 bytes, and each entry's list of the rows
+ * that attended it; contents on entry do not matter).
+ * Supported: q/kv dtypes F32 or BF16 (equal), d in {64, 128}, H <= 64,
+ * T <= 16384, B*T*k < 2^32.
  */
 size_t csa_attend_backward_workspace_size(int64_t B, int64_t T, int64_t d,
-                                          int k, int W);
+                                          int64_t n_cap, int k, int W);
 int csa_attend_backward(const void* q, int q_dtype, const void* kc,
                         const void* vc, int kv_dtype, const int32_t* idx,
                         int k, const void* kr, const void* vr,

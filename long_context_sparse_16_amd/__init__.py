@@ -64,7 +64,7 @@ _SIGNATURES = {
     "csa_attend": (_i, [_vp, _i, _vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _i64, _vp, _i64, _i64, _i64,
                         _i64, _i64, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "hca_attend_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64, _i]),
-    "csa_attend_backward_workspace_size": (_sz, [_i64, _i64, _i64, _i, _i]),
+    "csa_attend_backward_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i, _i]),
     "csa_attend_backward": (_i, [_vp, _i, _vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _i64, _vp, _i64,
                                  _i64, _i64, _i64, _i64, _i, _f, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _vp, _vp, _vp, _sz, _vp]),
@@ -464,6 +464,14 @@ def _bwd_common(q, kc, vc, kr, vr, raw_pos0, pos0, W, out, lse, dout):
     return dev, B, T, H, d, n_cap, R, grads
 
 
+def csa_attend_backward_workspace_size(B: int, T: int, d: int, n_cap: int, k: int, W: int) -> int:
+    return int(_lib.csa_attend_backward_workspace_size(B, T, d, n_cap, k, W))
+
+
+def hca_attend_backward_workspace_size(B: int, T: int, d: int, n_cap: int, W: int) -> int:
+    return int(_lib.hca_attend_backward_workspace_size(B, T, d, n_cap, W))
+
+
 def csa_attend_backward(q, kc, vc, idx, kr, vr, raw_pos0, pos0, W: int, scale: float, out, lse,
                         dout, ws=None, stream=None) -> dict:
     """Gradients of csa_attend: returns dict dq, dkc, dvc, dkr, dvr (fp32);
@@ -474,7 +482,7 @@ def csa_attend_backward(q, kc, vc, idx, kr, vr, raw_pos0, pos0, W: int, scale: f
         raise ValueError("idx must be int32 [B, T, k]")
     _contig("idx", idx)
     k = idx.shape[2]
-    need = int(_lib.csa_attend_backward_workspace_size(B, T, d, k, int(W)))
+    need = csa_attend_backward_workspace_size(B, T, d, n_cap, k, int(W))
     ws, nbytes = _workspace(ws, need, dev)
     _check("csa_attend_backward", _lib.csa_attend_backward(
         _ptr(q), _dtype_code(q), _ptr(kc), _ptr(vc), _dtype_code(kc), _ptr(idx), k, _ptr(kr),
@@ -489,7 +497,7 @@ def hca_attend_backward(q, kc, vc, m: int, kr, vr, raw_pos0, pos0, W: int, scale
     """Gradients of hca_attend (dict as csa_attend_backward)."""
     dev, B, T, H, d, n_cap, R, gr = _bwd_common(q, kc, vc, kr, vr, raw_pos0, pos0, W, out, lse,
                                                 dout)
-    need = int(_lib.hca_attend_backward_workspace_size(B, T, d, n_cap, int(W)))
+    need = hca_attend_backward_workspace_size(B, T, d, n_cap, int(W))
     ws, nbytes = _workspace(ws, need, dev)
     _check("hca_attend_backward", _lib.hca_attend_backward(
         _ptr(q), _dtype_code(q), _ptr(kc), _ptr(vc), _dtype_code(kc), int(m), _ptr(kr), _ptr(vr),
@@ -530,4 +538,5 @@ __all__ = [
     "csa_decode_index_topk",
     "csa_attend", "csa_attend_workspace_size", "hca_attend", "hca_attend_workspace_size",
     "csa_attend_backward", "hca_attend_backward", "csa_compress_backward",
+    "csa_attend_backward_workspace_size", "hca_attend_backward_workspace_size",
 ]

@@ -424,14 +424,15 @@ static int check_bwd_args(const float* out, const float* lse, const float* dout,
   return CSA_OK;
 }
 
-size_t csa_attend_backward_workspace_size(int64_t B, int64_t T, int64_t d, int k, int W) {
-  if (B < 1 || T < 1 || d < 1 || k < 0 || W < 0) return 0;
-  return round_up(csa::attend_bwd_workspace_bytes(B * T, d, k, W));
+size_t csa_attend_backward_workspace_size(int64_t B, int64_t T, int64_t d, int64_t n_cap, int k,
+                                          int W) {
+  if (B < 1 || T < 1 || d < 1 || n_cap < 1 || k < 0 || W < 0) return 0;
+  return round_up(csa::attend_bwd_workspace_bytes(B, T, d, k, W, n_cap, true));
 }
 
 size_t hca_attend_backward_workspace_size(int64_t B, int64_t T, int64_t d, int64_t n_cap, int W) {
   if (B < 1 || T < 1 || d < 1 || n_cap < 1 || W < 0) return 0;
-  return round_up(csa::attend_bwd_workspace_bytes(B * T, d, n_cap, W));
+  return round_up(csa::attend_bwd_workspace_bytes(B, T, d, n_cap, W, n_cap, false));
 }
 
 static int attend_backward_impl(const void* q, int q_dtype, const void* kc, const void* vc,
@@ -449,7 +450,7 @@ static int attend_backward_impl(const void* q, int q_dtype, const void* kc, cons
   if (rc) return rc;
   CSA_REQUIRE(B * T <= kMaxIndex, CSA_ERR_UNSUPPORTED, "%s: B*T too large", fn);
   const size_t need = hca_m > 0 ? hca_attend_backward_workspace_size(B, T, d, n_cap, W)
-                                : csa_attend_backward_workspace_size(B, T, d, k, W);
+                                : csa_attend_backward_workspace_size(B, T, d, n_cap, k, W);
   CSA_REQUIRE(ws && ws_bytes >= need, CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, got %zu",
               fn, need, ws ? ws_bytes : 0);
   CSA_REQUIRE(aligned16(ws), CSA_ERR_WORKSPACE, "%s: ws must be 16-byte aligned", fn);
@@ -470,6 +471,10 @@ int csa_attend_backward(const void* q, int q_dtype, const void* kc, const void* 
   const char* fn = "csa_attend_backward";
   CSA_REQUIRE(idx, CSA_ERR_NULL, "%s: idx must be non-NULL", fn);
   CSA_REQUIRE(k >= 1 && k <= 65536, CSA_ERR_UNSUPPORTED, "%s: k must be in [1, 65536]", fn);
+  CSA_REQUIRE(T <= csa::kBwdMaxRows, CSA_ERR_UNSUPPORTED, "%s: T must be <= %lld", fn,
+              static_cast<long long>(csa::kBwdMaxRows));
+  CSA_REQUIRE(B * T * k < (int64_t(1) << 32), CSA_ERR_UNSUPPORTED, "%s: B*T*k must be < 2^32",
+              fn);
   return attend_backward_impl(q, q_dtype, kc, vc, kv_dtype, idx, k, 0, kr, vr, raw_pos0, R, pos0,
                               B, T, H, d, n_cap, W, scale, out, lse, dout, dq, dkc, dvc, dkr, dvr,
                               ws, ws_bytes, stream, fn);

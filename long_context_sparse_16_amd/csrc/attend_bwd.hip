@@ -45,6 +45,11 @@ struct BwdParams {
   float* dvc;
   float* dkr;
   float* dvr;
+  // CSA: the query-row references of every entry, by counting sort
+  uint32_t* cnt;   // [B][n_cap] references per entry (zero on entry)
+  uint32_t* cur;   // [B][n_cap] fill cursors (zero on entry)
+  uint32_t* off;   // [B][n_cap] first reference of each entry in lst
+  uint32_t* lst;   // [B][T * k] references, row * k + slot, grouped by entry
   int64_t T, H, n_cap, R;
   int k, W, m;
   int n_ent_max;  // entry slots per staging row: k (CSA) or n_cap (HCA)
@@ -278,10 +283,9 @@ __global__ __launch_bounds__(256) void attend_bwd_rows_kernel(BwdParams p) {
   }
 }
 
-// Key / value gradients of one compressed entry j of sequence b: the sum of
-// the contributions of every query row that attended it, in ascending row
-// order.  CSA: a row attended j iff j is in its (ascending) index list,
-// found by binary search; HCA: every row that sees j.
+// HCA: key / value gradients of compressed entry j of sequence b, the sum
+// of the contributions of every query row that sees it (all of them attend
+// it), in ascending row order.
 template <int D, bool HCA>
 __global__ __launch_bounds__(256) void attend_bwd_entries_kernel(BwdParams p) {
   __shared__ int s_row[256];
@@ -304,20 +308,8 @@ __global__ __launch_bounds__(256) void attend_bwd_entries_kernel(BwdParams p) {
     int slot = -1;
     if (i < p.T) {
       const int64_t rowi = b * p.T + i;
-      if (HCA) {
-        slot = static_cast<int>(j);
-      } else {
-        // the list is ascending, then -1 padding: compared as unsigned the
-        // padding sorts last
-        const uint32_t* lst = reinterpret_cast<const uint32_t*>(p.idx + rowi * p.k);
-        const uint32_t key = static_cast<uint32_t>(j);
-        int lo = 0, hi = p.k;  // first position with lst[pos] >= j
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (lst[mid] < key) lo = mid + 1; else hi = mid;
-        }
-        if (lo < p.k && lst[lo] == key) slot = lo;
-      }
+      (void)rowi;
+      slot = static_cast<int>(j);
     }
     // compact the hits in row order (one block prefix over the flags)
     const unsigned long long bal = __ballot(slot >= 0);
@@ -354,6 +346,133 @@ __global__ __launch_bounds__(256) void attend_bwd_entries_kernel(BwdParams p) {
   } else if (tid < D) {
     p.dkc[o] = acc_k;
     p.dvc[o] = acc_v;
+  }
+}
+
+// ---- CSA: inverse of the index lists (which rows attended each entry)
+
+constexpr int kBwdMaxRefs = 16384;  // references of one entry kept in LDS (= rows per sequence)
+
+__device__ __forceinline__ bool bwd_entry_ok(int32_t e, int64_t n_cap) {
+  return e >= 0 && e < n_cap;
+}
+
+// cnt[b][j] = number of (row, slot) pairs of sequence b that hold entry j.
+__global__ __launch_bounds__(256) void attend_bwd_count_kernel(BwdParams p) {
+  const int64_t row = blockIdx.x;
+  const int64_t b = row / p.T;
+  for (int s = threadIdx.x; s < p.k; s += 256) {
+    const int32_t e = p.idx[row * p.k + s];
+    if (bwd_entry_ok(e, p.n_cap)) atomicAdd(&p.cnt[b * p.n_cap + e], 1u);
+  }
+}
+
+// off[b][:] = exclusive prefix sum of cnt[b][:] (one workgroup per sequence,
+// a contiguous run of entries per thread).
+__global__ __launch_bounds__(256) void attend_bwd_scan_kernel(BwdParams p) {
+  __shared__ uint32_t part[256];
+  const int64_t b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t per = (p.n_cap + 255) / 256;
+  const int64_t j0 = min(p.n_cap, tid * per), j1 = min(p.n_cap, j0 + per);
+  const uint32_t* c = p.cnt + b * p.n_cap;
+  uint32_t sum = 0;
+  for (int64_t j = j0; j < j1; ++j) sum += c[j];
+  part[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t a = 0;
+    for (int i = 0; i < 256; ++i) { const uint32_t v = part[i]; part[i] = a; a += v; }
+  }
+  __syncthreads();
+  uint32_t a = part[tid] + static_cast<uint32_t>(b * p.T * p.k);
+  uint32_t* o = p.off + b * p.n_cap;
+  for (int64_t j = j0; j < j1; ++j) { o[j] = a; a += c[j]; }
+}
+
+// lst[off[j] + i] = row * k + slot for the i-th reference to entry j (in
+// arrival order; the reduction sorts each entry's references).
+__global__ __launch_bounds__(256) void attend_bwd_fill_kernel(BwdParams p) {
+  const int64_t row = blockIdx.x;
+  const int64_t b = row / p.T;
+  const int64_t rl = row - b * p.T;
+  for (int s = threadIdx.x; s < p.k; s += 256) {
+    const int32_t e = p.idx[row * p.k + s];
+    if (bwd_entry_ok(e, p.n_cap)) {
+      const uint32_t at = p.off[b * p.n_cap + e] + atomicAdd(&p.cur[b * p.n_cap + e], 1u);
+      p.lst[at] = static_cast<uint32_t>(rl * p.k + s);
+    }
+  }
+}
+
+// Key / value gradients of entry j of sequence b: its references sorted
+// ascending (row order; a row holds an entry at most once), then the
+// contributions summed in that order, kBwdSumBatch loads in flight.  Lists
+// of up to CAP references are sorted in LDS by this kernel; the BIG variant
+// (CAP = kBwdMaxRefs) takes only the entries whose list is longer.
+constexpr int kBwdSmallRefs = 2048;
+constexpr int kBwdSumBatch = 16;
+
+template <int D, int CAP, bool BIG>
+__global__ __launch_bounds__(256) void attend_bwd_entries_csr_kernel(BwdParams p) {
+  __shared__ uint32_t refs[CAP];
+  const int tid = threadIdx.x;
+  const int64_t j = blockIdx.x;
+  const int64_t b = blockIdx.y;
+  // (at most one reference per row for index lists without repeats; the
+  // clamp only keeps invalid lists inside the buffer)
+  const int n_all = static_cast<int>(p.cnt[b * p.n_cap + j]);
+  if (BIG != (n_all > kBwdSmallRefs)) return;  // the other variant's entry
+  const int n = min(n_all, CAP);
+  const uint32_t o = p.off[b * p.n_cap + j];
+  int n2 = 1;
+  while (n2 < n) n2 <<= 1;
+  for (int i = tid; i < n2; i += 256) refs[i] = i < n ? p.lst[o + i] : 0xffffffffu;
+  __syncthreads();
+  for (int size = 2; size <= n2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < n2; i += 256) {
+        const int q = i ^ stride;
+        if (q > i) {
+          const uint32_t a = refs[i], c = refs[q];
+          if ((a > c) == ((i & size) == 0)) {
+            refs[i] = c;
+            refs[q] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const int64_t n_slots_row = p.n_ent_max + p.W;
+  const int dim = tid % D;
+  const bool is_v = D == 128 && tid >= D;
+  const float* src = is_v ? p.gv : p.gk;
+  float acc_k = 0.f, acc_v = 0.f;
+  for (int r0 = 0; r0 < n; r0 += kBwdSumBatch) {
+    float vk[kBwdSumBatch], vv[kBwdSumBatch];
+#pragma unroll
+    for (int u = 0; u < kBwdSumBatch; ++u) {
+      const uint32_t ref = refs[min(r0 + u, n - 1)];
+      const int64_t rl = ref / static_cast<uint32_t>(p.k), slot = ref % static_cast<uint32_t>(p.k);
+      const int64_t gi = ((b * p.T + rl) * n_slots_row + slot) * D + dim;
+      vk[u] = src[gi];
+      vv[u] = D == 128 ? 0.f : p.gv[gi];
+    }
+#pragma unroll
+    for (int u = 0; u < kBwdSumBatch; ++u) {
+      if (r0 + u < n) {
+        acc_k += vk[u];
+        acc_v += vv[u];
+      }
+    }
+  }
+  const int64_t oo = (b * p.n_cap + j) * D + dim;
+  if (D == 128) {
+    (is_v ? p.dvc : p.dkc)[oo] = acc_k;
+  } else if (tid < D) {
+    p.dkc[oo] = acc_k;
+    p.dvc[oo] = acc_v;
   }
 }
 
@@ -395,8 +514,17 @@ __global__ __launch_bounds__(256) void attend_bwd_raw_kernel(BwdParams p) {
   }
 }
 
-size_t attend_bwd_workspace_bytes(int64_t rows, int64_t D, int64_t n_ent_max, int W) {
-  return static_cast<size_t>(rows) * (n_ent_max + W) * D * sizeof(float) * 2;
+static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+// Workspace: the key / value contributions [B*T][n_ent_max + W][D] fp32,
+// then (CSA) cnt, cur, off [B][n_cap] and the reference list [B*T*k].
+size_t attend_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int64_t n_ent_max, int W,
+                                  int64_t n_cap, bool csa) {
+  size_t bytes = align256(static_cast<size_t>(B * T) * (n_ent_max + W) * D * sizeof(float) * 2);
+  if (csa)
+    bytes += 3 * align256(static_cast<size_t>(B * n_cap) * 4) +
+             align256(static_cast<size_t>(B * T) * n_ent_max * 4);
+  return bytes;
 }
 
 int launch_attend_bwd(const void* q, int dtype, const void* kc, const void* vc,
@@ -437,12 +565,33 @@ int launch_attend_bwd(const void* q, int dtype, const void* kc, const void* vc,
   float* base = static_cast<float*>(ws);
   p.gk = base;
   p.gv = base + rows * (p.n_ent_max + W) * D;
+  p.cnt = p.cur = p.off = p.lst = nullptr;
+  if (!hca) {
+    char* c = static_cast<char*>(ws) +
+              align256(static_cast<size_t>(rows) * (p.n_ent_max + W) * D * sizeof(float) * 2);
+    const size_t nb = align256(static_cast<size_t>(B * n_cap) * 4);
+    p.cnt = reinterpret_cast<uint32_t*>(c);
+    p.cur = reinterpret_cast<uint32_t*>(c + nb);
+    p.off = reinterpret_cast<uint32_t*>(c + 2 * nb);
+    p.lst = reinterpret_cast<uint32_t*>(c + 3 * nb);
+    // cnt and cur are adjacent: one zero-fill
+    if (launch_clear(p.cnt, 2 * nb, stream)) return -1;
+  }
 #define CSA_BWD_CASE(DT, DD)                                                                  \
   if (dtype == DT && D == DD) {                                                               \
     if (hca) attend_bwd_rows_kernel<DT, DD, true><<<dim3(rows), 256, 0, stream>>>(p);          \
     else attend_bwd_rows_kernel<DT, DD, false><<<dim3(rows), 256, 0, stream>>>(p);             \
-    if (hca) attend_bwd_entries_kernel<DD, true><<<dim3(n_cap, B), 256, 0, stream>>>(p);       \
-    else attend_bwd_entries_kernel<DD, false><<<dim3(n_cap, B), 256, 0, stream>>>(p);          \
+    if (hca) {                                                                                \
+      attend_bwd_entries_kernel<DD, true><<<dim3(n_cap, B), 256, 0, stream>>>(p);              \
+    } else {                                                                                  \
+      attend_bwd_count_kernel<<<dim3(rows), 256, 0, stream>>>(p);                              \
+      attend_bwd_scan_kernel<<<dim3(B), 256, 0, stream>>>(p);                                  \
+      attend_bwd_fill_kernel<<<dim3(rows), 256, 0, stream>>>(p);                               \
+      attend_bwd_entries_csr_kernel<DD, kBwdSmallRefs, false>                                  \
+          <<<dim3(n_cap, B), 256, 0, stream>>>(p);                                             \
+      attend_bwd_entries_csr_kernel<DD, kBwdMaxRefs, true>                                     \
+          <<<dim3(n_cap, B), 256, 0, stream>>>(p);                                             \
+    }                                                                                         \
     if (R > 0) attend_bwd_raw_kernel<DD><<<dim3(R, B), 256, 0, stream>>>(p);                   \
     return hipGetLastError() == hipSuccess ? 0 : -1;                                          \
   }

@@ -77,7 +77,9 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
 
 // Backward pass (fp32 gradients).  The workspace holds the per-row key /
 // value gradient contributions: attend_bwd_workspace_bytes() bytes.
-size_t attend_bwd_workspace_bytes(int64_t rows, int64_t D, int64_t n_ent_max, int W);
+size_t attend_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int64_t n_ent_max, int W,
+                                  int64_t n_cap, bool csa);
+constexpr int64_t kBwdMaxRows = 16384;  // CSA backward: query rows per sequence
 int launch_attend_bwd(const void* q, int dtype, const void* kc, const void* vc,
                       const int32_t* idx, int k, int hca_m, const void* kr, const void* vr,
                       const int64_t* raw_pos0, int64_t R, const int64_t* pos0, int64_t B,

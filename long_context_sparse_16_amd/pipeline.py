@@ -22,8 +22,9 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (csa_attend, csa_compress, csa_decode_index_topk, csa_index_scores,
-               csa_quantize_fp8_rows,
+from . import (csa_attend, csa_attend_backward, csa_attend_backward_workspace_size,
+               csa_compress, csa_compress_backward,
+               csa_decode_index_topk, csa_index_scores, csa_quantize_fp8_rows,
                csa_quantize_mxfp4_rows, csa_topk,
                csa_topk_workspace_size, csa_attend_workspace_size, hca_attend,
                hca_attend_workspace_size, workspace)
@@ -188,6 +189,29 @@ class CSAStep:
             self.index()
             self.topk()
         self.attend()
+
+    def backward(self, dout: torch.Tensor) -> dict:
+        """Backward pass of the step's attention (and of its compression when
+        the step appends entries) for the upstream gradient dout [B, T, H, d]
+        fp32, after run().  Returns dq, dkc, dvc, dkr, dvr and, for a
+        compressing step, dkr_c / dvr_c and dz_k / dz_v: the gradients that
+        reach the chunk's raw K / V tokens and logits through the
+        compressor (add dkr_c to dkr for the raw rows' total)."""
+        cfg = self.cfg
+        if getattr(self, "bwd_ws", None) is None:
+            self.bwd_ws = workspace(csa_attend_backward_workspace_size(
+                cfg.B, cfg.T, cfg.d, cfg.n_cap, cfg.k, cfg.W), self.device)
+        g = csa_attend_backward(self.q, self.kc, self.vc, self.idx, self.kr, self.vr,
+                                self.raw_pos0, self.pos0, cfg.W, cfg.scale, self.out, self.lse,
+                                dout, ws=self.bwd_ws)
+        if cfg.n_new_tokens:
+            r0, r1 = cfg.raw_before, cfg.raw_before + cfg.n_new_tokens
+            e0, e1 = cfg.n_ctx_entries, cfg.n_cap
+            g["dkr_c"], g["dz_k"] = csa_compress_backward(self.kr[:, r0:r1], self.z,
+                                                          g["dkc"][:, e0:e1].contiguous(), cfg.m)
+            g["dvr_c"], g["dz_v"] = csa_compress_backward(self.vr[:, r0:r1], self.z,
+                                                          g["dvc"][:, e0:e1].contiguous(), cfg.m)
+        return g
 
     def run_unfused(self) -> None:
         """The same step with the block compression as separate launches."""

@@ -160,3 +160,58 @@ def test_backward_tiny_prefill_f32_end_to_end():
                                         from_dev(g["dkc"])[0])
     assert np.max(np.abs(from_dev(dx)[0] - rdx)) <= 1e-5 * max(1.0, np.max(np.abs(rdx)))
     assert np.max(np.abs(from_dev(dz)[0] - rdz)) <= 1e-5 * max(1.0, np.max(np.abs(rdz)))
+
+
+def test_backward_chunked_prefill_256k_sampled():
+    """The backward of the chunked prefill at full size, in the launch
+    configuration the benchmark times: dq on sampled query rows, the key /
+    value gradients of sampled entries (old context, first and last new
+    entry) and raw rows from the oracle over exactly the rows that attended
+    them, and the compressor gradients of the chunk's new entries."""
+    cfg = WL.PREFILL_256K_BF16_BACKWARD
+    say("backward", cfg.name)
+    batch = WL.make_batch(cfg)
+    step = CSAStep(cfg, batch)
+    step.run()
+    g_rng = np.random.Generator(np.random.PCG64(cfg.seed))
+    dout = g_rng.standard_normal((cfg.B, cfg.T, cfg.H, cfg.d), dtype=np.float32)
+    g = step.backward(to_dev(dout))
+    torch.cuda.synchronize()
+    idx = from_dev(step.idx)[0]
+    kc, vc = decode(from_dev(step.kc)[0]), decode(from_dev(step.vc)[0])
+    q, kr, vr = decode(batch["q"][0]), decode(batch["kr"][0]), decode(batch["vr"][0])
+    pos_all = cfg.pos0 + np.arange(cfg.T)
+
+    def ref_over(rows):
+        return oracle.attend_backward(q[rows], kc, vc, idx[rows], kr, vr, cfg.raw_pos0,
+                                      pos_all[rows], cfg.W, cfg.scale, dout[0][rows])
+
+    rows = np.array([0, 31, 4095, 8191])
+    r = ref_over(rows)
+    _close("dq rows", from_dev(g["dq"])[0][rows], r["dq"], "bf16")
+    # old entries, the first and last new one, and the most attended new one
+    new_users = [(idx == j).any(axis=1).sum() for j in range(cfg.n_ctx_entries, cfg.n_cap, 7)]
+    j_hot = cfg.n_ctx_entries + 7 * int(np.argmax(new_users))
+    for j in (0, 33333, cfg.n_ctx_entries, cfg.n_cap - 1, j_hot):
+        users = np.nonzero((idx == j).any(axis=1))[0]
+        say("  entry", j, "attended by", users.size, "rows")
+        if users.size == 0:
+            assert np.all(from_dev(g["dkc"])[0][j] == 0)
+            continue
+        r = ref_over(users)
+        _close(f"dkc[{j}]", from_dev(g["dkc"])[0][j], r["dkc"][j], "bf16")
+        _close(f"dvc[{j}]", from_dev(g["dvc"])[0][j], r["dvc"][j], "bf16")
+    for rr in (cfg.raw_before, cfg.raw_before + 5000, cfg.R - 1):
+        p = cfg.raw_pos0 + rr
+        users = np.arange(max(0, p - cfg.pos0), min(cfg.T, p - cfg.pos0 + cfg.W))
+        r = ref_over(users)
+        _close(f"dkr[{rr}]", from_dev(g["dkr"])[0][rr], r["dkr"][rr], "bf16")
+        _close(f"dvr[{rr}]", from_dev(g["dvr"])[0][rr], r["dvr"][rr], "bf16")
+    # compressor gradients of the chunk's entries, fed the GPU's entry gradients
+    e0, e1 = cfg.n_ctx_entries, cfg.n_cap
+    r0, r1 = cfg.raw_before, cfg.raw_before + cfg.n_new_tokens
+    for x, dc, dxn, dzn in ((kr, "dkc", "dkr_c", "dz_k"), (vr, "dvc", "dvr_c", "dz_v")):
+        rdx, rdz = oracle.compress_backward(x[r0:r1], batch["z"][0], cfg.m,
+                                            from_dev(g[dc])[0][e0:e1])
+        assert np.max(np.abs(from_dev(g[dxn])[0] - rdx)) <= 1e-5 * max(1.0, np.max(np.abs(rdx)))
+        assert np.max(np.abs(from_dev(g[dzn])[0] - rdz)) <= 1e-5 * max(1.0, np.max(np.abs(rdz)))

@@ -54,6 +54,7 @@ class Workload:
     layers: tuple = ()         # hybrid stack: per-layer kinds "swa" / "csa" / "hca"
     block_end: bool = False    # decode token completes a block: the step compresses
                                # it into entry n_ctx_entries (logits for every raw row)
+    backward: bool = False     # the timed step is the backward pass of the forward step
     planted: int = 0           # planted high-affinity entries per sequence
     planted_spread: bool = False  # evenly spaced (else seeded distinct random)
     description: str = ""
@@ -150,9 +151,18 @@ DECODE_128K_BF16_BLOCK_END = DECODE_128K_BF16.replace(
                 "its token completes (entry 32767) and scores it with the 32767 older "
                 "entries; otherwise as csa_decode_128k_bf16")
 
+# The backward pass of the chunked prefill's attention and compression (the
+# training-shaped step: 8192 query tokens over 67584 entries, top-1024 +
+# window 128, 64 heads x 128), with a seeded upstream gradient N(0, 1).
+PREFILL_256K_BF16_BACKWARD = PREFILL_256K_BF16.replace(
+    name="csa_chunked_prefill_256k_8k_bf16_backward", number=8, backward=True,
+    description="backward pass of the chunked prefill (csa_chunked_prefill_256k_8k_bf16): "
+                "attention gradients for 8192 query tokens and the compressor gradients of "
+                "the chunk's 2048 new entries")
+
 WORKLOADS = [TINY_PREFILL_F32, DECODE_128K_BF16, PREFILL_256K_BF16,
              HCA_DECODE_1M_BF16, DECODE_1M_FP8, DECODE_1M_MXFP4, HYBRID_DECODE_128K_BF16,
-             DECODE_128K_BF16_BLOCK_END]
+             DECODE_128K_BF16_BLOCK_END, PREFILL_256K_BF16_BACKWARD]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
 
