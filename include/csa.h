@@ -338,7 +338,7 @@ int hca_attend(const void* q, int q_dtype, const void* kc, const void* vc,
  * contributions, B*T*(k+W)*d*8 bytes, and each entry's list of the rows
  * that attended it; contents on entry do not matter).
  * Supported: q/kv dtypes F32 or BF16 (equal), d in {64, 128}, H <= 64,
- * T <= 16384, B*T*k < 2^32.
+ * k <= 4096, T <= 16384, B*T*k < 2^32.
  */
 size_t csa_attend_backward_workspace_size(int64_t B, int64_t T, int64_t d,
                                           int64_t n_cap, int k, int W);

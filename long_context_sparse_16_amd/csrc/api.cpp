@@ -470,7 +470,7 @@ int csa_attend_backward(const void* q, int q_dtype, const void* kc, const void* 
                         void* stream) {
   const char* fn = "csa_attend_backward";
   CSA_REQUIRE(idx, CSA_ERR_NULL, "%s: idx must be non-NULL", fn);
-  CSA_REQUIRE(k >= 1 && k <= 65536, CSA_ERR_UNSUPPORTED, "%s: k must be in [1, 65536]", fn);
+  CSA_REQUIRE(k >= 1 && k <= 4096, CSA_ERR_UNSUPPORTED, "%s: k must be in [1, 4096]", fn);
   CSA_REQUIRE(T <= csa::kBwdMaxRows, CSA_ERR_UNSUPPORTED, "%s: T must be <= %lld", fn,
               static_cast<long long>(csa::kBwdMaxRows));
   CSA_REQUIRE(B * T * k < (int64_t(1) << 32), CSA_ERR_UNSUPPORTED, "%s: B*T*k must be < 2^32",

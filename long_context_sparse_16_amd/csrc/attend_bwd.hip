@@ -59,6 +59,7 @@ struct BwdParams {
 constexpr int kBwdChunk = 32;   // keys per chunk
 constexpr float kLog2eBwd = 1.4426950408889634f;
 constexpr int kBwdHeads = 64;   // head slots (4 waves x 16)
+constexpr int kBwdMaxK = 4096;  // longest index list (staged in LDS)
 
 template <int DTYPE>
 __device__ __forceinline__ void load_row_f32(const uint8_t* src, int e0, float* dst, int n);
@@ -99,6 +100,7 @@ __global__ __launch_bounds__(256) void attend_bwd_rows_kernel(BwdParams p) {
   __shared__ float sD[kBwdHeads];
   __shared__ int s_valid[kBwdChunk];
   __shared__ int s_gslot[kBwdChunk];
+  __shared__ int32_t s_ent[HCA ? 1 : kBwdMaxK];  // the row's index list
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -158,57 +160,86 @@ __global__ __launch_bounds__(256) void attend_bwd_rows_kernel(BwdParams p) {
   const uint8_t* kc_b = p.kc + b * p.n_cap * D * kEb;
   const uint8_t* vc_b = p.vc + b * p.n_cap * D * kEb;
   const int n_chunks = static_cast<int>((n_slots + kBwdChunk - 1) / kBwdChunk);
+  if (!HCA)
+    for (int i = tid; i < p.k; i += 256) s_ent[i] = p.idx[row * p.k + i];
   __syncthreads();
   const float Dh = sD[head];
+
+  // Slot s of the key list -> its K / V rows (absent keys: row 0, masked)
+  auto slot_rows = [&](int64_t s, const uint8_t*& ksrc, const uint8_t*& vsrc,
+                       int& ok) __attribute__((always_inline)) {
+    ksrc = kc_b;
+    vsrc = vc_b;
+    ok = 0;
+    if (s < n_ent) {
+      const int64_t e = HCA ? s : static_cast<int64_t>(s_ent[s]);
+      if (e >= 0 && e < p.n_cap) {
+        ksrc = kc_b + e * D * kEb;
+        vsrc = vc_b + e * D * kEb;
+        ok = 1;
+      }
+    } else if (s < n_slots) {
+      const int64_t pos = t - p.W + 1 + (s - n_ent);
+      const int64_t rr = pos - rp0;
+      if (pos >= 0 && rr >= 0 && rr < p.R) {
+        ksrc = p.kr + (b * p.R + rr) * D * kEb;
+        vsrc = p.vr + (b * p.R + rr) * D * kEb;
+        ok = 1;
+      }
+    }
+  };
+  // The next chunk's rows are loaded into registers while a chunk is
+  // computed: piece i = tid + 256 u is row i / kPieces, 16 bytes at i %
+  // kPieces.
+  constexpr int kIters = kBwdChunk * kPieces / 256;
+  static_assert(kIters * 256 == kBwdChunk * kPieces, "pieces split evenly over the threads");
+  u32x4 pk[kIters], pv[kIters];
+  auto fetch = [&](int c) __attribute__((always_inline)) {
+    const int64_t s0 = static_cast<int64_t>(min(c, n_chunks - 1)) * kBwdChunk;
+#pragma unroll
+    for (int u = 0; u < kIters; ++u) {
+      const int i = tid + 256 * u;
+      const uint8_t *ks, *vs;
+      int ok;
+      slot_rows(s0 + i / kPieces, ks, vs, ok);
+      pk[u] = *reinterpret_cast<const u32x4*>(ks + (i % kPieces) * 16);
+      pv[u] = *reinterpret_cast<const u32x4*>(vs + (i % kPieces) * 16);
+    }
+  };
+  auto put = [&](float* dst, u32x4 v) __attribute__((always_inline)) {
+    if (DTYPE == 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dst[2 * e] = __uint_as_float(v[e] << 16);
+        dst[2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = __uint_as_float(v[e]);
+    }
+  };
+  if (n_chunks > 0) fetch(0);
 
   for (int c = 0; c < n_chunks; ++c) {
     // ---- stage the chunk's key / value rows (fp32) and slot table
     const int64_t s0 = static_cast<int64_t>(c) * kBwdChunk;
     if (tid < kBwdChunk) {
       const int64_t s = s0 + tid;
-      int ok = 0, gs = 0;
-      if (s < n_ent) {
-        const int64_t e = HCA ? s : static_cast<int64_t>(p.idx[row * p.k + s]);
-        ok = e >= 0 && e < p.n_cap;
-        gs = static_cast<int>(s);
-      } else if (s < n_slots) {
-        const int64_t pos = t - p.W + 1 + (s - n_ent);
-        const int64_t rr = pos - rp0;
-        ok = pos >= 0 && rr >= 0 && rr < p.R;
-        gs = p.n_ent_max + static_cast<int>(s - n_ent);
-      }
+      const uint8_t *ks, *vs;
+      int ok;
+      slot_rows(s, ks, vs, ok);
       s_valid[tid] = ok;
-      s_gslot[tid] = gs;
+      s_gslot[tid] = s < n_ent ? static_cast<int>(s) : p.n_ent_max + static_cast<int>(s - n_ent);
     }
-    for (int i = tid; i < kBwdChunk * kPieces; i += 256) {
-      const int key = i / kPieces, pc = i % kPieces;
-      const int64_t s = s0 + key;
-      const uint8_t* ksrc = kc_b;  // absent keys: row 0 (masked below)
-      const uint8_t* vsrc = vc_b;
-      if (s < n_ent) {
-        const int64_t e = HCA ? s : static_cast<int64_t>(p.idx[row * p.k + s]);
-        if (e >= 0 && e < p.n_cap) {
-          ksrc = kc_b + e * D * kEb;
-          vsrc = vc_b + e * D * kEb;
-        }
-      } else if (s < n_slots) {
-        const int64_t pos = t - p.W + 1 + (s - n_ent);
-        const int64_t rr = pos - rp0;
-        if (pos >= 0 && rr >= 0 && rr < p.R) {
-          ksrc = p.kr + (b * p.R + rr) * D * kEb;
-          vsrc = p.vr + (b * p.R + rr) * D * kEb;
-        }
-      }
-      float kv[kPer], vv[kPer];
-      load_row_f32<DTYPE>(ksrc, pc * kPer, kv, kPer);
-      load_row_f32<DTYPE>(vsrc, pc * kPer, vv, kPer);
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        sK[key][pc * kPer + e] = kv[e];
-        sV[key][pc * kPer + e] = vv[e];
-      }
+    for (int u = 0; u < kIters; ++u) {
+      const int i = tid + 256 * u;
+      const int key = i / kPieces, e0 = (i % kPieces) * kPer;
+      put(&sK[key][e0], pk[u]);
+      put(&sV[key][e0], pv[u]);
     }
     __syncthreads();
+    fetch(c + 1);  // (past the end: the last chunk again, from cache)
 
     // ---- phase A (wave = 16 heads, all 32 keys): S^T, dP^T, P, dS, dq
     f32x4 sT[2], dpT[2];
