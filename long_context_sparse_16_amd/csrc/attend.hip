@@ -7,7 +7,10 @@
 //
 // One query token per workgroup row; every query head shares the single KV
 // head, so the gathered key/value rows are staged in LDS once and used by
-// all heads (4 waves x 16 heads).  The logical key list of a query is
+// all heads.  Eight waves: four tiles of 16 heads times the two 32-key
+// halves of each chunk, so two waves share a SIMD and one's softmax hides
+// the other's MFMA and LDS latency; each wave keeps its own softmax state
+// for its half, and the halves of a head are combined once at the end.  The logical key list of a query is
 //   slots [0, n_entries)            -> compressed entry (idx list or 0..V-1)
 //   slots [n_entries, n_entries+W)  -> raw window position t-W+1+w
 // and is cut into 64-key chunks; long lists are split over several
@@ -28,6 +31,7 @@
 namespace csa {
 
 constexpr int kAttChunk = 64;  // keys per LDS chunk
+constexpr int kAttThreads = 512;  // 8 waves: 4 head tiles x 2 key halves
 // CSA: a split's slice of the top-k list is staged in LDS, so a split spans
 // at most this many chunks.
 constexpr int kAttMaxSplitChunks = 32;
@@ -83,11 +87,13 @@ struct AttParams {
 };
 
 template <int DTYPE, int D, bool HCA>
-__global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
+__global__ __launch_bounds__(kAttThreads) void attend_kernel(AttParams p) {
   using Tr = AttTraits<DTYPE, D>;
   constexpr int RB = Tr::kRowBytes;
   constexpr int kPieces = RB / 16;             // 16-byte pieces per row
-  constexpr int kPerThread = kAttChunk * kPieces / 256;
+  constexpr int kPerThread = kAttChunk * kPieces / kAttThreads;
+  static_assert(kPerThread >= 1 && kPerThread * kAttThreads == kAttChunk * kPieces,
+                "a chunk must split evenly over the threads");
   constexpr int kKsStride = RB + 16;
   constexpr int kVsStride = Tr::kVsStride;
   // Two LDS buffers: chunk i+1 is staged into one while chunk i is computed
@@ -103,6 +109,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ht = wave & 3;  // head tile
+  const int kh = wave >> 2;  // key half of every chunk
   const int col = lane & 15;
   const int g = lane >> 4;
   const int64_t row = blockIdx.y;
@@ -118,8 +126,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
   const int64_t c_begin = static_cast<int64_t>(split) * p.chunks_per_split;
   const int64_t c_end = min(c_begin + p.chunks_per_split, (n_slots + kAttChunk - 1) / kAttChunk);
   const int n_ht = static_cast<int>((p.H + 15) >> 4);
-  const bool has_heads = wave < n_ht;
-  const int head = wave * 16 + col;
+  const bool has_heads = ht < n_ht;
+  const int head = ht * 16 + col;
 
   // Q^T fragments: this lane's head, one contiguous quarter of the row.
   // Lanes past the last head load it again (unconditional loads); their
@@ -139,12 +147,12 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
   const int64_t idx_row = row * p.k;
   if (!HCA) {
     const int64_t n_list = min(c_end * kAttChunk, n_ent) - s_begin;
-    for (int64_t i = tid; i < n_list; i += 256) s_ent[i] = p.idx[idx_row + s_begin + i];
+    for (int64_t i = tid; i < n_list; i += kAttThreads) s_ent[i] = p.idx[idx_row + s_begin + i];
   }
   if (tid == 0) s_partial[0] = s_partial[1] = 0;
 
   // Every thread gathers kPerThread 16-byte pieces of K and of V per chunk
-  // (piece r: key (tid + 256 r) / kPieces, same column pc), into one of two
+  // (piece r: key (tid + 512 r) / kPieces, same column pc), into one of two
   // register slots: while chunk i is computed, the loads of chunks i+2 and
   // i+3 are in flight.  Absent slots (padding, positions outside the raw
   // buffer) read row 0 of the sequence's cache instead, and chunks past the
@@ -172,7 +180,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
       // uniform fast path: every slot of the chunk is a compressed entry
 #pragma unroll
       for (int r = 0; r < kPerThread; ++r) {
-        const int key = key0 + r * (256 / kPieces);
+        const int key = key0 + r * (kAttThreads / kPieces);
         int64_t e;
         if (HCA) {
           e = s0 + key;
@@ -189,7 +197,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
       const int64_t raw_k = p.kr - kc_b, raw_v = p.vr - vc_b;
 #pragma unroll
       for (int r = 0; r < kPerThread; ++r) {
-        const int64_t s = s0 + key0 + r * (256 / kPieces);
+        const int64_t s = s0 + key0 + r * (kAttThreads / kPieces);
         int64_t ko = pc * 16, vo = pc * 16;
         bool ok = false;
         if (s < n_ent) {
@@ -221,7 +229,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
     constexpr int bf = decltype(buf)::value;
 #pragma unroll
     for (int r = 0; r < kPerThread; ++r) {
-      const int key = key0 + r * (256 / kPieces);
+      const int key = key0 + r * (kAttThreads / kPieces);
       *reinterpret_cast<u32x4*>(&ks[bf][key * kKsStride + pc * 16]) = S.k[r];
       *reinterpret_cast<u32x4*>(&vs[bf][key * kVsStride + pc * 16]) = S.v[r];
       if (pc == 0) {
@@ -246,23 +254,24 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
     const bool masked = s_partial[bf] == i + 1;
     const uint8_t* kb = ks[bf];
     const uint8_t* vb = vs[bf];
-    // S^T tiles: 4 tiles of 16 keys x 16 heads
-    f32x4 s[4];
+    // S^T tiles: this wave's 2 tiles of 16 keys x 16 heads (keys 32 kh ..)
+    f32x4 s[2];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) {
+      const int kt = 2 * kh + j;
+      s[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       const uint8_t* arow = kb + (kt * 16 + col) * kKsStride + g * (RB / 4);
       if (DTYPE == 1) {
 #pragma unroll
         for (int st = 0; st < Tr::kKSteps; ++st) {
           const u32x4 a = *reinterpret_cast<const u32x4*>(arow + st * 16);
-          s[kt] = mma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[st]), s[kt]);
+          s[j] = mma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[st]), s[j]);
         }
       } else {
 #pragma unroll
         for (int st = 0; st < Tr::kKSteps; ++st) {
           const float a = *reinterpret_cast<const float*>(arow + st * 4);
-          s[kt] = mma_f32(a, __uint_as_float(qf[st >> 2][st & 3]), s[kt]);
+          s[j] = mma_f32(a, __uint_as_float(qf[st >> 2][st & 3]), s[j]);
         }
       }
     }
@@ -272,22 +281,22 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
     {
 #pragma clang fp contract(off)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[kt][i] *= p.scale_log2;
+        for (int i = 0; i < 4; ++i) s[j][i] *= p.scale_log2;
     }
     if (masked) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (!valid[bf][kt * 16 + g * 4 + i]) s[kt][i] = -INFINITY;
+          if (!valid[bf][(2 * kh + j) * 16 + g * 4 + i]) s[j][i] = -INFINITY;
     }
     float mloc = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, s[kt][i]);
+      for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, s[j][i]);
     mloc = max_xor32(max_xor16(mloc));
     const float m_new = mloc > m_run + kAttMaxSlack ? mloc : m_run;
     if (m_new == -INFINITY) return;  // nothing valid so far (uniform per head)
@@ -300,11 +309,11 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
     m_run = m_new;
     float lsum = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float e = __builtin_amdgcn_exp2f(s[kt][i] - m_new);
-        s[kt][i] = e;
+        const float e = __builtin_amdgcn_exp2f(s[j][i] - m_new);
+        s[j][i] = e;
         lsum += e;
       }
     }
@@ -312,33 +321,31 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
 
     // O^T += V^T . P^T
     if (DTYPE == 1) {
-      // lane (dim col, group g) needs V[32kk + 4g + i][dim] (lo) and
-      // V[32kk + 16 + 4g + i][dim] (hi), i = 0..3
-      const uint8_t* vbase = vb + (4 * g + (col >> 2)) * kVsStride + (col & 3) * 8;
+      // lane (dim col, group g) needs V[32kh + 4g + i][dim] (lo) and
+      // V[32kh + 16 + 4g + i][dim] (hi), i = 0..3
+      const uint8_t* vbase = vb + (32 * kh + 4 * g + (col >> 2)) * kVsStride + (col & 3) * 8;
+      bf16x8 pb;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 pb;
+      for (int i = 0; i < 4; ++i) {
+        pb[i] = static_cast<__bf16>(s[0][i]);
+        pb[4 + i] = static_cast<__bf16>(s[1][i]);
+      }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[i] = static_cast<__bf16>(s[2 * kk][i]);
-          pb[4 + i] = static_cast<__bf16>(s[2 * kk + 1][i]);
-        }
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) {
-          const u32x2 lo = lds_read_tr16(vbase + 32 * kk * kVsStride + dt * 32);
-          const u32x2 hi = lds_read_tr16(vbase + (32 * kk + 16) * kVsStride + dt * 32);
-          const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
-          o[dt] = mma_bf16(__builtin_bit_cast(bf16x8, a), pb, o[dt]);
-        }
+      for (int dt = 0; dt < kDT; ++dt) {
+        const u32x2 lo = lds_read_tr16(vbase + dt * 32);
+        const u32x2 hi = lds_read_tr16(vbase + 16 * kVsStride + dt * 32);
+        const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        o[dt] = mma_bf16(__builtin_bit_cast(bf16x8, a), pb, o[dt]);
       }
     } else {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int j = 0; j < 2; ++j) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float* vrow = reinterpret_cast<const float*>(vb + (kt * 16 + 4 * g + i) * kVsStride);
+          const float* vrow = reinterpret_cast<const float*>(
+              vb + ((2 * kh + j) * 16 + 4 * g + i) * kVsStride);
 #pragma unroll
-          for (int dt = 0; dt < kDT; ++dt) o[dt] = mma_f32(vrow[dt * 16 + col], s[kt][i], o[dt]);
+          for (int dt = 0; dt < kDT; ++dt) o[dt] = mma_f32(vrow[dt * 16 + col], s[j][i], o[dt]);
         }
       }
     }
@@ -385,9 +392,38 @@ __global__ __launch_bounds__(256) void attend_kernel(AttParams p) {
     if (i < n_chunks) compute(I0{}, i);
   }
 
-  float l_tot = l_run;
-  l_tot = sum_xor32(sum_xor16(l_tot));
-  const bool writer = has_heads && head < p.H;
+  float l_tot = sum_xor32(sum_xor16(l_run));
+  // Combine the two key halves of each head: the second-half waves leave
+  // (O, max, sum) in the (now free) chunk buffers, the first-half waves fold
+  // them in and write the result.
+  {
+    static_assert(sizeof(ks) >= 4 * kDT * 64 * sizeof(f32x4), "combine buffer");
+    static_assert(sizeof(vs) >= 128 * sizeof(float), "combine buffer");
+    f32x4* xo = reinterpret_cast<f32x4*>(&ks[0][0]);  // [head tile][dim tile][lane]
+    float* xm = reinterpret_cast<float*>(&vs[0][0]);  // max [64], sum [64] per head slot
+    __syncthreads();  // every wave is done with the chunk buffers
+    if (kh == 1 && has_heads) {
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) xo[(ht * kDT + dt) * 64 + lane] = o[dt];
+      if (g == 0) {
+        xm[ht * 16 + col] = m_run;
+        xm[64 + ht * 16 + col] = l_tot;
+      }
+    }
+    __syncthreads();
+    if (kh == 1 || !has_heads) return;
+    const float m1 = xm[ht * 16 + col];
+    const float l1 = xm[64 + ht * 16 + col];
+    const float mm = fmaxf(m_run, m1);
+    if (mm != -INFINITY) {  // both halves empty: O and the sum stay 0
+      const float f0 = exp2f(m_run - mm), f1 = exp2f(m1 - mm);
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) o[dt] = o[dt] * f0 + xo[(ht * kDT + dt) * 64 + lane] * f1;
+      l_tot = l_tot * f0 + l1 * f1;
+      m_run = mm;
+    }
+  }
+  const bool writer = head < p.H;
   if (p.splits == 1) {
     if (!writer) return;
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
@@ -541,9 +577,9 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
 #define CSA_ATT_CASE(DT, DD)                                                        \
   if (dtype == DT && D == DD) {                                                     \
     if (hca)                                                                        \
-      attend_kernel<DT, DD, true><<<grid, 256, 0, stream>>>(p);                     \
+      attend_kernel<DT, DD, true><<<grid, kAttThreads, 0, stream>>>(p);             \
     else                                                                            \
-      attend_kernel<DT, DD, false><<<grid, 256, 0, stream>>>(p);                    \
+      attend_kernel<DT, DD, false><<<grid, kAttThreads, 0, stream>>>(p);            \
     if (sp.splits > 1)                                                              \
       attend_merge_kernel<DD><<<dim3(static_cast<unsigned>((H + kMergeThreads / (DD / 4) - 1) / \
                                                            (kMergeThreads / (DD / 4))),      \
