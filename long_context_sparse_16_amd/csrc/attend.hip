@@ -448,15 +448,16 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttParams p) {
 }
 
 // Merge the split partials of one query row: each thread owns 4 output dims
-// of one head.  Splits are taken in batches of kMergeBatch: every load of a
+// of one head.  Splits are taken in batches of MB (16, or 32 for rows of
+// more than 16 splits, so that up to 32 splits cost one round trip to
+// memory rather than two dependent ones): every load of a
 // batch (maxima, sums, partial outputs; indices clamped so none is
 // conditional) is issued before any is used, and the batch is folded into a
 // running (max, sum, O) in split order, so the result does not depend on
 // scheduling.
-constexpr int kMergeBatch = 16;
 constexpr int kMergeThreads = 256;
 
-template <int D>
+template <int D, int MB>
 __global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(AttParams p) {
   constexpr int kTPH = D / 4;  // threads per head
   constexpr int kHPB = kMergeThreads / kTPH;
@@ -467,11 +468,11 @@ __global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(AttParams p
   const int64_t base = row * p.splits * p.H + h;  // partial (row, split 0, head h)
   float M = -INFINITY, L = 0.f;
   f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < p.splits; s0 += kMergeBatch) {
-    float pm[kMergeBatch], pl[kMergeBatch];
-    f32x4 po[kMergeBatch];
+  for (int s0 = 0; s0 < p.splits; s0 += MB) {
+    float pm[MB], pl[MB];
+    f32x4 po[MB];
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
+    for (int j = 0; j < MB; ++j) {
       const int64_t sp = min(s0 + j, p.splits - 1);
       pm[j] = p.pm[base + sp * p.H];
       pl[j] = p.pl[base + sp * p.H];
@@ -479,7 +480,7 @@ __global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(AttParams p
     }
     float mb = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j)
+    for (int j = 0; j < MB; ++j)
       if (s0 + j < p.splits) mb = fmaxf(mb, pm[j]);
     const float m_new = fmaxf(M, mb);
     if (m_new == -INFINITY) continue;  // every split so far is empty
@@ -487,7 +488,7 @@ __global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(AttParams p
     L *= f;
     O *= f;
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
+    for (int j = 0; j < MB; ++j) {
       const float w = s0 + j < p.splits ? exp2f(pm[j] - m_new) : 0.f;  // 0 for empty splits
       L = fmaf(pl[j], w, L);
       O += po[j] * w;
@@ -574,17 +575,18 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
     p.pl = p.pm + rows * sp.splits * H;
   }
   dim3 grid(static_cast<unsigned>(sp.splits), static_cast<unsigned>(rows));
+  const dim3 mgrid(static_cast<unsigned>((H + kMergeThreads / (D / 4) - 1) / (kMergeThreads / (D / 4))),
+                   static_cast<unsigned>(rows));
 #define CSA_ATT_CASE(DT, DD)                                                        \
   if (dtype == DT && D == DD) {                                                     \
     if (hca)                                                                        \
       attend_kernel<DT, DD, true><<<grid, kAttThreads, 0, stream>>>(p);             \
     else                                                                            \
       attend_kernel<DT, DD, false><<<grid, kAttThreads, 0, stream>>>(p);            \
-    if (sp.splits > 1)                                                              \
-      attend_merge_kernel<DD><<<dim3(static_cast<unsigned>((H + kMergeThreads / (DD / 4) - 1) / \
-                                                           (kMergeThreads / (DD / 4))),      \
-                                     static_cast<unsigned>(rows)),                           \
-                                kMergeThreads, 0, stream>>>(p);                              \
+    if (sp.splits > 16)                                                             \
+      attend_merge_kernel<DD, 32><<<mgrid, kMergeThreads, 0, stream>>>(p);          \
+    else if (sp.splits > 1)                                                         \
+      attend_merge_kernel<DD, 16><<<mgrid, kMergeThreads, 0, stream>>>(p);          \
     return hipGetLastError() == hipSuccess ? 0 : -1;                                \
   }
   CSA_ATT_CASE(0, 64)
