@@ -58,7 +58,8 @@ struct BwdParams {
 
 constexpr int kBwdChunk = 32;   // keys per chunk
 constexpr float kLog2eBwd = 1.4426950408889634f;
-constexpr int kBwdHeads = 64;   // head slots (4 waves x 16)
+constexpr int kBwdHeads = 64;   // head slots (4 tiles of 16)
+constexpr int kBwdThreads = 512;  // row kernel: 8 waves = 4 head tiles x 2 key tiles
 constexpr int kBwdMaxK = 4096;  // longest index list (staged in LDS)
 
 template <int DTYPE>
@@ -83,7 +84,8 @@ __device__ __forceinline__ void load_row_f32<0>(const uint8_t* src, int e0, floa
 }
 
 template <int DTYPE, int D, bool HCA>
-__global__ __launch_bounds__(256) void attend_bwd_rows_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBwdThreads) void attend_bwd_rows_kernel(BwdParams p) {
+  constexpr int NT = kBwdThreads;
   constexpr int kEb = DTYPE == 1 ? 2 : 4;     // bytes per stored element
   constexpr int kPer = 16 / kEb;              // elements per 16-byte load
   constexpr int kPieces = D / kPer;           // 16-byte pieces per row
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(256) void attend_bwd_rows_kernel(BwdParams p) {
 
   // q and dout rows (fp32) of all heads; head slots past H hold zeros, so
   // their probabilities and gradients are zero (lse = +inf below).
-  for (int i = tid; i < kBwdHeads * kPieces; i += 256) {
+  for (int i = tid; i < kBwdHeads * kPieces; i += NT) {
     const int h = i / kPieces, pc = i % kPieces;
     float v[kPer];
     if (h < H) {
@@ -130,26 +132,31 @@ __global__ __launch_bounds__(256) void attend_bwd_rows_kernel(BwdParams p) {
 #pragma unroll
     for (int e = 0; e < kPer; ++e) sQ[h][pc * kPer + e] = v[e];
   }
-  for (int i = tid; i < kBwdHeads * (D / 4); i += 256) {
+  for (int i = tid; i < kBwdHeads * (D / 4); i += NT) {
     const int h = i / (D / 4), c4 = i % (D / 4);
     f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
     if (h < H) v = *reinterpret_cast<const f32x4*>(p.dout + (row * H + h) * D + c4 * 4);
     *reinterpret_cast<f32x4*>(&sdO[h][c4 * 4]) = v;
   }
-  // D[h] = dout . o: four threads per head, a quarter of the dims each
+  // D[h] = dout . o: eight threads per head, an eighth of the dims each
   {
-    const int h = tid >> 2, qd = tid & 3;
+    static_assert(NT == 8 * kBwdHeads, "eight threads per head slot");
+    const int h = tid >> 3, qd = tid & 7;
     float acc = 0.f;
     if (h < H) {
-      const float* orow = p.out + (row * H + h) * D + qd * (D / 4);
-      const float* grow = p.dout + (row * H + h) * D + qd * (D / 4);
-      for (int c = 0; c < D / 4; ++c) acc = fmaf(grow[c], orow[c], acc);
+      const float* orow = p.out + (row * H + h) * D + qd * (D / 8);
+      const float* grow = p.dout + (row * H + h) * D + qd * (D / 8);
+      for (int c = 0; c < D / 8; ++c) acc = fmaf(grow[c], orow[c], acc);
     }
     acc += __shfl_xor(acc, 1);
     acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
     if (qd == 0) sD[h] = acc;
   }
-  const int head = wave * 16 + col;
+  // wave = (key tile kh of each 32-key chunk, head tile ht)
+  const int ht = wave & 3;
+  const int kh = wave >> 2;
+  const int head = ht * 16 + col;
   const float lse2 = head < H ? p.lse[row * H + head] * kLog2eBwd : INFINITY;
   const float scale_log2 = p.scale * kLog2eBwd;
 
@@ -161,7 +168,7 @@ __global__ __launch_bounds__(256) void attend_bwd_rows_kernel(BwdParams p) {
   const uint8_t* vc_b = p.vc + b * p.n_cap * D * kEb;
   const int n_chunks = static_cast<int>((n_slots + kBwdChunk - 1) / kBwdChunk);
   if (!HCA)
-    for (int i = tid; i < p.k; i += 256) s_ent[i] = p.idx[row * p.k + i];
+    for (int i = tid; i < p.k; i += NT) s_ent[i] = p.idx[row * p.k + i];
   __syncthreads();
   const float Dh = sD[head];
 
@@ -189,16 +196,19 @@ __global__ __launch_bounds__(256) void attend_bwd_rows_kernel(BwdParams p) {
     }
   };
   // The next chunk's rows are loaded into registers while a chunk is
-  // computed: piece i = tid + 256 u is row i / kPieces, 16 bytes at i %
-  // kPieces.
-  constexpr int kIters = kBwdChunk * kPieces / 256;
-  static_assert(kIters * 256 == kBwdChunk * kPieces, "pieces split evenly over the threads");
+  // computed: piece i = tid + NT u is row i / kPieces, 16 bytes at i %
+  // kPieces.  (d = 64, bf16: 256 pieces for 512 threads; the upper half
+  // loads the lower half's pieces again and does not stage them.)
+  constexpr int kChunkPieces = kBwdChunk * kPieces;
+  constexpr int kIters = (kChunkPieces + NT - 1) / NT;
+  static_assert(kChunkPieces % NT == 0 || NT % kChunkPieces == 0,
+                "pieces split evenly over the threads");
   u32x4 pk[kIters], pv[kIters];
   auto fetch = [&](int c) __attribute__((always_inline)) {
     const int64_t s0 = static_cast<int64_t>(min(c, n_chunks - 1)) * kBwdChunk;
 #pragma unroll
     for (int u = 0; u < kIters; ++u) {
-      const int i = tid + 256 * u;
+      const int i = (tid + NT * u) % kChunkPieces;
       const uint8_t *ks, *vs;
       int ok;
       slot_rows(s0 + i / kPieces, ks, vs, ok);
@@ -233,60 +243,55 @@ __global__ __launch_bounds__(256) void attend_bwd_rows_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int u = 0; u < kIters; ++u) {
-      const int i = tid + 256 * u;
-      const int key = i / kPieces, e0 = (i % kPieces) * kPer;
-      put(&sK[key][e0], pk[u]);
-      put(&sV[key][e0], pv[u]);
+      const int i = tid + NT * u;
+      if (i < kChunkPieces) {
+        const int key = i / kPieces, e0 = (i % kPieces) * kPer;
+        put(&sK[key][e0], pk[u]);
+        put(&sV[key][e0], pv[u]);
+      }
     }
     __syncthreads();
     fetch(c + 1);  // (past the end: the last chunk again, from cache)
 
-    // ---- phase A (wave = 16 heads, all 32 keys): S^T, dP^T, P, dS, dq
-    f32x4 sT[2], dpT[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    // ---- phase A (wave = 16 heads x the 16 keys of key tile kh): S^T,
+    // dP^T, P, dS, and this key tile's share of dq
+    f32x4 sT, dpT;
+    {
       f32x4 as = f32x4{0.f, 0.f, 0.f, 0.f}, ad = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
       for (int ks = 0; ks < kKs; ++ks) {
-        const float kq = sK[kt * 16 + col][ks * 4 + g];
-        const float vq = sV[kt * 16 + col][ks * 4 + g];
+        const float kq = sK[kh * 16 + col][ks * 4 + g];
+        const float vq = sV[kh * 16 + col][ks * 4 + g];
         as = mma_f32(kq, sQ[head][ks * 4 + g], as);
         ad = mma_f32(vq, sdO[head][ks * 4 + g], ad);
       }
-      sT[kt] = as;
-      dpT[kt] = ad;
+      sT = as;
+      dpT = ad;
     }
-    float ps[2][4], dss[2][4];
+    float dss[4];
     {
 #pragma clang fp contract(off)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kt * 16 + g * 4 + i;
-          const float pr = s_valid[key] ? exp2f(sT[kt][i] * scale_log2 - lse2) : 0.f;
-          ps[kt][i] = pr;
-          dss[kt][i] = pr * (dpT[kt][i] - Dh) * p.scale;
-          sP[key][head] = pr;
-          sdS[key][head] = dss[kt][i];
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int key = kh * 16 + g * 4 + i;
+        const float pr = s_valid[key] ? exp2f(sT[i] * scale_log2 - lse2) : 0.f;
+        dss[i] = pr * (dpT[i] - Dh) * p.scale;
+        sP[key][head] = pr;
+        sdS[key][head] = dss[i];
+      }
     }
     // dq^T[dim][head] += sum_key K[key][dim] dS[head][key] (scale folded)
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dq[dt] = mma_f32(sK[kt * 16 + g * 4 + i][dt * 16 + col], dss[kt][i], dq[dt]);
+      for (int i = 0; i < 4; ++i)
+        dq[dt] = mma_f32(sK[kh * 16 + g * 4 + i][dt * 16 + col], dss[i], dq[dt]);
     __syncthreads();
 
-    // ---- phase B (wave = D/4 dims, all keys, all heads): the chunk's key
-    // and value gradient contributions, summed over heads
-    constexpr int kDW = D / 4 / 16;  // dim tiles per wave (>= 1 for D >= 64)
-#pragma unroll
-    for (int dd = 0; dd < kDW; ++dd) {
-      const int dim0 = wave * (D / 4) + dd * 16;
+    // ---- phase B (wave = one 16-dim tile, all keys, all heads): the
+    // chunk's key and value gradient contributions, summed over heads
+    for (int dd = wave; dd < D / 16; dd += NT / 64) {
+      const int dim0 = dd * 16;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         f32x4 ak = f32x4{0.f, 0.f, 0.f, 0.f}, av = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -307,10 +312,20 @@ __global__ __launch_bounds__(256) void attend_bwd_rows_kernel(BwdParams p) {
     }
     __syncthreads();
   }
-  if (head < H) {
+  // dq: the two key tiles' shares of each head, added in a fixed order
+  // through the (now free) query buffer
+  static_assert(sizeof(sQ) >= 4 * kDT * 64 * sizeof(f32x4), "dq exchange buffer");
+  f32x4* xq = reinterpret_cast<f32x4*>(&sQ[0][0]);  // [head tile][dim tile][lane]
+  if (kh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt) xq[(ht * kDT + dt) * 64 + lane] = dq[dt];
+  }
+  __syncthreads();
+  if (kh == 0 && head < H) {
     float* dst = p.dq + (row * H + head) * D;
 #pragma unroll
-    for (int dt = 0; dt < kDT; ++dt) *reinterpret_cast<f32x4*>(dst + dt * 16 + g * 4) = dq[dt];
+    for (int dt = 0; dt < kDT; ++dt)
+      *reinterpret_cast<f32x4*>(dst + dt * 16 + g * 4) = dq[dt] + xq[(ht * kDT + dt) * 64 + lane];
   }
 }
 
@@ -610,8 +625,8 @@ int launch_attend_bwd(const void* q, int dtype, const void* kc, const void* vc,
   }
 #define CSA_BWD_CASE(DT, DD)                                                                  \
   if (dtype == DT && D == DD) {                                                               \
-    if (hca) attend_bwd_rows_kernel<DT, DD, true><<<dim3(rows), 256, 0, stream>>>(p);          \
-    else attend_bwd_rows_kernel<DT, DD, false><<<dim3(rows), 256, 0, stream>>>(p);             \
+    if (hca) attend_bwd_rows_kernel<DT, DD, true><<<dim3(rows), kBwdThreads, 0, stream>>>(p);  \
+    else attend_bwd_rows_kernel<DT, DD, false><<<dim3(rows), kBwdThreads, 0, stream>>>(p);     \
     if (hca) {                                                                                \
       attend_bwd_entries_kernel<DD, true><<<dim3(n_cap, B), 256, 0, stream>>>(p);              \
     } else {                                                                                  \
