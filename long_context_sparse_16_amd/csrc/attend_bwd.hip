@@ -255,15 +255,27 @@ __global__ __launch_bounds__(kBwdThreads) void attend_bwd_rows_kernel(BwdParams 
 
     // ---- phase A (wave = 16 heads x the 16 keys of key tile kh): S^T,
     // dP^T, P, dS, and this key tile's share of dq
+    // (the dims are summed in the order lane group g takes dims
+    // g kKs .. g kKs + kKs - 1, so each lane reads its K, V, q and dout
+    // values as contiguous 16-byte pieces)
     f32x4 sT, dpT;
     {
       f32x4 as = f32x4{0.f, 0.f, 0.f, 0.f}, ad = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int ks = 0; ks < kKs; ++ks) {
-        const float kq = sK[kh * 16 + col][ks * 4 + g];
-        const float vq = sV[kh * 16 + col][ks * 4 + g];
-        as = mma_f32(kq, sQ[head][ks * 4 + g], as);
-        ad = mma_f32(vq, sdO[head][ks * 4 + g], ad);
+      const float* krow = &sK[kh * 16 + col][g * kKs];
+      const float* vrow = &sV[kh * 16 + col][g * kKs];
+      const float* qrow = &sQ[head][g * kKs];
+      const float* orow = &sdO[head][g * kKs];
+#pragma unroll 2
+      for (int k4 = 0; k4 < kKs / 4; ++k4) {
+        const f32x4 kq = *reinterpret_cast<const f32x4*>(krow + 4 * k4);
+        const f32x4 vq = *reinterpret_cast<const f32x4*>(vrow + 4 * k4);
+        const f32x4 qq = *reinterpret_cast<const f32x4*>(qrow + 4 * k4);
+        const f32x4 oq = *reinterpret_cast<const f32x4*>(orow + 4 * k4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          as = mma_f32(kq[j], qq[j], as);
+          ad = mma_f32(vq[j], oq[j], ad);
+        }
       }
       sT = as;
       dpT = ad;
@@ -295,11 +307,20 @@ __global__ __launch_bounds__(kBwdThreads) void attend_bwd_rows_kernel(BwdParams 
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         f32x4 ak = f32x4{0.f, 0.f, 0.f, 0.f}, av = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int ks = 0; ks < kBwdHeads / 4; ++ks) {
-          const int h = ks * 4 + g;
-          ak = mma_f32(sQ[h][dim0 + col], sdS[kt * 16 + col][h], ak);
-          av = mma_f32(sdO[h][dim0 + col], sP[kt * 16 + col][h], av);
+        // (heads summed in the order lane group g takes heads 16 g ..
+        // 16 g + 15: a lane's dS and P values are contiguous)
+        const float* dsrow = &sdS[kt * 16 + col][g * (kBwdHeads / 4)];
+        const float* prow = &sP[kt * 16 + col][g * (kBwdHeads / 4)];
+#pragma unroll 2
+        for (int k4 = 0; k4 < kBwdHeads / 16; ++k4) {
+          const f32x4 dsv = *reinterpret_cast<const f32x4*>(dsrow + 4 * k4);
+          const f32x4 pv4 = *reinterpret_cast<const f32x4*>(prow + 4 * k4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int h = g * (kBwdHeads / 4) + 4 * k4 + j;
+            ak = mma_f32(sQ[h][dim0 + col], dsv[j], ak);
+            av = mma_f32(sdO[h][dim0 + col], pv4[j], av);
+          }
         }
         // lane (key col, g) holds dims dim0 + 4 g .. + 3 of key kt*16 + col
         const int key = kt * 16 + col;
