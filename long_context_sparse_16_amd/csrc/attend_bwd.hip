@@ -93,8 +93,11 @@ __global__ __launch_bounds__(kBwdThreads) void attend_bwd_rows_kernel(BwdParams 
   constexpr int kDT = D / 16;                 // dim tiles
   constexpr int kS = D + 4;                   // padded fp32 row stride
   constexpr int kHs = kBwdHeads + 4;          // padded [key][head] stride
-  __shared__ __attribute__((aligned(16))) float sQ[kBwdHeads][kS];
-  __shared__ __attribute__((aligned(16))) float sdO[kBwdHeads][kS];
+  // q and dout transposed ([dim][head]): the key / value phase reads a
+  // lane's 16 heads of one dim as contiguous 16-byte pieces; the score
+  // phase keeps its lane's share of its head's row in registers
+  __shared__ __attribute__((aligned(16))) float sQt[D][kHs];
+  __shared__ __attribute__((aligned(16))) float sdOt[D][kHs];
   __shared__ __attribute__((aligned(16))) float sK[kBwdChunk][kS];
   __shared__ __attribute__((aligned(16))) float sV[kBwdChunk][kS];
   __shared__ __attribute__((aligned(16))) float sP[kBwdChunk][kHs];
@@ -130,13 +133,14 @@ __global__ __launch_bounds__(kBwdThreads) void attend_bwd_rows_kernel(BwdParams 
       for (int e = 0; e < kPer; ++e) v[e] = 0.f;
     }
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) sQ[h][pc * kPer + e] = v[e];
+    for (int e = 0; e < kPer; ++e) sQt[pc * kPer + e][h] = v[e];
   }
   for (int i = tid; i < kBwdHeads * (D / 4); i += NT) {
     const int h = i / (D / 4), c4 = i % (D / 4);
     f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
     if (h < H) v = *reinterpret_cast<const f32x4*>(p.dout + (row * H + h) * D + c4 * 4);
-    *reinterpret_cast<f32x4*>(&sdO[h][c4 * 4]) = v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sdOt[c4 * 4 + e][h] = v[e];
   }
   // D[h] = dout . o: eight threads per head, an eighth of the dims each
   {
@@ -171,6 +175,13 @@ __global__ __launch_bounds__(kBwdThreads) void attend_bwd_rows_kernel(BwdParams 
     for (int i = tid; i < p.k; i += NT) s_ent[i] = p.idx[row * p.k + i];
   __syncthreads();
   const float Dh = sD[head];
+  // this lane's dims g kKs .. g kKs + kKs - 1 of its head's q and dout rows
+  float qreg[kKs], oreg[kKs];
+#pragma unroll
+  for (int k = 0; k < kKs; ++k) {
+    qreg[k] = sQt[g * kKs + k][head];
+    oreg[k] = sdOt[g * kKs + k][head];
+  }
 
   // Slot s of the key list -> its K / V rows (absent keys: row 0, masked)
   auto slot_rows = [&](int64_t s, const uint8_t*& ksrc, const uint8_t*& vsrc,
@@ -263,18 +274,14 @@ __global__ __launch_bounds__(kBwdThreads) void attend_bwd_rows_kernel(BwdParams 
       f32x4 as = f32x4{0.f, 0.f, 0.f, 0.f}, ad = f32x4{0.f, 0.f, 0.f, 0.f};
       const float* krow = &sK[kh * 16 + col][g * kKs];
       const float* vrow = &sV[kh * 16 + col][g * kKs];
-      const float* qrow = &sQ[head][g * kKs];
-      const float* orow = &sdO[head][g * kKs];
-#pragma unroll 2
+#pragma unroll
       for (int k4 = 0; k4 < kKs / 4; ++k4) {
         const f32x4 kq = *reinterpret_cast<const f32x4*>(krow + 4 * k4);
         const f32x4 vq = *reinterpret_cast<const f32x4*>(vrow + 4 * k4);
-        const f32x4 qq = *reinterpret_cast<const f32x4*>(qrow + 4 * k4);
-        const f32x4 oq = *reinterpret_cast<const f32x4*>(orow + 4 * k4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          as = mma_f32(kq[j], qq[j], as);
-          ad = mma_f32(vq[j], oq[j], ad);
+          as = mma_f32(kq[j], qreg[4 * k4 + j], as);
+          ad = mma_f32(vq[j], oreg[4 * k4 + j], ad);
         }
       }
       sT = as;
@@ -311,15 +318,18 @@ __global__ __launch_bounds__(kBwdThreads) void attend_bwd_rows_kernel(BwdParams 
         // 16 g + 15: a lane's dS and P values are contiguous)
         const float* dsrow = &sdS[kt * 16 + col][g * (kBwdHeads / 4)];
         const float* prow = &sP[kt * 16 + col][g * (kBwdHeads / 4)];
-#pragma unroll 2
+        const float* qtrow = &sQt[dim0 + col][g * (kBwdHeads / 4)];
+        const float* otrow = &sdOt[dim0 + col][g * (kBwdHeads / 4)];
+#pragma unroll
         for (int k4 = 0; k4 < kBwdHeads / 16; ++k4) {
           const f32x4 dsv = *reinterpret_cast<const f32x4*>(dsrow + 4 * k4);
           const f32x4 pv4 = *reinterpret_cast<const f32x4*>(prow + 4 * k4);
+          const f32x4 qv = *reinterpret_cast<const f32x4*>(qtrow + 4 * k4);
+          const f32x4 ov = *reinterpret_cast<const f32x4*>(otrow + 4 * k4);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int h = g * (kBwdHeads / 4) + 4 * k4 + j;
-            ak = mma_f32(sQ[h][dim0 + col], dsv[j], ak);
-            av = mma_f32(sdO[h][dim0 + col], pv4[j], av);
+            ak = mma_f32(qv[j], dsv[j], ak);
+            av = mma_f32(ov[j], pv4[j], av);
           }
         }
         // lane (key col, g) holds dims dim0 + 4 g .. + 3 of key kt*16 + col
@@ -335,8 +345,8 @@ __global__ __launch_bounds__(kBwdThreads) void attend_bwd_rows_kernel(BwdParams 
   }
   // dq: the two key tiles' shares of each head, added in a fixed order
   // through the (now free) query buffer
-  static_assert(sizeof(sQ) >= 4 * kDT * 64 * sizeof(f32x4), "dq exchange buffer");
-  f32x4* xq = reinterpret_cast<f32x4*>(&sQ[0][0]);  // [head tile][dim tile][lane]
+  static_assert(sizeof(sQt) >= 4 * kDT * 64 * sizeof(f32x4), "dq exchange buffer");
+  f32x4* xq = reinterpret_cast<f32x4*>(&sQt[0][0]);  // [head tile][dim tile][lane]
   if (kh == 1) {
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt) xq[(ht * kDT + dt) * 64 + lane] = dq[dt];
