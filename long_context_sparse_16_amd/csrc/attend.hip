@@ -448,9 +448,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttParams p) {
 }
 
 // Merge the split partials of one query row: each thread owns 4 output dims
-// of one head.  Splits are taken in batches of MB (16, or 32 for rows of
-// more than 16 splits, so that up to 32 splits cost one round trip to
-// memory rather than two dependent ones): every load of a
+// of one head.  Splits are taken in batches of MB (8, 16 or 32: the
+// smallest that holds a row's splits, so up to 32 splits cost one round
+// trip to memory and few splits issue few redundant loads): every load of a
 // batch (maxima, sums, partial outputs; indices clamped so none is
 // conditional) is issued before any is used, and the batch is folded into a
 // running (max, sum, O) in split order, so the result does not depend on
@@ -585,8 +585,10 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
       attend_kernel<DT, DD, false><<<grid, kAttThreads, 0, stream>>>(p);            \
     if (sp.splits > 16)                                                             \
       attend_merge_kernel<DD, 32><<<mgrid, kMergeThreads, 0, stream>>>(p);          \
-    else if (sp.splits > 1)                                                         \
+    else if (sp.splits > 8)                                                         \
       attend_merge_kernel<DD, 16><<<mgrid, kMergeThreads, 0, stream>>>(p);          \
+    else if (sp.splits > 1)                                                         \
+      attend_merge_kernel<DD, 8><<<mgrid, kMergeThreads, 0, stream>>>(p);           \
     return hipGetLastError() == hipSuccess ? 0 : -1;                                \
   }
   CSA_ATT_CASE(0, 64)
