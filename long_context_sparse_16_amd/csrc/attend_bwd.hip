@@ -61,6 +61,13 @@ constexpr float kLog2eBwd = 1.4426950408889634f;
 constexpr int kBwdHeads = 64;   // head slots (4 tiles of 16)
 constexpr int kBwdThreads = 512;  // row kernel: 8 waves = 4 head tiles x 2 key tiles
 constexpr int kBwdMaxK = 4096;  // longest index list (staged in LDS)
+// A reference (query row within the sequence, list slot) is packed as
+// row << kBwdSlotBits | slot: ascending references are rows in ascending
+// order, and unpacking needs no division.
+constexpr int kBwdSlotBits = 12;
+static_assert((1 << kBwdSlotBits) == kBwdMaxK, "slot field holds every list slot");
+static_assert(kBwdMaxRows << kBwdSlotBits <= (int64_t(1) << 32),
+              "packed references fit 32 bits");
 
 template <int DTYPE>
 __device__ __forceinline__ void load_row_f32(const uint8_t* src, int e0, float* dst, int n);
@@ -477,7 +484,7 @@ __global__ __launch_bounds__(256) void attend_bwd_fill_kernel(BwdParams p) {
     const int32_t e = p.idx[row * p.k + s];
     if (bwd_entry_ok(e, p.n_cap)) {
       const uint32_t at = p.off[b * p.n_cap + e] + atomicAdd(&p.cur[b * p.n_cap + e], 1u);
-      p.lst[at] = static_cast<uint32_t>(rl * p.k + s);
+      p.lst[at] = static_cast<uint32_t>((rl << kBwdSlotBits) | s);
     }
   }
 }
@@ -531,7 +538,7 @@ __global__ __launch_bounds__(256) void attend_bwd_entries_csr_kernel(BwdParams p
 #pragma unroll
     for (int u = 0; u < kBwdSumBatch; ++u) {
       const uint32_t ref = refs[min(r0 + u, n - 1)];
-      const int64_t rl = ref / static_cast<uint32_t>(p.k), slot = ref % static_cast<uint32_t>(p.k);
+      const int64_t rl = ref >> kBwdSlotBits, slot = ref & (kBwdMaxK - 1);
       const int64_t gi = ((b * p.T + rl) * n_slots_row + slot) * D + dim;
       vk[u] = src[gi];
       vv[u] = D == 128 ? 0.f : p.gv[gi];
