@@ -54,7 +54,7 @@ struct FinishShared {
   // 4096-bin first-digit histogram in the row kernel
   uint32_t bitmap[kBitmapMaxEntries / 32 + kBitmapMaxEntries / 1024];
   uint32_t scan[32];
-  uint32_t misc[8];  // [0] bin [1] above [4] selected [5] candidates [6] flag [7] count
+  uint32_t misc[8];  // [0] bin [1] above [2] [3] cut [4] selected [5] candidates [6] flag [7] count
 };
 
 // ------------------------------------------------------------ block helpers
@@ -139,7 +139,46 @@ __device__ Cut resolve_cut(FinishShared& sm, Visit visit_all, uint32_t r) {
   digit_pass<NT>(sm, visit_all, 10, 1024, r);  // key bits 19..10
   const uint32_t b2 = sm.misc[0];
   const uint32_t r2 = r - sm.misc[1];
+  const uint32_t n2 = sm.hist[b2];  // candidates sharing the cut's top 20 key bits
   __syncthreads();
+  if (n2 <= 64) {
+    // Few of them (the usual case): collect them in LDS and let one wave
+    // rank them by (key desc, index asc); the r2-th is the cut.  Three
+    // barriers instead of the further digit passes.
+    uint32_t* ck = sm.hist;        // keys [64]
+    uint32_t* cj = sm.hist + 64;   // indices [64]
+    uint32_t* cn = sm.hist + 128;  // count
+    if (threadIdx.x == 0) *cn = 0u;
+    __syncthreads();
+    visit_all([&](uint32_t key, int32_t j) {
+      if (((key >> 10) & 1023u) == b2) {
+        const uint32_t q = atomicAdd(cn, 1u);
+        ck[q] = key;
+        cj[q] = static_cast<uint32_t>(j);
+      }
+    });
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int l = threadIdx.x;
+      const bool have = static_cast<uint32_t>(l) < n2;
+      const uint32_t lo = have ? (ck[l] & 0xfffffu) : 0u;
+      const int32_t jj = have ? static_cast<int32_t>(cj[l]) : 0x7fffffff;
+      uint32_t rank = 0;  // candidates that come before this one
+      for (uint32_t q = 0; q < n2; ++q) {
+        const uint32_t lo_q = __shfl(lo, static_cast<int>(q));
+        const int32_t j_q = __shfl(jj, static_cast<int>(q));
+        rank += (lo_q > lo || (lo_q == lo && j_q < jj)) ? 1u : 0u;
+      }
+      if (have && rank == r2 - 1u) {
+        sm.misc[2] = lo;
+        sm.misc[3] = static_cast<uint32_t>(jj);
+      }
+    }
+    __syncthreads();
+    const Cut c{sm.misc[2], static_cast<int32_t>(sm.misc[3])};
+    __syncthreads();
+    return c;
+  }
   auto visit_b2 = [&](auto f) {
     visit_all([&](uint32_t key, int32_t j) {
       if (((key >> 10) & 1023u) == b2) f(key, j);

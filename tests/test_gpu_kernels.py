@@ -342,6 +342,23 @@ def test_topk_edge_rows():
     assert np.array_equal(got[0, 0], np.r_[np.arange(15), 5000])
 
 
+@pytest.mark.parametrize("n_cap,T", [(70000, 2), (9000, 3), (3000, 300)])
+def test_topk_cut_inside_small_tie_group(n_cap, T):
+    """The k-th largest score shared by a handful of entries (fewer than 64
+    share its top 20 key bits, the case the cut search ranks in one wave):
+    the lowest indices among them win, on every top-k path."""
+    say("topk small tie group at the cut", n_cap, T)
+    rng = np.random.default_rng(502 + T)
+    k = 100
+    s = (rng.standard_normal((1, T, n_cap)) * 30 + 140).astype(np.float32)
+    for i in range(T):
+        order = np.argsort(-s[0, i], kind="stable")
+        group = order[k - 4:k + 6]                 # ranks 97 .. 106 -> one value
+        s[0, i, group] = s[0, i, order[k - 1]]
+    V = n_cap - T + 1 + np.arange(T, dtype=np.int64)[None]   # the last row sees all
+    _topk_case(s, V, k)
+
+
 def test_topk_split_lists_past_prefetch():
     """Split path: the finishing kernel prefetches a prefix of every slice's
     list; here one slice holds almost all the selected entries, so its list
