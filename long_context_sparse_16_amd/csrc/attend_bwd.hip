@@ -47,9 +47,12 @@ struct BwdParams {
   float* dvr;
   // CSA: the query-row references of every entry, by counting sort
   uint32_t* cnt;   // [B][n_cap] references per entry (zero on entry)
-  uint32_t* cur;   // [B][n_cap] fill cursors (zero on entry)
   uint32_t* off;   // [B][n_cap] first reference of each entry in lst
-  uint32_t* lst;   // [B][T * k] references, row * k + slot, grouped by entry
+  uint32_t* lst;   // [B][T * k] packed references, grouped by entry
+  // [B * T][k] arrival rank of each reference within its entry's count;
+  // lives in the (not yet written) gk staging area: the counting sort runs
+  // before the row kernel
+  uint32_t* rank;
   int64_t T, H, n_cap, R;
   int k, W, m;
   int n_ent_max;  // entry slots per staging row: k (CSA) or n_cap (HCA)
@@ -447,7 +450,7 @@ __global__ __launch_bounds__(256) void attend_bwd_count_kernel(BwdParams p) {
   const int64_t b = row / p.T;
   for (int s = threadIdx.x; s < p.k; s += 256) {
     const int32_t e = p.idx[row * p.k + s];
-    if (bwd_entry_ok(e, p.n_cap)) atomicAdd(&p.cnt[b * p.n_cap + e], 1u);
+    if (bwd_entry_ok(e, p.n_cap)) p.rank[row * p.k + s] = atomicAdd(&p.cnt[b * p.n_cap + e], 1u);
   }
 }
 
@@ -474,8 +477,9 @@ __global__ __launch_bounds__(256) void attend_bwd_scan_kernel(BwdParams p) {
   for (int64_t j = j0; j < j1; ++j) { o[j] = a; a += c[j]; }
 }
 
-// lst[off[j] + i] = row * k + slot for the i-th reference to entry j (in
-// arrival order; the reduction sorts each entry's references).
+// lst[off[j] + i] = the packed (row, slot) of the reference to entry j that
+// arrived i-th in the count kernel (its rank, so no atomics here; the
+// reduction sorts each entry's references).
 __global__ __launch_bounds__(256) void attend_bwd_fill_kernel(BwdParams p) {
   const int64_t row = blockIdx.x;
   const int64_t b = row / p.T;
@@ -483,7 +487,7 @@ __global__ __launch_bounds__(256) void attend_bwd_fill_kernel(BwdParams p) {
   for (int s = threadIdx.x; s < p.k; s += 256) {
     const int32_t e = p.idx[row * p.k + s];
     if (bwd_entry_ok(e, p.n_cap)) {
-      const uint32_t at = p.off[b * p.n_cap + e] + atomicAdd(&p.cur[b * p.n_cap + e], 1u);
+      const uint32_t at = p.off[b * p.n_cap + e] + p.rank[row * p.k + s];
       p.lst[at] = static_cast<uint32_t>((rl << kBwdSlotBits) | s);
     }
   }
@@ -601,12 +605,12 @@ __global__ __launch_bounds__(256) void attend_bwd_raw_kernel(BwdParams p) {
 static size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 // Workspace: the key / value contributions [B*T][n_ent_max + W][D] fp32,
-// then (CSA) cnt, cur, off [B][n_cap] and the reference list [B*T*k].
+// then (CSA) cnt, off [B][n_cap] and the reference list [B*T*k].
 size_t attend_bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int64_t n_ent_max, int W,
                                   int64_t n_cap, bool csa) {
   size_t bytes = align256(static_cast<size_t>(B * T) * (n_ent_max + W) * D * sizeof(float) * 2);
   if (csa)
-    bytes += 3 * align256(static_cast<size_t>(B * n_cap) * 4) +
+    bytes += 2 * align256(static_cast<size_t>(B * n_cap) * 4) +
              align256(static_cast<size_t>(B * T) * n_ent_max * 4);
   return bytes;
 }
@@ -649,28 +653,29 @@ int launch_attend_bwd(const void* q, int dtype, const void* kc, const void* vc,
   float* base = static_cast<float*>(ws);
   p.gk = base;
   p.gv = base + rows * (p.n_ent_max + W) * D;
-  p.cnt = p.cur = p.off = p.lst = nullptr;
+  p.cnt = p.off = p.lst = p.rank = nullptr;
   if (!hca) {
     char* c = static_cast<char*>(ws) +
               align256(static_cast<size_t>(rows) * (p.n_ent_max + W) * D * sizeof(float) * 2);
     const size_t nb = align256(static_cast<size_t>(B * n_cap) * 4);
     p.cnt = reinterpret_cast<uint32_t*>(c);
-    p.cur = reinterpret_cast<uint32_t*>(c + nb);
-    p.off = reinterpret_cast<uint32_t*>(c + 2 * nb);
-    p.lst = reinterpret_cast<uint32_t*>(c + 3 * nb);
-    // cnt and cur are adjacent: one zero-fill
-    if (launch_clear(p.cnt, 2 * nb, stream)) return -1;
+    p.off = reinterpret_cast<uint32_t*>(c + nb);
+    p.lst = reinterpret_cast<uint32_t*>(c + 2 * nb);
+    p.rank = reinterpret_cast<uint32_t*>(p.gk);  // rows * k words <= the gk area
+    if (launch_clear(p.cnt, nb, stream)) return -1;
   }
 #define CSA_BWD_CASE(DT, DD)                                                                  \
   if (dtype == DT && D == DD) {                                                               \
-    if (hca) attend_bwd_rows_kernel<DT, DD, true><<<dim3(rows), kBwdThreads, 0, stream>>>(p);  \
-    else attend_bwd_rows_kernel<DT, DD, false><<<dim3(rows), kBwdThreads, 0, stream>>>(p);     \
     if (hca) {                                                                                \
+      attend_bwd_rows_kernel<DT, DD, true><<<dim3(rows), kBwdThreads, 0, stream>>>(p);         \
       attend_bwd_entries_kernel<DD, true><<<dim3(n_cap, B), 256, 0, stream>>>(p);              \
     } else {                                                                                  \
+      /* the counting sort needs only the index lists; its ranks use the */                   \
+      /* staging area before the row kernel fills it */                                       \
       attend_bwd_count_kernel<<<dim3(rows), 256, 0, stream>>>(p);                              \
       attend_bwd_scan_kernel<<<dim3(B), 256, 0, stream>>>(p);                                  \
       attend_bwd_fill_kernel<<<dim3(rows), 256, 0, stream>>>(p);                               \
+      attend_bwd_rows_kernel<DT, DD, false><<<dim3(rows), kBwdThreads, 0, stream>>>(p);        \
       attend_bwd_entries_csr_kernel<DD, kBwdSmallRefs, false>                                  \
           <<<dim3(n_cap, B), 256, 0, stream>>>(p);                                             \
       attend_bwd_entries_csr_kernel<DD, kBwdMaxRefs, true>                                     \
