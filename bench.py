@@ -5,8 +5,16 @@ blocks the step completes (none at the decode positions used here), the
 Lightning Indexer, top-k and attention over the selected entries plus the
 window.  The default workload is CSA decode at a 131072-token context:
 batch 32, bf16 compressed KV (32768 entries, d=128), indexer 64 x 128,
-top-k 1024, 64 query heads, window 128.  Inputs are seeded synthetic data
+top-k 1024, 64 query heads, window 128.  The 1M-token decode workloads (CSA
+with fp8 indexer keys, batch 4; HCA at m' = 128, batch 16) are timed in the
+same run and reported under "workloads".  Inputs are seeded synthetic data
 already resident in HBM when the timed region starts.
+
+Timing is cold-cache: before every timed step (and every per-stage sample) a
+1 GiB buffer is copied into another (1 GiB read + 1 GiB written, outside the
+events), which evicts the 256 MB Infinity Cache and the L2s; each step is
+bracketed by its own pair of HIP events on the launch stream, and the median
+(p10, p90) is reported.  Back-to-back warm steps are reported as context.
 
 Prints one JSON line.  Only one GPU is supported.
 """
@@ -14,6 +22,7 @@ Prints one JSON line.  Only one GPU is supported.
 from __future__ import annotations
 
 import argparse
+import glob
 import json
 import os
 import sys
@@ -24,6 +33,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 10100.0, "f32": 157.3}
+FLUSH_BYTES = 1 << 30
+DEFAULT_WORKLOAD = "csa_decode_128k_bf16"
+# timed in the same run as the default workload (the 1M-token half of the metric)
+EXTRA_WORKLOADS = ("csa_decode_1m_fp8", "hca_decode_1m_bf16")
 
 
 def parse():
@@ -31,11 +44,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="csa_decode_128k_bf16")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only --workload (not the 1M-token decode workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true",
-                    help="replay one HIP graph per step instead of launching each stage "
-                         "directly (slower here: each graph replay adds ~13 us)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -43,9 +55,10 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode_128k_traffic.md")
-INDEXER_SOURCES = [os.path.join(ROOT, "long_context_sparse_16_amd", "csrc", f)
-                   for f in ("indexer.hip", "common.h", "kernels.h")]
+# ------------------------------------------------------------ HBM counters
+
+CSRC = os.path.join(ROOT, "long_context_sparse_16_amd", "csrc")
+TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "*_traffic.md")
 
 
 def source_digest(paths) -> str:
@@ -57,23 +70,42 @@ def source_digest(paths) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(cfg):
-    """HBM bytes per indexer launch from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by the same
-    counter's reading for a plain copy of known size), or None when the
-    summary is for another workload or for a different indexer source."""
-    t = {}
-    try:
-        with open(TRAFFIC_FILE) as f:
+def kernel_sources(kernel: str) -> list:
+    """The source files a kernel's machine code depends on."""
+    main = {"indexer_kernel": "indexer.hip", "indexer_prefill_kernel": "indexer.hip",
+            "attend_kernel": "attend.hip", "attend_merge_kernel": "attend.hip",
+            "attend_select_kernel": "attend.hip",
+            "topk_classify_kernel": "topk.hip", "topk_finish_kernel": "topk.hip",
+            "topk_row_kernel": "topk.hip"}[kernel]
+    return [os.path.join(CSRC, f) for f in (main, "common.h", "kernels.h")]
+
+
+def traffic_summaries() -> list:
+    """The key/value block of every committed counter summary."""
+    out = []
+    for path in sorted(glob.glob(TRAFFIC_GLOB)):
+        t = {"file": os.path.basename(path)}
+        with open(path) as f:
             for line in f:
                 if line.startswith("- ") and ": " in line:
                     key, val = line[2:].strip().split(": ", 1)
                     t[key] = val
-    except OSError:
-        return None
-    if t.get("workload") != cfg.name or t.get("source_sha256") != source_digest(INDEXER_SOURCES):
-        return None
-    return float(t["traffic_bytes_per_launch"])
+        out.append(t)
+    return out
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` in `workload` from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE per dispatch, each
+    scaled by the same counter's reading for a plain copy of known size), or
+    None when there is none or the kernel's sources changed since."""
+    for t in traffic_summaries():
+        if t.get("workload") != workload or t.get("kernel") != kernel:
+            continue
+        if t.get("source_sha256") != source_digest(kernel_sources(kernel)):
+            return None
+        return float(t["traffic_bytes_per_launch"])
+    return None
 
 
 def copy_calibration():
@@ -90,24 +122,53 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
 
 
+# ------------------------------------------------------- algorithmic work
+
+def visible(cfg, t: int) -> int:
+    return max(0, min(cfg.n_cap, (t + 1) // cfg.m))
+
+
 def visible_sum(cfg) -> int:
     """Sum over the step's queries of the causally visible entries V(t)."""
-    return sum(min(cfg.n_cap, (cfg.pos0 + i + 1) // cfg.m) for i in range(cfg.T))
+    return sum(visible(cfg, cfg.pos0 + i) for i in range(cfg.T))
 
 
-def indexer_bytes(cfg, V: int) -> int:
-    """Algorithmic HBM bytes of one indexer launch: every visible key (and
-    its fp8 scale or MXFP4 block scales) read once per sequence, one fp32
-    score written per (query, visible entry), the queries (with their
-    scales) and head weights read once."""
+def ki_row_bytes(cfg) -> int:
+    """Bytes of one indexer key row with its scales."""
     if cfg.ki_mxfp4:
-        row = cfg.d_I // 2 + cfg.d_I // 32          # E2M1 codes + E8M0 scales
-    elif cfg.ki_fp8:
-        row = cfg.d_I + 4                           # E4M3 codes + fp32 scale
-    else:
-        row = cfg.d_I * (2 if cfg.storage == "bf16" else 4)
-    q_bytes = cfg.T * cfg.H_I * (row + 4)
-    return cfg.B * (V * row + 4 * visible_sum(cfg) + q_bytes)
+        return cfg.d_I // 2 + cfg.d_I // 32          # E2M1 codes + E8M0 scales
+    if cfg.ki_fp8:
+        return cfg.d_I + 4                           # E4M3 codes + fp32 scale
+    return cfg.d_I * (2 if cfg.storage == "bf16" else 4)
+
+
+def indexer_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one indexer launch: every visible key (and
+    its scales) read once per sequence, one fp32 score written per (query,
+    visible entry), the queries (with their scales) and head weights read
+    once."""
+    V = visible(cfg, cfg.pos0 + cfg.T - 1)
+    q_bytes = cfg.T * cfg.H_I * (ki_row_bytes(cfg) + 4)
+    return cfg.B * (V * ki_row_bytes(cfg) + 4 * visible_sum(cfg) + q_bytes)
+
+
+def step_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one decode step: the indexer's key scan
+    (with scales), the K/V rows each query attends (its top-k entries, or
+    every visible entry for HCA, plus its window rows), the queries, head
+    weights and the fp32 outputs.  The indexer's score round trip is not
+    counted (it is the implementation's, not the method's)."""
+    eb = 2 if cfg.storage == "bf16" else 4
+    tot = 0
+    for i in range(cfg.T):
+        t = cfg.pos0 + i
+        V = visible(cfg, t)
+        keys = (V if cfg.hca else min(cfg.k, V)) + min(cfg.W, t + 1)
+        q = cfg.H * cfg.d * eb + cfg.H * cfg.d * 4
+        if cfg.k > 0:
+            q += V * ki_row_bytes(cfg) + cfg.H_I * (ki_row_bytes(cfg) + 4)
+        tot += keys * 2 * cfg.d * eb + q
+    return cfg.B * tot
 
 
 def index_dtype(cfg) -> str:
@@ -127,22 +188,33 @@ def backward_flops(cfg) -> int:
     tot = 0
     for i in range(cfg.T):
         t = cfg.pos0 + i
-        V = min(cfg.n_cap, (t + 1) // cfg.m)
-        tot += min(cfg.k, V) + min(cfg.W, t + 1)
+        tot += min(cfg.k, visible(cfg, t)) + min(cfg.W, t + 1)
     return 10 * cfg.d * cfg.H * cfg.B * tot
 
 
-def hca_bytes(cfg, V: int) -> int:
+def hca_bytes(cfg) -> int:
     """Algorithmic HBM bytes of one HCA attention launch: every visible K/V
     entry and window row once, queries in, fp32 outputs out."""
-    eb = 2 if cfg.storage == "bf16" else 4
-    return cfg.B * ((V + cfg.W) * 2 * cfg.d * eb + cfg.T * cfg.H * cfg.d * (eb + 4))
+    return step_bytes(cfg)
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(cfg, budget_s: float):
     """The fp64 oracle on the host cores over a bounded sample of sequences."""
     import numpy as np
-    import oracle
     import workloads as WL
     try:
         from threadpoolctl import threadpool_info
@@ -151,6 +223,7 @@ def cpu_baseline(cfg, budget_s: float):
         threads = len(os.sched_getaffinity(0))
     done, t_total = 0, 0.0
     layer_cfgs = WL.layer_workloads(cfg) if cfg.layers else [cfg]
+    base = {"unit": "queries/s", "cores": int(threads), "cpu_model": cpu_model(), "kind": "oracle"}
     if cfg.T >= 8:
         # prefill-shaped: a sample of query rows (i = 31 mod 32) of the first
         # sequence, grown while the budget lasts
@@ -164,7 +237,7 @@ def cpu_baseline(cfg, budget_s: float):
             if dt * 2 > budget_s or n >= sample.size:
                 break
             n = min(sample.size, n * 2)
-        return {"value": n / dt, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+        return {"value": n / dt, **base,
                 "sample": f"{n} query rows (i = 31 mod 32) of sequence 0 of {cfg.name}, fp64 "
                           f"NumPy, {dt:.1f} s"}
     # the batch's sequences in turn (again from the first once all are
@@ -180,7 +253,7 @@ def cpu_baseline(cfg, budget_s: float):
         if t_total >= budget_s:
             break
     q = done * cfg.T
-    return {"value": q / t_total, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+    return {"value": q / t_total, **base,
             "sample": f"{done} sequence steps ({q} queries; the batch's {cfg.B} sequences in "
                       f"turn) of {cfg.name}, fp64 NumPy, {t_total:.1f} s"}
 
@@ -240,6 +313,197 @@ def _oracle_sequence(cfg, s, rows=None):
                                              dc[cfg.n_ctx_entries:cfg.n_cap])
 
 
+# ------------------------------------------------------------------ timing
+
+class Timer:
+    """Cold-cache event timing on one stream.  flush() (outside the events)
+    overwrites a 1 GiB buffer with a copy of another and then reads the
+    source back: afterwards no input of the timed work is left in the 256 MB
+    Infinity Cache or the L2s, and the dirty lines the overwrite left in the
+    Infinity Cache have been written back.  (Without the read-back, that
+    write-back -- up to 256 MB -- lands inside the next timed kernel: a
+    268 MB streaming read measured 49 us after copy + read, 78 us after the
+    copy alone, 104 us after a 1 GiB fill, 43 us warm.)"""
+
+    def __init__(self, torch, stream):
+        self.torch = torch
+        self.stream = stream
+        self.src = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda:0").fill_(1)
+        self.dst = torch.empty_like(self.src)
+        self.sink = torch.empty((), dtype=torch.int64, device="cuda:0")
+
+    def flush(self):
+        self.dst.copy_(self.src)
+        self.torch.sum(self.src, dim=(0,), dtype=self.torch.int64, out=self.sink)
+
+    def samples(self, fn, n, cold=True, pre=None, post=None):
+        """Durations (us) of n calls of fn, each between its own events;
+        pre() / post() run outside the events."""
+        torch = self.torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a, b in evs:
+            if cold:
+                self.flush()
+            if pre:
+                pre()
+            a.record(self.stream)
+            fn()
+            b.record(self.stream)
+            if post:
+                post()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 for a, b in evs]
+
+    def staged(self, stages, n, cold=True):
+        """Per-stage durations (us) of n cold passes over `stages` (a list of
+        (name, fn)), with one event between consecutive stages."""
+        torch = self.torch
+        runs = []
+        for _ in range(n):
+            if cold:
+                self.flush()
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+            evs[0].record(self.stream)
+            for i, (_, fn) in enumerate(stages):
+                fn()
+                evs[i + 1].record(self.stream)
+            runs.append(evs)
+        torch.cuda.synchronize()
+        return {name: [evs[i].elapsed_time(evs[i + 1]) * 1e3 for evs in runs]
+                for i, (name, _) in enumerate(stages)}
+
+
+def stats(xs) -> dict:
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "mean": float(a.mean())}
+
+
+def attainable_bandwidth(torch, timer) -> dict:
+    """HBM bandwidth a plain device copy and a plain read (sum) of 1 GiB
+    reach (GB/s, median of 10 cold runs): the practical ceiling beside the
+    nominal 8 TB/s."""
+    n = FLUSH_BYTES
+    a = torch.empty(n // 4, dtype=torch.int32, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    out = torch.empty((), dtype=torch.int64, device="cuda:0")
+    cp = stats(timer.samples(lambda: b.copy_(a), 10))["median"]
+    rd = stats(timer.samples(lambda: torch.sum(a, dim=(0,), dtype=torch.int64, out=out),
+                             10))["median"]
+    del a, b
+    return {"copy_gbs": 2 * n / (cp * 1e3), "read_gbs": n / (rd * 1e3)}
+
+
+# -------------------------------------------------------------- workloads
+
+def make_step(cfg):
+    """The step object, the function that runs one step, and the stages of a
+    step as (name, fn) for per-stage timing."""
+    import numpy as np
+    import torch
+    import workloads as WL
+    from long_context_sparse_16_amd.pipeline import CSAStep, HybridStep
+    if cfg.layers:
+        layer_cfgs = WL.layer_workloads(cfg)
+        h = HybridStep(layer_cfgs, [WL.make_batch(c) for c in layer_cfgs])
+        stages = [(f"layer{i}_{k}", lay.run) for i, (k, lay) in enumerate(zip(cfg.layers, h.layers))]
+        return h, h.run, stages
+    batch = WL.make_batch(cfg)
+    step = CSAStep(cfg, batch)
+    del batch
+    if cfg.backward:
+        # the forward once (its outputs, lse and indices feed the backward),
+        # then a seeded upstream gradient N(0, 1)
+        step.run()
+        g_rng = np.random.Generator(np.random.PCG64(cfg.seed))
+        step.dout = torch.from_numpy(g_rng.standard_normal((cfg.B, cfg.T, cfg.H, cfg.d),
+                                                           dtype=np.float32)).to("cuda:0")
+        fn = lambda: step.backward(step.dout)  # noqa: E731
+        return step, fn, [("backward", fn)]
+    return step, step.run, step.stages()
+
+
+def measure(cfg, K, W, timer, torch):
+    """Cold and warm step times, per-stage times and the roofline of one
+    workload."""
+    obj, run, stages = make_step(cfg)
+    for _ in range(W):
+        timer.flush()
+        run()
+    torch.cuda.synchronize()
+    cold = timer.samples(run, K)
+    warm = timer.samples(run, max(10, K // 2), cold=False)
+    st = timer.staged(stages, max(10, K // 2))
+    st_stats = {k: stats(v) for k, v in st.items()}
+    res = {"step_us": {**stats(cold), "warm_median": stats(warm)["median"]},
+           "stage_us": {k: round(v["median"], 2) for k, v in st_stats.items()}}
+    med = res["step_us"]["median"]
+    res["queries_per_s"] = cfg.B * cfg.T / (med * 1e-6)
+    n_indexed = (sum(1 for k in cfg.layers if k == "csa") if cfg.layers else 1) if cfg.k > 0 else 0
+    if n_indexed and not cfg.backward:
+        res["entries_scored_per_s"] = n_indexed * cfg.B * visible_sum(cfg) / (med * 1e-6)
+    # roofline of the dominant kernel (mean of its event-timed cold launches,
+    # which is what a rocprofv3 kernel trace of this run averages)
+    if cfg.backward:
+        fl = backward_flops(cfg)
+        t_us = st_stats["backward"]["mean"]
+        roof = {"kernel": "attend_bwd (rows + reductions)", "bound": "mfma",
+                "achieved": fl / (t_us * 1e6), "peak": MFMA_PEAK_TFLOPS["f32"],
+                "unit": "TFLOP/s", "traffic": None, "algorithmic_flops": fl}
+    elif cfg.layers:
+        i = next(i for i, k in enumerate(cfg.layers) if k == "csa")
+        lay = WL_layer(cfg, i)
+        roof = {"kernel": f"layer {i} (csa) step", "bound": "hbm", "unit": "GB/s",
+                "achieved": step_bytes(lay) / (st_stats[f"layer{i}_csa"]["mean"] * 1e3),
+                "peak": HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": step_bytes(lay)}
+    elif cfg.hca:
+        kb = hca_bytes(cfg)
+        roof = {"kernel": "attend_kernel (HCA) + merge", "bound": "hbm",
+                "achieved": kb / (st_stats["attend"]["mean"] * 1e3), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "traffic": measured_traffic(cfg.name, "attend_kernel"),
+                "algorithmic_bytes": kb}
+    elif cfg.T >= 8:
+        fl = indexer_flops(cfg)
+        roof = {"kernel": "indexer_prefill_kernel", "bound": "mfma",
+                "achieved": fl / (st_stats["index"]["mean"] * 1e6),
+                "peak": MFMA_PEAK_TFLOPS[index_dtype(cfg)], "unit": "TFLOP/s",
+                "traffic": None, "algorithmic_flops": fl}
+    else:
+        ib = indexer_bytes(cfg)
+        stage = "index" if "index" in st_stats else "select"
+        roof = {"kernel": "indexer_kernel", "bound": "hbm",
+                "achieved": ib / (st_stats[stage]["mean"] * 1e3), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "traffic": measured_traffic(cfg.name, "indexer_kernel"),
+                "algorithmic_bytes": ib}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    if cfg.T == 1 and not cfg.backward:
+        sb = step_bytes(cfg) if not cfg.layers else sum(
+            step_bytes(WL_layer(cfg, i)) for i in range(len(cfg.layers)))
+        roof["step_bytes"] = sb
+        roof["step_gbs"] = sb / (med * 1e3)
+        roof["step_frac"] = roof["step_gbs"] / HBM_PEAK_GBS
+    res["roofline"] = roof
+    del obj, run, stages
+    return res
+
+
+def WL_layer(cfg, i):
+    import workloads as WL
+    return WL.layer_workloads(cfg)[i]
+
+
+def config_of(cfg) -> dict:
+    V = visible(cfg, cfg.pos0 + cfg.T - 1)
+    return {"workload": cfg.name, "batch": cfg.B, "query_tokens": cfg.T,
+            "context_tokens": cfg.pos0, "compressed_entries": V, "m": cfg.m,
+            "indexer": f"{cfg.H_I}x{cfg.d_I}" if cfg.k else None,
+            "indexer_dtype": index_dtype(cfg) if cfg.k else None,
+            "top_k": cfg.k, "heads": cfg.H, "head_dim": cfg.d, "window": cfg.W,
+            **({"layers": list(cfg.layers)} if cfg.layers else {})}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -249,187 +513,53 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    import numpy as np
     import torch
 
     import workloads as WL
-    if not os.path.exists(os.path.join(ROOT, "long_context_sparse_16_amd", "libcsa.so")):
-        import __graft_entry__
-        __graft_entry__._build_module().build()
-    from long_context_sparse_16_amd.pipeline import CSAStep
-
+    import __graft_entry__
+    __graft_entry__._build_module().ensure_current()
     cfg = WL.BY_NAME[args.workload]
-    if cfg.layers:
-        # hybrid stack: every layer runs in the step; the stage timings and
-        # the roofline are those of its first CSA layer
-        from long_context_sparse_16_amd.pipeline import HybridStep
-        layer_cfgs = WL.layer_workloads(cfg)
-        hstep = HybridStep(layer_cfgs, [WL.make_batch(c) for c in layer_cfgs])
-        run_once = hstep.run
-        first_csa = next(i for i, c in enumerate(layer_cfgs) if c.k > 0)
-        step, rcfg = hstep.layers[first_csa], layer_cfgs[first_csa]
-    else:
-        batch = WL.make_batch(cfg)
-        step = CSAStep(cfg, batch)
-        del batch
-        run_once, rcfg = step.run, cfg
-        if cfg.backward:
-            # the forward once (its outputs, lse and indices feed the
-            # backward), then a seeded upstream gradient N(0, 1)
-            step.run()
-            g_rng = np.random.Generator(np.random.PCG64(cfg.seed))
-            dout = torch.from_numpy(g_rng.standard_normal((cfg.B, cfg.T, cfg.H, cfg.d),
-                                                          dtype=np.float32)).to("cuda:0")
-
-            def run_once():
-                step.backward(dout)
-    for _ in range(args.warmup):
-        run_once()
-    torch.cuda.synchronize()
-
-    # The timed step launches each stage directly on the current stream
-    # (--graph: one HIP graph per step instead).  Each stage is also timed on
-    # its own with events over back-to-back calls; the dominant kernel's
-    # duration for the roofline comes from those.
     stream = torch.cuda.current_stream()
-    if not args.graph:
-        run_step = run_once
-    else:
-        g_step = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_step):
-            run_once()
-        run_step = g_step.replay
-        for _ in range(args.warmup):
-            run_step()
-    torch.cuda.synchronize()
+    timer = Timer(torch, stream)
+    attain = attainable_bandwidth(torch, timer)
 
     K = args.steps
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(K):
-        run_step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    main_res = measure(cfg, K, args.warmup, timer, torch)
     wall = time.perf_counter() - t0
-    step_event_ms = ev0.elapsed_time(ev1) / K
+    torch.cuda.empty_cache()
+    extra = {}
+    if not args.no_extra and cfg.name == DEFAULT_WORKLOAD:
+        for name in EXTRA_WORKLOADS:
+            ec = WL.BY_NAME[name]
+            r = measure(ec, K, args.warmup, timer, torch)
+            extra[name] = {"config": config_of(ec), **r}
+            torch.cuda.empty_cache()
 
-    # per-stage timing: R back-to-back calls of one stage (--graph: one graph
-    # holding them).
-    # The indexer also accumulates the top-k histogram into the top-k
-    # workspace, which only the following top-k call consumes: the index
-    # stage is timed alone and the workspace cleared afterwards, and top-k
-    # is timed as (index + top-k) minus index.
-    import long_context_sparse_16_amd as csa_lib
-
-    def timed(fn, R=20, reps=3):
-        """Per-call time of fn: one graph holding R calls back to back,
-        replayed `reps` times between events (default: R*reps direct calls)."""
-        if not args.graph:
-            def rep():
-                for _ in range(R):
-                    fn()
-        else:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for _ in range(R):
-                    fn()
-            rep = g.replay
-        rep()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            rep()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / (R * reps)
-
-    st = {}
-    if cfg.layers:
-        for i, lay in enumerate(hstep.layers):
-            st[f"layer{i}_{cfg.layers[i]}"] = timed(lay.run)
-    cfg_all, cfg = cfg, rcfg  # stage timings and roofline: the (first CSA) layer
-    if cfg.backward:
-        csa_lib_ = __import__("long_context_sparse_16_amd")
-        st["attend_backward"] = timed(lambda: csa_lib_.csa_attend_backward(
-            step.q, step.kc, step.vc, step.idx, step.kr, step.vr, step.raw_pos0, step.pos0,
-            cfg.W, cfg.scale, step.out, step.lse, dout, ws=step.bwd_ws), R=5, reps=2)
-        st["backward_step"] = step_event_ms
-    elif cfg.n_new_tokens:
-        st["compress"] = timed(step.compress)
-    if cfg.k > 0 and not cfg.backward:
-        st["index"] = timed(step.index)
-        csa_lib.csa_workspace_clear(step.topk_ws)
-
-        def index_topk():
-            step.index()
-            step.topk()
-        st["topk"] = timed(index_topk) - st["index"]
-    if not cfg.backward:
-        st["attend"] = timed(step.attend)
-    if cfg.block_end:
-        # the fused selection (block compression inside the indexer launch,
-        # then top-k) against the same step with separate compress launches
-        st["select_fused"] = timed(step.select)
-        st["compress_unfused"] = timed(step.compress)
-        st["step_unfused"] = timed(step.run_unfused)
-    st["step_events"] = step_event_ms
-    cfg = cfg_all
-
-    queries = cfg.B * cfg.T
-    n_indexed = ((sum(1 for k in cfg.layers if k == "csa") if cfg.layers else 1)
-                 if cfg.k > 0 and not cfg.backward else 0)
-    V = int(min(cfg.n_cap, (cfg.pos0 + cfg.T) // cfg.m))
-    ms_per_step = wall * 1e3 / K
-    value = queries * K / wall
-    if cfg.backward:
-        # the attention backward's products (S, dP, dq, dK, dV: 10 d FLOP per
-        # query row, key and head) on the fp32 MFMA, against the whole call
-        # (row kernel + the two deterministic reductions)
-        fl = backward_flops(cfg)
-        roof = {"kernel": "attend_bwd (rows + reductions)", "bound": "mfma",
-                "achieved": fl / (st["attend_backward"] * 1e9), "peak": MFMA_PEAK_TFLOPS["f32"],
-                "unit": "TFLOP/s", "traffic": None, "algorithmic_flops": fl}
-    elif cfg.hca:
-        kb = hca_bytes(cfg, V)
-        roof = {"kernel": "attend_kernel (HCA)", "bound": "hbm", "achieved": kb / (st["attend"] * 1e6),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None}
-    elif cfg.T >= 8:
-        # prefill: the indexer is one MFMA score GEMM per sequence
-        fl = indexer_flops(cfg)
-        dt = index_dtype(cfg)
-        roof = {"kernel": "indexer_prefill_kernel", "bound": "mfma",
-                "achieved": fl / (st["index"] * 1e9), "peak": MFMA_PEAK_TFLOPS[dt],
-                "unit": "TFLOP/s", "traffic": None, "algorithmic_flops": fl}
-    else:
-        ib = indexer_bytes(cfg, V)
-        roof = {"kernel": "indexer_kernel", "bound": "hbm", "achieved": ib / (st["index"] * 1e6),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": measured_traffic(cfg),
-                "algorithmic_bytes": ib}
-    roof["frac"] = roof["achieved"] / roof["peak"]
+    med_ms = main_res["step_us"]["median"] * 1e-3
+    roof = main_res.pop("roofline")
+    roof["attainable"] = attain
     line = {
         "metric": "CSA decode queries/s + indexer entries scored/s at 128K/1M ctx; % HBM/MFMA peak",
-        "value": value,
+        "value": main_res.pop("queries_per_s"),
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": med_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32" if cfg.backward else index_dtype(cfg),
         "data": "synthetic (seeded N(0,1) K/V/q, U(0,1) head weights, planted entries)",
-        "config": {"workload": cfg.name, "batch": cfg.B, "context_tokens": cfg.pos0,
-                   "compressed_entries": V, "m": cfg.m, "indexer": f"{cfg.H_I}x{cfg.d_I}",
-                   "top_k": cfg.k, "heads": cfg.H, "head_dim": cfg.d, "window": cfg.W,
-                   **({"layers": list(cfg.layers)} if cfg.layers else {})},
-        "entries_scored_per_s": (n_indexed * cfg.B * visible_sum(cfg) * K / wall) if n_indexed else None,
-        "stage_ms": st,
-        "launch": "hip_graph_per_step" if args.graph else "direct",
+        "config": config_of(cfg),
+        "timing": "cold cache: a 1 GiB device copy before every timed step, outside the events; "
+                  "one event pair per step on the launch stream; value = queries / median step",
+        **main_res,
+        "timed_region_s": wall,
         "roofline": roof,
+        "workloads": extra,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)

@@ -85,6 +85,9 @@ const char* csa_status_string(int status);
 const char* csa_last_error(void);
 /* ABI version of this library (incremented on incompatible changes). */
 int csa_abi_version(void);
+/* sha256 (64 hex digits) of the sources, headers and flags the library was
+ * built from; callers compare it with the tree to refuse a stale build. */
+const char* csa_build_digest(void);
 
 /* Zero `ws_bytes` bytes of a device workspace on `stream` (a kernel, so it
  * may be captured in a HIP graph).  ws 16-byte aligned, ws_bytes % 4 == 0. */

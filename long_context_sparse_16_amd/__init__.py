@@ -47,6 +47,7 @@ _SIGNATURES = {
     "csa_status_string": (ctypes.c_char_p, [_i]),
     "csa_last_error": (ctypes.c_char_p, []),
     "csa_abi_version": (_i, []),
+    "csa_build_digest": (ctypes.c_char_p, []),
     "csa_workspace_clear": (_i, [_vp, _sz, _vp]),
     "csa_compress": (_i, [_vp, _i, _vp, _i64, _i64, _i64, _i, _i64, _i64, _vp, _i, _i64, _i64, _vp]),
     "csa_quantize_fp8_rows": (_i, [_vp, _i, _i64, _i64, _vp, _vp, _vp]),
@@ -82,6 +83,20 @@ for _name, (_res, _args) in _SIGNATURES.items():
     _fn = getattr(_lib, _name)
     _fn.restype = _res
     _fn.argtypes = _args
+
+
+def _source_digest() -> str:
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_csa_build", os.path.join(_HERE, "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.source_digest()
+
+
+if _lib.csa_build_digest().decode() != _source_digest():
+    raise ImportError(
+        f"{LIB_PATH} was built from other sources than the ones in this tree: rebuild it "
+        "(python -m long_context_sparse_16_amd.build)")
 
 
 def header_functions() -> list:

@@ -30,6 +30,8 @@ SOURCE_FLAGS = {
     "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 HEADERS = ["common.h", "kernels.h"]
+PUBLIC_HEADER = os.path.join(ROOT, "include", "csa.h")
+DIGEST_TAG = b"csa-source-digest:"
 
 ARCH = "gfx950"
 FLAGS = [
@@ -51,10 +53,54 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str) -> str:
+def source_digest() -> str:
+    """sha256 over every source, header and compile flag the library is
+    built from (embedded in the library, so a stale build is detectable)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in [*SOURCES, *HEADERS]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    with open(PUBLIC_HEADER, "rb") as fh:
+        h.update(fh.read())
+    h.update(repr((FLAGS[:-1], SOURCE_FLAGS)).encode())
+    return h.hexdigest()
+
+
+def library_digest(path: str = LIB):
+    """The source digest embedded in a built library (read from the file,
+    without loading it), or None."""
+    try:
+        with open(path, "rb") as fh:
+            data = fh.read()
+    except OSError:
+        return None
+    i = data.find(DIGEST_TAG)
+    if i < 0:
+        return None
+    return data[i + len(DIGEST_TAG):i + len(DIGEST_TAG) + 64].decode("ascii", "replace")
+
+
+def ensure_current(verbose: bool = True) -> str:
+    """Build the library when it is missing or was built from other sources
+    than the ones in the tree."""
+    want = source_digest()
+    have = library_digest()
+    if have != want:
+        if verbose:
+            print(f"libcsa.so {'missing' if have is None else 'stale'}: building", file=sys.stderr)
+        build(verbose=verbose)
+        if library_digest() != want:
+            raise RuntimeError("libcsa.so does not carry the digest of its sources after a build")
+    return LIB
+
+
+def _compile(src: str, digest: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = [f'-DCSA_SOURCE_DIGEST="{digest}"'] if src == "api.cpp" else []
+    cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), *extra, *lang, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
@@ -64,8 +110,9 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = min(len(SOURCES), max(1, (os.cpu_count() or 2)))
+    digest = source_digest()
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, digest), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -148,7 +148,16 @@ const char* csa_status_string(int status) {
 
 const char* csa_last_error(void) { return g_last_error; }
 
-int csa_abi_version(void) { return 2; }
+int csa_abi_version(void) { return 3; }
+
+#ifndef CSA_SOURCE_DIGEST
+#define CSA_SOURCE_DIGEST "unknown"
+#endif
+// The build embeds the sha256 of the sources it compiled; the tag lets the
+// build scripts read it from the file without loading the library.
+static const char kSourceDigest[] = "csa-source-digest:" CSA_SOURCE_DIGEST;
+
+const char* csa_build_digest(void) { return kSourceDigest + sizeof("csa-source-digest:") - 1; }
 
 int csa_workspace_clear(void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "csa_workspace_clear";

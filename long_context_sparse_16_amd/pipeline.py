@@ -176,6 +176,19 @@ class CSAStep:
             csa_attend(self.q, self.kc, self.vc, self.idx, self.kr, self.vr, self.raw_pos0,
                        self.pos0, cfg.W, cfg.scale, out=self.out, lse=self.lse, ws=self.att_ws)
 
+    def stages(self) -> list:
+        """The step as (name, call) pairs, in order (for per-stage timing)."""
+        cfg = self.cfg
+        if self.fused_select:
+            return [("select", self.select), ("attend", self.attend)]
+        out = []
+        if cfg.n_new_tokens or cfg.block_end:
+            out.append(("compress", self.compress))
+        if cfg.k > 0:
+            out += [("index", self.index), ("topk", self.topk)]
+        out.append(("attend", self.attend))
+        return out
+
     def run(self) -> None:
         """The whole step: compress (if the step completes blocks), then
         indexer + top-k + attention (CSA), dense attention (HCA) or

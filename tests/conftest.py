@@ -26,9 +26,8 @@ def load_golden():
 
 
 def ensure_library():
-    """Build libcsa.so if it is not there yet (hipcc cross-compiles on CPU)."""
-    lib = os.path.join(ROOT, "long_context_sparse_16_amd", "libcsa.so")
-    if not os.path.exists(lib):
-        import __graft_entry__
-        __graft_entry__._build_module().build()
-    return lib
+    """Build libcsa.so if it is missing or was built from other sources than
+    the tree's (its embedded source digest differs); hipcc cross-compiles on
+    the CPU, so a stale library is never the one under test."""
+    import __graft_entry__
+    return __graft_entry__._build_module().ensure_current()

@@ -25,14 +25,16 @@ def test_every_declared_function_is_exported():
         assert hasattr(raw, n), n
     # the binding wraps every compute entry point under the same name
     for n in names:
-        if not n.endswith("_string") and n not in ("csa_last_error", "csa_abi_version"):
+        if not n.endswith("_string") and n not in ("csa_last_error", "csa_abi_version",
+                                                    "csa_build_digest"):
             assert hasattr(csa, n) or n.endswith("workspace_size"), n
 
 
 def test_status_strings_and_version():
     assert lib.csa_status_string(0) == b"CSA_OK"
     assert lib.csa_status_string(-5) == b"CSA_ERR_WORKSPACE"
-    assert lib.csa_abi_version() == 2
+    assert lib.csa_abi_version() == 3
+    assert len(lib.csa_build_digest()) == 64
 
 
 def _last():
