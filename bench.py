@@ -74,7 +74,6 @@ def kernel_sources(kernel: str) -> list:
     """The source files a kernel's machine code depends on."""
     main = {"indexer_kernel": "indexer.hip", "indexer_prefill_kernel": "indexer.hip",
             "attend_kernel": "attend.hip", "attend_merge_kernel": "attend.hip",
-            "attend_select_kernel": "attend.hip",
             "topk_classify_kernel": "topk.hip", "topk_finish_kernel": "topk.hip",
             "topk_row_kernel": "topk.hip"}[kernel]
     return [os.path.join(CSRC, f) for f in (main, "common.h", "kernels.h")]
@@ -382,18 +381,15 @@ def stats(xs) -> dict:
 
 
 def attainable_bandwidth(torch, timer) -> dict:
-    """HBM bandwidth a plain device copy and a plain read (sum) of 1 GiB
-    reach (GB/s, median of 10 cold runs): the practical ceiling beside the
-    nominal 8 TB/s."""
+    """HBM bandwidth a plain device copy of 1 GiB reaches (read + write bytes,
+    GB/s, median of 10 cold runs): a practical ceiling beside the nominal
+    8 TB/s."""
     n = FLUSH_BYTES
     a = torch.empty(n // 4, dtype=torch.int32, device="cuda:0").fill_(1)
     b = torch.empty_like(a)
-    out = torch.empty((), dtype=torch.int64, device="cuda:0")
     cp = stats(timer.samples(lambda: b.copy_(a), 10))["median"]
-    rd = stats(timer.samples(lambda: torch.sum(a, dim=(0,), dtype=torch.int64, out=out),
-                             10))["median"]
     del a, b
-    return {"copy_gbs": 2 * n / (cp * 1e3), "read_gbs": n / (rd * 1e3)}
+    return {"copy_gbs": 2 * n / (cp * 1e3)}
 
 
 # -------------------------------------------------------------- workloads

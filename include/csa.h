@@ -302,6 +302,50 @@ int csa_attend(const void* q, int q_dtype, const void* kc, const void* vc,
                float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa_decode -- one whole CSA step for a batch of queries in one call
+ * ("DeepSeek V4 technical review", takeshell.com, section 2.1: compress,
+ * index, select, attend): the Lightning Indexer's scores (csa_index_scores,
+ * which also builds the top-k histogram), the top-k selection (csa_topk)
+ * and the attention over the selected entries plus the window (csa_attend),
+ * and -- when zk and zv are given -- the compression of the block that the
+ * query token completes, done inside the indexer launch as in
+ * csa_decode_index_topk.  Outputs are bit-identical to those calls made one
+ * after another; the query q has kv_dtype.
+ *
+ *   qi .. ki_scale   the indexer inputs of csa_index_scores (act, H_I, d_I)
+ *   q, kc, vc, kv_dtype, kr, vr, raw_pos0, R   the attention inputs of
+ *                    csa_attend; kc / vc are written only by the block
+ *                    compression
+ *   zk, zv           NULL, or the compressor logits [B][R][d] fp32 of the
+ *                    raw rows (block compression: needs T == 1, ki == kc,
+ *                    bf16, R >= m, m <= 4)
+ *   scores           [B][T][n_cap] fp32 output, or NULL to keep the scores in
+ *                    the workspace
+ *   idx, out, lse    outputs as csa_topk / csa_attend
+ *   ws               device workspace of csa_decode_workspace_size(B, T, H,
+ *                    d, n_cap, k, W, scores == NULL) bytes, 16-byte aligned,
+ *                    zero before first use and left zero (workspace protocol
+ *                    above)
+ * Errors: CSA_ERR_WORKSPACE for a missing or short workspace, then the
+ * argument checks of csa_index_scores, csa_topk and csa_attend in that
+ * order; CSA_ERR_UNSUPPORTED for a block compression outside the limits
+ * above.  Nothing is launched when a check fails.
+ */
+size_t csa_decode_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d,
+                                 int64_t n_cap, int k, int W,
+                                 int scores_in_workspace);
+int csa_decode(const void* qi, int qi_dtype, const void* qi_scale,
+               const float* w, const void* ki, int ki_dtype,
+               const void* ki_scale, const void* q, void* kc, void* vc,
+               int kv_dtype, const void* kr, const void* vr, const float* zk,
+               const float* zv, const int64_t* raw_pos0, int64_t R,
+               const int64_t* pos0, int64_t B, int64_t T, int64_t H_I,
+               int64_t d_I, int64_t H, int64_t d, int64_t n_cap, int m,
+               int act, int k, int W, float scale, float* scores,
+               int32_t* idx, float* out, float* lse, void* ws,
+               size_t ws_bytes, void* stream);
+
+/*
  * hca_attend -- Heavily Compressed Attention (takeshell.com 2.2: m' = 128;
  * octagono.org: dense attention over the heavily compressed entries, no
  * sparse selection), with the same sliding-window branch.  Identical to

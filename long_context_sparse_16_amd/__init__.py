@@ -4,7 +4,7 @@ Argument marshalling only: every function takes PyTorch tensors (device
 memory) and passes their data pointers, sizes and the current HIP stream to
 the library entry point of the same name.  All computation happens in the
 HIP kernels; there is no fallback path.  Importing this module fails if the
-library has not been built (``python -m long_context_sparse_16_amd.build``).
+library has not been built (``python long_context_sparse_16_amd/build.py``).
 
 Output tensors and workspaces that are not supplied are allocated with
 PyTorch on the inputs' device.
@@ -37,7 +37,7 @@ class CSAError(RuntimeError):
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build the HIP library first "
-        "(python -m long_context_sparse_16_amd.build)")
+        "(python long_context_sparse_16_amd/build.py)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -62,6 +62,10 @@ _SIGNATURES = {
     "csa_decode_index_topk": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64,
                                    _i64, _i64, _i64, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "csa_attend_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i, _i]),
+    "csa_decode_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64, _i, _i, _i]),
+    "csa_decode": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
+                        _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i, _i, _i, _i,
+                        _f, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "csa_attend": (_i, [_vp, _i, _vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _i64, _vp, _i64, _i64, _i64,
                         _i64, _i64, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "hca_attend_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64, _i]),
@@ -96,7 +100,7 @@ def _source_digest() -> str:
 if _lib.csa_build_digest().decode() != _source_digest():
     raise ImportError(
         f"{LIB_PATH} was built from other sources than the ones in this tree: rebuild it "
-        "(python -m long_context_sparse_16_amd.build)")
+        "(python long_context_sparse_16_amd/build.py)")
 
 
 def header_functions() -> list:
@@ -464,6 +468,47 @@ def hca_attend(q, kc, vc, m: int, kr, vr, raw_pos0, pos0, W: int, scale: float, 
 
 
 # ------------------------------------------------------------- backward pass
+
+# -------------------------------------------------------------- decode step
+
+def csa_decode_workspace_size(B: int, T: int, H: int, d: int, n_cap: int, k: int, W: int,
+                              scores_in_workspace: bool) -> int:
+    return int(_lib.csa_decode_workspace_size(B, T, H, d, n_cap, k, W,
+                                              int(bool(scores_in_workspace))))
+
+
+def csa_decode(qi, w, ki, q, kc, vc, kr, vr, raw_pos0, pos0, m: int, k: int, W: int,
+               scale: float, act="relu", qi_scale=None, ki_scale=None, zk=None, zv=None,
+               scores=None, idx=None, out=None, lse=None, want_lse=True, ws=None,
+               keep_scores=True, stream=None):
+    """One whole decode step: indexer scores, top-k and attention (and, with
+    zk / zv, the block the query token completes compressed into kc / vc
+    first).  Returns (scores or None, idx, out, lse)."""
+    dev = _dev(qi, w, ki, q, kc, pos0)
+    B, T, H_I, d_I, n_cap = _index_shapes(qi, w, ki, pos0)
+    Bq, Tq, H, d, n_cap2, R = _attend_shapes(q, kc, vc, kr, vr, raw_pos0, pos0, W)
+    if (Bq, Tq, n_cap2) != (B, T, n_cap):
+        raise ValueError("indexer and attention inputs disagree on B, T or n_cap")
+    for name, t in (("zk", zk), ("zv", zv)):
+        if t is not None:
+            _contig(name, t)
+            if t.shape != kr.shape or t.dtype != torch.float32:
+                raise ValueError(f"{name} must be float32 [B, R, d]")
+    if scores is None and keep_scores:
+        scores = torch.empty((B, T, n_cap), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((B, T, k), dtype=torch.int32, device=dev)
+    out, lse = _outputs(out, lse, B, T, H, d, dev, want_lse)
+    ws, nbytes = _workspace(ws, csa_decode_workspace_size(B, T, H, d, n_cap, k, W, scores is None),
+                            dev)
+    _check("csa_decode", _lib.csa_decode(
+        _ptr(qi), _dtype_code(qi), _ptr(qi_scale), _ptr(w), _ptr(ki), _dtype_code(ki),
+        _ptr(ki_scale), _ptr(q), _ptr(kc), _ptr(vc), _dtype_code(kc), _ptr(kr), _ptr(vr),
+        _ptr(zk), _ptr(zv), _ptr(raw_pos0), R, _ptr(pos0), B, T, H_I, d_I, H, d, n_cap, int(m),
+        _act_code(act), int(k), int(W), float(scale), _ptr(scores), _ptr(idx), _ptr(out),
+        _ptr(lse), _ptr(ws), nbytes, _stream(stream, dev)))
+    return scores, idx, out, lse
+
 
 def _bwd_common(q, kc, vc, kr, vr, raw_pos0, pos0, W, out, lse, dout):
     dev = _dev(q, kc, vc, pos0)

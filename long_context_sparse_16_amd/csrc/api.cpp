@@ -389,6 +389,78 @@ int csa_attend(const void* q, int q_dtype, const void* kc, const void* vc, int k
                     fn);
 }
 
+// ------------------------------------------------------ the decode step
+
+size_t csa_decode_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d, int64_t n_cap, int k,
+                                 int W, int scores_in_workspace) {
+  if (B < 1 || T < 1 || H < 1 || d < 1 || n_cap < 1 || k < 1 || W < 0) return 0;
+  size_t s = csa_topk_workspace_size(B, T, n_cap, k) + csa_attend_workspace_size(B, T, H, d, k, W);
+  if (scores_in_workspace) s += round_up(static_cast<size_t>(B * T) * n_cap * sizeof(float));
+  return s;
+}
+
+int csa_decode(const void* qi, int qi_dtype, const void* qi_scale, const float* w, const void* ki,
+               int ki_dtype, const void* ki_scale, const void* q, void* kc, void* vc,
+               int kv_dtype, const void* kr, const void* vr, const float* zk, const float* zv,
+               const int64_t* raw_pos0, int64_t R, const int64_t* pos0, int64_t B, int64_t T,
+               int64_t H_I, int64_t d_I, int64_t H, int64_t d, int64_t n_cap, int m, int act,
+               int k, int W, float scale, float* scores, int32_t* idx, float* out, float* lse,
+               void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "csa_decode";
+  const bool compress = zk != nullptr || zv != nullptr;
+  const size_t need = csa_decode_workspace_size(B, T, H, d, n_cap, k, W, scores == nullptr ? 1 : 0);
+  CSA_REQUIRE(ws && ws_bytes >= need && aligned16(ws), CSA_ERR_WORKSPACE,
+              "%s: workspace of %zu bytes (16-byte aligned) needed, got %zu", fn, need,
+              ws ? ws_bytes : 0);
+  char* p = static_cast<char*>(ws);
+  float* sc = scores;
+  if (sc == nullptr) {
+    sc = reinterpret_cast<float*>(p);
+    p += round_up(static_cast<size_t>(B * T) * n_cap * sizeof(float));
+  }
+  void* topk_ws = p;
+  p += csa_topk_workspace_size(B, T, n_cap, k);
+  void* att_ws = p;
+  int rc = check_index_args(qi, qi_dtype, qi_scale, w, ki, ki_dtype, ki_scale, pos0, B, T, H_I,
+                            d_I, n_cap, m, act, sc, fn);
+  if (rc) return rc;
+  rc = check_topk_args(sc, pos0, B, T, n_cap, m, k, idx, fn);
+  if (rc) return rc;
+  rc = check_attend_args(q, kv_dtype, kc, vc, kv_dtype, kr, vr, raw_pos0, R, pos0, B, T, H, d,
+                         n_cap, W, scale, out, fn);
+  if (rc) return rc;
+  csa::FusedCompress fc{};
+  if (compress) {
+    CSA_REQUIRE(zk && zv && kr && vr && raw_pos0, CSA_ERR_NULL,
+                "%s: block compression needs zk, zv, kr, vr and raw_pos0", fn);
+    CSA_REQUIRE(T == 1 && ki == kc && ki_dtype == CSA_BF16 && kv_dtype == CSA_BF16, CSA_ERR_UNSUPPORTED,
+                "%s: block compression needs T == 1 and bf16 indexer keys that are kc", fn);
+    CSA_REQUIRE(R >= m && m <= csa::kFusedMaxM, CSA_ERR_UNSUPPORTED,
+                "%s: block compression needs R >= m and m <= %d", fn, csa::kFusedMaxM);
+    fc.kr = static_cast<const uint16_t*>(kr);
+    fc.vr = static_cast<const uint16_t*>(vr);
+    fc.zk = zk;
+    fc.zv = zv;
+    fc.raw_pos0 = raw_pos0;
+    fc.kc = static_cast<uint16_t*>(kc);
+    fc.vc = static_cast<uint16_t*>(vc);
+    fc.R = R;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* hist = csa::topk_hist_ptr(topk_ws, B, T);
+  rc = hip_result(csa::launch_index_scores(qi, qi_dtype, qi_scale, w, ki, ki_scale, pos0, B, T,
+                                           H_I, d_I, n_cap, m, act, sc, hist, k,
+                                           compress ? &fc : nullptr, s),
+                  fn);
+  if (rc) return rc;
+  rc = hip_result(csa::launch_topk(sc, pos0, B, T, n_cap, m, k, idx, topk_ws, hist != nullptr, s),
+                  fn);
+  if (rc) return rc;
+  return hip_result(csa::launch_attend(q, kv_dtype, kc, vc, idx, k, 0, kr, vr, raw_pos0, R, pos0,
+                                       B, T, H, d, n_cap, W, scale, out, lse, att_ws, s),
+                    fn);
+}
+
 size_t hca_attend_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d, int64_t n_cap,
                                  int W) {
   if (B < 1 || T < 1 || H < 1 || d < 1 || n_cap < 1 || W < 0) return 0;

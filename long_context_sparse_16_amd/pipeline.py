@@ -11,6 +11,9 @@ time them individually:
               and top-k with the compression folded into the indexer launch
   attend()    attention over the selected entries + sliding window
               (HCA: dense attention over every visible entry + window)
+  decode()    the whole step of a decode batch in one call (csa_decode:
+              indexer, top-k, attention; at a block boundary the block
+              compression inside the indexer launch)
 
 Every stage is one library call; this module only allocates tensors and
 passes them on.  Inputs are given in storage form: float32 arrays, or uint16
@@ -23,11 +26,14 @@ import numpy as np
 import torch
 
 from . import (csa_attend, csa_attend_backward, csa_attend_backward_workspace_size,
-               csa_compress, csa_compress_backward,
-               csa_decode_index_topk, csa_index_scores, csa_quantize_fp8_rows,
+               csa_compress, csa_compress_backward, csa_decode, csa_decode_index_topk,
+               csa_decode_workspace_size, csa_index_scores, csa_quantize_fp8_rows,
                csa_quantize_mxfp4_rows, csa_topk,
                csa_topk_workspace_size, csa_attend_workspace_size, hca_attend,
                hca_attend_workspace_size, workspace)
+
+# Query rows (B * T) up to which a CSA step runs as one csa_decode call.
+DECODE_MAX_ROWS = 256
 
 
 def to_device(a: np.ndarray, device, storage: str) -> torch.Tensor:
@@ -101,6 +107,11 @@ class CSAStep:
         self.idx = torch.empty((B, T, cfg.k), dtype=torch.int32, device=dev)
         self.topk_ws = workspace(csa_topk_workspace_size(B, T, n_cap, cfg.k), dev)
         self.att_ws = workspace(csa_attend_workspace_size(B, T, cfg.H, d, cfg.k, cfg.W), dev)
+        # decode-shaped steps run as csa_decode (its own workspace)
+        self.use_decode = B * T <= DECODE_MAX_ROWS
+        self.dec_ws = (workspace(csa_decode_workspace_size(B, T, cfg.H, d, n_cap, cfg.k, cfg.W,
+                                                           False), dev)
+                       if self.use_decode else None)
 
     # ------------------------------------------------------------ stages
     def quantize_keys(self, first: int, last: int) -> None:
@@ -142,6 +153,25 @@ class CSAStep:
         csa_decode_index_topk(self.qi, self.w, self.kc, self.vc, self.kr, self.vr, self.z,
                               self.z, self.raw_pos0, self.pos0, cfg.m, cfg.k, act=self.act,
                               scores=self.scores, idx=self.idx, ws=self.topk_ws)
+
+    def index_inputs(self):
+        """(qi, ki, qi_scale, ki_scale) as the indexer takes them."""
+        if self.cfg.ki_fp8:
+            return self.qi_codes, self.ki_codes, self.qi_scale, self.ki_scale
+        if self.cfg.ki_mxfp4:
+            return (self.qi_codes, self.ki_codes.view(torch.float4_e2m1fn_x2), self.qi_scale,
+                    self.ki_scale.view(torch.float8_e8m0fnu))
+        return self.qi, self.kc, None, None
+
+    def decode(self) -> None:
+        """The whole decode step in one library call (csa_decode)."""
+        cfg = self.cfg
+        qi, ki, qs, ks = self.index_inputs()
+        fuse = self.fused_select  # block compression inside the indexer launch
+        csa_decode(qi, self.w, ki, self.q, self.kc, self.vc, self.kr, self.vr, self.raw_pos0,
+                   self.pos0, cfg.m, cfg.k, cfg.W, cfg.scale, act=self.act, qi_scale=qs,
+                   ki_scale=ks, zk=self.z if fuse else None, zv=self.z if fuse else None,
+                   scores=self.scores, idx=self.idx, out=self.out, lse=self.lse, ws=self.dec_ws)
 
     def index(self) -> None:
         """Indexer scores; also builds the top-k histogram in the top-k
@@ -192,7 +222,13 @@ class CSAStep:
     def run(self) -> None:
         """The whole step: compress (if the step completes blocks), then
         indexer + top-k + attention (CSA), dense attention (HCA) or
-        window-only attention (sliding-window layers)."""
+        window-only attention (sliding-window layers).  Decode batches with
+        a top-k run as one csa_decode call."""
+        if self.cfg.k > 0 and self.use_decode and (self.fused_select or not self.cfg.block_end):
+            if not self.fused_select:
+                self.compress()
+            self.decode()
+            return
         if self.fused_select:
             self.select()
             self.attend()
