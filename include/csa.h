@@ -39,9 +39,11 @@
  * - Workspaces (`ws`): device memory owned by the caller, sized by the
  *   matching *_workspace_size() query.  Top-k workspaces must be zero
  *   before first use (a zero-filled allocation, or csa_workspace_clear);
- *   every call leaves them ready for the next (the parts read before being
- *   written -- histograms and counters -- are returned to zero), so they
- *   are reused call after call without clearing.  Attention workspaces
+ *   every call leaves them ready for the next call with the same B, T and
+ *   n_cap (the parts read before being written -- histograms and counters
+ *   -- are returned to zero), so they are reused call after call without
+ *   clearing; their layout depends on those sizes, so a workspace reused
+ *   for other sizes must be cleared first.  Attention workspaces
  *   hold per-call partial results and may contain anything on entry.
  *   Calls that share a workspace must be ordered (same stream); concurrent
  *   calls on one workspace race.
@@ -344,6 +346,36 @@ int csa_decode(const void* qi, int qi_dtype, const void* qi_scale,
                int act, int k, int W, float scale, float* scores,
                int32_t* idx, float* out, float* lse, void* ws,
                size_t ws_bytes, void* stream);
+
+/*
+ * csa_decode_noalloc -- csa_decode without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  It
+ * computes exactly what csa_decode computes, with the same arguments minus
+ * ws / ws_bytes, and allocates nothing: its workspace is a fixed array of
+ * csa_decode_noalloc_max_bytes() bytes (64 MiB) inside the library, one
+ * per GPU, held until the process ends.  Sizes whose
+ * csa_decode_workspace_size(..., scores == NULL) exceeds it return
+ * CSA_ERR_UNSUPPORTED; other errors as csa_decode.
+ * The array is zeroed by a fill kernel on the caller's stream at its first
+ * use on a device, after a call that failed once kernels were enqueued,
+ * and in its leading histogram part whenever B*T or n_cap differ from the
+ * previous call's.  Every call on a GPU shares that GPU's array: calls
+ * that may overlap on one GPU (other streams, other threads) race and must
+ * be ordered by the caller.
+ */
+size_t csa_decode_noalloc_max_bytes(void);
+int csa_decode_noalloc(const void* qi, int qi_dtype, const void* qi_scale,
+                       const float* w, const void* ki, int ki_dtype,
+                       const void* ki_scale, const void* q, void* kc,
+                       void* vc, int kv_dtype, const void* kr,
+                       const void* vr, const float* zk, const float* zv,
+                       const int64_t* raw_pos0, int64_t R,
+                       const int64_t* pos0, int64_t B, int64_t T,
+                       int64_t H_I, int64_t d_I, int64_t H, int64_t d,
+                       int64_t n_cap, int m, int act, int k, int W,
+                       float scale, float* scores, int32_t* idx,
+                       float* out, float* lse, void* stream);
 
 /*
  * hca_attend -- Heavily Compressed Attention (takeshell.com 2.2: m' = 128;

@@ -63,6 +63,10 @@ _SIGNATURES = {
                                    _i64, _i64, _i64, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "csa_attend_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i, _i]),
     "csa_decode_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64, _i, _i, _i]),
+    "csa_decode_noalloc_max_bytes": (_sz, []),
+    "csa_decode_noalloc": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp,
+                                _vp, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                _i64, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _vp]),
     "csa_decode": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp,
                         _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i, _i, _i, _i,
                         _f, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -484,6 +488,30 @@ def csa_decode(qi, w, ki, q, kc, vc, kr, vr, raw_pos0, pos0, m: int, k: int, W: 
     """One whole decode step: indexer scores, top-k and attention (and, with
     zk / zv, the block the query token completes compressed into kc / vc
     first).  Returns (scores or None, idx, out, lse)."""
+    return _decode(False, qi, w, ki, q, kc, vc, kr, vr, raw_pos0, pos0, m, k, W, scale, act,
+                   qi_scale, ki_scale, zk, zv, scores, idx, out, lse, want_lse, ws, keep_scores,
+                   stream)
+
+
+def csa_decode_noalloc_max_bytes() -> int:
+    return int(_lib.csa_decode_noalloc_max_bytes())
+
+
+def csa_decode_noalloc(qi, w, ki, q, kc, vc, kr, vr, raw_pos0, pos0, m: int, k: int, W: int,
+                       scale: float, act="relu", qi_scale=None, ki_scale=None, zk=None,
+                       zv=None, scores=None, idx=None, out=None, lse=None, want_lse=True,
+                       keep_scores=False, stream=None):
+    """csa_decode on the library's fixed per-GPU scratch instead of a
+    workspace.  The library call allocates nothing; this wrapper allocates
+    only the outputs that are not passed in."""
+    return _decode(True, qi, w, ki, q, kc, vc, kr, vr, raw_pos0, pos0, m, k, W, scale, act,
+                   qi_scale, ki_scale, zk, zv, scores, idx, out, lse, want_lse, None,
+                   keep_scores, stream)
+
+
+def _decode(noalloc, qi, w, ki, q, kc, vc, kr, vr, raw_pos0, pos0, m, k, W, scale, act,
+            qi_scale, ki_scale, zk, zv, scores, idx, out, lse, want_lse, ws, keep_scores,
+            stream):
     dev = _dev(qi, w, ki, q, kc, pos0)
     B, T, H_I, d_I, n_cap = _index_shapes(qi, w, ki, pos0)
     Bq, Tq, H, d, n_cap2, R = _attend_shapes(q, kc, vc, kr, vr, raw_pos0, pos0, W)
@@ -499,14 +527,17 @@ def csa_decode(qi, w, ki, q, kc, vc, kr, vr, raw_pos0, pos0, m: int, k: int, W: 
     if idx is None:
         idx = torch.empty((B, T, k), dtype=torch.int32, device=dev)
     out, lse = _outputs(out, lse, B, T, H, d, dev, want_lse)
-    ws, nbytes = _workspace(ws, csa_decode_workspace_size(B, T, H, d, n_cap, k, W, scores is None),
-                            dev)
-    _check("csa_decode", _lib.csa_decode(
-        _ptr(qi), _dtype_code(qi), _ptr(qi_scale), _ptr(w), _ptr(ki), _dtype_code(ki),
-        _ptr(ki_scale), _ptr(q), _ptr(kc), _ptr(vc), _dtype_code(kc), _ptr(kr), _ptr(vr),
-        _ptr(zk), _ptr(zv), _ptr(raw_pos0), R, _ptr(pos0), B, T, H_I, d_I, H, d, n_cap, int(m),
-        _act_code(act), int(k), int(W), float(scale), _ptr(scores), _ptr(idx), _ptr(out),
-        _ptr(lse), _ptr(ws), nbytes, _stream(stream, dev)))
+    args = (_ptr(qi), _dtype_code(qi), _ptr(qi_scale), _ptr(w), _ptr(ki), _dtype_code(ki),
+            _ptr(ki_scale), _ptr(q), _ptr(kc), _ptr(vc), _dtype_code(kc), _ptr(kr), _ptr(vr),
+            _ptr(zk), _ptr(zv), _ptr(raw_pos0), R, _ptr(pos0), B, T, H_I, d_I, H, d, n_cap,
+            int(m), _act_code(act), int(k), int(W), float(scale), _ptr(scores), _ptr(idx),
+            _ptr(out), _ptr(lse))
+    if noalloc:
+        _check("csa_decode_noalloc", _lib.csa_decode_noalloc(*args, _stream(stream, dev)))
+    else:
+        ws, nbytes = _workspace(
+            ws, csa_decode_workspace_size(B, T, H, d, n_cap, k, W, scores is None), dev)
+        _check("csa_decode", _lib.csa_decode(*args, _ptr(ws), nbytes, _stream(stream, dev)))
     return scores, idx, out, lse
 
 
@@ -595,7 +626,8 @@ __all__ = [
     "csa_compress", "csa_quantize_fp8_rows", "csa_quantize_mxfp4_rows", "csa_index_scores",
     "csa_topk",
     "csa_topk_workspace_size", "csa_index_topk", "csa_index_topk_workspace_size",
-    "csa_decode_index_topk",
+    "csa_decode_index_topk", "csa_decode", "csa_decode_workspace_size", "csa_decode_noalloc",
+    "csa_decode_noalloc_max_bytes",
     "csa_attend", "csa_attend_workspace_size", "hca_attend", "hca_attend_workspace_size",
     "csa_attend_backward", "hca_attend_backward", "csa_compress_backward",
     "csa_attend_backward_workspace_size", "hca_attend_backward_workspace_size",

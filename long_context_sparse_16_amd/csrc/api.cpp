@@ -148,7 +148,7 @@ const char* csa_status_string(int status) {
 
 const char* csa_last_error(void) { return g_last_error; }
 
-int csa_abi_version(void) { return 3; }
+int csa_abi_version(void) { return 4; }
 
 #ifndef CSA_SOURCE_DIGEST
 #define CSA_SOURCE_DIGEST "unknown"
@@ -399,6 +399,82 @@ size_t csa_decode_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d, int
   return s;
 }
 
+// The arguments of a decode step.
+struct DecodeArgs {
+  const void* qi; int qi_dtype; const void* qi_scale; const float* w; const void* ki;
+  int ki_dtype; const void* ki_scale; const void* q; void* kc; void* vc; int kv_dtype;
+  const void* kr; const void* vr; const float* zk; const float* zv; const int64_t* raw_pos0;
+  int64_t R; const int64_t* pos0; int64_t B, T, H_I, d_I, H, d, n_cap; int m, act, k, W;
+  float scale; float* scores; int32_t* idx; float* out; float* lse;
+};
+
+// Argument checks of a decode step (everything but the workspace).
+static int decode_check(const DecodeArgs& a, const char* fn) {
+  // scores == NULL is valid (they then live in the workspace)
+  static const float kInWorkspace = 0.f;
+  const float* sc = a.scores ? a.scores : &kInWorkspace;
+  int rc = check_index_args(a.qi, a.qi_dtype, a.qi_scale, a.w, a.ki, a.ki_dtype, a.ki_scale,
+                            a.pos0, a.B, a.T, a.H_I, a.d_I, a.n_cap, a.m, a.act, sc, fn);
+  if (rc) return rc;
+  rc = check_topk_args(sc, a.pos0, a.B, a.T, a.n_cap, a.m, a.k, a.idx, fn);
+  if (rc) return rc;
+  rc = check_attend_args(a.q, a.kv_dtype, a.kc, a.vc, a.kv_dtype, a.kr, a.vr, a.raw_pos0, a.R,
+                         a.pos0, a.B, a.T, a.H, a.d, a.n_cap, a.W, a.scale, a.out, fn);
+  if (rc) return rc;
+  if (a.zk != nullptr || a.zv != nullptr) {
+    CSA_REQUIRE(a.zk && a.zv && a.kr && a.vr && a.raw_pos0, CSA_ERR_NULL,
+                "%s: block compression needs zk, zv, kr, vr and raw_pos0", fn);
+    CSA_REQUIRE(a.T == 1 && a.ki == a.kc && a.ki_dtype == CSA_BF16 && a.kv_dtype == CSA_BF16,
+                CSA_ERR_UNSUPPORTED,
+                "%s: block compression needs T == 1 and bf16 indexer keys that are kc", fn);
+    CSA_REQUIRE(a.R >= a.m && a.m <= csa::kFusedMaxM, CSA_ERR_UNSUPPORTED,
+                "%s: block compression needs R >= m and m <= %d", fn, csa::kFusedMaxM);
+  }
+  return CSA_OK;
+}
+
+// The launches of a checked decode step on a workspace of
+// csa_decode_workspace_size() bytes: the top-k workspace (whose zero-state
+// part leads it) first, then the scores when they live in the workspace,
+// then the attention partials.
+static int decode_launch(const DecodeArgs& a, void* ws, hipStream_t s, const char* fn) {
+  const int64_t B = a.B, T = a.T, n_cap = a.n_cap;
+  char* p = static_cast<char*>(ws);
+  void* topk_ws = p;
+  p += csa_topk_workspace_size(B, T, n_cap, a.k);
+  float* sc = a.scores;
+  if (sc == nullptr) {
+    sc = reinterpret_cast<float*>(p);
+    p += round_up(static_cast<size_t>(B * T) * n_cap * sizeof(float));
+  }
+  void* att_ws = p;
+  csa::FusedCompress fc{};
+  const bool compress = a.zk != nullptr;
+  if (compress) {
+    fc.kr = static_cast<const uint16_t*>(a.kr);
+    fc.vr = static_cast<const uint16_t*>(a.vr);
+    fc.zk = a.zk;
+    fc.zv = a.zv;
+    fc.raw_pos0 = a.raw_pos0;
+    fc.kc = static_cast<uint16_t*>(a.kc);
+    fc.vc = static_cast<uint16_t*>(a.vc);
+    fc.R = a.R;
+  }
+  uint32_t* hist = csa::topk_hist_ptr(topk_ws, B, T);
+  int rc = hip_result(csa::launch_index_scores(a.qi, a.qi_dtype, a.qi_scale, a.w, a.ki,
+                                               a.ki_scale, a.pos0, B, T, a.H_I, a.d_I, n_cap, a.m,
+                                               a.act, sc, hist, a.k, compress ? &fc : nullptr, s),
+                      fn);
+  if (rc) return rc;
+  rc = hip_result(
+      csa::launch_topk(sc, a.pos0, B, T, n_cap, a.m, a.k, a.idx, topk_ws, hist != nullptr, s), fn);
+  if (rc) return rc;
+  return hip_result(csa::launch_attend(a.q, a.kv_dtype, a.kc, a.vc, a.idx, a.k, 0, a.kr, a.vr,
+                                       a.raw_pos0, a.R, a.pos0, B, T, a.H, a.d, n_cap, a.W,
+                                       a.scale, a.out, a.lse, att_ws, s),
+                    fn);
+}
+
 int csa_decode(const void* qi, int qi_dtype, const void* qi_scale, const float* w, const void* ki,
                int ki_dtype, const void* ki_scale, const void* q, void* kc, void* vc,
                int kv_dtype, const void* kr, const void* vr, const float* zk, const float* zv,
@@ -407,58 +483,47 @@ int csa_decode(const void* qi, int qi_dtype, const void* qi_scale, const float* 
                int k, int W, float scale, float* scores, int32_t* idx, float* out, float* lse,
                void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "csa_decode";
-  const bool compress = zk != nullptr || zv != nullptr;
+  const DecodeArgs a{qi, qi_dtype, qi_scale, w, ki, ki_dtype, ki_scale, q, kc, vc, kv_dtype,
+                     kr, vr, zk, zv, raw_pos0, R, pos0, B, T, H_I, d_I, H, d, n_cap, m, act, k,
+                     W, scale, scores, idx, out, lse};
+  int rc = decode_check(a, fn);
+  if (rc) return rc;
   const size_t need = csa_decode_workspace_size(B, T, H, d, n_cap, k, W, scores == nullptr ? 1 : 0);
   CSA_REQUIRE(ws && ws_bytes >= need && aligned16(ws), CSA_ERR_WORKSPACE,
               "%s: workspace of %zu bytes (16-byte aligned) needed, got %zu", fn, need,
               ws ? ws_bytes : 0);
-  char* p = static_cast<char*>(ws);
-  float* sc = scores;
-  if (sc == nullptr) {
-    sc = reinterpret_cast<float*>(p);
-    p += round_up(static_cast<size_t>(B * T) * n_cap * sizeof(float));
-  }
-  void* topk_ws = p;
-  p += csa_topk_workspace_size(B, T, n_cap, k);
-  void* att_ws = p;
-  int rc = check_index_args(qi, qi_dtype, qi_scale, w, ki, ki_dtype, ki_scale, pos0, B, T, H_I,
-                            d_I, n_cap, m, act, sc, fn);
+  return decode_launch(a, ws, static_cast<hipStream_t>(stream), fn);
+}
+
+size_t csa_decode_noalloc_max_bytes(void) { return csa::kStaticScratchBytes; }
+
+int csa_decode_noalloc(const void* qi, int qi_dtype, const void* qi_scale, const float* w,
+                       const void* ki, int ki_dtype, const void* ki_scale, const void* q, void* kc,
+                       void* vc, int kv_dtype, const void* kr, const void* vr, const float* zk,
+                       const float* zv, const int64_t* raw_pos0, int64_t R, const int64_t* pos0,
+                       int64_t B, int64_t T, int64_t H_I, int64_t d_I, int64_t H, int64_t d,
+                       int64_t n_cap, int m, int act, int k, int W, float scale, float* scores,
+                       int32_t* idx, float* out, float* lse, void* stream) {
+  const char* fn = "csa_decode_noalloc";
+  const DecodeArgs a{qi, qi_dtype, qi_scale, w, ki, ki_dtype, ki_scale, q, kc, vc, kv_dtype,
+                     kr, vr, zk, zv, raw_pos0, R, pos0, B, T, H_I, d_I, H, d, n_cap, m, act, k,
+                     W, scale, scores, idx, out, lse};
+  int rc = decode_check(a, fn);
   if (rc) return rc;
-  rc = check_topk_args(sc, pos0, B, T, n_cap, m, k, idx, fn);
-  if (rc) return rc;
-  rc = check_attend_args(q, kv_dtype, kc, vc, kv_dtype, kr, vr, raw_pos0, R, pos0, B, T, H, d,
-                         n_cap, W, scale, out, fn);
-  if (rc) return rc;
-  csa::FusedCompress fc{};
-  if (compress) {
-    CSA_REQUIRE(zk && zv && kr && vr && raw_pos0, CSA_ERR_NULL,
-                "%s: block compression needs zk, zv, kr, vr and raw_pos0", fn);
-    CSA_REQUIRE(T == 1 && ki == kc && ki_dtype == CSA_BF16 && kv_dtype == CSA_BF16, CSA_ERR_UNSUPPORTED,
-                "%s: block compression needs T == 1 and bf16 indexer keys that are kc", fn);
-    CSA_REQUIRE(R >= m && m <= csa::kFusedMaxM, CSA_ERR_UNSUPPORTED,
-                "%s: block compression needs R >= m and m <= %d", fn, csa::kFusedMaxM);
-    fc.kr = static_cast<const uint16_t*>(kr);
-    fc.vr = static_cast<const uint16_t*>(vr);
-    fc.zk = zk;
-    fc.zv = zv;
-    fc.raw_pos0 = raw_pos0;
-    fc.kc = static_cast<uint16_t*>(kc);
-    fc.vc = static_cast<uint16_t*>(vc);
-    fc.R = R;
-  }
+  const size_t need = csa_decode_workspace_size(B, T, H, d, n_cap, k, W, scores == nullptr ? 1 : 0);
+  CSA_REQUIRE(need <= csa::kStaticScratchBytes, CSA_ERR_UNSUPPORTED,
+              "%s: these sizes need %zu bytes of scratch; the fixed scratch holds %zu "
+              "(use csa_decode with a workspace)",
+              fn, need, csa::kStaticScratchBytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uint32_t* hist = csa::topk_hist_ptr(topk_ws, B, T);
-  rc = hip_result(csa::launch_index_scores(qi, qi_dtype, qi_scale, w, ki, ki_scale, pos0, B, T,
-                                           H_I, d_I, n_cap, m, act, sc, hist, k,
-                                           compress ? &fc : nullptr, s),
-                  fn);
-  if (rc) return rc;
-  rc = hip_result(csa::launch_topk(sc, pos0, B, T, n_cap, m, k, idx, topk_ws, hist != nullptr, s),
-                  fn);
-  if (rc) return rc;
-  return hip_result(csa::launch_attend(q, kv_dtype, kc, vc, idx, k, 0, kr, vr, raw_pos0, R, pos0,
-                                       B, T, H, d, n_cap, W, scale, out, lse, att_ws, s),
-                    fn);
+  void* ws = nullptr;
+  CSA_REQUIRE(csa::static_scratch(s, B * T, n_cap, csa::topk_zero_state_bytes(B, T), &ws) == 0,
+              CSA_ERR_HIP, "%s: the fixed scratch could not be located or cleared: %s", fn,
+              hipGetErrorString(hipGetLastError()));
+  rc = decode_launch(a, ws, s, fn);
+  // a launch that failed part way may leave the histograms dirty
+  if (rc != CSA_OK) csa::static_scratch_mark_dirty();
+  return rc;
 }
 
 size_t hca_attend_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d, int64_t n_cap,

@@ -57,10 +57,27 @@ size_t topk_workspace_bytes(int64_t B, int64_t T, int64_t n_cap, int k);
 // The first-digit histogram inside a top-k workspace (nullptr when the row
 // path, which keeps its histogram in LDS, will be used).
 uint32_t* topk_hist_ptr(void* ws, int64_t B, int64_t T);
+// Bytes at the start of a top-k workspace that must be zero on entry (the
+// histograms and counters; the rest is written before it is read).
+size_t topk_zero_state_bytes(int64_t B, int64_t T);
 int launch_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, int64_t n_cap,
                 int m, int k, int32_t* idx, void* ws, bool hist_ready, hipStream_t s);
 // Zero-fill (a kernel, so it may be captured in a graph).
 int launch_clear(void* p, size_t bytes, hipStream_t s);
+
+// The fixed per-device scratch of the allocation-free entry points.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+// The current device's scratch address for a call with `rows` query rows
+// over n_cap entries whose first zero_bytes bytes must be zero on entry.
+// The whole array is zeroed (on stream s) at its first use on the device
+// and after a failed call marked it dirty; otherwise the first zero_bytes
+// are zeroed when (rows, n_cap) differ from the previous call's, since a
+// call of the same sizes leaves that part zero.  Returns 0, or -1 when the
+// HIP runtime reported an error.
+int static_scratch(hipStream_t s, int64_t rows, int64_t n_cap, size_t zero_bytes, void** out);
+// A call that launched work and then failed may leave the zero-state parts
+// of the scratch (the top-k histograms) dirty: clear all of it next time.
+void static_scratch_mark_dirty();
 
 struct AttSplit {
   int splits;

@@ -899,6 +899,13 @@ size_t topk_workspace_bytes(int64_t B, int64_t T, int64_t n_cap, int k) {
   return rows <= kTopkSplitMaxRows ? split_ws_bytes(rows, n_cap) : 0;
 }
 
+size_t topk_zero_state_bytes(int64_t B, int64_t T) {
+  // hist then ctrl lead the split workspace
+  const int64_t rows = B * T;
+  return rows <= kTopkSplitMaxRows ? static_cast<size_t>(rows) * (kHistBins + 4) * sizeof(uint32_t)
+                                   : 0;
+}
+
 uint32_t* topk_hist_ptr(void* ws, int64_t B, int64_t T) {
   // the histogram leads the workspace whatever n_cap is
   return B * T <= kTopkSplitMaxRows ? static_cast<uint32_t*>(ws) : nullptr;

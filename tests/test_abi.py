@@ -33,7 +33,7 @@ def test_every_declared_function_is_exported():
 def test_status_strings_and_version():
     assert lib.csa_status_string(0) == b"CSA_OK"
     assert lib.csa_status_string(-5) == b"CSA_ERR_WORKSPACE"
-    assert lib.csa_abi_version() == 3
+    assert lib.csa_abi_version() == 4
     assert len(lib.csa_build_digest()) == 64
 
 
@@ -170,3 +170,30 @@ def test_backward_validation():
     assert lib.csa_compress_backward(FAKE, 2, FAKE, FAKE, 1, 8, 4, 4, 32, 32, FAKE, FAKE, NULL) == -3
     assert lib.csa_compress_backward(FAKE, 1, FAKE, FAKE, 1, 6, 4, 4, 32, 32, FAKE, FAKE, NULL) == -2
     assert lib.csa_compress_backward(FAKE, 1, FAKE, FAKE, 1, 8, 4, 4, 16, 32, FAKE, FAKE, NULL) == -2
+
+
+def _decode(noalloc, B=32, T=1, n_cap=32768, k=1024, scores=FAKE, zk=NULL, ws=FAKE,
+            ws_bytes=1 << 40):
+    # qi, qi_dtype, qi_scale, w, ki, ki_dtype, ki_scale, q, kc, vc, kv_dtype, kr, vr, zk, zv,
+    # raw_pos0, R, pos0, B, T, H_I, d_I, H, d, n_cap, m, act, k, W, scale, scores, idx, out, lse
+    args = [FAKE, 1, NULL, FAKE, FAKE, 1, NULL, FAKE, FAKE, FAKE, 1, FAKE, FAKE, zk, NULL,
+            FAKE, 131, FAKE, B, T, 64, 128, 64, 128, n_cap, 4, 0, k, 128, 0.088, scores, FAKE,
+            FAKE, FAKE]
+    if noalloc:
+        return lib.csa_decode_noalloc(*args, NULL)
+    return lib.csa_decode(*args, ws, ws_bytes, NULL)
+
+
+def test_decode_validation():
+    """Both decode entry points check every argument before touching the
+    GPU; the allocation-free one also refuses sizes beyond its fixed
+    scratch (here the scores of 256 x 2^20 entries kept in it)."""
+    for noalloc in (False, True):
+        assert _decode(noalloc, B=0) == -2
+        assert _decode(noalloc, k=0) == -4
+        assert _decode(noalloc, zk=FAKE) == -1  # zk without zv
+    assert _decode(False, ws=NULL) == -5
+    assert _decode(False, ws_bytes=16) == -5
+    assert csa.csa_decode_noalloc_max_bytes() == 64 << 20
+    assert _decode(True, B=256, n_cap=1 << 20, scores=NULL) == -4
+    assert "fixed scratch" in _last()
