@@ -304,11 +304,39 @@ int csa_attend(const void* q, int q_dtype, const void* kc, const void* vc,
                float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa_select_attend -- the top-k selection and the core attention of a CSA
+ * step ("DeepSeek V4 technical review", takeshell.com, section 2.1: the
+ * indexer's top-k entries, then attention over them only; octagono.org:
+ * top-1,024 plus a 128-token window), from csa_index_scores' scores.
+ * Computes exactly what csa_topk (same ws, same hist_ready) followed by
+ * csa_attend compute: idx receives csa_topk's selection, out / lse the
+ * attention over it.  For up to 256 query rows over n_cap <= 2^20 entries
+ * (n_cap > 8192) the selection is made inside the attention launch from
+ * the top-k's classified lists (one launch fewer); other sizes run
+ * csa_topk's kernels first.
+ *
+ *   scores, topk_ws, topk_ws_bytes, hist_ready, pos0, m, k   as csa_topk
+ *   q, kc, vc, kv_dtype, kr, vr, raw_pos0, R, W, scale, out, lse, ws,
+ *   ws_bytes   as csa_attend (the query has kv_dtype; attention workspace
+ *              of csa_attend_workspace_size(B, T, H, d, k, W) bytes)
+ *   idx        [B][T][k] int32 output
+ * Errors: those of csa_topk's and csa_attend's checks, in that order.
+ */
+int csa_select_attend(const float* scores, void* topk_ws, size_t topk_ws_bytes,
+                      int hist_ready, const int64_t* pos0, int m, int k,
+                      const void* q, const void* kc, const void* vc,
+                      int kv_dtype, const void* kr, const void* vr,
+                      const int64_t* raw_pos0, int64_t R, int64_t B, int64_t T,
+                      int64_t H, int64_t d, int64_t n_cap, int W, float scale,
+                      int32_t* idx, float* out, float* lse, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/*
  * csa_decode -- one whole CSA step for a batch of queries in one call
  * ("DeepSeek V4 technical review", takeshell.com, section 2.1: compress,
  * index, select, attend): the Lightning Indexer's scores (csa_index_scores,
- * which also builds the top-k histogram), the top-k selection (csa_topk)
- * and the attention over the selected entries plus the window (csa_attend),
+ * which also builds the top-k histogram), then the top-k selection and the
+ * attention over the selected entries plus the window (csa_select_attend),
  * and -- when zk and zv are given -- the compression of the block that the
  * query token completes, done inside the indexer launch as in
  * csa_decode_index_topk.  Outputs are bit-identical to those calls made one
@@ -412,7 +440,9 @@ int hca_attend(const void* q, int q_dtype, const void* kc, const void* vc,
  * (with one query row t, head h over its key list, p = exp(scale q.K - lse),
  * dp = V dout, D = dout . out, ds = p (dp - D): dq = scale ds K,
  * dK += scale ds q, dV += p dout).  idx rows must be strictly ascending
- * then -1 padded (as csa_topk emits them).  ws: device workspace of
+ * then -1 padded (as csa_topk emits them): a row never repeats an entry,
+ * so an entry is referenced at most T times; rows that break this give
+ * undefined dkc / dvc (not detected).  ws: device workspace of
  * csa_attend_backward_workspace_size() bytes (the per-row key/value
  * contributions, B*T*(k+W)*d*8 bytes, and each entry's list of the rows
  * that attended it; contents on entry do not matter).

@@ -62,6 +62,9 @@ _SIGNATURES = {
     "csa_decode_index_topk": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64,
                                    _i64, _i64, _i64, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "csa_attend_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i, _i]),
+    "csa_select_attend": (_i, [_vp, _vp, _sz, _i, _vp, _i, _i, _vp, _vp, _vp, _i, _vp, _vp,
+                               _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i, _f, _vp, _vp, _vp,
+                               _vp, _sz, _vp]),
     "csa_decode_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64, _i, _i, _i]),
     "csa_decode_noalloc_max_bytes": (_sz, []),
     "csa_decode_noalloc": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp,
@@ -475,6 +478,30 @@ def hca_attend(q, kc, vc, m: int, kr, vr, raw_pos0, pos0, W: int, scale: float, 
 
 # -------------------------------------------------------------- decode step
 
+def csa_select_attend(scores, topk_ws, pos0, m: int, k: int, q, kc, vc, kr, vr, raw_pos0,
+                      W: int, scale: float, hist_ready=True, idx=None, out=None, lse=None,
+                      want_lse=True, ws=None, stream=None):
+    """Top-k selection (from csa_index_scores' scores and, with hist_ready,
+    the histogram it built in topk_ws) and attention over the selection.
+    Returns (idx, out, lse)."""
+    dev = _dev(scores, q, kc, pos0)
+    B, T, H, d, n_cap, R = _attend_shapes(q, kc, vc, kr, vr, raw_pos0, pos0, W)
+    _contig("scores", scores)
+    if scores.shape != (B, T, n_cap) or scores.dtype != torch.float32:
+        raise ValueError("scores must be float32 [B, T, n_cap]")
+    if idx is None:
+        idx = torch.empty((B, T, k), dtype=torch.int32, device=dev)
+    out, lse = _outputs(out, lse, B, T, H, d, dev, want_lse)
+    ws, nbytes = _workspace(ws, csa_attend_workspace_size(B, T, H, d, k, W), dev)
+    tws_bytes = topk_ws.numel() * topk_ws.element_size() if topk_ws is not None else 0
+    _check("csa_select_attend", _lib.csa_select_attend(
+        _ptr(scores), _ptr(topk_ws), tws_bytes, int(bool(hist_ready)), _ptr(pos0), int(m),
+        int(k), _ptr(q), _ptr(kc), _ptr(vc), _dtype_code(kc), _ptr(kr), _ptr(vr),
+        _ptr(raw_pos0), R, B, T, H, d, n_cap, int(W), float(scale), _ptr(idx), _ptr(out),
+        _ptr(lse), _ptr(ws), nbytes, _stream(stream, dev)))
+    return idx, out, lse
+
+
 def csa_decode_workspace_size(B: int, T: int, H: int, d: int, n_cap: int, k: int, W: int,
                               scores_in_workspace: bool) -> int:
     return int(_lib.csa_decode_workspace_size(B, T, H, d, n_cap, k, W,
@@ -626,7 +653,8 @@ __all__ = [
     "csa_compress", "csa_quantize_fp8_rows", "csa_quantize_mxfp4_rows", "csa_index_scores",
     "csa_topk",
     "csa_topk_workspace_size", "csa_index_topk", "csa_index_topk_workspace_size",
-    "csa_decode_index_topk", "csa_decode", "csa_decode_workspace_size", "csa_decode_noalloc",
+    "csa_decode_index_topk", "csa_select_attend", "csa_decode", "csa_decode_workspace_size",
+    "csa_decode_noalloc",
     "csa_decode_noalloc_max_bytes",
     "csa_attend", "csa_attend_workspace_size", "hca_attend", "hca_attend_workspace_size",
     "csa_attend_backward", "hca_attend_backward", "csa_compress_backward",

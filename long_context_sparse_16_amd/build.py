@@ -30,7 +30,7 @@ SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "topk.hip", "attend.hip", "
 SOURCE_FLAGS = {
     "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
-HEADERS = ["common.h", "kernels.h"]
+HEADERS = ["common.h", "kernels.h", "select.h"]
 PUBLIC_HEADER = os.path.join(ROOT, "include", "csa.h")
 DIGEST_TAG = b"csa-source-digest:"
 

@@ -399,6 +399,60 @@ size_t csa_decode_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d, int
   return s;
 }
 
+// Top-k selection and attention on a checked top-k workspace: for few long
+// rows the classify launch, then the attention launch that makes the
+// selection from its lists; otherwise csa_topk's kernels, then attention.
+static int select_attend_launch(const float* scores, void* topk_ws, bool hist_ready,
+                                const int64_t* pos0, int m, int k, const void* q, int kv_dtype,
+                                const void* kc, const void* vc, const void* kr, const void* vr,
+                                const int64_t* raw_pos0, int64_t R, int64_t B, int64_t T,
+                                int64_t H, int64_t d, int64_t n_cap, int W, float scale,
+                                int32_t* idx, float* out, float* lse, void* att_ws, hipStream_t s,
+                                const char* fn) {
+  csa::TopkLists lists{};
+  int rc = csa::launch_topk_lists(scores, pos0, B, T, n_cap, m, k, topk_ws, hist_ready, &lists, s);
+  if (rc < 0) return hip_result(rc, fn);
+  if (rc == 0) {
+    lists.idx = idx;
+    return hip_result(csa::launch_attend(q, kv_dtype, kc, vc, nullptr, k, 0, kr, vr, raw_pos0, R,
+                                         pos0, B, T, H, d, n_cap, W, scale, out, lse, att_ws, s,
+                                         &lists),
+                      fn);
+  }
+  rc = hip_result(csa::launch_topk(scores, pos0, B, T, n_cap, m, k, idx, topk_ws, hist_ready, s),
+                  fn);
+  if (rc) return rc;
+  return hip_result(csa::launch_attend(q, kv_dtype, kc, vc, idx, k, 0, kr, vr, raw_pos0, R, pos0,
+                                       B, T, H, d, n_cap, W, scale, out, lse, att_ws, s),
+                    fn);
+}
+
+int csa_select_attend(const float* scores, void* topk_ws, size_t topk_ws_bytes, int hist_ready,
+                      const int64_t* pos0, int m, int k, const void* q, const void* kc,
+                      const void* vc, int kv_dtype, const void* kr, const void* vr,
+                      const int64_t* raw_pos0, int64_t R, int64_t B, int64_t T, int64_t H,
+                      int64_t d, int64_t n_cap, int W, float scale, int32_t* idx, float* out,
+                      float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "csa_select_attend";
+  int rc = check_topk_args(scores, pos0, B, T, n_cap, m, k, idx, fn);
+  if (rc) return rc;
+  rc = check_attend_args(q, kv_dtype, kc, vc, kv_dtype, kr, vr, raw_pos0, R, pos0, B, T, H, d,
+                         n_cap, W, scale, out, fn);
+  if (rc) return rc;
+  const size_t need_t = csa_topk_workspace_size(B, T, n_cap, k);
+  CSA_REQUIRE(need_t == 0 || (topk_ws && topk_ws_bytes >= need_t && aligned16(topk_ws)),
+              CSA_ERR_WORKSPACE,
+              "%s: top-k workspace of %zu bytes (16-byte aligned) needed, got %zu", fn, need_t,
+              topk_ws ? topk_ws_bytes : 0);
+  const size_t need = csa_attend_workspace_size(B, T, H, d, k, W);
+  CSA_REQUIRE(need == 0 || (ws && ws_bytes >= need && aligned16(ws)), CSA_ERR_WORKSPACE,
+              "%s: workspace of %zu bytes (16-byte aligned) needed, got %zu", fn, need,
+              ws ? ws_bytes : 0);
+  return select_attend_launch(scores, topk_ws, hist_ready != 0 && need_t != 0, pos0, m, k, q,
+                              kv_dtype, kc, vc, kr, vr, raw_pos0, R, B, T, H, d, n_cap, W, scale,
+                              idx, out, lse, ws, static_cast<hipStream_t>(stream), fn);
+}
+
 // The arguments of a decode step.
 struct DecodeArgs {
   const void* qi; int qi_dtype; const void* qi_scale; const float* w; const void* ki;
@@ -466,13 +520,9 @@ static int decode_launch(const DecodeArgs& a, void* ws, hipStream_t s, const cha
                                                a.act, sc, hist, a.k, compress ? &fc : nullptr, s),
                       fn);
   if (rc) return rc;
-  rc = hip_result(
-      csa::launch_topk(sc, a.pos0, B, T, n_cap, a.m, a.k, a.idx, topk_ws, hist != nullptr, s), fn);
-  if (rc) return rc;
-  return hip_result(csa::launch_attend(a.q, a.kv_dtype, a.kc, a.vc, a.idx, a.k, 0, a.kr, a.vr,
-                                       a.raw_pos0, a.R, a.pos0, B, T, a.H, a.d, n_cap, a.W,
-                                       a.scale, a.out, a.lse, att_ws, s),
-                    fn);
+  return select_attend_launch(sc, topk_ws, hist != nullptr, a.pos0, a.m, a.k, a.q, a.kv_dtype,
+                              a.kc, a.vc, a.kr, a.vr, a.raw_pos0, a.R, B, T, a.H, a.d, n_cap, a.W,
+                              a.scale, a.idx, a.out, a.lse, att_ws, s, fn);
 }
 
 int csa_decode(const void* qi, int qi_dtype, const void* qi_scale, const float* w, const void* ki,

@@ -27,6 +27,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace csa {
 
@@ -84,9 +85,309 @@ struct AttParams {
   int k, W, m;
   int splits, chunks_per_split;
   float scale_log2;  // scale * log2(e)
+  TopkLists sel;     // the selection's lists (SEL variant)
 };
 
-template <int DTYPE, int D, bool HCA>
+// ---- the top-k selection made inside the launch (CSA, SEL variant)
+//
+// Every workgroup of a row reads the row's classified lists (sure entries
+// and candidates, a few thousand entries for decode rows) into LDS, finds
+// the cut among the candidates, and keeps the slots of the sorted
+// selection that its split attends; each split writes its own range of the
+// index output, and split 0 returns the row's first-digit histogram
+// (consumed by the classify launch) to zero.  The selection is the one the
+// top-k finishing kernel makes: the r best candidates by (key, lower index
+// first).  With up to 2 NT candidates it is found by ranking every
+// candidate against all others (a handful of barriers); more candidates go
+// through the digit passes, and lists longer than the LDS space are read
+// from global memory (only with very many ties).
+struct AttSelShared {
+  uint32_t hist[2048];  // digit passes; the packed candidates on the ranking path
+  uint32_t scan[32];
+  uint32_t misc[8];
+  uint64_t scan64[8];
+  uint32_t table[2 * kSelMaxSlices];  // per slice: list offset, length
+};
+constexpr int kAttSelPre = 8;    // prefetched list entries per thread
+constexpr int kAttSelBatch = 8;  // loads in flight per thread past the prefix
+
+// Exclusive prefix sum of v over the workgroup, and its total, with one
+// barrier: per-wave scans, the wave totals through sm[0 .. NT / 64), each
+// thread adding those of the waves before its own.  sm must not be written
+// again before the caller's next barrier.
+template <int NT, typename U>
+__device__ __forceinline__ U block_scan_1b(U v, U* sm, U* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  U x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const U y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sm[wv] = x;
+  __syncthreads();
+  U base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const U c = sm[w];
+    base += w < wv ? c : U(0);
+    tot += c;
+  }
+  *total = tot;
+  return base + x - v;
+}
+
+template <int NT, int CAP>
+__device__ __forceinline__ void attend_select(const TopkLists& sel, int64_t row, int64_t t,
+                                              int64_t n_cap, int k, int64_t s_begin,
+                                              int64_t s_end, int split, int32_t* s_ent,
+                                              uint32_t* ck, int32_t* ci, AttSelShared& ss) {
+  static_assert(NT >= kSelMaxSlices, "one slice count per thread");
+  constexpr int kEnt = 4096;  // entries per classified slice
+  const int tid = threadIdx.x;
+  const int64_t slot0 = row * sel.n_sl;
+  const int n_alloc = static_cast<int>(sel.n_sl);
+  // Loaded before the row's length is known: the slice counts, a prefix of
+  // every slice's list (P entries each, slot q = tid + NT i is entry q % P
+  // of slice q / P; slices clamped to the workspace's), the bucket.
+  const int64_t my_slot = slot0 + (tid < n_alloc ? tid : n_alloc - 1);
+  const uint32_t cl0 = sel.cnt[my_slot * 2];
+  const uint32_t cc0 = sel.cnt[my_slot * 2 + 1];
+  int lp = 0;
+  while (lp < 9 && (n_alloc << (lp + 1)) <= NT * kAttSelPre) ++lp;
+  int32_t pi[kAttSelPre];
+  uint32_t pk[kAttSelPre];
+#pragma unroll
+  for (int i = 0; i < kAttSelPre; ++i) {
+    const int q = tid + NT * i;
+    const int sl = q >> lp;
+    const int64_t at = (slot0 + (sl < n_alloc ? sl : n_alloc - 1)) * kEnt + (q & ((1 << lp) - 1));
+    pi[i] = sel.lidx[at];
+    pk[i] = sel.lkey[at];
+  }
+  const uint32_t b1 = sel.ctrl[row * 4];
+  const int64_t V = uniform64(visible_entries(t, sel.m, n_cap));
+  int32_t* out = sel.idx + row * k;
+  if (split == 0)
+    for (int i = tid; i < kTopkHistBins; i += NT) sel.hist[row * kTopkHistBins + i] = 0u;
+  if (V <= k) {  // every visible entry, then -1
+    for (int64_t i = s_begin + tid; i < s_end; i += NT) {
+      const int32_t e = i < V ? static_cast<int32_t>(i) : -1;
+      s_ent[i - s_begin] = e;
+      out[i] = e;
+    }
+    return;
+  }
+  // list offsets of the slices (listed and candidate counts in one scan)
+  const int n_sl = static_cast<int>((V + kEnt - 1) / kEnt);
+  const uint32_t cl = tid < n_sl ? cl0 : 0u, cc = tid < n_sl ? cc0 : 0u;
+  uint64_t tot;
+  const uint64_t ex = block_scan_1b<NT>(static_cast<uint64_t>(cl) | (static_cast<uint64_t>(cc) << 32),
+                                        ss.scan64, &tot);
+  const uint32_t n_list = static_cast<uint32_t>(tot), nc = static_cast<uint32_t>(tot >> 32);
+  if (tid < n_sl) {
+    ss.table[2 * tid] = static_cast<uint32_t>(ex);
+    ss.table[2 * tid + 1] = cl;
+  }
+  const bool more = __syncthreads_or(tid < n_sl && cl > (1u << lp));  // a list past its prefix
+  const uint32_t r = static_cast<uint32_t>(k) - (n_list - nc);  // winners among candidates
+  const bool fits = n_list <= static_cast<uint32_t>(CAP);
+  if (fits) {
+#pragma unroll
+    for (int i = 0; i < kAttSelPre; ++i) {
+      const int q = tid + NT * i;
+      const int sl = q >> lp;
+      const uint32_t pos = static_cast<uint32_t>(q & ((1 << lp) - 1));
+      if (sl < n_sl && pos < ss.table[2 * sl + 1]) {
+        const uint32_t at = ss.table[2 * sl] + pos;
+        ck[at] = pk[i];
+        ci[at] = pi[i];
+      }
+    }
+    if (more) {
+      // entries past the prefixes: 2^lt threads per slice, kAttSelBatch
+      // loads in flight per thread
+      int lt = 0;
+      while ((n_sl << (lt + 1)) <= NT) ++lt;
+      const uint32_t step = 1u << lt;
+      for (int base = 0; base < (n_sl << lt); base += NT) {
+        const int q = base + tid;
+        const int sl = q >> lt;
+        if (sl < n_sl) {
+          const uint32_t o = ss.table[2 * sl], c = ss.table[2 * sl + 1];
+          const int64_t g0 = (slot0 + sl) * kEnt;
+          for (uint32_t p0 = (1u << lp) + static_cast<uint32_t>(q & (step - 1)); p0 < c;
+               p0 += step * kAttSelBatch) {
+            int32_t vi[kAttSelBatch];
+            uint32_t vk[kAttSelBatch];
+#pragma unroll
+            for (int u = 0; u < kAttSelBatch; ++u) {
+              const uint32_t pos = p0 + u * step;
+              const int64_t at = g0 + (pos < c ? pos : c - 1);
+              vi[u] = sel.lidx[at];
+              vk[u] = sel.lkey[at];
+            }
+#pragma unroll
+            for (int u = 0; u < kAttSelBatch; ++u) {
+              const uint32_t pos = p0 + u * step;
+              if (pos < c) {
+                ck[o + pos] = vk[u];
+                ci[o + pos] = vi[u];
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+  // second-digit histogram of the candidates (key bits 19..10), cleared
+  // before the barrier that publishes the list; bin b at word b + b / 16,
+  // so the 16 consecutive bins each lane reads below sit 17 words from the
+  // next lane's (no bank conflicts)
+  uint32_t* h2 = ss.hist;
+  auto h2_at = [](uint32_t b) __attribute__((always_inline)) { return b + (b >> 4); };
+  for (int i = tid; i < 1024 + 64; i += NT) h2[i] = 0u;
+  if (tid == 0) ss.misc[6] = 0u;  // candidates collected at the cut's prefix
+  __syncthreads();  // the list is in LDS
+  // list entry i (sure entries and candidates of all slices, in entry
+  // order): from LDS, or found in its slice's global list
+  auto entry = [&](uint32_t i, uint32_t& key, int32_t& j) __attribute__((always_inline)) {
+    if (fits) {
+      key = ck[i];
+      j = ci[i];
+      return;
+    }
+    int lo = 0, hi = n_sl - 1;  // the last slice whose list starts at or before i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ss.table[2 * mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    const int64_t at = (slot0 + lo) * kEnt + (i - ss.table[2 * lo]);
+    key = sel.lkey[at];
+    j = sel.lidx[at];
+  };
+  // this thread's run of the list
+  const uint32_t per = (n_list + NT - 1) / NT;
+  const uint32_t i0 = min(n_list, tid * per), i1 = min(n_list, i0 + per);
+  Cut c{0u, 0x7fffffff};  // r == nc: every candidate wins
+  bool general = r < nc && !fits;
+  if (r < nc && fits) {
+    // a histogram of the candidates' second digits gives the 20-bit prefix
+    // of the cut; the few candidates that share it are ranked by one wave
+    for (uint32_t i = i0; i < i1; ++i) {
+      const uint32_t key = ck[i];
+      if ((key >> kTopkDigit1Shift) == b1) atomicAdd(&h2[h2_at((key >> 10) & 1023u)], 1u);
+    }
+    __syncthreads();
+    // every wave finds the bucket b2 of the r-th best candidate's second
+    // digit (lane l holds bins 1023 - 16 l - q, q = 0..15, highest first)
+    const int lane = tid & 63;
+    uint32_t hb[16];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      hb[q] = h2[h2_at(1023u - 16u * lane - q)];
+      sum += hb[q];
+    }
+    uint32_t incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const uint32_t excl = incl - sum;
+    const bool mine = excl < r && r <= incl;
+    uint32_t b2 = 0, above = 0;
+    if (mine) {
+      uint32_t acc = excl;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        if (acc < r && r <= acc + hb[q]) {
+          b2 = 1023u - 16u * lane - q;
+          above = acc;
+        }
+        acc += hb[q];
+      }
+    }
+    const int owner = __ffsll(static_cast<long long>(__ballot(mine))) - 1;
+    b2 = __shfl(b2, owner);
+    above = __shfl(above, owner);
+    const uint32_t n2 = h2[h2_at(b2)];
+    general = n2 > 64u;  // too many share the cut's prefix: the digit passes
+    uint64_t* tmp = reinterpret_cast<uint64_t*>(h2 + 1152);  // 64 slots
+    if (!general) {
+      // the n2 candidates with prefix (b1, b2), any order
+      const uint32_t prefix = (b1 << 10) | b2;
+      for (uint32_t i = i0; i < i1; ++i) {
+        const uint32_t key = ck[i];
+        if ((key >> 10) == prefix)
+          tmp[atomicAdd(&ss.misc[6], 1u)] =
+              (static_cast<uint64_t>(key & 0xfffffu) << 32) | static_cast<uint32_t>(ci[i]);
+      }
+    }
+    __syncthreads();
+    if (!general && tid < 64) {
+      // rank them by (key desc, index asc): the (r - above)-th is the cut
+      const uint32_t r2 = r - above;
+      const bool have = static_cast<uint32_t>(lane) < n2;
+      const uint64_t v = have ? tmp[lane] : 0u;
+      const uint32_t lo = static_cast<uint32_t>(v >> 32);
+      const int32_t jj = have ? static_cast<int32_t>(static_cast<uint32_t>(v)) : 0x7fffffff;
+      uint32_t rank = 0;
+      for (uint32_t q = 0; q < n2; ++q) {
+        const uint32_t lo_q = __shfl(lo, static_cast<int>(q));
+        const int32_t j_q = __shfl(jj, static_cast<int>(q));
+        rank += (lo_q > lo || (lo_q == lo && j_q < jj)) ? 1u : 0u;
+      }
+      if (have && rank == r2 - 1u) {
+        ss.misc[2] = lo;
+        ss.misc[3] = static_cast<uint32_t>(jj);
+      }
+    }
+    __syncthreads();
+    c = Cut{ss.misc[2], static_cast<int32_t>(ss.misc[3])};
+  }
+  if (general) {
+    auto visit = [&](auto f) {
+      for (uint32_t i = tid; i < n_list; i += NT) {
+        uint32_t key;
+        int32_t j;
+        entry(i, key, j);
+        if ((key >> kTopkDigit1Shift) == b1) f(key, j);
+      }
+    };
+    c = resolve_cut<NT>(ss, visit, r);
+  }
+  // sure entries and winning candidates in entry order: this split's
+  // positions [s_begin, s_end) of the sorted list
+  auto keep = [&](uint32_t key, int32_t j) __attribute__((always_inline)) {
+    return (key >> kTopkDigit1Shift) > b1 || r >= nc || cut_wins(c, key, j);
+  };
+  uint32_t cnt = 0;
+  for (uint32_t i = i0; i < i1; ++i) {
+    uint32_t key;
+    int32_t j;
+    entry(i, key, j);
+    cnt += keep(key, j) ? 1u : 0u;
+  }
+  uint32_t unused;
+  int64_t pos = block_scan_1b<NT>(cnt, ss.scan + 8, &unused);
+  for (uint32_t i = i0; i < i1 && pos < s_end; ++i) {
+    uint32_t key;
+    int32_t j;
+    entry(i, key, j);
+    if (keep(key, j)) {
+      if (pos >= s_begin) {
+        s_ent[pos - s_begin] = j;
+        out[pos] = j;
+      }
+      ++pos;
+    }
+  }
+}
+
+template <int DTYPE, int D, bool HCA, bool SEL>
 __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttParams p) {
   using Tr = AttTraits<DTYPE, D>;
   constexpr int RB = Tr::kRowBytes;
@@ -145,7 +446,19 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttParams p) {
   // gathers never wait on index loads.
   const int64_t s_begin = c_begin * kAttChunk;
   const int64_t idx_row = row * p.k;
-  if (!HCA) {
+  if (SEL) {
+    // the selection itself: keys in ks, then the shared state and the
+    // indices in vs (both free until the first chunk is staged)
+    constexpr int kCapK = static_cast<int>(sizeof(ks) / 4);
+    constexpr int kCapI = static_cast<int>((sizeof(vs) - sizeof(AttSelShared)) / 4);
+    constexpr int kCap = kCapK < kCapI ? kCapK : kCapI;
+    static_assert(sizeof(AttSelShared) % 16 == 0 && kCap >= 2048, "selection LDS");
+    AttSelShared& ss = *reinterpret_cast<AttSelShared*>(&vs[0][0]);
+    attend_select<kAttThreads, kCap>(
+        p.sel, row, t, p.n_cap, p.k, s_begin, min(c_end * kAttChunk, n_ent), split, s_ent,
+        reinterpret_cast<uint32_t*>(&ks[0][0]),
+        reinterpret_cast<int32_t*>(&vs[0][0] + sizeof(AttSelShared)), ss);
+  } else if (!HCA) {
     const int64_t n_list = min(c_end * kAttChunk, n_ent) - s_begin;
     for (int64_t i = tid; i < n_list; i += kAttThreads) s_ent[i] = p.idx[idx_row + s_begin + i];
   }
@@ -539,8 +852,9 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
                   int k, int hca_m, const void* kr, const void* vr, const int64_t* raw_pos0,
                   int64_t R, const int64_t* pos0, int64_t B, int64_t T, int64_t H, int64_t D,
                   int64_t n_cap, int W, float scale, float* out, float* lse, void* ws,
-                  hipStream_t stream) {
+                  hipStream_t stream, const TopkLists* sel) {
   const bool hca = hca_m > 0;
+  if (sel != nullptr && hca) return -2;
   const int64_t rows = B * T;
   const int64_t n_slots_max = (hca ? n_cap : k) + W;
   const AttSplit sp = attend_split(rows, n_slots_max, hca);
@@ -568,6 +882,7 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
   p.chunks_per_split = sp.chunks_per_split;
   p.scale_log2 = scale * kLog2e;
   p.po = p.pm = p.pl = nullptr;
+  p.sel = sel ? *sel : TopkLists{};
   if (sp.splits > 1) {
     float* base = static_cast<float*>(ws);
     p.po = base;
@@ -580,9 +895,11 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
 #define CSA_ATT_CASE(DT, DD)                                                        \
   if (dtype == DT && D == DD) {                                                     \
     if (hca)                                                                        \
-      attend_kernel<DT, DD, true><<<grid, kAttThreads, 0, stream>>>(p);             \
+      attend_kernel<DT, DD, true, false><<<grid, kAttThreads, 0, stream>>>(p);      \
+    else if (sel)                                                                   \
+      attend_kernel<DT, DD, false, true><<<grid, kAttThreads, 0, stream>>>(p);      \
     else                                                                            \
-      attend_kernel<DT, DD, false><<<grid, kAttThreads, 0, stream>>>(p);            \
+      attend_kernel<DT, DD, false, false><<<grid, kAttThreads, 0, stream>>>(p);     \
     if (sp.splits > 16)                                                             \
       attend_merge_kernel<DD, 32><<<mgrid, kMergeThreads, 0, stream>>>(p);          \
     else if (sp.splits > 8)                                                         \

@@ -439,6 +439,10 @@ __global__ __launch_bounds__(256) void attend_bwd_entries_kernel(BwdParams p) {
 // ---- CSA: inverse of the index lists (which rows attended each entry)
 
 constexpr int kBwdMaxRefs = 16384;  // references of one entry kept in LDS (= rows per sequence)
+// A row's index list is strictly ascending (the ABI's contract, which
+// csa_topk's output meets), so an entry has at most one reference per query
+// row and at most kBwdMaxRows per sequence: the largest list fits.
+static_assert(kBwdMaxRefs >= kBwdMaxRows, "an entry's references must fit the reduction's LDS");
 
 __device__ __forceinline__ bool bwd_entry_ok(int32_t e, int64_t n_cap) {
   return e >= 0 && e < n_cap;
@@ -507,8 +511,9 @@ __global__ __launch_bounds__(256) void attend_bwd_entries_csr_kernel(BwdParams p
   const int tid = threadIdx.x;
   const int64_t j = blockIdx.x;
   const int64_t b = blockIdx.y;
-  // (at most one reference per row for index lists without repeats; the
-  // clamp only keeps invalid lists inside the buffer)
+  // (at most one reference per row, since index rows are strictly
+  // ascending; the clamp only keeps lists that break that contract inside
+  // the buffer)
   const int n_all = static_cast<int>(p.cnt[b * p.n_cap + j]);
   if (BIG != (n_all > kBwdSmallRefs)) return;  // the other variant's entry
   const int n = min(n_all, CAP);

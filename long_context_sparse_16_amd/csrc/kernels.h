@@ -62,6 +62,27 @@ uint32_t* topk_hist_ptr(void* ws, int64_t B, int64_t T);
 size_t topk_zero_state_bytes(int64_t B, int64_t T);
 int launch_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, int64_t n_cap,
                 int m, int k, int32_t* idx, void* ws, bool hist_ready, hipStream_t s);
+
+// The split top-k's per-slice lists (every entry whose first digit is at or
+// above the row's cut bucket, in entry order, with its key), from which the
+// attention launch can make the selection itself.
+constexpr int64_t kSelMaxSlices = 256;  // rows of up to 2^20 entries
+struct TopkLists {
+  const uint32_t* cnt;   // [rows][n_sl][2]: listed entries, candidates among them
+  const int32_t* lidx;   // [rows][n_sl][4096]
+  const uint32_t* lkey;  // [rows][n_sl][4096]
+  const uint32_t* ctrl;  // [rows][4]: [0] the cut bucket b1
+  uint32_t* hist;        // [rows][4096]: first-digit histograms, zeroed by the consumer
+  int64_t n_sl;          // slices allocated per row
+  int m;                 // compression ratio (visible entries V(t))
+  int32_t* idx;          // [rows][k] output: the selection, ascending, -1 padded
+};
+// Only the first half of the split top-k (classify); returns 1 (nothing
+// launched) when the split path does not apply to these sizes or the row
+// needs more than kSelMaxSlices slices.
+int launch_topk_lists(const float* scores, const int64_t* pos0, int64_t B, int64_t T,
+                      int64_t n_cap, int m, int k, void* ws, bool hist_ready, TopkLists* lists,
+                      hipStream_t s);
 // Zero-fill (a kernel, so it may be captured in a graph).
 int launch_clear(void* p, size_t bytes, hipStream_t s);
 
@@ -85,12 +106,14 @@ struct AttSplit {
 };
 AttSplit attend_split(int64_t rows, int64_t n_slots_max, bool hca);
 size_t attend_workspace_bytes(int64_t rows, int64_t H, int64_t D, int64_t n_slots_max, bool hca);
-// hca_m > 0 selects HCA (all visible entries, idx ignored).
+// hca_m > 0 selects HCA (all visible entries, idx ignored).  sel
+// (nullable, CSA): make the top-k selection from these lists inside the
+// launch (writing sel->idx) instead of reading idx.
 int launch_attend(const void* q, int dtype, const void* kc, const void* vc, const int32_t* idx,
                   int k, int hca_m, const void* kr, const void* vr, const int64_t* raw_pos0,
                   int64_t R, const int64_t* pos0, int64_t B, int64_t T, int64_t H, int64_t D,
                   int64_t n_cap, int W, float scale, float* out, float* lse, void* ws,
-                  hipStream_t stream);
+                  hipStream_t stream, const TopkLists* sel = nullptr);
 
 // Backward pass (fp32 gradients).  The workspace holds the per-row key /
 // value gradient contributions: attend_bwd_workspace_bytes() bytes.

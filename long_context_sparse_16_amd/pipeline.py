@@ -11,8 +11,10 @@ time them individually:
               and top-k with the compression folded into the indexer launch
   attend()    attention over the selected entries + sliding window
               (HCA: dense attention over every visible entry + window)
+  select_attend()  top-k selection and attention after index()
+              (csa_select_attend)
   decode()    the whole step of a decode batch in one call (csa_decode:
-              indexer, top-k, attention; at a block boundary the block
+              index() then select_attend(); at a block boundary the block
               compression inside the indexer launch)
 
 Every stage is one library call; this module only allocates tensors and
@@ -28,7 +30,7 @@ import torch
 from . import (csa_attend, csa_attend_backward, csa_attend_backward_workspace_size,
                csa_compress, csa_compress_backward, csa_decode, csa_decode_index_topk,
                csa_decode_workspace_size, csa_index_scores, csa_quantize_fp8_rows,
-               csa_quantize_mxfp4_rows, csa_topk,
+               csa_quantize_mxfp4_rows, csa_select_attend, csa_topk,
                csa_topk_workspace_size, csa_attend_workspace_size, hca_attend,
                hca_attend_workspace_size, workspace)
 
@@ -194,6 +196,15 @@ class CSAStep:
         csa_topk(self.scores, self.pos0, self.cfg.m, self.cfg.k, idx=self.idx, ws=self.topk_ws,
                  hist_ready=True)
 
+    def select_attend(self) -> None:
+        """Top-k selection and attention after index() (csa_select_attend:
+        for few long rows the selection is made inside the attention
+        launch)."""
+        cfg = self.cfg
+        csa_select_attend(self.scores, self.topk_ws, self.pos0, cfg.m, cfg.k, self.q, self.kc,
+                          self.vc, self.kr, self.vr, self.raw_pos0, cfg.W, cfg.scale,
+                          idx=self.idx, out=self.out, lse=self.lse, ws=self.att_ws)
+
     def attend(self) -> None:
         cfg = self.cfg
         if cfg.hca:
@@ -214,6 +225,9 @@ class CSAStep:
         out = []
         if cfg.n_new_tokens or cfg.block_end:
             out.append(("compress", self.compress))
+        if cfg.k > 0 and self.use_decode:
+            # the launches csa_decode makes
+            return out + [("index", self.index), ("select_attend", self.select_attend)]
         if cfg.k > 0:
             out += [("index", self.index), ("topk", self.topk)]
         out.append(("attend", self.attend))

@@ -94,6 +94,33 @@ def test_csa_attend_backward_parity(storage, H, d):
             _close(f"{key}[{b}]", from_dev(g[key])[b], ref[key], storage)
 
 
+def test_csa_attend_backward_hot_entries():
+    """Entries that every query row selects: 2304 references each, more
+    than the small-list variant of the key/value reduction holds, so the
+    large-list variant sorts and sums them."""
+    say("csa attend backward, hot entries")
+    rng = np.random.default_rng(8123)
+    B, T, H, d, n_cap, k, W, m = 1, 2304, 8, 64, 600, 12, 8, 4
+    pos0s = [4 * n_cap - 1]                          # every entry visible
+    q, kc, vc, kr, vr, pos0, raw_pos0, idx, dout = _case(rng, "f32", B, T, H, d, n_cap, k, W, m,
+                                                         pos0s)
+    hot = np.array([0, 7, 300, 599], np.int32)
+    for i in range(T):
+        rest = rng.choice(np.setdiff1d(np.arange(n_cap), hot), size=k - hot.size, replace=False)
+        idx[0, i] = np.sort(np.concatenate([hot, rest.astype(np.int32)]))
+    scale = 1.0 / np.sqrt(d)
+    args = (to_dev(q), to_dev(kc), to_dev(vc), to_dev(idx), to_dev(kr), to_dev(vr),
+            to_dev(raw_pos0), to_dev(pos0), W, scale)
+    out, lse = csa.csa_attend(*args)
+    g = csa.csa_attend_backward(*args, out, lse, to_dev(dout))
+    torch.cuda.synchronize()
+    ref = oracle.attend_backward(q[0], kc[0], vc[0], idx[0], kr[0], vr[0], raw_pos0[0],
+                                 pos0[0] + np.arange(T), W, scale, dout[0])
+    for key in ("dkc", "dvc"):
+        _close(f"{key} hot", from_dev(g[key])[0][hot], ref[key][hot], "f32")
+        _close(key, from_dev(g[key])[0], ref[key], "f32")
+
+
 @pytest.mark.parametrize("storage", ["f32", "bf16"])
 def test_hca_attend_backward_parity(storage):
     say("hca attend backward", storage)

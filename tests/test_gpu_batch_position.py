@@ -82,6 +82,32 @@ def test_csa_decode_batch_position(n_cap):
         _same(f"scores[{src}]", a["scores"][src, 0, :V], b["scores"][j, 0, :V])
 
 
+def test_csa_decode_batch_size():
+    """A sequence decoded alone (B = 1) and inside a batch of 6: the scores
+    and top-k lists are bit-identical (every score is a fixed-order sum of
+    its own row), while the attention output and lse may differ in the last
+    bits, because the number of key splits -- and so the order of the merge's
+    fp32 sums -- follows the batch's query rows (B*T)."""
+    say("batch size: csa decode")
+    rng = np.random.default_rng(9150)
+    B, n_cap, H_I, d_I, H, d, W, m, k = 6, 9000, 16, 128, 64, 128, 64, 4, 256
+    x = _decode_inputs(rng, B, n_cap, H_I, d_I, H, d, W, m)
+    a = _csa_decode(x, m, k, W, x["kc"])
+    pos = x["pos0"].cpu().numpy()
+    for src in (0, 3, 5):
+        one = {key: v[src:src + 1].contiguous() for key, v in x.items()}
+        b = _csa_decode(one, m, k, W, one["kc"])
+        torch.cuda.synchronize()
+        V = int(min(n_cap, (pos[src] + 1) // m))
+        _same(f"scores[{src}]", a["scores"][src, 0, :V], b["scores"][0, 0, :V])
+        _same(f"idx[{src}]", a["idx"][src:src + 1], b["idx"])
+        for key, tol in (("out", 1e-5), ("lse", 1e-6)):
+            ref = a[key][src:src + 1].double()
+            err = float((b[key].double() - ref).abs().max() / ref.abs().max())
+            say("  ", key, src, "max rel diff", err)
+            assert err <= tol, (key, src, err)
+
+
 def test_hca_decode_batch_position():
     say("batch position: hca decode")
     rng = np.random.default_rng(9200)

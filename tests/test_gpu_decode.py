@@ -1,6 +1,8 @@
-"""The whole decode step in one call (csa_decode) against the same step as
-separate calls (csa_index_topk, then csa_attend): scores, indices, outputs
-and lse must be bit-identical, since csa_decode runs the same kernels.  The
+"""The whole decode step in one call (csa_decode), and the top-k selection
+with attention (csa_select_attend), against the same step as separate calls
+(csa_index_topk, then csa_attend): scores, indices, outputs and lse must be
+bit-identical -- the selection made inside the attention launch is the
+top-k kernels' exact one, and the attention arithmetic is shared.  The
 cases cover rows that keep every visible entry, ragged positions per
 sequence, long rows, ties that fill the top-k's candidate lists, fp32 /
 bf16 / fp8 / MXFP4 indexer keys, the block compression of a
@@ -126,6 +128,15 @@ CASES = {
                  {"ki_kind": "fp8", "H": 64, "H_I": 64, "W": 128}),
     "mxfp4": (2, 1, 33000, [4 * 33000 - 1, 4 * 30000], 512, {"ki_kind": "mxfp4", "H_I": 16}),
     "k_ge_V": (3, 1, 600, [4 * 600 - 1, 300, 3], 1024, {}),
+    # rows past 8192 entries take the split top-k, whose selection is made
+    # inside the attention launch: rows that keep every visible entry, rows
+    # of one slice, ragged T = 2, fp32 at d = 64
+    "ragged_T2_long": (3, 2, 20000, [17, 4 * 20000 - 2, 9000], 512,
+                       {"H": 64, "H_I": 64, "W": 128}),
+    "f32_d64_long": (2, 1, 12000, [4 * 12000 - 1, 30000], 64,
+                     {"storage": "f32", "d": 64, "d_I": 64, "W": 32}),
+    "bf16_d64_long": (2, 1, 70000, [4 * 70000 - 1, 4 * 9000], 2048,
+                      {"d": 64, "d_I": 64, "H": 16, "W": 64}),
 }
 
 
@@ -142,6 +153,33 @@ def test_decode_matches_separate_calls(name):
         torch.cuda.synchronize()
         _same_all(got, ref, pos0, inp["m"], f"{name} call {call}")
     _check_oracle_topk(got[0], got[1], pos0, T, inp["m"], k)
+
+
+@pytest.mark.parametrize("name,hist_ready", [("long_rows", True), ("ragged_T2_long", True),
+                                              ("fp8_long", True), ("f32_d64_long", False),
+                                              ("short_rows_mixed", True)])
+def test_select_attend_matches_separate_calls(name, hist_ready):
+    """csa_select_attend after csa_index_scores (with or without the fused
+    histogram) against csa_topk + csa_attend; two calls on one top-k
+    workspace, whose histograms must come back to zero."""
+    B, T, n_cap, pos0, k, extra = CASES[name]
+    say("select_attend vs separate", name, hist_ready)
+    inp = _inputs(sum(map(ord, name)) + 11, B, T, n_cap, pos0, **extra)
+    ref = _separate(inp, k)
+    tws = csa.workspace(csa.csa_topk_workspace_size(B, T, n_cap, k), DEV)
+    for call in range(2):
+        sc = csa.csa_index_scores(inp["qi"], inp["w"], inp["ki"], inp["pos0"], inp["m"],
+                                  qi_scale=inp["qi_scale"], ki_scale=inp["ki_scale"],
+                                  topk_ws=tws if hist_ready else None, k=k)
+        idx, out, lse = csa.csa_select_attend(sc, tws, inp["pos0"], inp["m"], k, inp["q"],
+                                              inp["kc"], inp["vc"], inp["kr"], inp["vr"],
+                                              inp["raw_pos0"], inp["W"], inp["scale"],
+                                              hist_ready=hist_ready)
+        torch.cuda.synchronize()
+        _same_all((sc, idx, out, lse), ref, pos0, inp["m"], f"{name} call {call}")
+    if tws.numel():
+        hist = tws[:B * T * 4096 * 4].view(torch.int32)
+        assert int(hist.abs().sum()) == 0
 
 
 @pytest.mark.parametrize("n_keys,n_cap", [(1, 40000), (3, 40000), (2, 6000)])
