@@ -202,11 +202,18 @@ int csa_index_scores(const void* qi, int qi_dtype, const void* qi_scale,
  *   scores [B][T][n_cap] fp32 (only j < V(t) is read)
  *   idx    [B][T][k] int32
  *   ws     device workspace of csa_topk_workspace_size() bytes (top-k
- *          workspace protocol above; the size is 0, and ws may be NULL, when B*T is
- *          large enough for one workgroup per query row).
+ *          workspace protocol above).  For B*T <= 256 it is required.  For
+ *          more query rows (one workgroup per row) it is optional: it
+ *          holds per row a 2048-bin histogram of the scores' top 11 key
+ *          bits and a flag, which csa_index_scores writes when its
+ *          many-token kernel runs (BF16 / FP8, d_I = 128, T >= 8) and this
+ *          call uses instead of a histogram pass over the row; every flag
+ *          is cleared here, and csa_index_scores clears them when it
+ *          writes no histograms.
  *   hist_ready  1 if the directly preceding csa_index_scores was given
  *          this ws (and k) and so already built the first-digit
- *          histogram; 0 otherwise.
+ *          histogram; 0 otherwise (for more than 256 rows the flags
+ *          decide).
  * 1 <= k <= 4096.
  */
 size_t csa_topk_workspace_size(int64_t B, int64_t T, int64_t n_cap, int k);

@@ -237,6 +237,7 @@ int csa_index_scores(const void* qi, int qi_dtype, const void* qi_scale, const f
                             d_I, n_cap, m, act, scores, fn);
   if (rc) return rc;
   uint32_t* hist = nullptr;
+  csa::CoarseHist coarse{nullptr, nullptr};
   if (topk_ws) {
     CSA_REQUIRE(k >= 1 && k <= 4096, CSA_ERR_UNSUPPORTED, "%s: k must be in [1, 4096]", fn);
     const size_t need = csa_topk_workspace_size(B, T, n_cap, k);
@@ -244,12 +245,17 @@ int csa_index_scores(const void* qi, int qi_dtype, const void* qi_scale, const f
                 "%s: top-k workspace of %zu bytes needed, got %zu", fn, need, topk_ws_bytes);
     CSA_REQUIRE(aligned16(topk_ws), CSA_ERR_WORKSPACE, "%s: ws must be 16-byte aligned", fn);
     hist = need ? csa::topk_hist_ptr(topk_ws, B, T) : nullptr;
+    coarse = csa::topk_coarse_hist(topk_ws, B, T);
   }
   return hip_result(csa::launch_index_scores(qi, qi_dtype, qi_scale, w, ki, ki_scale, pos0, B, T,
                                              H_I, d_I, n_cap, m, act, scores, hist, k, nullptr,
-                                             static_cast<hipStream_t>(stream)),
+                                             static_cast<hipStream_t>(stream), &coarse),
                     fn);
 }
+
+// Top-k workspaces of more than kTopkSplitMaxRows query rows only carry the
+// prefill indexer's histograms: they may be omitted.
+static bool topk_ws_optional(int64_t B, int64_t T) { return B * T > csa::kTopkSplitMaxRows; }
 
 size_t csa_topk_workspace_size(int64_t B, int64_t T, int64_t n_cap, int k) {
   if (B < 1 || T < 1) return 0;
@@ -262,8 +268,9 @@ int csa_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, int
   int rc = check_topk_args(scores, pos0, B, T, n_cap, m, k, idx, fn);
   if (rc) return rc;
   const size_t need = csa_topk_workspace_size(B, T, n_cap, k);
-  CSA_REQUIRE(need == 0 || (ws && ws_bytes >= need), CSA_ERR_WORKSPACE,
-              "%s: workspace of %zu bytes needed, got %zu", fn, need, ws ? ws_bytes : 0);
+  CSA_REQUIRE(need == 0 || (ws && ws_bytes >= need) || (!ws && topk_ws_optional(B, T)),
+              CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, got %zu", fn, need,
+              ws ? ws_bytes : 0);
   CSA_REQUIRE(ws == nullptr || aligned16(ws), CSA_ERR_WORKSPACE, "%s: ws must be 16-byte aligned",
               fn);
   return hip_result(csa::launch_topk(scores, pos0, B, T, n_cap, m, k, idx, ws, hist_ready != 0,
@@ -286,8 +293,10 @@ int csa_index_topk(const void* qi, int qi_dtype, const void* qi_scale, const flo
   const char* fn = "csa_index_topk";
   const bool scores_in_ws = scores == nullptr;
   const size_t need = csa_index_topk_workspace_size(B, T, n_cap, k, scores_in_ws ? 1 : 0);
-  CSA_REQUIRE(need == 0 || (ws && ws_bytes >= need), CSA_ERR_WORKSPACE,
-              "%s: workspace of %zu bytes needed, got %zu", fn, need, ws ? ws_bytes : 0);
+  CSA_REQUIRE(need == 0 || (ws && ws_bytes >= need) ||
+                  (!ws && !scores_in_ws && topk_ws_optional(B, T)),
+              CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, got %zu", fn, need,
+              ws ? ws_bytes : 0);
   CSA_REQUIRE(ws == nullptr || aligned16(ws), CSA_ERR_WORKSPACE, "%s: ws must be 16-byte aligned",
               fn);
   float* sc = scores;
@@ -303,8 +312,10 @@ int csa_index_topk(const void* qi, int qi_dtype, const void* qi_scale, const flo
   if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint32_t* hist = csa::topk_hist_ptr(topk_ws, B, T);
+  const csa::CoarseHist coarse = csa::topk_coarse_hist(topk_ws, B, T);
   rc = hip_result(csa::launch_index_scores(qi, qi_dtype, qi_scale, w, ki, ki_scale, pos0, B, T,
-                                           H_I, d_I, n_cap, m, act, sc, hist, k, nullptr, s),
+                                           H_I, d_I, n_cap, m, act, sc, hist, k, nullptr, s,
+                                           &coarse),
                   fn);
   if (rc) return rc;
   return hip_result(csa::launch_topk(sc, pos0, B, T, n_cap, m, k, idx, topk_ws, hist != nullptr, s),
@@ -327,8 +338,10 @@ int csa_decode_index_topk(const void* qi, const float* w, void* kc, void* vc, co
   const int64_t T = 1;
   const bool scores_in_ws = scores == nullptr;
   const size_t need = csa_index_topk_workspace_size(B, T, n_cap, k, scores_in_ws ? 1 : 0);
-  CSA_REQUIRE(need == 0 || (ws && ws_bytes >= need), CSA_ERR_WORKSPACE,
-              "%s: workspace of %zu bytes needed, got %zu", fn, need, ws ? ws_bytes : 0);
+  CSA_REQUIRE(need == 0 || (ws && ws_bytes >= need) ||
+                  (!ws && !scores_in_ws && topk_ws_optional(B, T)),
+              CSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, got %zu", fn, need,
+              ws ? ws_bytes : 0);
   CSA_REQUIRE(ws == nullptr || aligned16(ws), CSA_ERR_WORKSPACE, "%s: ws must be 16-byte aligned",
               fn);
   float* sc = scores;
@@ -353,8 +366,9 @@ int csa_decode_index_topk(const void* qi, const float* w, void* kc, void* vc, co
   fc.R = R;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint32_t* hist = csa::topk_hist_ptr(topk_ws, B, T);
+  const csa::CoarseHist coarse = csa::topk_coarse_hist(topk_ws, B, T);
   rc = hip_result(csa::launch_index_scores(qi, CSA_BF16, nullptr, w, kc, nullptr, pos0, B, T, H_I,
-                                           d, n_cap, m, act, sc, hist, k, &fc, s),
+                                           d, n_cap, m, act, sc, hist, k, &fc, s, &coarse),
                   fn);
   if (rc) return rc;
   return hip_result(csa::launch_topk(sc, pos0, B, T, n_cap, m, k, idx, topk_ws, hist != nullptr, s),
@@ -515,9 +529,11 @@ static int decode_launch(const DecodeArgs& a, void* ws, hipStream_t s, const cha
     fc.R = a.R;
   }
   uint32_t* hist = csa::topk_hist_ptr(topk_ws, B, T);
+  const csa::CoarseHist coarse = csa::topk_coarse_hist(topk_ws, B, T);
   int rc = hip_result(csa::launch_index_scores(a.qi, a.qi_dtype, a.qi_scale, a.w, a.ki,
                                                a.ki_scale, a.pos0, B, T, a.H_I, a.d_I, n_cap, a.m,
-                                               a.act, sc, hist, a.k, compress ? &fc : nullptr, s),
+                                               a.act, sc, hist, a.k, compress ? &fc : nullptr, s,
+                                               &coarse),
                       fn);
   if (rc) return rc;
   return select_attend_launch(sc, topk_ws, hist != nullptr, a.pos0, a.m, a.k, a.q, a.kv_dtype,

@@ -452,12 +452,16 @@ constexpr int kPfThreads = 64 * kPfTok;
 // Score rows of the prefill path are addressed with 32-bit byte offsets.
 constexpr int64_t kPfMaxEntries = int64_t(1) << 28;
 
-template <int DTYPE, bool RELU>
+//
+// HIST: each wave also counts its token's scores into a 2048-bin histogram
+// of their top 11 key bits in LDS (one atomic per lane for every 4 column
+// tiles), then writes it whole to the top-k workspace with the row's flag.
+template <int DTYPE, bool RELU, bool HIST>
 __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
     const uint8_t* __restrict__ qi, const float* __restrict__ qi_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ ki,
     const float* __restrict__ ki_scale, const int64_t* __restrict__ pos0, int64_t T,
-    int H_I, int64_t n_cap, int m, float* __restrict__ scores) {
+    int H_I, int64_t n_cap, int m, float* __restrict__ scores, CoarseHist coarse) {
   constexpr int DI = 128;
   using Tr = IdxTraits<DTYPE, DI>;
   constexpr int kVec = Tr::kLaneBytes / 16;
@@ -466,6 +470,7 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
   constexpr int kLoads = kPfTile * RB / 16 / kPfThreads;  // 16-byte loads per thread per tile
   __shared__ __attribute__((aligned(16))) uint8_t bt[2][kPfTile * kStride];
   __shared__ float s_ksc[2][DTYPE == 2 ? kPfTile : 1];  // fp8 key scales of the staged tiles
+  __shared__ uint32_t s_hist[HIST ? kPfTok * kTopkCoarseBins : 1];  // per wave (token)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -485,6 +490,9 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
   const int64_t row = b * T + (tok_ok ? tok : 0);
   const int64_t Vt = uniform64(tok_ok ? visible_entries(p0 + tok, m, n_cap) : 0);
   const __amdgpu_buffer_rsrc_t srsrc = store_rsrc(scores + row * n_cap, static_cast<int>(Vt * 4));
+  uint32_t* my_hist = s_hist + (HIST ? wave * kTopkCoarseBins : 0);
+  if (HIST)  // (only this wave touches its token's bins: no barrier)
+    for (int i = lane; i < kTopkCoarseBins; i += 64) my_hist[i] = 0u;
   QueryFrags<DTYPE, DI> qf;
   qf.issue(qi, qi_scale, w, row, H_I, col, g);
   const auto& a = qf.a;
@@ -558,6 +566,7 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
   // store offsets: lane group ct % 4 writes column ct's 16 sums; the other
   // lanes' offsets start at 2^31, past the descriptor's range (the entry
   // part added to them stays below 2^30), so their stores are dropped
+  float x_own = 0.f;  // this lane group's column sum of the current group of 4 (HIST)
   uint32_t lane_off[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) lane_off[c] = g == c ? static_cast<uint32_t>(col) * 4u : 0x80000000u;
@@ -574,6 +583,13 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
     if (DTYPE == 2) x *= s_ksc[tile & 1][ct * 16 + col];
     const uint32_t off = lane_off[ct & 3] + static_cast<uint32_t>(tile * kPfTile + ct * 16) * 4u;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), srsrc, off, 0, 0);
+    if (HIST) {
+      // lane group g keeps the sum of column tile 4q + g; after every
+      // fourth column tile all 64 lanes count theirs in one LDS atomic
+      if (g == (ct & 3)) x_own = x;
+      if ((ct & 3) == 3 && tile * kPfTile + (ct - 3 + g) * 16 + col < Vt)
+        atomicAdd(&my_hist[score_key(x_own) >> kTopkCoarseShift], 1u);
+    }
   };
 
   using I0 = std::integral_constant<int, 0>;
@@ -583,6 +599,7 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
   // epilogue of each column tile runs under the next one's MFMAs (the last
   // column tile's under the next tile's first).
   static_assert(kPfCt % 2 == 0, "column tiles alternate two accumulator sets");
+  static_assert(kPfCt % 4 == 0, "histogram groups of 4 column tiles stay within a tile");
   auto do_tile = [&](auto buf, int t) __attribute__((always_inline)) {
     store_tile(buf);
     __syncthreads();
@@ -611,6 +628,11 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(
     ++t;
   }
   epi_ct(t - 1, kPfCt - 1, acc1);
+  if (HIST && tok_ok) {
+    uint32_t* gh = coarse.hist + row * kTopkCoarseBins;
+    for (int i = lane; i < kTopkCoarseBins; i += 64) gh[i] = my_hist[i];
+    if (lane == 0) coarse.flag[row] = 1u;
+  }
 }
 
 // Compute units of the current device (cached per device).
@@ -631,7 +653,7 @@ template <int DTYPE, int DI>
 static void launch_idx_t(const void* qi, const float* qs, const float* w, const void* ki,
                          const float* ks, const int64_t* pos0, int64_t B, int64_t T, int H_I,
                          int64_t n_cap, int m, bool relu, float* scores, uint32_t* hist, int k,
-                         const FusedCompress& fc, hipStream_t s) {
+                         const FusedCompress& fc, hipStream_t s, const CoarseHist* coarse) {
   // Chunk size: about one workgroup per compute unit over the whole grid
   // (measured best for this streaming kernel), in whole rounds of load
   // groups for the 4 waves, and no more than a row.
@@ -651,14 +673,22 @@ static void launch_idx_t(const void* qi, const float* qs, const float* w, const 
       n_cap <= kPfMaxEntries && fc.kr == nullptr) {
     constexpr int DT = DTYPE == 2 ? 2 : 1;
     dim3 pgrid(static_cast<unsigned>((T + kPfTok - 1) / kPfTok), static_cast<unsigned>(B));
-    if (relu)
-      indexer_prefill_kernel<DT, true><<<pgrid, kPfThreads, 0, s>>>(q8, qs, w, k8, ks, pos0, T,
-                                                                    H_I, n_cap, m, scores);
-    else
-      indexer_prefill_kernel<DT, false><<<pgrid, kPfThreads, 0, s>>>(q8, qs, w, k8, ks, pos0, T,
-                                                                     H_I, n_cap, m, scores);
+    const CoarseHist ch = coarse ? *coarse : CoarseHist{nullptr, nullptr};
+#define CSA_PF_GO(R, H)                                                                        \
+  indexer_prefill_kernel<DT, R, H><<<pgrid, kPfThreads, 0, s>>>(q8, qs, w, k8, ks, pos0, T, H_I, \
+                                                                n_cap, m, scores, ch)
+    if (ch.hist) {
+      if (relu) CSA_PF_GO(true, true); else CSA_PF_GO(false, true);
+    } else {
+      if (relu) CSA_PF_GO(true, false); else CSA_PF_GO(false, false);
+    }
+#undef CSA_PF_GO
     return;
   }
+  // no coarse histograms from this path: clear their flags, so the top-k
+  // reads its rows instead
+  if (coarse != nullptr && coarse->flag != nullptr)
+    launch_clear(coarse->flag, static_cast<size_t>(B * T) * sizeof(uint32_t), s);
   // (the fused block compression has kernels of its own, so the plain
   // decode kernels keep their register allocation)
 #define CSA_IDX_GO(R, HST)                                                                   \
@@ -682,7 +712,7 @@ int launch_index_scores(const void* qi, int dtype, const void* qs_v, const float
                         const void* ki, const void* ks_v, const int64_t* pos0, int64_t B,
                         int64_t T, int64_t H_I, int64_t d_I, int64_t n_cap, int m, int act,
                         float* scores, uint32_t* hist, int k, const FusedCompress* fc,
-                        hipStream_t s) {
+                        hipStream_t s, const CoarseHist* coarse) {
   const bool relu = act == 0;
   const FusedCompress none{};
   const FusedCompress& fcr = fc ? *fc : none;
@@ -693,7 +723,7 @@ int launch_index_scores(const void* qi, int dtype, const void* qs_v, const float
 #define CSA_IDX_CASE(DT, DI)                                                                  \
   if (dtype == DT && d_I == DI) {                                                             \
     launch_idx_t<DT, DI>(qi, qs, w, ki, ks, pos0, B, T, H, n_cap, m, relu, scores, hist, k,    \
-                         fcr, s);                                                             \
+                         fcr, s, coarse);                                                     \
     return hipGetLastError() == hipSuccess ? 0 : -1;                                          \
   }
   CSA_IDX_CASE(0, 64)

@@ -40,18 +40,31 @@ int launch_quantize_mxfp4_rows(const void* x, int dtype, int64_t rows, int64_t d
 constexpr int kTopkDigit1Shift = 20;
 constexpr int kTopkHistBins = 1 << (32 - kTopkDigit1Shift);
 
+// Coarse first-digit histograms of the many-row top-k (the top 11 key
+// bits, 2048 bins per row), each written whole by the prefill indexer
+// together with a per-row flag that the top-k clears after use.
+constexpr int kTopkCoarseShift = 21;
+constexpr int kTopkCoarseBins = 1 << (32 - kTopkCoarseShift);
+struct CoarseHist {
+  uint32_t* hist;  // [rows][kTopkCoarseBins]
+  uint32_t* flag;  // [rows]: 1 when hist holds this call's row
+};
+
 // hist (nullable): per-row first-digit histogram accumulated for csa_topk
-// (rows with V <= k are skipped).  It must be zero on entry.  qs / ks are
-// fp32 row scales (dtype 2, FP8) or E8M0 block-scale bytes (dtype 3, MXFP4).
-// fc (nullable): block compression fused into the launch (bf16, T == 1).
+// (rows with V <= k are skipped).  It must be zero on entry.  coarse
+// (nullable): the many-row histograms, written when the prefill kernel
+// runs.  qs / ks are fp32 row scales (dtype 2, FP8) or E8M0 block-scale
+// bytes (dtype 3, MXFP4).  fc (nullable): block compression fused into the
+// launch (bf16, T == 1).
 int launch_index_scores(const void* qi, int dtype, const void* qs, const float* w,
                         const void* ki, const void* ks, const int64_t* pos0, int64_t B,
                         int64_t T, int64_t H_I, int64_t d_I, int64_t n_cap, int m, int act,
                         float* scores, uint32_t* hist, int k, const FusedCompress* fc,
-                        hipStream_t s);
+                        hipStream_t s, const CoarseHist* coarse = nullptr);
 
 // Rows (B*T) up to this count use the multi-workgroup split top-k, which
-// needs a workspace; more rows use one workgroup per row and none.
+// needs a workspace; more rows use one workgroup per row, whose workspace
+// (optional) holds the coarse histograms.
 constexpr int64_t kTopkSplitMaxRows = 256;
 size_t topk_workspace_bytes(int64_t B, int64_t T, int64_t n_cap, int k);
 // The first-digit histogram inside a top-k workspace (nullptr when the row
@@ -60,6 +73,9 @@ uint32_t* topk_hist_ptr(void* ws, int64_t B, int64_t T);
 // Bytes at the start of a top-k workspace that must be zero on entry (the
 // histograms and counters; the rest is written before it is read).
 size_t topk_zero_state_bytes(int64_t B, int64_t T);
+// The coarse histograms inside a many-row top-k workspace ({nullptr,
+// nullptr} for B*T <= kTopkSplitMaxRows or no workspace).
+CoarseHist topk_coarse_hist(void* ws, int64_t B, int64_t T);
 int launch_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, int64_t n_cap,
                 int m, int k, int32_t* idx, void* ws, bool hist_ready, hipStream_t s);
 

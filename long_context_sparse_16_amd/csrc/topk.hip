@@ -174,12 +174,22 @@ constexpr int kRowRegs = 32;  // register-resident rows: V <= 32768 (1024 thread
 
 // hist_io (nullable): the rows' first-digit histograms built by the
 // indexer; used instead of a histogram pass and returned to zero.
-template <int REGS>
+// COARSE: the rows' 2048-bin histograms of the top 11 key bits from the
+// prefill indexer instead (each used when its flag says this call wrote it;
+// every flag is cleared).  The row is then classified against the coarse
+// bucket in its one pass, which also counts the bucket's upper half; that
+// count decides which half holds the k-th key, and the candidates in LDS
+// are narrowed to it (the upper half joining the sure entries when the cut
+// is in the lower one).  Should the coarse candidates overflow the LDS
+// list, the row is classified again against the exact 12-bit bucket.
+template <int REGS, bool COARSE>
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ pos0, int64_t T,
-    int64_t n_cap, int m, int k, int32_t* __restrict__ idx, uint32_t* __restrict__ hist_io) {
+    int64_t n_cap, int m, int k, int32_t* __restrict__ idx, uint32_t* __restrict__ hist_io,
+    CoarseHist coarse) {
   __shared__ FinishShared sm;
   constexpr int kHistPer = kHistBins / kRowThreads;
+  constexpr int kCoarsePer = kTopkCoarseBins / kRowThreads;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int64_t b = seq_of_row(row, T);
@@ -187,15 +197,25 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
   const int64_t V = uniform64(visible_entries(t, m, n_cap));
   int32_t* out = idx + row * k;
   if (V <= k) {
+    if (COARSE && tid == 0) coarse.flag[row] = 0u;
     write_iota(out, V, k);
     return;
   }
   const float* srow = scores + row * n_cap;
   uint32_t* h1 = sm.bitmap;  // first-digit histogram (the bitmap is used later)
-  uint32_t* gh = hist_io ? hist_io + row * kHistBins : nullptr;
+  uint32_t* gh = !COARSE && hist_io ? hist_io + row * kHistBins : nullptr;
+  // (all threads read the flag before thread 0 clears it, after the barrier)
+  const bool use_coarse = COARSE && coarse.flag[row] != 0u;
   uint32_t hv[kHistPer];
 #pragma unroll
-  for (int q = 0; q < kHistPer; ++q) hv[q] = gh ? gh[tid + q * kRowThreads] : 0u;
+  for (int q = 0; q < kHistPer; ++q) {
+    if (COARSE)
+      hv[q] = q < kCoarsePer && use_coarse
+                  ? coarse.hist[row * kTopkCoarseBins + tid + q * kRowThreads]
+                  : 0u;
+    else
+      hv[q] = gh ? gh[tid + q * kRowThreads] : 0u;
+  }
   float rv[REGS > 0 ? REGS : 1];
   if (REGS > 0) {
 #pragma unroll
@@ -208,7 +228,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
   for (int q = 0; q < kHistPer; ++q) h1[tid + q * kRowThreads] = hv[q];
   if (tid < 8) sm.misc[tid] = 0u;
   __syncthreads();
-  if (!gh) {
+  if (COARSE && tid == 0) coarse.flag[row] = 0u;
+  const bool have_hist = use_coarse || gh != nullptr;
+  if (!have_hist) {
     if (REGS > 0) {
 #pragma unroll
       for (int u = 0; u < REGS; ++u) {
@@ -231,82 +253,151 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
       }
     }
     __syncthreads();
-  } else {
+  } else if (gh) {
 #pragma unroll
     for (int q = 0; q < kHistPer; ++q) gh[tid + q * kRowThreads] = 0u;
   }
-  block_find_top<kRowThreads>(h1, kHistBins, static_cast<uint32_t>(k), sm.scan, sm.misc);
-  const uint32_t b1 = sm.misc[0];
-  const uint32_t above = sm.misc[1];
+  const int shift = use_coarse ? kTopkCoarseShift : kTopkDigit1Shift;
+  block_find_top<kRowThreads>(h1, use_coarse ? kTopkCoarseBins : kHistBins,
+                              static_cast<uint32_t>(k), sm.scan, sm.misc);
+  const uint32_t bk0 = sm.misc[0];
+  const uint32_t above0 = sm.misc[1];
   if (REGS > 0) {
 #pragma unroll
     for (int u = 0; u < REGS; ++u)
       if (tid + static_cast<int64_t>(u) * kRowThreads >= V) rv[u] = -INFINITY;
-    // The bucket test runs on the floats: bucket(v) > b1 iff v >= hi and
-    // bucket(v) == b1 iff lo <= v < hi, with lo / hi the smallest floats of
-    // buckets b1 and b1 + 1 (finite scores keep b1 in 8 .. 0xff7, so both
-    // are proper floats).  Slots past V hold -inf, below every bucket of a
-    // finite score.  Count, one packed prefix sum, then write at the
-    // thread's positions; only hits compute their key.  Packing: sure
-    // entries in the low 12 bits (fewer than k <= 4096 in the whole row),
-    // candidates above them (at most V <= 32768).
-    const float lo = key_floor_float(b1 << kTopkDigit1Shift);
-    const float hi = key_floor_float((b1 + 1u) << kTopkDigit1Shift);
-    uint32_t ns = 0, nc = 0;
+  }
+  // One classification of the row against bucket bk of the digit at
+  // `shift`: sure entries (higher buckets) to sm.sel, candidates to the LDS
+  // list; with count_up, also the candidates in the upper half of the
+  // bucket (misc[6]).
+  auto classify = [&](int sh, uint32_t bk, bool count_up) __attribute__((always_inline)) {
+    if (REGS > 0) {
+      // The bucket test runs on the floats: bucket(v) > bk iff v >= hi and
+      // bucket(v) == bk iff lo <= v < hi, with lo / hi the smallest floats
+      // of buckets bk and bk + 1 (finite scores keep both proper floats).
+      // Slots past V hold -inf, below every bucket of a finite score.
+      // Count, one packed prefix sum, then write at the thread's positions;
+      // only hits compute their key.  Packing: sure entries in the low 12
+      // bits (fewer than k <= 4096 in the whole row), candidates above them
+      // (at most V <= 32768).
+      const float lo = key_floor_float(bk << sh);
+      const float hi = key_floor_float((bk + 1u) << sh);
+      const float mid = key_floor_float(((2u * bk + 1u) << (sh - 1)));
+      uint32_t ns = 0, nc = 0, nup = 0;
 #pragma unroll
-    for (int u = 0; u < REGS; ++u) {
-      ns += rv[u] >= hi ? 1u : 0u;
-      nc += rv[u] >= lo ? 1u : 0u;
-    }
-    nc -= ns;
-    const uint32_t packed = block_excl_scan<kRowThreads>(ns | (nc << 12), sm.scan);
-    uint32_t ps = packed & 0xfffu, pcand = packed >> 12;
-    if (tid == kRowThreads - 1) sm.misc[5] = pcand + nc;  // total candidates
+      for (int u = 0; u < REGS; ++u) {
+        ns += rv[u] >= hi ? 1u : 0u;
+        nc += rv[u] >= lo ? 1u : 0u;
+        nup += rv[u] >= mid ? 1u : 0u;
+      }
+      nup -= ns;
+      nc -= ns;
+      if (count_up) {
+        for (int o = 1; o < 64; o <<= 1) nup += __shfl_xor(nup, o);
+        if ((tid & 63) == 0) atomicAdd(&sm.misc[6], nup);
+      }
+      const uint32_t packed = block_excl_scan<kRowThreads>(ns | (nc << 12), sm.scan);
+      uint32_t ps = packed & 0xfffu, pcand = packed >> 12;
+      if (tid == kRowThreads - 1) sm.misc[5] = pcand + nc;  // total candidates
 #pragma unroll
-    for (int u = 0; u < REGS; ++u) {
-      if (rv[u] >= lo) {
-        const int32_t j = tid + u * kRowThreads;
-        if (rv[u] >= hi) {
-          if (ps < static_cast<uint32_t>(kMaxK)) sm.sel[ps] = j;
-          ++ps;
-        } else {
-          if (pcand < static_cast<uint32_t>(kCandCap)) {
-            sm.ckey[pcand] = score_key(rv[u]);
-            sm.cidx[pcand] = j;
+      for (int u = 0; u < REGS; ++u) {
+        if (rv[u] >= lo) {
+          const int32_t j = tid + u * kRowThreads;
+          if (rv[u] >= hi) {
+            if (ps < static_cast<uint32_t>(kMaxK)) sm.sel[ps] = j;
+            ++ps;
+          } else {
+            if (pcand < static_cast<uint32_t>(kCandCap)) {
+              sm.ckey[pcand] = score_key(rv[u]);
+              sm.cidx[pcand] = j;
+            }
+            ++pcand;
           }
-          ++pcand;
+        }
+      }
+      if (tid == kRowThreads - 1) sm.misc[4] = ps;  // sure entries (== above)
+    } else {
+      for (int64_t base = 0; base < V; base += static_cast<int64_t>(kRowThreads) * kRowBatch) {
+        float v[kRowBatch];
+#pragma unroll
+        for (int u = 0; u < kRowBatch; ++u) {
+          const int64_t j = base + tid + static_cast<int64_t>(u) * kRowThreads;
+          v[u] = srow[j < V ? j : V - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < kRowBatch; ++u) {
+          const int64_t j = base + tid + static_cast<int64_t>(u) * kRowThreads;
+          const uint32_t key = score_key(v[u]);
+          const uint32_t bq = key >> sh;
+          if (j < V && bq > bk) {
+            const uint32_t p = atomicAdd(&sm.misc[4], 1u);
+            if (p < kMaxK) sm.sel[p] = static_cast<int32_t>(j);
+          } else if (j < V && bq == bk) {
+            const uint32_t p = atomicAdd(&sm.misc[5], 1u);
+            if (p < kCandCap) {
+              sm.ckey[p] = key;
+              sm.cidx[p] = static_cast<int32_t>(j);
+            }
+            if (count_up && ((key >> (sh - 1)) & 1u)) atomicAdd(&sm.misc[6], 1u);
+          }
         }
       }
     }
-    if (tid == kRowThreads - 1) sm.misc[4] = ps;  // sure entries (== above)
-  } else {
-    for (int64_t base = 0; base < V; base += static_cast<int64_t>(kRowThreads) * kRowBatch) {
-      float v[kRowBatch];
+    __syncthreads();
+  };
+  classify(shift, bk0, use_coarse);
+  uint32_t b1 = bk0, above = above0;
+  uint32_t nc = sm.misc[5];
+  if (use_coarse) {
+    // the exact 12-bit bucket: the upper half of the coarse one when it
+    // holds the k-th key
+    const uint32_t n_up = sm.misc[6];
+    const bool up = above0 + n_up >= static_cast<uint32_t>(k);
+    b1 = 2u * bk0 + (up ? 1u : 0u);
+    above = up ? above0 : above0 + n_up;
+    if (nc <= static_cast<uint32_t>(kCandCap)) {
+      // narrow the LDS candidates to bucket b1 (in place: every thread
+      // reads its run, then the barrier, then the kept ones are written
+      // at their compacted positions); the other half is dropped or, when
+      // the cut lies in the lower half, joins the sure entries
+      constexpr int kRun = kCandCap / kRowThreads;
+      const uint32_t c0 = min(nc, static_cast<uint32_t>(tid * kRun));
+      const uint32_t c1 = min(nc, c0 + kRun);
+      uint32_t rk[kRun];
+      int32_t rj[kRun];
+      uint32_t kept = 0;
 #pragma unroll
-      for (int u = 0; u < kRowBatch; ++u) {
-        const int64_t j = base + tid + static_cast<int64_t>(u) * kRowThreads;
-        v[u] = srow[j < V ? j : V - 1];
+      for (int u = 0; u < kRun; ++u) {
+        const uint32_t i = c0 + u;
+        rk[u] = i < c1 ? sm.ckey[i] : 0u;
+        rj[u] = i < c1 ? sm.cidx[i] : 0;
+        kept += i < c1 && (rk[u] >> kTopkDigit1Shift) == b1 ? 1u : 0u;
       }
+      uint32_t pos = block_excl_scan<kRowThreads>(kept, sm.scan);
+      if (tid == kRowThreads - 1) sm.misc[5] = pos + kept;
 #pragma unroll
-      for (int u = 0; u < kRowBatch; ++u) {
-        const int64_t j = base + tid + static_cast<int64_t>(u) * kRowThreads;
-        const uint32_t key = score_key(v[u]);
-        const uint32_t bk = key >> kTopkDigit1Shift;
-        if (j < V && bk > b1) {
+      for (int u = 0; u < kRun; ++u) {
+        if (c0 + u >= c1) continue;
+        if ((rk[u] >> kTopkDigit1Shift) == b1) {
+          sm.ckey[pos] = rk[u];
+          sm.cidx[pos] = rj[u];
+          ++pos;
+        } else if (!up) {
           const uint32_t p = atomicAdd(&sm.misc[4], 1u);
-          if (p < kMaxK) sm.sel[p] = static_cast<int32_t>(j);
-        } else if (j < V && bk == b1) {
-          const uint32_t p = atomicAdd(&sm.misc[5], 1u);
-          if (p < kCandCap) {
-            sm.ckey[p] = key;
-            sm.cidx[p] = static_cast<int32_t>(j);
-          }
+          if (p < kMaxK) sm.sel[p] = rj[u];
         }
       }
+      __syncthreads();
+      nc = sm.misc[5];
+    } else {
+      // the coarse candidates did not fit: classify again, exactly
+      if (tid < 8) sm.misc[tid] = 0u;
+      __syncthreads();
+      classify(kTopkDigit1Shift, b1, false);
+      nc = sm.misc[5];
     }
   }
-  __syncthreads();
-  const uint32_t nc = sm.misc[5];
   finish_row<kRowThreads>(sm, srow, V, b1, static_cast<uint32_t>(k) - above, nc, k, out);
 }
 
@@ -726,14 +817,25 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p
 size_t topk_workspace_bytes(int64_t B, int64_t T, int64_t n_cap, int k) {
   (void)k;
   const int64_t rows = B * T;
-  return rows <= kTopkSplitMaxRows ? split_ws_bytes(rows, n_cap) : 0;
+  return rows <= kTopkSplitMaxRows
+             ? split_ws_bytes(rows, n_cap)
+             : static_cast<size_t>(rows) * (kTopkCoarseBins + 1) * sizeof(uint32_t);
+}
+
+CoarseHist topk_coarse_hist(void* ws, int64_t B, int64_t T) {
+  const int64_t rows = B * T;
+  if (rows <= kTopkSplitMaxRows || ws == nullptr) return CoarseHist{nullptr, nullptr};
+  uint32_t* h = static_cast<uint32_t*>(ws);
+  return CoarseHist{h, h + rows * kTopkCoarseBins};
 }
 
 size_t topk_zero_state_bytes(int64_t B, int64_t T) {
-  // hist then ctrl lead the split workspace
+  // hist then ctrl lead the split workspace; the many-row one ends with the
+  // coarse histograms' flags
   const int64_t rows = B * T;
-  return rows <= kTopkSplitMaxRows ? static_cast<size_t>(rows) * (kHistBins + 4) * sizeof(uint32_t)
-                                   : 0;
+  return rows <= kTopkSplitMaxRows
+             ? static_cast<size_t>(rows) * (kHistBins + 4) * sizeof(uint32_t)
+             : static_cast<size_t>(rows) * (kTopkCoarseBins + 1) * sizeof(uint32_t);
 }
 
 uint32_t* topk_hist_ptr(void* ws, int64_t B, int64_t T) {
@@ -743,13 +845,18 @@ uint32_t* topk_hist_ptr(void* ws, int64_t B, int64_t T) {
 
 // One workgroup per row; rows that fit are held in registers.
 static void launch_row_kernel(const float* scores, const int64_t* pos0, int64_t T, int64_t n_cap,
-                              int m, int k, int32_t* idx, uint32_t* hist, int64_t rows,
-                              hipStream_t s) {
+                              int m, int k, int32_t* idx, uint32_t* hist, const CoarseHist& ch,
+                              int64_t rows, hipStream_t s) {
   const unsigned g = static_cast<unsigned>(rows);
-  if (n_cap <= static_cast<int64_t>(kRowThreads) * kRowRegs)
-    topk_row_kernel<kRowRegs><<<g, kRowThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, idx, hist);
-  else
-    topk_row_kernel<0><<<g, kRowThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, idx, hist);
+  const bool regs = n_cap <= static_cast<int64_t>(kRowThreads) * kRowRegs;
+#define CSA_ROW_GO(R, C) \
+  topk_row_kernel<R, C><<<g, kRowThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, idx, hist, ch)
+  if (ch.flag) {
+    if (regs) CSA_ROW_GO(kRowRegs, true); else CSA_ROW_GO(0, true);
+  } else {
+    if (regs) CSA_ROW_GO(kRowRegs, false); else CSA_ROW_GO(0, false);
+  }
+#undef CSA_ROW_GO
 }
 
 int launch_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, int64_t n_cap,
@@ -766,9 +873,10 @@ int launch_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, 
     topk_finish_kernel<<<static_cast<unsigned>(rows), kFinThreads, 0, s>>>(scores, pos0, T, n_cap,
                                                                            m, k, w, idx);
   } else {
-    // one workgroup per row, using the indexer's histogram when it built one
+    // one workgroup per row, using the indexer's histogram when it built
+    // one (the coarse ones are checked, and their flags cleared, per row)
     uint32_t* h = rows <= kTopkSplitMaxRows && hist_ready ? static_cast<uint32_t*>(ws) : nullptr;
-    launch_row_kernel(scores, pos0, T, n_cap, m, k, idx, h, rows, s);
+    launch_row_kernel(scores, pos0, T, n_cap, m, k, idx, h, topk_coarse_hist(ws, B, T), rows, s);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

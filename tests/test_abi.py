@@ -107,8 +107,11 @@ def test_topk_validation_and_workspace():
     assert lib.csa_topk(FAKE, FAKE, 32, 1, 32768, 4, 1024, FAKE, NULL, 0, 0, NULL) == -5
     assert lib.csa_topk(FAKE, FAKE, 32, 1, 32768, 4, 1024, FAKE, FAKE, need - 1, 0, NULL) == -5
     assert "workspace" in _last()
-    # many rows use one workgroup per row and need no workspace
-    assert lib.csa_topk_workspace_size(1, 8192, 67584, 1024) == 0
+    # many rows use one workgroup per row: the workspace (the prefill
+    # indexer's coarse histograms and their flags) is optional
+    many = lib.csa_topk_workspace_size(1, 8192, 67584, 1024)
+    assert many >= 8192 * (2048 + 1) * 4
+    assert lib.csa_topk(FAKE, FAKE, 1, 8192, 67584, 4, 1024, FAKE, FAKE, many - 1, 0, NULL) == -5
     with_scores = lib.csa_index_topk_workspace_size(32, 1, 32768, 1024, 1)
     assert with_scores >= need + 32 * 32768 * 4
 
