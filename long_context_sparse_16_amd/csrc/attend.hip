@@ -84,6 +84,7 @@ struct AttParams {
   int64_t T, H, n_cap, R;
   int k, W, m;
   int splits, chunks_per_split;
+  int64_t xcd_rows;  // > 0: 1-D grid in XCD row order (xcd_row_item), else (splits, rows)
   float scale_log2;  // scale * log2(e)
   TopkLists sel;     // the selection's lists (SEL variant)
 };
@@ -414,8 +415,14 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttParams p) {
   const int kh = wave >> 2;  // key half of every chunk
   const int col = lane & 15;
   const int g = lane >> 4;
-  const int64_t row = blockIdx.y;
-  const int split = blockIdx.x;
+  int64_t row;
+  int split;
+  if (p.xcd_rows > 0) {  // a row's splits on one XCD (shared q, lists)
+    if (!xcd_row_item(blockIdx.x, p.splits, p.xcd_rows, &row, &split)) return;
+  } else {
+    row = blockIdx.y;
+    split = blockIdx.x;
+  }
   const int64_t b = seq_of_row(row, p.T);
   // both position loads are unconditional, so they are in flight together
   // (raw_pos0 may be NULL when W == 0; its value is then unused)
@@ -889,7 +896,9 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
     p.pm = base + rows * sp.splits * H * D;
     p.pl = p.pm + rows * sp.splits * H;
   }
-  dim3 grid(static_cast<unsigned>(sp.splits), static_cast<unsigned>(rows));
+  p.xcd_rows = xcd_mappable(rows) ? rows : 0;
+  const dim3 grid = p.xcd_rows ? dim3(static_cast<unsigned>(xcd_grid_size(rows, sp.splits)))
+                               : dim3(static_cast<unsigned>(sp.splits), static_cast<unsigned>(rows));
   const dim3 mgrid(static_cast<unsigned>((H + kMergeThreads / (D / 4) - 1) / (kMergeThreads / (D / 4))),
                    static_cast<unsigned>(rows));
 #define CSA_ATT_CASE(DT, DD)                                                        \

@@ -173,6 +173,27 @@ __device__ __forceinline__ int64_t seq_of_row(int64_t row, int64_t T) {
       static_cast<int>(static_cast<uint32_t>(row) / static_cast<uint32_t>(T)));
 }
 
+// Grids of `items` workgroups for each of `rows` rows whose workgroups share
+// per-row data (a query row, a histogram, lists): the hardware hands
+// consecutive workgroups to the 8 XCDs in turn, so with a 1-D grid of
+// xcd_grid_size() workgroups, workgroup id goes to row id % 8 + 8 (id / 8 /
+// items) and item id / 8 % items, which keeps all of a row's workgroups on
+// one XCD and its shared data in one L2.  Used for rows >= 8 (xcd_mappable;
+// with fewer rows, measured no better than the 2-D grid); xcd_row_item
+// returns false for the padding workgroups.
+constexpr int kXcds = 8;
+inline bool xcd_mappable(int64_t rows) { return rows >= kXcds; }
+inline int64_t xcd_grid_size(int64_t rows, int64_t items) {
+  return kXcds * ((rows + kXcds - 1) / kXcds) * items;
+}
+__device__ __forceinline__ bool xcd_row_item(int64_t id, int items, int64_t rows, int64_t* row,
+                                             int* item) {
+  const int64_t k = id / kXcds;
+  *row = (id % kXcds) + kXcds * (k / items);
+  *item = static_cast<int>(k % items);
+  return *row < rows;
+}
+
 // A wave-uniform 64-bit value moved to scalar registers (so loop bounds and
 // addresses derived from it stay scalar).
 __device__ __forceinline__ int64_t uniform64(int64_t x) {

@@ -504,10 +504,11 @@ struct ClassifyShared {
   uint32_t tab[kSelPer * kSelWaves];  // (pass, wave) counts, sure | cand << 16
 };
 
-// Classify slice blockIdx.x of row `row` (entries [j0, j1), j0 < V, V > k):
-// writes the slice's lists and counts and returns the bucket b1.
+// Classify slice sl of row `row` (entries [j0, j1), j0 < V, V > k): writes
+// the slice's lists and counts and returns the bucket b1.
 __device__ uint32_t classify_slice(ClassifyShared& cs, const float* __restrict__ srow,
-                                   int64_t row, int64_t j0, int64_t j1, int k, SplitWs ws) {
+                                   int64_t row, int sl, int64_t j0, int64_t j1, int k,
+                                   SplitWs ws) {
   uint32_t* scan = cs.scan;
   uint32_t* res = cs.res;
   uint32_t* tab = cs.tab;
@@ -569,17 +570,17 @@ __device__ uint32_t classify_slice(ClassifyShared& cs, const float* __restrict__
     }
     tab[lane] = x - c;
     if (lane == 63) {
-      const int64_t slot = row * ws.n_sl + blockIdx.x;
+      const int64_t slot = row * ws.n_sl + sl;
       ws.cnt[slot * 2] = x & 0xffffu;
       ws.cnt[slot * 2 + 1] = x >> 16;
-      if (blockIdx.x == 0) {
+      if (sl == 0) {
         ws.ctrl[row * 4] = b1;
         ws.ctrl[row * 4 + 1] = res[1];
       }
     }
   }
   __syncthreads();
-  const int64_t slot = row * ws.n_sl + blockIdx.x;
+  const int64_t slot = row * ws.n_sl + sl;
   int32_t* gi = ws.lidx + slot * kSelEntries;
   uint32_t* gk = ws.lkey + slot * kSelEntries;
 #pragma unroll
@@ -597,17 +598,36 @@ __device__ uint32_t classify_slice(ClassifyShared& cs, const float* __restrict__
   return b1;
 }
 
+// xcd_rows > 0: a 1-D grid in XCD row order (the slices of a row share its
+// histogram in one L2); else the grid is (slices, rows).
 __global__ __launch_bounds__(kSelThreads) void topk_classify_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ pos0, int64_t T,
-    int64_t n_cap, int m, int k, SplitWs ws) {
+    int64_t n_cap, int m, int k, SplitWs ws, int64_t xcd_rows) {
   __shared__ ClassifyShared cs;
-  const int64_t row = blockIdx.y;
+  int64_t row;
+  int sl;
+  if (xcd_rows > 0) {
+    if (!xcd_row_item(blockIdx.x, static_cast<int>(ws.n_sl), xcd_rows, &row, &sl)) return;
+  } else {
+    row = blockIdx.y;
+    sl = blockIdx.x;
+  }
   const int64_t b = seq_of_row(row, T);
   const int64_t t = pos0[b] + (row - b * T);
   const int64_t V = uniform64(visible_entries(t, m, n_cap));
-  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kSelEntries;
+  const int64_t j0 = static_cast<int64_t>(sl) * kSelEntries;
   if (V <= k || j0 >= V) return;
-  classify_slice(cs, scores + row * n_cap, row, j0, min(V, j0 + kSelEntries), k, ws);
+  classify_slice(cs, scores + row * n_cap, row, sl, j0, min(V, j0 + kSelEntries), k, ws);
+}
+
+static void launch_classify(const float* scores, const int64_t* pos0, int64_t T, int64_t n_cap,
+                            int m, int k, const SplitWs& w, int64_t rows, hipStream_t s) {
+  if (xcd_mappable(rows))
+    topk_classify_kernel<<<dim3(static_cast<unsigned>(xcd_grid_size(rows, w.n_sl))), kSelThreads,
+                           0, s>>>(scores, pos0, T, n_cap, m, k, w, rows);
+  else
+    topk_classify_kernel<<<dim3(static_cast<unsigned>(w.n_sl), static_cast<unsigned>(rows)),
+                           kSelThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, w, 0);
 }
 
 // Resolve one row from its slices' lists and return its histogram and
@@ -869,7 +889,7 @@ int launch_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, 
     SplitWs w = split_ws(ws, rows, n_cap);
     dim3 grid(static_cast<unsigned>(w.n_sl), static_cast<unsigned>(rows));
     if (!hist_ready) topk_hist_kernel<<<grid, kSelThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, w);
-    topk_classify_kernel<<<grid, kSelThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, w);
+    launch_classify(scores, pos0, T, n_cap, m, k, w, rows, s);
     topk_finish_kernel<<<static_cast<unsigned>(rows), kFinThreads, 0, s>>>(scores, pos0, T, n_cap,
                                                                            m, k, w, idx);
   } else {
@@ -891,7 +911,7 @@ int launch_topk_lists(const float* scores, const int64_t* pos0, int64_t B, int64
   SplitWs w = split_ws(ws, rows, n_cap);
   dim3 grid(static_cast<unsigned>(w.n_sl), static_cast<unsigned>(rows));
   if (!hist_ready) topk_hist_kernel<<<grid, kSelThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, w);
-  topk_classify_kernel<<<grid, kSelThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, w);
+  launch_classify(scores, pos0, T, n_cap, m, k, w, rows, s);
   lists->cnt = w.cnt;
   lists->lidx = w.lidx;
   lists->lkey = w.lkey;
