@@ -445,8 +445,11 @@ def measure(cfg, K, W, timer, torch):
     if cfg.backward:
         fl = backward_flops(cfg)
         t_us = st_stats["backward"]["mean"]
+        # bf16 storage: the products run on the bf16 MFMA (fp32 operands as
+        # bf16 hi + lo pairs); fp32 storage: on the fp32 MFMA
+        pk = "bf16" if cfg.storage == "bf16" else "f32"
         roof = {"kernel": "attend_bwd (rows + reductions)", "bound": "mfma",
-                "achieved": fl / (t_us * 1e6), "peak": MFMA_PEAK_TFLOPS["f32"],
+                "achieved": fl / (t_us * 1e6), "peak": MFMA_PEAK_TFLOPS[pk],
                 "unit": "TFLOP/s", "traffic": None, "algorithmic_flops": fl}
     elif cfg.layers:
         i = next(i for i, k in enumerate(cfg.layers) if k == "csa")

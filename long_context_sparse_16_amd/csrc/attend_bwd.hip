@@ -19,8 +19,11 @@
 // sums their contributions in ascending row order.  Every result is
 // bitwise reproducible.
 //
-// Arithmetic: fp32 throughout (bf16 inputs are exact in fp32), on the
-// 16x16x4 fp32 MFMA.
+// Arithmetic: fp32 storage on the 16x16x4 fp32 MFMA; bf16 storage on the
+// 16x16x32 bf16 MFMA, the fp32 operands (dout, P, dS) as bf16 hi + lo pairs
+// (attend_bwd_rows_bf16_kernel).  Accumulation is fp32 either way.  The
+// per-row contributions (B*T x slots x d x 8 bytes; 9.7 GB for 8192 query
+// rows of 1152 slots at d = 128) are the dominant HBM traffic.
 #include "common.h"
 #include "kernels.h"
 
@@ -370,6 +373,323 @@ __global__ __launch_bounds__(kBwdThreads) void attend_bwd_rows_kernel(BwdParams 
   }
 }
 
+// bf16 storage: every product on the 16x16x32 bf16 MFMA.  q, K and V are
+// bf16 values; the fp32 operands (dout, and the probabilities P and score
+// gradients dS formed here) enter as two bf16 values hi + lo (hi the
+// rounded value, lo the rounded remainder: 16 significant bits, relative
+// error <= 2^-17), so x y = hi_x y + lo_x y for a bf16 y and x y ~ hi_x hi_y
+// + hi_x lo_y + lo_x hi_y for two such operands; accumulation is fp32.
+// Per 32-key chunk:
+//   phase A (wave = head tile ht x dim half dh): S^T = K q^T and dP^T =
+//     V dout^T for both 16-key tiles (each head tile's two waves compute
+//     them alike), P, dS, and dq^T = K^T dS for the wave's half of the
+//     dims (K^T through the LDS transpose read, keys in the order of the
+//     lane's P / dS registers); the dh = 0 waves store P and dS (hi, lo) in
+//     LDS as [key][head];
+//   phase B (wave = one 16-dim tile): dK^T = q^T dS and dV^T = dout^T P
+//     over all heads, written to the staging buffer as the fp32 kernel
+//     does, so the same reductions follow.
+template <int D, bool HCA>
+__global__ __launch_bounds__(kBwdThreads) void attend_bwd_rows_bf16_kernel(BwdParams p) {
+  constexpr int NT = kBwdThreads;
+  constexpr int RB = D * 2;            // bytes of a bf16 row
+  constexpr int kPieces = RB / 16;     // 16-byte pieces per row
+  constexpr int kSteps = D / 32;       // MFMA k-steps over the dims
+  constexpr int kSpan = D / 4;         // dims of one lane group (kSteps x 8)
+  constexpr int kDT = D / 16;          // dim tiles
+  constexpr int kHalfDT = kDT / 2;     // dim tiles of a phase A wave
+  constexpr int kRs = RB + 32;         // K / V LDS row stride (bytes)
+  constexpr int kHp = kBwdHeads + 8;   // [x][head] bf16 LDS row stride (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t sQt[D][kHp];   // q^T
+  __shared__ __attribute__((aligned(16))) uint16_t sOtH[D][kHp];  // dout^T, hi
+  __shared__ __attribute__((aligned(16))) uint16_t sOtL[D][kHp];  // dout^T, lo
+  __shared__ __attribute__((aligned(16))) uint8_t sK[kBwdChunk * kRs];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[kBwdChunk * kRs];
+  __shared__ __attribute__((aligned(16))) uint16_t sPH[kBwdChunk][kHp];
+  __shared__ __attribute__((aligned(16))) uint16_t sPL[kBwdChunk][kHp];
+  __shared__ __attribute__((aligned(16))) uint16_t sSH[kBwdChunk][kHp];
+  __shared__ __attribute__((aligned(16))) uint16_t sSL[kBwdChunk][kHp];
+  __shared__ float sD[kBwdHeads];
+  __shared__ int s_valid[kBwdChunk];
+  __shared__ int s_gslot[kBwdChunk];
+  __shared__ int32_t s_ent[HCA ? 1 : kBwdMaxK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int64_t row = blockIdx.x;
+  const int64_t b = seq_of_row(row, p.T);
+  const int64_t t = p.pos0[b] + (row - b * p.T);
+  const int64_t rp0 = (p.W > 0 ? p.raw_pos0 : p.pos0)[b];
+  const int64_t n_ent =
+      HCA ? uniform64(visible_entries(t, p.m, p.n_cap)) : static_cast<int64_t>(p.k);
+  const int64_t n_slots = n_ent + p.W;
+  const int64_t H = p.H;
+  auto split = [](float x, uint16_t& hi, uint16_t& lo) __attribute__((always_inline)) {
+    hi = f32_to_bf16(x);
+    lo = f32_to_bf16(x - bf16_to_f32(hi));
+  };
+
+  // q^T and dout^T (hi, lo) of all heads in LDS; head slots past H hold
+  // zeros (their probabilities and gradients are zero: lse = +inf below)
+  for (int i = tid; i < kBwdHeads * kPieces; i += NT) {
+    const int h = i / kPieces, pc = i % kPieces;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (h < H) v = *reinterpret_cast<const u32x4*>(p.q + ((row * H + h) * D + pc * 8) * 2);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sQt[pc * 8 + 2 * e][h] = static_cast<uint16_t>(v[e] & 0xffffu);
+      sQt[pc * 8 + 2 * e + 1][h] = static_cast<uint16_t>(v[e] >> 16);
+    }
+  }
+  for (int i = tid; i < kBwdHeads * (D / 4); i += NT) {
+    const int h = i / (D / 4), c4 = i % (D / 4);
+    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (h < H) v = *reinterpret_cast<const f32x4*>(p.dout + (row * H + h) * D + c4 * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split(v[e], sOtH[c4 * 4 + e][h], sOtL[c4 * 4 + e][h]);
+  }
+  // D[h] = dout . o: eight threads per head, an eighth of the dims each
+  {
+    static_assert(NT == 8 * kBwdHeads, "eight threads per head slot");
+    const int h = tid >> 3, qd = tid & 7;
+    float acc = 0.f;
+    if (h < H) {
+      const float* orow = p.out + (row * H + h) * D + qd * (D / 8);
+      const float* grow = p.dout + (row * H + h) * D + qd * (D / 8);
+      for (int c = 0; c < D / 8; ++c) acc = fmaf(grow[c], orow[c], acc);
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    if (qd == 0) sD[h] = acc;
+  }
+  // phase A roles
+  const int ht = wave & 3;
+  const int dh = wave >> 2;
+  const int head = ht * 16 + col;
+  const float lse2 = head < H ? p.lse[row * H + head] * kLog2eBwd : INFINITY;
+  const float scale_log2 = p.scale * kLog2eBwd;
+  // this lane's B operands of S^T and dP^T: its head's q and dout (hi, lo)
+  // at dims g kSpan + 8 st .. + 8 (the K / V A operands use the same dims)
+  bf16x8 qf[kSteps], ofh[kSteps], ofl[kSteps];
+  {
+    const int64_t hq = head < H ? head : 0;
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      const int d0 = g * kSpan + st * 8;
+      u32x4 v = *reinterpret_cast<const u32x4*>(p.q + ((row * H + hq) * D + d0) * 2);
+      if (head >= H) v = u32x4{0u, 0u, 0u, 0u};
+      qf[st] = __builtin_bit_cast(bf16x8, v);
+      const float* dr = p.dout + (row * H + hq) * D + d0;
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(dr);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(dr + 4);
+      uint16_t h8[8], l8[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        split(head < H ? x0[e] : 0.f, h8[e], l8[e]);
+        split(head < H ? x1[e] : 0.f, h8[4 + e], l8[4 + e]);
+      }
+      u32x4 ph, pl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ph[e] = static_cast<uint32_t>(h8[2 * e]) | (static_cast<uint32_t>(h8[2 * e + 1]) << 16);
+        pl[e] = static_cast<uint32_t>(l8[2 * e]) | (static_cast<uint32_t>(l8[2 * e + 1]) << 16);
+      }
+      ofh[st] = __builtin_bit_cast(bf16x8, ph);
+      ofl[st] = __builtin_bit_cast(bf16x8, pl);
+    }
+  }
+
+  f32x4 dq[kHalfDT];
+#pragma unroll
+  for (int i = 0; i < kHalfDT; ++i) dq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint8_t* kc_b = p.kc + b * p.n_cap * RB;
+  const uint8_t* vc_b = p.vc + b * p.n_cap * RB;
+  const int n_chunks = static_cast<int>((n_slots + kBwdChunk - 1) / kBwdChunk);
+  if (!HCA)
+    for (int i = tid; i < p.k; i += NT) s_ent[i] = p.idx[row * p.k + i];
+  __syncthreads();
+  const float Dh = sD[head];
+
+  // Slot s of the key list -> its K / V rows (absent keys: row 0, masked)
+  auto slot_rows = [&](int64_t s, const uint8_t*& ksrc, const uint8_t*& vsrc,
+                       int& ok) __attribute__((always_inline)) {
+    ksrc = kc_b;
+    vsrc = vc_b;
+    ok = 0;
+    if (s < n_ent) {
+      const int64_t e = HCA ? s : static_cast<int64_t>(s_ent[s]);
+      if (e >= 0 && e < p.n_cap) {
+        ksrc = kc_b + e * RB;
+        vsrc = vc_b + e * RB;
+        ok = 1;
+      }
+    } else if (s < n_slots) {
+      const int64_t pos = t - p.W + 1 + (s - n_ent);
+      const int64_t rr = pos - rp0;
+      if (pos >= 0 && rr >= 0 && rr < p.R) {
+        ksrc = p.kr + (b * p.R + rr) * RB;
+        vsrc = p.vr + (b * p.R + rr) * RB;
+        ok = 1;
+      }
+    }
+  };
+  // the next chunk's rows are loaded into registers while a chunk is
+  // computed: piece i = tid + NT u is row i / kPieces, 16 bytes at i %
+  // kPieces (d = 64: the upper half of the threads repeats the lower's)
+  constexpr int kChunkPieces = kBwdChunk * kPieces;
+  constexpr int kIters = (kChunkPieces + NT - 1) / NT;
+  static_assert(kChunkPieces % NT == 0 || NT % kChunkPieces == 0,
+                "pieces split evenly over the threads");
+  u32x4 pk[kIters], pv[kIters];
+  auto fetch = [&](int c) __attribute__((always_inline)) {
+    const int64_t s0 = static_cast<int64_t>(min(c, n_chunks - 1)) * kBwdChunk;
+#pragma unroll
+    for (int u = 0; u < kIters; ++u) {
+      const int i = (tid + NT * u) % kChunkPieces;
+      const uint8_t *ks, *vs;
+      int ok;
+      slot_rows(s0 + i / kPieces, ks, vs, ok);
+      pk[u] = *reinterpret_cast<const u32x4*>(ks + (i % kPieces) * 16);
+      pv[u] = *reinterpret_cast<const u32x4*>(vs + (i % kPieces) * 16);
+    }
+  };
+  if (n_chunks > 0) fetch(0);
+
+  for (int c = 0; c < n_chunks; ++c) {
+    // ---- stage the chunk's key / value rows and slot table
+    const int64_t s0 = static_cast<int64_t>(c) * kBwdChunk;
+    if (tid < kBwdChunk) {
+      const int64_t s = s0 + tid;
+      const uint8_t *ks, *vs;
+      int ok;
+      slot_rows(s, ks, vs, ok);
+      s_valid[tid] = ok;
+      s_gslot[tid] = s < n_ent ? static_cast<int>(s) : p.n_ent_max + static_cast<int>(s - n_ent);
+    }
+#pragma unroll
+    for (int u = 0; u < kIters; ++u) {
+      const int i = tid + NT * u;
+      if (i < kChunkPieces) {
+        const int key = i / kPieces, pc = i % kPieces;
+        *reinterpret_cast<u32x4*>(&sK[key * kRs + pc * 16]) = pk[u];
+        *reinterpret_cast<u32x4*>(&sV[key * kRs + pc * 16]) = pv[u];
+      }
+    }
+    __syncthreads();
+    fetch(c + 1);  // (past the end: the last chunk again, from cache)
+
+    // ---- phase A: S^T, dP^T for both key tiles (rows 16 j + 4 g + i of
+    // this lane's head column), P, dS
+    uint16_t ph8[8], pl8[8], sh8[8], sl8[8];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      f32x4 sT = f32x4{0.f, 0.f, 0.f, 0.f}, dpT = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint8_t* krow = &sK[(j * 16 + col) * kRs + g * kSpan * 2];
+      const uint8_t* vrow = &sV[(j * 16 + col) * kRs + g * kSpan * 2];
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + st * 16));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vrow + st * 16));
+        sT = mma_bf16(ka, qf[st], sT);
+        dpT = mma_bf16(va, ofh[st], dpT);
+        dpT = mma_bf16(va, ofl[st], dpT);
+      }
+      {
+#pragma clang fp contract(off)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = j * 16 + g * 4 + i;
+          const float pr = s_valid[key] ? exp2f(sT[i] * scale_log2 - lse2) : 0.f;
+          const float ds = pr * (dpT[i] - Dh) * p.scale;
+          split(pr, ph8[j * 4 + i], pl8[j * 4 + i]);
+          split(ds, sh8[j * 4 + i], sl8[j * 4 + i]);
+        }
+      }
+    }
+    if (dh == 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = j * 16 + g * 4 + i;
+          sPH[key][head] = ph8[j * 4 + i];
+          sPL[key][head] = pl8[j * 4 + i];
+          sSH[key][head] = sh8[j * 4 + i];
+          sSL[key][head] = sl8[j * 4 + i];
+        }
+    }
+    // dq^T[dim][head] += sum_key K[key][dim] dS[head][key] (scale folded):
+    // A = K^T read transposed, keys 4 g .. 4 g + 3 and 16 + 4 g .. + 3 in the
+    // order of the lane's dS values
+    {
+      u32x4 bh, bl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bh[e] = static_cast<uint32_t>(sh8[2 * e]) | (static_cast<uint32_t>(sh8[2 * e + 1]) << 16);
+        bl[e] = static_cast<uint32_t>(sl8[2 * e]) | (static_cast<uint32_t>(sl8[2 * e + 1]) << 16);
+      }
+      const bf16x8 dsh = __builtin_bit_cast(bf16x8, bh), dsl = __builtin_bit_cast(bf16x8, bl);
+      const uint8_t* kbase = sK + (4 * g + (col >> 2)) * kRs + (col & 3) * 8;
+#pragma unroll
+      for (int d = 0; d < kHalfDT; ++d) {
+        const int dt = dh * kHalfDT + d;
+        const u32x2 lo = lds_read_tr16(kbase + dt * 32);
+        const u32x2 hi = lds_read_tr16(kbase + 16 * kRs + dt * 32);
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        dq[d] = mma_bf16(ka, dsh, dq[d]);
+        dq[d] = mma_bf16(ka, dsl, dq[d]);
+      }
+    }
+    __syncthreads();
+
+    // ---- phase B (wave = one 16-dim tile, both key tiles, all heads):
+    // dK^T = q^T dS and dV^T = dout^T P; lane (key col, g) ends with dims
+    // 4 g .. 4 g + 3 of its key
+    for (int dd = wave; dd < kDT; dd += NT / 64) {
+      const int dim = dd * 16 + col;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int key = kt * 16 + col;
+        f32x4 ak = f32x4{0.f, 0.f, 0.f, 0.f}, av = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int hb = 0; hb < kBwdHeads / 32; ++hb) {
+          const int h0 = hb * 32 + g * 8;
+          const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sQt[dim][h0]));
+          const bf16x8 oah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sOtH[dim][h0]));
+          const bf16x8 oal = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sOtL[dim][h0]));
+          const bf16x8 sbh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sSH[key][h0]));
+          const bf16x8 sbl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sSL[key][h0]));
+          const bf16x8 pbh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sPH[key][h0]));
+          const bf16x8 pbl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sPL[key][h0]));
+          ak = mma_bf16(qa, sbh, ak);
+          ak = mma_bf16(qa, sbl, ak);
+          av = mma_bf16(oah, pbh, av);
+          av = mma_bf16(oah, pbl, av);
+          av = mma_bf16(oal, pbh, av);
+        }
+        if (s_valid[key]) {
+          const int64_t gi = (row * (p.n_ent_max + p.W) + s_gslot[key]) * D + dd * 16 + g * 4;
+          *reinterpret_cast<f32x4*>(p.gk + gi) = ak;
+          *reinterpret_cast<f32x4*>(p.gv + gi) = av;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // dq: each dim half from its own wave
+  if (head < H) {
+    float* dst = p.dq + (row * H + head) * D;
+#pragma unroll
+    for (int d = 0; d < kHalfDT; ++d)
+      *reinterpret_cast<f32x4*>(dst + (dh * kHalfDT + d) * 16 + g * 4) = dq[d];
+  }
+}
+
 // HCA: key / value gradients of compressed entry j of sequence b, the sum
 // of the contributions of every query row that sees it (all of them attend
 // it), in ascending row order.
@@ -672,7 +992,10 @@ int launch_attend_bwd(const void* q, int dtype, const void* kc, const void* vc,
 #define CSA_BWD_CASE(DT, DD)                                                                  \
   if (dtype == DT && D == DD) {                                                               \
     if (hca) {                                                                                \
-      attend_bwd_rows_kernel<DT, DD, true><<<dim3(rows), kBwdThreads, 0, stream>>>(p);         \
+      if (DT == 1)                                                                            \
+        attend_bwd_rows_bf16_kernel<DD, true><<<dim3(rows), kBwdThreads, 0, stream>>>(p);      \
+      else                                                                                    \
+        attend_bwd_rows_kernel<DT, DD, true><<<dim3(rows), kBwdThreads, 0, stream>>>(p);       \
       attend_bwd_entries_kernel<DD, true><<<dim3(n_cap, B), 256, 0, stream>>>(p);              \
     } else {                                                                                  \
       /* the counting sort needs only the index lists; its ranks use the */                   \
@@ -680,7 +1003,10 @@ int launch_attend_bwd(const void* q, int dtype, const void* kc, const void* vc,
       attend_bwd_count_kernel<<<dim3(rows), 256, 0, stream>>>(p);                              \
       attend_bwd_scan_kernel<<<dim3(B), 256, 0, stream>>>(p);                                  \
       attend_bwd_fill_kernel<<<dim3(rows), 256, 0, stream>>>(p);                               \
-      attend_bwd_rows_kernel<DT, DD, false><<<dim3(rows), kBwdThreads, 0, stream>>>(p);        \
+      if (DT == 1)                                                                            \
+        attend_bwd_rows_bf16_kernel<DD, false><<<dim3(rows), kBwdThreads, 0, stream>>>(p);     \
+      else                                                                                    \
+        attend_bwd_rows_kernel<DT, DD, false><<<dim3(rows), kBwdThreads, 0, stream>>>(p);      \
       attend_bwd_entries_csr_kernel<DD, kBwdSmallRefs, false>                                  \
           <<<dim3(n_cap, B), 256, 0, stream>>>(p);                                             \
       attend_bwd_entries_csr_kernel<DD, kBwdMaxRefs, true>                                     \
