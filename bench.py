@@ -553,7 +553,7 @@ def main():
         "dtype": "f32" if cfg.backward else index_dtype(cfg),
         "data": "synthetic (seeded N(0,1) K/V/q, U(0,1) head weights, planted entries)",
         "config": config_of(cfg),
-        "timing": "cold cache: a 1 GiB device copy before every timed step, outside the events; "
+        "timing": "cold cache: a 1 GiB device copy and a read-back of its source before every timed step, outside the events; "
                   "one event pair per step on the launch stream; value = queries / median step",
         **main_res,
         "timed_region_s": wall,
