@@ -137,6 +137,15 @@ CASES = {
                      {"storage": "f32", "d": 64, "d_I": 64, "W": 32}),
     "bf16_d64_long": (2, 1, 70000, [4 * 70000 - 1, 4 * 9000], 2048,
                       {"d": 64, "d_I": 64, "H": 16, "W": 64}),
+    # k not a multiple of the 64-key chunk, no window (W = 0)
+    "odd_k_no_window": (3, 1, 20000, [4 * 20000 - 1, 4 * 15000 + 2, 4 * 9000], 1000,
+                        {"H": 64, "H_I": 64, "W": 0}),
+    # the largest k: lists longer than the attention launch's LDS space
+    # (read from global memory)
+    "k_max": (2, 1, 70000, [4 * 70000 - 1, 4 * 50000], 4096, {"H": 16, "H_I": 16, "W": 128}),
+    # 8 or more rows: the XCD-ordered grids
+    "xcd_rows_T2": (5, 2, 12000, [4 * 12000 - 2, 4 * 11000, 4 * 6000, 4 * 3000, 4 * 9999],
+                    256, {"H": 32, "H_I": 32, "W": 32}),
 }
 
 
