@@ -86,7 +86,8 @@ struct AttParams {
   int splits, chunks_per_split;
   int64_t xcd_rows;  // > 0: 1-D grid in XCD row order (xcd_row_item), else (splits, rows)
   float scale_log2;  // scale * log2(e)
-  TopkLists sel;     // the selection's lists (SEL variant)
+  TopkLists sel;     // the selection's lists or scores (SEL variants)
+  uint32_t* hist_zero;  // [rows][kTopkHistBins] histograms the merge launch zeroes, or NULL
 };
 
 // ---- the top-k selection made inside the launch (CSA, SEL variant)
@@ -388,7 +389,328 @@ __device__ __forceinline__ void attend_select(const TopkLists& sel, int64_t row,
   }
 }
 
-template <int DTYPE, int D, bool HCA, bool SEL>
+// ---- the top-k selection from the row's scores held in registers (SEL 2)
+//
+// For rows of at most kSelRegEntries entries no classify launch precedes
+// the attention: every workgroup of the row loads the row's first-digit
+// histogram (8 bins per thread, thread 0 the highest) and then the whole
+// row of scores (64 per thread: float4 q of wave w covers entries 4096 w +
+// 256 q + 4 lane .. + 3).  One block scan of the bin totals gives the
+// bucket b1 of the k-th key, the count above it and the number nc of
+// candidates (first digit b1).  Every workgroup of a row redoes this work,
+// and with two waves per SIMD each instruction of it costs the workgroup
+// about 8 cycles, so the pass over the registers is one max and one
+// compare per float4 against the bucket's lower bound (slots past V hold
+// -inf; finite scores assumed, as in the row top-k): a float4 holding a
+// listed score (in bucket b1 or above) goes, with its first entry number,
+// to its wave's region of an LDS group list (slot numbered by ballot).
+// Each wave then splits its own groups' listed scores, without a barrier:
+// sure entries (above b1) are set in an LDS bitmap of the row in entry
+// order, candidates go with their keys to the wave's region of a candidate
+// list (numbered by ballot) while their second digits are counted.  The
+// cut among the candidates is found (the 20-bit prefix from that
+// histogram, the few candidates sharing it ranked by all waves, else the
+// general digit passes) and the winners are set in the bitmap.  Each
+// thread then owns 64 consecutive bits of it: one block scan of their
+// counts numbers the kept entries in entry order, and each split keeps,
+// and writes out, the slots it attends.  A wave region that overflows
+// (clustered scores) sends the selection to passes over the scores in
+// memory.  The row's histogram goes back to zero in the merge launch, or
+// here when the row has one split (each thread clears the bins it read).
+constexpr int kAttSelRegs = 64;     // scores per thread
+constexpr int kAttSelGroups = 384;  // listed float4 groups per wave region
+static_assert(kAttThreads * kAttSelRegs == kSelRegEntries, "a row's scores fill the registers");
+static_assert(kAttThreads * 8 == kTopkHistBins, "8 histogram bins per thread");
+
+// The entries of float4 q of a thread: e0 + 256 q + 0..3.
+__device__ __forceinline__ f32x4 sel_regs_load(const float* srow, int64_t n_cap, int e0, int q) {
+  const int64_t e = e0 + 256 * q;
+  return *reinterpret_cast<const f32x4*>(srow + (e + 4 <= n_cap ? e : n_cap - 4));
+}
+
+template <int NT>
+__device__ __forceinline__ void attend_select_regs(const TopkLists& sel, int64_t row, int64_t t,
+                                                   int64_t n_cap, int k, int64_t s_begin,
+                                                   int64_t s_end, bool zero_hist,
+                                                   int32_t* s_ent, AttSelShared& ss, f32x4* gx,
+                                                   uint32_t* gj, uint32_t* kept, uint32_t* lst,
+                                                   int lwcap) {
+  constexpr int kQ = kAttSelRegs / 4;  // float4 loads per thread
+  constexpr int NW = NT / 64;
+  constexpr int gcap = kAttSelGroups;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  const int e0 = wv * (64 * kAttSelRegs) + 4 * lane;
+  const float* srow = sel.scores + row * n_cap;
+  // the histogram first: loads complete in order, so the bucket is found
+  // while the scores are still arriving
+  u32x4* gh = reinterpret_cast<u32x4*>(sel.hist + row * kTopkHistBins +
+                                       (kTopkHistBins - 8 * (tid + 1)));
+  const u32x4 h0 = gh[0], h1 = gh[1];  // bins base .. base + 7
+  f32x4 sv[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) sv[q] = sel_regs_load(srow, n_cap, e0, q);
+  // second-digit histogram (bin b at word b + b / 16: the 16 consecutive
+  // bins each lane reads below sit 17 words from the next lane's), the
+  // prefix candidates' counter and ranks, the overflow flag and the kept
+  // bitmap (entry j at bit j % 32 of word j / 32), cleared before the first
+  // barrier
+  uint32_t* h2 = ss.hist;
+  auto h2_at = [](uint32_t b) __attribute__((always_inline)) { return b + (b >> 4); };
+  uint64_t* tmp = reinterpret_cast<uint64_t*>(h2 + 1152);  // 64 prefix candidates
+  uint32_t* rank = h2 + 1280;                               // their ranks
+  for (int i = tid; i < 1344; i += NT) h2[i] = 0u;
+  for (int i = tid; i < kSelRegEntries / 32; i += NT) kept[i] = 0u;
+  if (tid == 0) ss.misc[5] = ss.misc[6] = 0u;
+  const uint32_t hb[8] = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+  uint32_t local = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) local += hb[i];
+  const uint32_t kk = static_cast<uint32_t>(k);
+  uint32_t total;
+  const uint32_t excl = block_scan_1b<NT>(local, ss.scan, &total);
+  if (excl < kk && kk <= excl + local) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {  // highest bin first
+      if (acc < kk && kk <= acc + hb[i]) {
+        ss.misc[0] = static_cast<uint32_t>(kTopkHistBins - 8 * (tid + 1) + i);
+        ss.misc[1] = acc;
+        ss.misc[4] = hb[i];
+      }
+      acc += hb[i];
+    }
+  }
+  // the bins were summed above, so their loads are complete
+  if (zero_hist) gh[0] = gh[1] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  const int64_t V = uniform64(visible_entries(t, sel.m, n_cap));
+  int32_t* out = sel.idx + row * k;
+  if (V <= k) {  // every visible entry, then -1
+    for (int64_t i = s_begin + tid; i < s_end; i += NT) {
+      const int32_t e = i < V ? static_cast<int32_t>(i) : -1;
+      s_ent[i - s_begin] = e;
+      out[i] = e;
+    }
+    return;
+  }
+  const int V32 = static_cast<int>(V);  // V <= n_cap <= kSelRegEntries
+  const uint32_t b1 = ss.misc[0];
+  const uint32_t nc = ss.misc[4];
+  const uint32_t r = kk - ss.misc[1];  // winners among the candidates
+  const bool all_win = r >= nc;
+  // bucket(v) > b1 iff v >= hi, bucket(v) == b1 iff lo <= v < hi (finite
+  // scores; hi is NaN for the top bucket, which nothing is above)
+  const float lo = key_floor_float(b1 << kTopkDigit1Shift);
+  const float hi = key_floor_float((b1 + 1u) << kTopkDigit1Shift);
+  auto set_kept = [&](int j) __attribute__((always_inline)) {
+    atomicOr(&kept[j >> 5], 1u << (j & 31));
+  };
+  // the pass over the registers: float4 groups holding a listed score
+  f32x4* wgx = gx + wvu * gcap;
+  uint32_t* wgj = gj + wvu * gcap;
+  uint32_t gcount = 0;  // this wave's groups (wave-uniform)
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    f32x4 x = sv[q];
+    if (wvu * (64 * kAttSelRegs) + 256 * (q + 1) > V32) {  // part of this group lies past V
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e0 + 256 * q + e >= V32) x[e] = -INFINITY;
+    }
+    const bool listed = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])) >= lo;
+    const unsigned long long m = __ballot(listed);
+    if (listed) {
+      const uint32_t at = gcount + lanes_below(m);
+      if (at < static_cast<uint32_t>(gcap)) {
+        wgx[at] = x;
+        wgj[at] = static_cast<uint32_t>(e0 + 256 * q);
+      }
+    }
+    gcount += static_cast<uint32_t>(__popcll(m));
+  }
+  // this wave's groups: sure entries into the bitmap, candidates into the
+  // wave's list region and the second-digit histogram
+  uint32_t* lkey = lst + wvu * lwcap;
+  int32_t* lidx = reinterpret_cast<int32_t*>(lst + NW * lwcap) + wvu * lwcap;
+  uint32_t lcount = 0;  // this wave's candidates (wave-uniform)
+  const uint32_t gn = min(gcount, static_cast<uint32_t>(gcap));
+  for (uint32_t g0 = 0; g0 < gn; g0 += 64) {
+    const uint32_t g = g0 + lane;
+    const bool have = g < gn;
+    const f32x4 x = wgx[have ? g : 0];
+    const int j0 = static_cast<int>(wgj[have ? g : 0]);
+    uint32_t sn = 0, cn = 0;  // sure and candidate entries of the group
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool su = x[e] >= hi;
+      sn |= su ? 1u << e : 0u;
+      cn |= !su && x[e] >= lo ? 1u << e : 0u;
+    }
+    if (!have) sn = cn = 0u;
+    if (all_win) {
+      sn |= cn;
+      cn = 0u;
+    }
+    // the group's 4 entries share a bitmap word
+    if (sn) atomicOr(&kept[j0 >> 5], sn << (j0 & 31));
+    // the lane's candidates at the wave's next slots (a prefix over the
+    // lanes of counts 0..4, from their three bits)
+    const uint32_t nl = static_cast<uint32_t>(__popc(cn));
+    const unsigned long long c0 = __ballot(nl & 1u), c1 = __ballot(nl & 2u),
+                             c2 = __ballot(nl & 4u);
+    uint32_t at = lcount + lanes_below(c0) + 2u * lanes_below(c1) + 4u * lanes_below(c2);
+    lcount += static_cast<uint32_t>(__popcll(c0) + 2 * __popcll(c1) + 4 * __popcll(c2));
+    while (cn) {
+      const int e = __builtin_ctz(cn);
+      cn &= cn - 1u;
+      const float v = e == 0 ? x[0] : e == 1 ? x[1] : e == 2 ? x[2] : x[3];
+      const uint32_t ky = score_key(v);
+      atomicAdd(&h2[h2_at((ky >> 10) & 1023u)], 1u);
+      if (at < static_cast<uint32_t>(lwcap)) {
+        lkey[at] = ky;
+        lidx[at] = j0 + e;
+      }
+      ++at;
+    }
+  }
+  if (lane == 0 && (gcount > static_cast<uint32_t>(gcap) || lcount > static_cast<uint32_t>(lwcap)))
+    ss.misc[5] = 1u;  // a wave region overflowed
+  __syncthreads();  // the bitmap's sure entries, the lists and the histogram
+  if (ss.misc[5] == 0u) {
+    if (!all_win) {
+      // every wave finds the bucket b2 of the r-th best candidate's second
+      // digit (lane l holds bins 1023 - 16 l - q, q = 0..15, highest first)
+      uint32_t hq[16];
+      uint32_t sum = 0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        hq[q] = h2[h2_at(1023u - 16u * lane - q)];
+        sum += hq[q];
+      }
+      uint32_t incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      const uint32_t ex2 = incl - sum;
+      const bool mine = ex2 < r && r <= incl;
+      uint32_t b2 = 0, above = 0;
+      if (mine) {
+        uint32_t acc = ex2;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          if (acc < r && r <= acc + hq[q]) {
+            b2 = 1023u - 16u * lane - q;
+            above = acc;
+          }
+          acc += hq[q];
+        }
+      }
+      const int owner = __ffsll(static_cast<long long>(__ballot(mine))) - 1;
+      b2 = __builtin_amdgcn_readlane(b2, owner & 63);
+      above = __builtin_amdgcn_readlane(above, owner & 63);
+      const uint32_t n2 = h2[h2_at(b2)];
+      Cut c;
+      if (n2 <= 64u) {
+        const uint32_t prefix = (b1 << 10) | b2;
+        for (uint32_t i = lane; i < lcount; i += 64) {
+          const uint32_t ky = lkey[i];
+          if ((ky >> 10) == prefix) {
+            const uint32_t at = atomicAdd(&ss.misc[6], 1u);
+            if (at < 64u)
+              tmp[at] = (static_cast<uint64_t>(ky & 0xfffffu) << 32) |
+                        static_cast<uint32_t>(lidx[i]);
+          }
+        }
+        __syncthreads();
+        // their ranks by (key desc, index asc), every wave comparing all of
+        // them with its eighth (LDS broadcast reads, all in flight at once)
+        const bool have = static_cast<uint32_t>(lane) < n2;
+        const uint64_t v = tmp[lane];
+        const uint32_t lo20 = static_cast<uint32_t>(v >> 32);
+        const int32_t jj = static_cast<int32_t>(static_cast<uint32_t>(v));
+        uint64_t u[64 / NW];
+#pragma unroll
+        for (int i = 0; i < 64 / NW; ++i) u[i] = tmp[wvu + NW * i];
+        uint32_t part = 0;
+#pragma unroll
+        for (int i = 0; i < 64 / NW; ++i) {
+          const uint32_t lo_q = static_cast<uint32_t>(u[i] >> 32);
+          const int32_t j_q = static_cast<int32_t>(static_cast<uint32_t>(u[i]));
+          const bool before = lo_q > lo20 || (lo_q == lo20 && j_q < jj);
+          part += static_cast<uint32_t>(wvu + NW * i) < n2 && before ? 1u : 0u;
+        }
+        if (have && part) atomicAdd(&rank[lane], part);
+        __syncthreads();
+        // the (r - above)-th of them is the cut (every wave finds it)
+        const int who =
+            __ffsll(static_cast<long long>(__ballot(have && rank[lane] == r - above - 1u))) - 1;
+        c = Cut{static_cast<uint32_t>(__builtin_amdgcn_readlane(lo20, who & 63)),
+                static_cast<int32_t>(__builtin_amdgcn_readlane(static_cast<uint32_t>(jj),
+                                                               who & 63))};
+      } else {
+        // every candidate, visited by the threads of the wave that listed it
+        auto visit = [&](auto f) {
+          for (uint32_t i = lane; i < lcount; i += 64) f(lkey[i], lidx[i]);
+        };
+        // (every wave took this branch; the digit passes clear the
+        // histogram the others may still be reading)
+        __syncthreads();
+        c = resolve_cut<NT>(ss, visit, r);
+      }
+      // the winning candidates into the bitmap
+      for (uint32_t i = lane; i < lcount; i += 64) {
+        const int32_t j = lidx[i];
+        if (cut_wins(c, lkey[i], j)) set_kept(j);
+      }
+    }
+  } else {
+    // a wave region overflowed: the same over the scores in memory
+    auto visit_mem = [&](auto f) {
+      for (int q = 0; q < kQ; ++q) {
+        const f32x4 v = sel_regs_load(srow, n_cap, e0, q);
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          if (e0 + 256 * q + x < V32 && v[x] >= lo) f(v[x], e0 + 256 * q + x);
+      }
+    };
+    Cut c{0u, 0x7fffffff};
+    if (!all_win) {
+      auto visit = [&](auto f) {
+        visit_mem([&](float v, int j) {
+          if (!(v >= hi)) f(score_key(v), j);
+        });
+      };
+      c = resolve_cut<NT>(ss, visit, r);
+    }
+    visit_mem([&](float v, int j) {
+      if (v >= hi || all_win || cut_wins(c, score_key(v), j)) set_kept(j);
+    });
+  }
+  __syncthreads();  // the kept bitmap
+  // thread t: entries 64 t .. 64 t + 63, numbered by one block scan
+  uint64_t bits = kept[2 * tid] | (static_cast<uint64_t>(kept[2 * tid + 1]) << 32);
+  uint32_t unused;
+  int at = static_cast<int>(block_scan_1b<NT>(static_cast<uint32_t>(__popcll(bits)),
+                                              ss.scan + 16, &unused));
+  const int sb0 = static_cast<int>(s_begin), se0 = static_cast<int>(s_end);
+  while (bits && at < se0) {
+    const int i = __builtin_ctzll(bits);
+    bits &= bits - 1;
+    if (at >= sb0) {
+      const int32_t j = 64 * tid + i;
+      s_ent[at - sb0] = j;
+      out[at] = j;
+    }
+    ++at;
+  }
+}
+
+// SEL: 0 the selection is given (idx), 1 made from the classified lists,
+// 2 made from the scores held in registers.
+template <int DTYPE, int D, bool HCA, int SEL>
 __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttParams p) {
   using Tr = AttTraits<DTYPE, D>;
   constexpr int RB = Tr::kRowBytes;
@@ -407,6 +729,13 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttParams p) {
   // had absent keys, so no flag ever has to be cleared
   __shared__ int s_partial[2];
   __shared__ int32_t s_ent[HCA ? 1 : kAttMaxSplitChunks * kAttChunk];
+  // SEL 2: the float4 groups of listed scores, per wave region, in the K
+  // buffers when they are large enough (fp32 rows), else in LDS of their own
+  constexpr int kSelGroupSlots = kAttSelGroups * (kAttThreads / 64);
+  constexpr bool kGroupsInKs = sizeof(ks) >= 20 * kSelGroupSlots;
+  constexpr int kOwnSlots = SEL == 2 && !kGroupsInKs ? kSelGroupSlots : 1;
+  __shared__ f32x4 s_gx[kOwnSlots];
+  __shared__ uint32_t s_ginfo[kOwnSlots];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -453,7 +782,25 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttParams p) {
   // gathers never wait on index loads.
   const int64_t s_begin = c_begin * kAttChunk;
   const int64_t idx_row = row * p.k;
-  if (SEL) {
+  if constexpr (SEL == 2) {
+    // the listed groups in the K buffers when they are large enough (fp32
+    // rows; the candidate lists then after the shared state and the kept
+    // bitmap in vs), else in LDS of their own (the lists in ks); ks and vs
+    // are free until the first chunk is staged
+    constexpr int kVsUsed = static_cast<int>(sizeof(AttSelShared)) + kSelRegEntries / 8;
+    constexpr int kListBytes =
+        kGroupsInKs ? static_cast<int>(sizeof(vs)) - kVsUsed : static_cast<int>(sizeof(ks));
+    constexpr int kListWaveCap = kListBytes / (8 * (kAttThreads / 64));
+    static_assert(kVsUsed <= static_cast<int>(sizeof(vs)) && kListWaveCap >= 256,
+                  "selection LDS");
+    attend_select_regs<kAttThreads>(
+        p.sel, row, t, p.n_cap, p.k, s_begin, min(c_end * kAttChunk, n_ent), p.splits == 1,
+        s_ent, *reinterpret_cast<AttSelShared*>(&vs[0][0]),
+        kGroupsInKs ? reinterpret_cast<f32x4*>(&ks[0][0]) : s_gx,
+        kGroupsInKs ? reinterpret_cast<uint32_t*>(&ks[0][0] + 16 * kSelGroupSlots) : s_ginfo,
+        reinterpret_cast<uint32_t*>(&vs[0][0] + sizeof(AttSelShared)),
+        reinterpret_cast<uint32_t*>(kGroupsInKs ? &vs[0][0] + kVsUsed : &ks[0][0]), kListWaveCap);
+  } else if constexpr (SEL == 1) {
     // the selection itself: keys in ks, then the shared state and the
     // indices in vs (both free until the first chunk is staged)
     constexpr int kCapK = static_cast<int>(sizeof(ks) / 4);
@@ -784,6 +1131,12 @@ __global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(AttParams p
   const int64_t row = blockIdx.y;
   const int64_t h = static_cast<int64_t>(blockIdx.x) * kHPB + threadIdx.x / kTPH;
   const int d4 = threadIdx.x % kTPH;
+  if (p.hist_zero) {  // the row's top-k histogram, read by every split of the attention launch
+    uint32_t* hz = p.hist_zero + row * kTopkHistBins;
+    for (int i = blockIdx.x * kMergeThreads + threadIdx.x; i < kTopkHistBins;
+         i += gridDim.x * kMergeThreads)
+      hz[i] = 0u;
+  }
   if (h >= p.H) return;
   const int64_t base = row * p.splits * p.H + h;  // partial (row, split 0, head h)
   float M = -INFINITY, L = 0.f;
@@ -890,6 +1243,7 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
   p.scale_log2 = scale * kLog2e;
   p.po = p.pm = p.pl = nullptr;
   p.sel = sel ? *sel : TopkLists{};
+  p.hist_zero = sel && sel->regs && sp.splits > 1 ? sel->hist : nullptr;
   if (sp.splits > 1) {
     float* base = static_cast<float*>(ws);
     p.po = base;
@@ -904,11 +1258,13 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
 #define CSA_ATT_CASE(DT, DD)                                                        \
   if (dtype == DT && D == DD) {                                                     \
     if (hca)                                                                        \
-      attend_kernel<DT, DD, true, false><<<grid, kAttThreads, 0, stream>>>(p);      \
+      attend_kernel<DT, DD, true, 0><<<grid, kAttThreads, 0, stream>>>(p);          \
+    else if (sel && sel->regs)                                                      \
+      attend_kernel<DT, DD, false, 2><<<grid, kAttThreads, 0, stream>>>(p);         \
     else if (sel)                                                                   \
-      attend_kernel<DT, DD, false, true><<<grid, kAttThreads, 0, stream>>>(p);      \
+      attend_kernel<DT, DD, false, 1><<<grid, kAttThreads, 0, stream>>>(p);         \
     else                                                                            \
-      attend_kernel<DT, DD, false, false><<<grid, kAttThreads, 0, stream>>>(p);     \
+      attend_kernel<DT, DD, false, 0><<<grid, kAttThreads, 0, stream>>>(p);         \
     if (sp.splits > 16)                                                             \
       attend_merge_kernel<DD, 32><<<mgrid, kMergeThreads, 0, stream>>>(p);          \
     else if (sp.splits > 8)                                                         \

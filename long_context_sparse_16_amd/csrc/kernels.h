@@ -79,10 +79,14 @@ CoarseHist topk_coarse_hist(void* ws, int64_t B, int64_t T);
 int launch_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, int64_t n_cap,
                 int m, int k, int32_t* idx, void* ws, bool hist_ready, hipStream_t s);
 
-// The split top-k's per-slice lists (every entry whose first digit is at or
-// above the row's cut bucket, in entry order, with its key), from which the
-// attention launch can make the selection itself.
-constexpr int64_t kSelMaxSlices = 256;  // rows of up to 2^20 entries
+// What the attention launch needs to make the top-k selection itself: the
+// split top-k's per-slice lists (every entry whose first digit is at or
+// above the row's cut bucket, in entry order, with its key), or, for rows
+// of at most kSelRegEntries entries (regs != 0), only the scores and the
+// first-digit histograms (each workgroup then holds its row's scores in
+// registers and no classify launch precedes it).
+constexpr int64_t kSelMaxSlices = 256;      // rows of up to 2^20 entries
+constexpr int64_t kSelRegEntries = 32768;   // 64 scores per thread of a 512-thread workgroup
 struct TopkLists {
   const uint32_t* cnt;   // [rows][n_sl][2]: listed entries, candidates among them
   const int32_t* lidx;   // [rows][n_sl][4096]
@@ -91,11 +95,15 @@ struct TopkLists {
   uint32_t* hist;        // [rows][4096]: first-digit histograms, zeroed by the consumer
   int64_t n_sl;          // slices allocated per row
   int m;                 // compression ratio (visible entries V(t))
+  int regs;              // select from the scores (n_cap <= kSelRegEntries, n_cap % 4 == 0)
+  const float* scores;   // [rows][n_cap], 16-byte aligned (regs only)
   int32_t* idx;          // [rows][k] output: the selection, ascending, -1 padded
 };
-// Only the first half of the split top-k (classify); returns 1 (nothing
-// launched) when the split path does not apply to these sizes or the row
-// needs more than kSelMaxSlices slices.
+// Only the first half of the split top-k (classify; nothing but the
+// histograms, when the indexer did not build them, for rows the attention
+// launch selects from registers); returns 1 (nothing launched) when the
+// split path does not apply to these sizes or the row needs more than
+// kSelMaxSlices slices.
 int launch_topk_lists(const float* scores, const int64_t* pos0, int64_t B, int64_t T,
                       int64_t n_cap, int m, int k, void* ws, bool hist_ready, TopkLists* lists,
                       hipStream_t s);

@@ -11,6 +11,12 @@
 
 namespace csa {
 
+// Number of lanes below this one whose bit is set in a wave mask.
+__device__ __forceinline__ uint32_t lanes_below(unsigned long long mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
+
 template <int NT>
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* sm) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;

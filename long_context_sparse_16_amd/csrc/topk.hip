@@ -493,11 +493,6 @@ constexpr int kSelPer = kSelEntries / kSelThreads;   // 16 passes
 constexpr int kHistPerSel = kHistBins / kSelThreads;  // 16 bins per thread
 constexpr int kSelWaves = kSelThreads / 64;
 
-__device__ __forceinline__ uint32_t lanes_below(unsigned long long mask) {
-  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
-                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
-}
-
 struct ClassifyShared {
   uint32_t scan[32];
   uint32_t res[2];
@@ -911,7 +906,11 @@ int launch_topk_lists(const float* scores, const int64_t* pos0, int64_t B, int64
   SplitWs w = split_ws(ws, rows, n_cap);
   dim3 grid(static_cast<unsigned>(w.n_sl), static_cast<unsigned>(rows));
   if (!hist_ready) topk_hist_kernel<<<grid, kSelThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, w);
-  launch_classify(scores, pos0, T, n_cap, m, k, w, rows, s);
+  // rows that fit the attention workgroup's registers need no lists
+  lists->regs = n_cap <= kSelRegEntries && n_cap % 4 == 0 &&
+                (reinterpret_cast<uintptr_t>(scores) & 15u) == 0;
+  lists->scores = scores;
+  if (!lists->regs) launch_classify(scores, pos0, T, n_cap, m, k, w, rows, s);
   lists->cnt = w.cnt;
   lists->lidx = w.lidx;
   lists->lkey = w.lkey;

@@ -146,6 +146,16 @@ CASES = {
     # 8 or more rows: the XCD-ordered grids
     "xcd_rows_T2": (5, 2, 12000, [4 * 12000 - 2, 4 * 11000, 4 * 6000, 4 * 3000, 4 * 9999],
                     256, {"H": 32, "H_I": 32, "W": 32}),
+    # rows of at most 32768 entries select from registers: every register
+    # holding an entry (V = 32768, and 32767), V = k + 1 (every candidate
+    # usually wins), a row of one attention split
+    # (k + W = 64: the launch itself clears the histogram), and a row
+    # length that is no multiple of 4 (the classified lists instead)
+    "full_row_regs": (4, 1, 32768, [4 * 32768 - 1, 4 * 32768 - 3, 4 * 20000, 4 * 1025 - 1],
+                      1024, {"H": 16, "H_I": 16, "W": 64}),
+    "one_split": (2, 1, 12000, [4 * 12000 - 1, 4 * 10000], 48, {"W": 16}),
+    "odd_n_cap_lists": (2, 1, 20001, [4 * 20001 - 1, 4 * 15000], 512,
+                        {"H": 64, "H_I": 64, "W": 128}),
 }
 
 
@@ -166,7 +176,8 @@ def test_decode_matches_separate_calls(name):
 
 @pytest.mark.parametrize("name,hist_ready", [("long_rows", True), ("ragged_T2_long", True),
                                               ("fp8_long", True), ("f32_d64_long", False),
-                                              ("short_rows_mixed", True)])
+                                              ("short_rows_mixed", True), ("one_split", True),
+                                              ("full_row_regs", False)])
 def test_select_attend_matches_separate_calls(name, hist_ready):
     """csa_select_attend after csa_index_scores (with or without the fused
     histogram) against csa_topk + csa_attend; two calls on one top-k
@@ -191,11 +202,15 @@ def test_select_attend_matches_separate_calls(name, hist_ready):
         assert int(hist.abs().sum()) == 0
 
 
-@pytest.mark.parametrize("n_keys,n_cap", [(1, 40000), (3, 40000), (2, 6000)])
+@pytest.mark.parametrize("n_keys,n_cap", [(1, 40000), (3, 40000), (2, 6000), (1, 30000),
+                                           (3, 30000), (16, 30000)])
 def test_decode_ties(n_keys, n_cap):
     """Keys drawn from n_keys distinct rows: whole rows of equal scores.  One
     distinct key puts every entry in the cut's bucket; the cut then falls
-    among equal scores, which go to the lower indices."""
+    among equal scores, which go to the lower indices.  At 30000 entries
+    (selection from registers) 1 and 3 keys leave more candidates than the
+    LDS list holds, 16 keys a list whose cut needs the general digit
+    passes."""
     say("ties", n_keys, n_cap)
     rng = np.random.default_rng(n_keys)
     key_values = rng.standard_normal((n_keys, 128))
@@ -203,9 +218,10 @@ def test_decode_ties(n_keys, n_cap):
     pos0 = [4 * n_cap - 1, 4 * (n_cap - 777)]
     inp = _inputs(50 + n_keys, B, 1, n_cap, pos0, key_values=key_values, H=8, H_I=4, W=16)
     ref = _separate(inp, k)
-    got = _decode(inp, k)
-    torch.cuda.synchronize()
-    _same_all(got, ref, pos0, 4, f"ties {n_keys}")
+    for rep in range(3):  # several calls: the selection's waves must not race
+        got = _decode(inp, k)
+        torch.cuda.synchronize()
+        _same_all(got, ref, pos0, 4, f"ties {n_keys} call {rep}")
     _check_oracle_topk(got[0], got[1], pos0, 1, 4, k)
 
 
