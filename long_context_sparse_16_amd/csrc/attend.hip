@@ -1128,13 +1128,20 @@ template <int D, int MB>
 __global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(AttParams p) {
   constexpr int kTPH = D / 4;  // threads per head
   constexpr int kHPB = kMergeThreads / kTPH;
-  const int64_t row = blockIdx.y;
-  const int64_t h = static_cast<int64_t>(blockIdx.x) * kHPB + threadIdx.x / kTPH;
+  const int n_tiles = static_cast<int>((p.H + kHPB - 1) / kHPB);
+  int64_t row;
+  int tile;
+  if (p.xcd_rows > 0) {  // a row's tiles on the XCD whose L2 holds its partials
+    if (!xcd_row_item(blockIdx.x, n_tiles, p.xcd_rows, &row, &tile)) return;
+  } else {
+    row = blockIdx.y;
+    tile = blockIdx.x;
+  }
+  const int64_t h = static_cast<int64_t>(tile) * kHPB + threadIdx.x / kTPH;
   const int d4 = threadIdx.x % kTPH;
   if (p.hist_zero) {  // the row's top-k histogram, read by every split of the attention launch
     uint32_t* hz = p.hist_zero + row * kTopkHistBins;
-    for (int i = blockIdx.x * kMergeThreads + threadIdx.x; i < kTopkHistBins;
-         i += gridDim.x * kMergeThreads)
+    for (int i = tile * kMergeThreads + threadIdx.x; i < kTopkHistBins; i += n_tiles * kMergeThreads)
       hz[i] = 0u;
   }
   if (h >= p.H) return;
@@ -1253,8 +1260,9 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
   p.xcd_rows = xcd_mappable(rows) ? rows : 0;
   const dim3 grid = p.xcd_rows ? dim3(static_cast<unsigned>(xcd_grid_size(rows, sp.splits)))
                                : dim3(static_cast<unsigned>(sp.splits), static_cast<unsigned>(rows));
-  const dim3 mgrid(static_cast<unsigned>((H + kMergeThreads / (D / 4) - 1) / (kMergeThreads / (D / 4))),
-                   static_cast<unsigned>(rows));
+  const int64_t m_tiles = (H + kMergeThreads / (D / 4) - 1) / (kMergeThreads / (D / 4));
+  const dim3 mgrid = p.xcd_rows ? dim3(static_cast<unsigned>(xcd_grid_size(rows, m_tiles)))
+                                : dim3(static_cast<unsigned>(m_tiles), static_cast<unsigned>(rows));
 #define CSA_ATT_CASE(DT, DD)                                                        \
   if (dtype == DT && D == DD) {                                                     \
     if (hca)                                                                        \
