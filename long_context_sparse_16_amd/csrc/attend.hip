@@ -248,7 +248,9 @@ __device__ __forceinline__ void attend_select(const TopkLists& sel, int64_t row,
   // next lane's (no bank conflicts)
   uint32_t* h2 = ss.hist;
   auto h2_at = [](uint32_t b) __attribute__((always_inline)) { return b + (b >> 4); };
-  for (int i = tid; i < 1024 + 64; i += NT) h2[i] = 0u;
+  uint64_t* tmp = reinterpret_cast<uint64_t*>(h2 + 1152);  // 64 prefix candidates
+  uint32_t* rank = h2 + 1280;                               // their ranks
+  for (int i = tid; i < 1344; i += NT) h2[i] = 0u;
   if (tid == 0) ss.misc[6] = 0u;  // candidates collected at the cut's prefix
   __syncthreads();  // the list is in LDS
   // list entry i (sure entries and candidates of all slices, in entry
@@ -317,7 +319,6 @@ __device__ __forceinline__ void attend_select(const TopkLists& sel, int64_t row,
     above = __shfl(above, owner);
     const uint32_t n2 = h2[h2_at(b2)];
     general = n2 > 64u;  // too many share the cut's prefix: the digit passes
-    uint64_t* tmp = reinterpret_cast<uint64_t*>(h2 + 1152);  // 64 slots
     if (!general) {
       // the n2 candidates with prefix (b1, b2), any order
       const uint32_t prefix = (b1 << 10) | b2;
@@ -329,26 +330,34 @@ __device__ __forceinline__ void attend_select(const TopkLists& sel, int64_t row,
       }
     }
     __syncthreads();
-    if (!general && tid < 64) {
-      // rank them by (key desc, index asc): the (r - above)-th is the cut
-      const uint32_t r2 = r - above;
-      const bool have = static_cast<uint32_t>(lane) < n2;
-      const uint64_t v = have ? tmp[lane] : 0u;
-      const uint32_t lo = static_cast<uint32_t>(v >> 32);
-      const int32_t jj = have ? static_cast<int32_t>(static_cast<uint32_t>(v)) : 0x7fffffff;
-      uint32_t rank = 0;
-      for (uint32_t q = 0; q < n2; ++q) {
-        const uint32_t lo_q = __shfl(lo, static_cast<int>(q));
-        const int32_t j_q = __shfl(jj, static_cast<int>(q));
-        rank += (lo_q > lo || (lo_q == lo && j_q < jj)) ? 1u : 0u;
+    // their ranks by (key desc, index asc), every wave comparing all of
+    // them with its share (LDS broadcast reads, all in flight at once)
+    constexpr int NW = NT / 64;
+    const int wvu = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool have = !general && static_cast<uint32_t>(lane) < n2;
+    const uint64_t v = tmp[lane];
+    const uint32_t lo20 = static_cast<uint32_t>(v >> 32);
+    const int32_t jj = static_cast<int32_t>(static_cast<uint32_t>(v));
+    if (!general) {
+      uint64_t u[64 / NW];
+#pragma unroll
+      for (int i = 0; i < 64 / NW; ++i) u[i] = tmp[wvu + NW * i];
+      uint32_t part = 0;
+#pragma unroll
+      for (int i = 0; i < 64 / NW; ++i) {
+        const uint32_t lo_q = static_cast<uint32_t>(u[i] >> 32);
+        const int32_t j_q = static_cast<int32_t>(static_cast<uint32_t>(u[i]));
+        const bool before = lo_q > lo20 || (lo_q == lo20 && j_q < jj);
+        part += static_cast<uint32_t>(wvu + NW * i) < n2 && before ? 1u : 0u;
       }
-      if (have && rank == r2 - 1u) {
-        ss.misc[2] = lo;
-        ss.misc[3] = static_cast<uint32_t>(jj);
-      }
+      if (have && part) atomicAdd(&rank[lane], part);
     }
     __syncthreads();
-    c = Cut{ss.misc[2], static_cast<int32_t>(ss.misc[3])};
+    // the (r - above)-th of them is the cut (every wave finds it)
+    const int who =
+        __ffsll(static_cast<long long>(__ballot(have && rank[lane] == r - above - 1u))) - 1;
+    c = Cut{static_cast<uint32_t>(__builtin_amdgcn_readlane(lo20, who & 63)),
+            static_cast<int32_t>(__builtin_amdgcn_readlane(static_cast<uint32_t>(jj), who & 63))};
   }
   if (general) {
     auto visit = [&](auto f) {
