@@ -318,9 +318,12 @@ int csa_attend(const void* q, int q_dtype, const void* kc, const void* vc,
  * Computes exactly what csa_topk (same ws, same hist_ready) followed by
  * csa_attend compute: idx receives csa_topk's selection, out / lse the
  * attention over it.  For up to 256 query rows over n_cap <= 2^20 entries
- * (n_cap > 8192) the selection is made inside the attention launch from
+ * (n_cap > 8192) the selection is made inside the attention launch: from
+ * the scores themselves when n_cap <= 32768, n_cap is a multiple of 4 and
+ * scores is 16-byte aligned (no top-k launch when hist_ready), else from
  * the top-k's classified lists (one launch fewer); other sizes run
- * csa_topk's kernels first.
+ * csa_topk's kernels first.  Scores are taken to be finite (the bucket
+ * tests run on the floats, as in csa_topk's row kernel).
  *
  *   scores, topk_ws, topk_ws_bytes, hist_ready, pos0, m, k   as csa_topk
  *   q, kc, vc, kv_dtype, kr, vr, raw_pos0, R, W, scale, out, lse, ws,
