@@ -90,7 +90,7 @@ struct AttParams {
   uint32_t* hist_zero;  // [rows][kTopkHistBins] histograms the merge launch zeroes, or NULL
 };
 
-// ---- the top-k selection made inside the launch (CSA, SEL variant)
+// ---- the top-k selection made inside the launch from lists (CSA, SEL 1)
 //
 // Every workgroup of a row reads the row's classified lists (sure entries
 // and candidates, a few thousand entries for decode rows) into LDS, finds
@@ -99,10 +99,11 @@ struct AttParams {
 // index output, and split 0 returns the row's first-digit histogram
 // (consumed by the classify launch) to zero.  The selection is the one the
 // top-k finishing kernel makes: the r best candidates by (key, lower index
-// first).  With up to 2 NT candidates it is found by ranking every
-// candidate against all others (a handful of barriers); more candidates go
-// through the digit passes, and lists longer than the LDS space are read
-// from global memory (only with very many ties).
+// first).  A histogram of the candidates' second digit gives the cut's
+// 20-bit prefix, and the few candidates sharing it (at most 64) are ranked
+// by all waves; more go through the general digit passes, and lists longer
+// than the LDS space are read from global memory (only with very many
+// ties).
 struct AttSelShared {
   uint32_t hist[2048];  // digit passes; the packed candidates on the ranking path
   uint32_t scan[32];
@@ -278,7 +279,7 @@ __device__ __forceinline__ void attend_select(const TopkLists& sel, int64_t row,
   bool general = r < nc && !fits;
   if (r < nc && fits) {
     // a histogram of the candidates' second digits gives the 20-bit prefix
-    // of the cut; the few candidates that share it are ranked by one wave
+    // of the cut; the few candidates that share it are ranked by all waves
     for (uint32_t i = i0; i < i1; ++i) {
       const uint32_t key = ck[i];
       if ((key >> kTopkDigit1Shift) == b1) atomicAdd(&h2[h2_at((key >> 10) & 1023u)], 1u);
