@@ -29,6 +29,10 @@ SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "topk.hip", "attend.hip", "
 # keeps the accumulators out of AGPRs, saving one copy per value.
 SOURCE_FLAGS = {
     "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    # the top-k kernels' per-thread atomics on one LDS counter (list slots):
+    # the wave's values are summed with a DPP scan and one lane issues the
+    # atomic, instead of a scalar loop over the active lanes
+    "topk.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=DPP"],
 }
 HEADERS = ["common.h", "kernels.h", "select.h"]
 PUBLIC_HEADER = os.path.join(ROOT, "include", "csa.h")

@@ -166,10 +166,11 @@ __device__ void finish_row(FinishShared& sm, const float* srow, int64_t V, uint3
 // the histogram loads go out first, then the row's, so the histogram is
 // usable before the row has arrived, and the row is read once.  Longer rows
 // (REGS == 0) are read in batches of kRowBatch independent loads per thread
-// (twice when the histogram is built here).  Classification counts each
-// thread's sure entries and candidates, takes list positions from one
-// block prefix sum of the packed counts and writes without atomics.
-constexpr int kRowBatch = 16;
+// (twice when the histogram is built here).  Register rows are classified
+// by counting each thread's sure entries and candidates, one block prefix
+// sum of the packed counts and writes without atomics; batched rows take
+// their list slots with one LDS atomic per thread, list and batch.
+constexpr int kRowBatch = 32;
 constexpr int kRowRegs = 32;  // register-resident rows: V <= 32768 (1024 threads x 32)
 
 // hist_io (nullable): the rows' first-digit histograms built by the
@@ -318,30 +319,56 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
       }
       if (tid == kRowThreads - 1) sm.misc[4] = ps;  // sure entries (== above)
     } else {
-      for (int64_t base = 0; base < V; base += static_cast<int64_t>(kRowThreads) * kRowBatch) {
+      // The same float bucket tests batch by batch: each thread counts its
+      // batch's sure entries and candidates and takes its slots in the two
+      // lists with one atomic each (wave-aggregated: one LDS atomic per wave
+      // and list per batch), then writes; the lists' order is free (the
+      // output is sorted through the row bitmap, the cut is order-free).
+      const float lo = key_floor_float(bk << sh);
+      const float hi = key_floor_float((bk + 1u) << sh);
+      const float mid = key_floor_float(((2u * bk + 1u) << (sh - 1)));
+      uint32_t nup = 0;  // entries at or above mid, less the sure ones
+      constexpr int64_t kStep = static_cast<int64_t>(kRowThreads) * kRowBatch;
+      // (the loads are unconditional: past the row's end a lane reads entry
+      // V - 1, and its value is replaced; 32-bit indices, V < 2^31)
+      const int V32 = static_cast<int>(V);
+      for (int64_t base = 0; base < V; base += kStep) {
+        const int j0 = static_cast<int>(base) + tid;
         float v[kRowBatch];
 #pragma unroll
-        for (int u = 0; u < kRowBatch; ++u) {
-          const int64_t j = base + tid + static_cast<int64_t>(u) * kRowThreads;
-          v[u] = srow[j < V ? j : V - 1];
-        }
+        for (int u = 0; u < kRowBatch; ++u) v[u] = srow[min(j0 + u * kRowThreads, V32 - 1)];
+        uint32_t ns = 0, nc = 0;
 #pragma unroll
         for (int u = 0; u < kRowBatch; ++u) {
-          const int64_t j = base + tid + static_cast<int64_t>(u) * kRowThreads;
-          const uint32_t key = score_key(v[u]);
-          const uint32_t bq = key >> sh;
-          if (j < V && bq > bk) {
-            const uint32_t p = atomicAdd(&sm.misc[4], 1u);
-            if (p < kMaxK) sm.sel[p] = static_cast<int32_t>(j);
-          } else if (j < V && bq == bk) {
-            const uint32_t p = atomicAdd(&sm.misc[5], 1u);
-            if (p < kCandCap) {
-              sm.ckey[p] = key;
-              sm.cidx[p] = static_cast<int32_t>(j);
+          if (j0 + u * kRowThreads >= V32) v[u] = -INFINITY;  // below every finite bucket
+          ns += v[u] >= hi ? 1u : 0u;
+          nc += v[u] >= lo ? 1u : 0u;
+          nup += v[u] >= mid ? 1u : 0u;
+        }
+        nc -= ns;
+        nup -= ns;
+        uint32_t ps = atomicAdd(&sm.misc[4], ns);
+        uint32_t pc = atomicAdd(&sm.misc[5], nc);
+#pragma unroll
+        for (int u = 0; u < kRowBatch; ++u) {
+          if (v[u] >= lo) {
+            const int32_t j = j0 + u * kRowThreads;
+            if (v[u] >= hi) {
+              if (ps < static_cast<uint32_t>(kMaxK)) sm.sel[ps] = j;
+              ++ps;
+            } else {
+              if (pc < static_cast<uint32_t>(kCandCap)) {
+                sm.ckey[pc] = score_key(v[u]);
+                sm.cidx[pc] = j;
+              }
+              ++pc;
             }
-            if (count_up && ((key >> (sh - 1)) & 1u)) atomicAdd(&sm.misc[6], 1u);
           }
         }
+      }
+      if (count_up) {
+        for (int o = 1; o < 64; o <<= 1) nup += __shfl_xor(nup, o);
+        if ((tid & 63) == 0) atomicAdd(&sm.misc[6], nup);
       }
     }
     __syncthreads();
