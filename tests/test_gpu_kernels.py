@@ -294,10 +294,12 @@ def _topk_case(scores, V, k):
     return got
 
 
-@pytest.mark.parametrize("path", ["split", "few_rows", "row"])
+@pytest.mark.parametrize("path", ["split", "few_rows", "row", "row_long", "row_longer"])
 def test_topk_random_and_ties(path):
     """split: few rows longer than one workgroup handles (classify + finish
-    kernels); few_rows: few short rows, one workgroup each; row: many rows."""
+    kernels); few_rows: few short rows, one workgroup each; row: many rows
+    (short ones, held in registers); row_long, row_longer: many rows read
+    in batches of 32768 entries (two and three batches, the last ragged)."""
     say("topk", path)
     rng = np.random.default_rng(500)
     k = 100
@@ -305,8 +307,12 @@ def test_topk_random_and_ties(path):
         B, T, n_cap = 2, 4, 70000
     elif path == "few_rows":
         B, T, n_cap = 5, 4, 9000
-    else:
+    elif path == "row":
         B, T, n_cap = 1, 300, 3000
+    elif path == "row_long":
+        B, T, n_cap = 1, 264, 40000
+    else:
+        B, T, n_cap = 1, 260, 72000
     s = rng.standard_normal((B, T, n_cap)).astype(np.float32) * 30 + 140
     s[:, 1] = rng.integers(0, 40, size=s[:, 1].shape)          # heavy ties
     s[:, 2] = np.where(rng.random(s[:, 2].shape) < 0.5, -0.0, 0.0)  # signed zeros
@@ -342,7 +348,7 @@ def test_topk_edge_rows():
     assert np.array_equal(got[0, 0], np.r_[np.arange(15), 5000])
 
 
-@pytest.mark.parametrize("n_cap,T", [(70000, 2), (9000, 3), (3000, 300)])
+@pytest.mark.parametrize("n_cap,T", [(70000, 2), (9000, 3), (3000, 300), (40000, 264)])
 def test_topk_cut_inside_small_tie_group(n_cap, T):
     """The k-th largest score shared by a handful of entries (fewer than 64
     share its top 20 key bits, the case the cut search ranks in one wave):

@@ -2,7 +2,8 @@
 (csa_index_scores given a top-k workspace for more than 256 query rows,
 then csa_topk with hist_ready): every row's selection must equal the
 oracle's top-k of the GPU's own scores bit for bit.  The cases cover rows
-held in registers (n_cap <= 32768) and rows read in batches, k-th keys in
+held in registers (n_cap <= 32768) and rows read in batches (two and
+three of them), k-th keys in
 the upper and in the lower half of their coarse bucket (both asserted to
 occur), ties that overflow the LDS candidate list (the exact
 re-classification), fp8 keys, the per-row flags (set by the indexer,
@@ -82,6 +83,7 @@ CASES = {
     "regs_rows": (2, 160, 6000, [4 * 5000, 4 * 6000 - 200], 512, {}),
     "long_rows": (1, 264, 40000, [4 * 39000], 1024, {}),
     "fp8_long": (1, 272, 36000, [4 * 35500], 1024, {"fp8": True}),
+    "batched_rows": (1, 264, 72000, [4 * 71000], 1024, {}),
 }
 
 
@@ -106,7 +108,7 @@ def test_prefill_topk_from_coarse_histograms(name):
     assert halves == {0, 1}, f"both halves of the coarse bucket should occur, saw {halves}"
 
 
-@pytest.mark.parametrize("n_cap,T", [(20000, 264), (40000, 260)])
+@pytest.mark.parametrize("n_cap,T", [(20000, 264), (40000, 260), (72000, 260)])
 def test_prefill_topk_coarse_candidates_overflow(n_cap, T):
     """Keys from 2 distinct rows: every score takes one of two values per
     query, so the coarse bucket holds far more candidates than the LDS
