@@ -33,6 +33,9 @@ namespace csa {
 
 constexpr int kAttChunk = 64;  // keys per LDS chunk
 constexpr int kAttThreads = 512;  // 8 waves: 4 head tiles x 2 key halves
+// Grids of at least this many workgroups (two per CU of the 256) take the
+// two-per-CU build where it exists.
+constexpr int64_t kAttWideGroups = 512;
 // CSA: a split's slice of the top-k list is staged in LDS, so a split spans
 // at most this many chunks.
 constexpr int kAttMaxSplitChunks = 32;
@@ -721,7 +724,7 @@ __device__ __forceinline__ void attend_select_regs(const TopkLists& sel, int64_t
 // SEL: 0 the selection is given (idx), 1 made from the classified lists,
 // 2 made from the scores held in registers.
 template <int DTYPE, int D, bool HCA, int SEL>
-__global__ __launch_bounds__(kAttThreads) void attend_kernel(AttParams p) {
+__device__ __forceinline__ void attend_body(const AttParams& p) {
   using Tr = AttTraits<DTYPE, D>;
   constexpr int RB = Tr::kRowBytes;
   constexpr int kPieces = RB / 16;             // 16-byte pieces per row
@@ -1124,6 +1127,20 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttParams p) {
   }
 }
 
+template <int DTYPE, int D, bool HCA, int SEL>
+__global__ __launch_bounds__(kAttThreads) void attend_kernel(AttParams p) {
+  attend_body<DTYPE, D, HCA, SEL>(p);
+}
+
+// The same kernel held to 128 VGPRs (at least 4 waves per SIMD), so that two
+// workgroups share a CU when their LDS fits twice: each hides the other's
+// gather latency.  Used for grids of many rows (the chunked prefill); the
+// decode grids, about one workgroup per CU, keep the unconstrained build.
+template <int DTYPE, int D, bool HCA, int SEL>
+__global__ __launch_bounds__(kAttThreads, 4) void attend_wide_kernel(AttParams p) {
+  attend_body<DTYPE, D, HCA, SEL>(p);
+}
+
 // Merge the split partials of one query row: each thread owns 4 output dims
 // of one head.  Splits are taken in batches of MB (8, 16 or 32: the
 // smallest that holds a row's splits, so up to 32 splits cost one round
@@ -1270,6 +1287,8 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
   p.xcd_rows = xcd_mappable(rows) ? rows : 0;
   const dim3 grid = p.xcd_rows ? dim3(static_cast<unsigned>(xcd_grid_size(rows, sp.splits)))
                                : dim3(static_cast<unsigned>(sp.splits), static_cast<unsigned>(rows));
+  // (bf16 keys, d 128, given indices: its LDS fits twice in a CU)
+  const bool wide = static_cast<int64_t>(grid.x) * grid.y >= kAttWideGroups;
   const int64_t m_tiles = (H + kMergeThreads / (D / 4) - 1) / (kMergeThreads / (D / 4));
   const dim3 mgrid = p.xcd_rows ? dim3(static_cast<unsigned>(xcd_grid_size(rows, m_tiles)))
                                 : dim3(static_cast<unsigned>(m_tiles), static_cast<unsigned>(rows));
@@ -1281,6 +1300,8 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
       attend_kernel<DT, DD, false, 2><<<grid, kAttThreads, 0, stream>>>(p);         \
     else if (sel)                                                                   \
       attend_kernel<DT, DD, false, 1><<<grid, kAttThreads, 0, stream>>>(p);         \
+    else if (DT == 1 && DD == 128 && wide)                                          \
+      attend_wide_kernel<1, 128, false, 0><<<grid, kAttThreads, 0, stream>>>(p);    \
     else                                                                            \
       attend_kernel<DT, DD, false, 0><<<grid, kAttThreads, 0, stream>>>(p);         \
     if (sp.splits > 16)                                                             \

@@ -431,13 +431,17 @@ def _attend_case(storage, B, T, H, d, N, k, W, R, raw_off, seed, hca_m=0, fill=0
 
 @pytest.mark.parametrize("storage,H,d", [("f32", 8, 64), ("f32", 64, 128), ("bf16", 64, 128),
                                          ("bf16", 16, 64), ("bf16", 40, 128)])
-@pytest.mark.parametrize("rows", ["few", "many"])
+@pytest.mark.parametrize("rows", ["few", "many", "wide"])
 def test_attend_parity(storage, H, d, rows):
+    """few: split rows and the merge; many: one workgroup per query; wide:
+    a grid of 600 rows, which bf16 at d 128 runs two workgroups per CU."""
     say("attend", storage, H, d, rows)
     if rows == "few":   # split over several workgroups + merge
         B, T, k, N, W, R = 3, 2, 700, 3000, 128, 200
-    else:               # one workgroup per query
+    elif rows == "many":  # one workgroup per query
         B, T, k, N, W, R = 1, 300, 64, 600, 32, 400
+    else:
+        B, T, k, N, W, R = 1, 600, 96, 1200, 48, 800
     err, rel = _attend_case(storage, B, T, H, d, N, k, W, R, [100 * b + 2500 for b in range(B)]
                             if rows == "few" else [2000], seed=600 + H + d)
     tol = 1e-4 if storage == "f32" else 2e-2
