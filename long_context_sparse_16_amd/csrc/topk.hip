@@ -46,21 +46,31 @@ constexpr int kSelEntries = 4096;               // entries per select workgroup
 constexpr int kRowThreads = 1024;
 constexpr int64_t kRowSplitMinEntries = 8192;  // few rows longer than this take the split path
 
-struct FinishShared {
+// LDS of the finishing and row kernels: CAND candidates resolved in LDS,
+// bitmap output for rows of up to BM entries.
+template <int CAND, int BM>
+struct FinishSharedT {
+  static constexpr int kCand = CAND;
+  static constexpr int kBitmapEntries = BM;
   uint32_t hist[2048];                    // digit passes 2.. (<= 2048 bins)
-  uint32_t ckey[kCandCap];
-  int32_t cidx[kCandCap];
+  uint32_t ckey[CAND];
+  int32_t cidx[CAND];
   int32_t sel[kMaxK];
   // row bitmap, one pad word after every 32 (see bm_slot); also holds the
   // 4096-bin first-digit histogram in the row kernel
-  uint32_t bitmap[kBitmapMaxEntries / 32 + kBitmapMaxEntries / 1024];
+  uint32_t bitmap[BM / 32 + BM / 1024];
   uint32_t scan[32];
   uint32_t misc[8];  // [0] bin [1] above [2] [3] cut [4] selected [5] candidates [6] flag [7] count
 };
+using FinishShared = FinishSharedT<kCandCap, kBitmapMaxEntries>;
+// The 512-thread row kernel, two workgroups per CU: 72.6 KB of LDS
+// (4096 candidates; the bitmap area still holds the 4096-bin histogram).
+using RowShared2 = FinishSharedT<4096, 131072>;
+static_assert(131072 / 32 >= kHistBins, "the bitmap area holds the first-digit histogram");
 
 // resolve_cut, then append the winners to sm.sel at sm.misc[4].
-template <int NT, typename Visit>
-__device__ void resolve_candidates(FinishShared& sm, Visit visit_all, uint32_t r) {
+template <int NT, typename SM, typename Visit>
+__device__ void resolve_candidates(SM& sm, Visit visit_all, uint32_t r) {
   const Cut c = resolve_cut<NT>(sm, visit_all, r);
   visit_all([&](uint32_t key, int32_t j) {
     if (cut_wins(c, key, j)) {
@@ -76,14 +86,14 @@ __device__ void resolve_candidates(FinishShared& sm, Visit visit_all, uint32_t r
 __device__ __forceinline__ int bm_slot(int w) { return w + (w >> 5); }
 
 // Emit sm.sel[0..k) in ascending order to out[0..k).  Rows up to
-// kBitmapMaxEntries long use a bitmap over the row: each thread owns a run
+// SM::kBitmapEntries long use a bitmap over the row: each thread owns a run
 // of consecutive words, counts their bits, takes its output position from
 // a block prefix sum and writes its entries in order.  Longer rows sort
 // with a bitonic network.
-template <int NT>
-__device__ void emit_sorted(FinishShared& sm, int k, int64_t V, int32_t* out) {
+template <int NT, typename SM>
+__device__ void emit_sorted(SM& sm, int k, int64_t V, int32_t* out) {
   const int tid = threadIdx.x;
-  if (V <= kBitmapMaxEntries) {
+  if (V <= SM::kBitmapEntries) {
     const int nw = static_cast<int>((V + 31) >> 5);
     for (int i = tid; i < bm_slot(nw); i += NT) sm.bitmap[i] = 0u;
     __syncthreads();
@@ -139,11 +149,11 @@ __device__ __forceinline__ void write_iota(int32_t* out, int64_t V, int k) {
 }
 
 // Resolve r winners among the candidates (first digit == b1), either from
-// LDS (nc <= kCandCap) or from the score row, then emit the row.
-template <int NT>
-__device__ void finish_row(FinishShared& sm, const float* srow, int64_t V, uint32_t b1,
+// LDS (nc <= SM::kCand) or from the score row, then emit the row.
+template <int NT, typename SM>
+__device__ void finish_row(SM& sm, const float* srow, int64_t V, uint32_t b1,
                            uint32_t r, uint32_t nc, int k, int32_t* out) {
-  if (nc <= static_cast<uint32_t>(kCandCap)) {
+  if (nc <= static_cast<uint32_t>(SM::kCand)) {
     auto visit = [&](auto f) {
       for (uint32_t i = threadIdx.x; i < nc; i += NT) f(sm.ckey[i], sm.cidx[i]);
     };
@@ -171,7 +181,16 @@ __device__ void finish_row(FinishShared& sm, const float* srow, int64_t V, uint3
 // sum of the packed counts and writes without atomics; batched rows take
 // their list slots with one LDS atomic per thread, list and batch.
 constexpr int kRowBatch = 32;
+// Batched rows run 512-thread workgroups with the small LDS layout, two per
+// CU, so one row's cut and output phases overlap the other's reads.
+constexpr int kRowBatchedThreads = 512;
 constexpr int kRowRegs = 32;  // register-resident rows: V <= 32768 (1024 threads x 32)
+
+// LDS layout of the row kernel by workgroup size: 1024 threads (one
+// workgroup per CU) use the full layout, 512 threads (two per CU) the small
+// one.
+template <int NT> struct RowShm { using T = FinishShared; };
+template <> struct RowShm<512> { using T = RowShared2; };
 
 // hist_io (nullable): the rows' first-digit histograms built by the
 // indexer; used instead of a histogram pass and returned to zero.
@@ -183,14 +202,15 @@ constexpr int kRowRegs = 32;  // register-resident rows: V <= 32768 (1024 thread
 // are narrowed to it (the upper half joining the sure entries when the cut
 // is in the lower one).  Should the coarse candidates overflow the LDS
 // list, the row is classified again against the exact 12-bit bucket.
-template <int REGS, bool COARSE>
-__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
+template <int REGS, bool COARSE, int NT>
+__global__ __launch_bounds__(NT) void topk_row_kernel(
     const float* __restrict__ scores, const int64_t* __restrict__ pos0, int64_t T,
     int64_t n_cap, int m, int k, int32_t* __restrict__ idx, uint32_t* __restrict__ hist_io,
     CoarseHist coarse) {
-  __shared__ FinishShared sm;
-  constexpr int kHistPer = kHistBins / kRowThreads;
-  constexpr int kCoarsePer = kTopkCoarseBins / kRowThreads;
+  using SM = typename RowShm<NT>::T;
+  __shared__ SM sm;
+  constexpr int kHistPer = kHistBins / NT;
+  constexpr int kCoarsePer = kTopkCoarseBins / NT;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int64_t b = seq_of_row(row, T);
@@ -212,21 +232,21 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
   for (int q = 0; q < kHistPer; ++q) {
     if (COARSE)
       hv[q] = q < kCoarsePer && use_coarse
-                  ? coarse.hist[row * kTopkCoarseBins + tid + q * kRowThreads]
+                  ? coarse.hist[row * kTopkCoarseBins + tid + q * NT]
                   : 0u;
     else
-      hv[q] = gh ? gh[tid + q * kRowThreads] : 0u;
+      hv[q] = gh ? gh[tid + q * NT] : 0u;
   }
   float rv[REGS > 0 ? REGS : 1];
   if (REGS > 0) {
 #pragma unroll
     for (int u = 0; u < REGS; ++u) {
-      const int64_t j = tid + static_cast<int64_t>(u) * kRowThreads;
+      const int64_t j = tid + static_cast<int64_t>(u) * NT;
       rv[u] = srow[j < V ? j : V - 1];
     }
   }
 #pragma unroll
-  for (int q = 0; q < kHistPer; ++q) h1[tid + q * kRowThreads] = hv[q];
+  for (int q = 0; q < kHistPer; ++q) h1[tid + q * NT] = hv[q];
   if (tid < 8) sm.misc[tid] = 0u;
   __syncthreads();
   if (COARSE && tid == 0) coarse.flag[row] = 0u;
@@ -235,20 +255,20 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
     if (REGS > 0) {
 #pragma unroll
       for (int u = 0; u < REGS; ++u) {
-        const int64_t j = tid + static_cast<int64_t>(u) * kRowThreads;
+        const int64_t j = tid + static_cast<int64_t>(u) * NT;
         if (j < V) atomicAdd(&h1[score_key(rv[u]) >> kTopkDigit1Shift], 1u);
       }
     } else {
-      for (int64_t base = 0; base < V; base += static_cast<int64_t>(kRowThreads) * kRowBatch) {
+      for (int64_t base = 0; base < V; base += static_cast<int64_t>(NT) * kRowBatch) {
         float v[kRowBatch];
 #pragma unroll
         for (int u = 0; u < kRowBatch; ++u) {
-          const int64_t j = base + tid + static_cast<int64_t>(u) * kRowThreads;
+          const int64_t j = base + tid + static_cast<int64_t>(u) * NT;
           v[u] = srow[j < V ? j : V - 1];
         }
 #pragma unroll
         for (int u = 0; u < kRowBatch; ++u) {
-          const int64_t j = base + tid + static_cast<int64_t>(u) * kRowThreads;
+          const int64_t j = base + tid + static_cast<int64_t>(u) * NT;
           if (j < V) atomicAdd(&h1[score_key(v[u]) >> kTopkDigit1Shift], 1u);
         }
       }
@@ -256,17 +276,17 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
     __syncthreads();
   } else if (gh) {
 #pragma unroll
-    for (int q = 0; q < kHistPer; ++q) gh[tid + q * kRowThreads] = 0u;
+    for (int q = 0; q < kHistPer; ++q) gh[tid + q * NT] = 0u;
   }
   const int shift = use_coarse ? kTopkCoarseShift : kTopkDigit1Shift;
-  block_find_top<kRowThreads>(h1, use_coarse ? kTopkCoarseBins : kHistBins,
+  block_find_top<NT>(h1, use_coarse ? kTopkCoarseBins : kHistBins,
                               static_cast<uint32_t>(k), sm.scan, sm.misc);
   const uint32_t bk0 = sm.misc[0];
   const uint32_t above0 = sm.misc[1];
   if (REGS > 0) {
 #pragma unroll
     for (int u = 0; u < REGS; ++u)
-      if (tid + static_cast<int64_t>(u) * kRowThreads >= V) rv[u] = -INFINITY;
+      if (tid + static_cast<int64_t>(u) * NT >= V) rv[u] = -INFINITY;
   }
   // One classification of the row against bucket bk of the digit at
   // `shift`: sure entries (higher buckets) to sm.sel, candidates to the LDS
@@ -298,18 +318,18 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
         for (int o = 1; o < 64; o <<= 1) nup += __shfl_xor(nup, o);
         if ((tid & 63) == 0) atomicAdd(&sm.misc[6], nup);
       }
-      const uint32_t packed = block_excl_scan<kRowThreads>(ns | (nc << 12), sm.scan);
+      const uint32_t packed = block_excl_scan<NT>(ns | (nc << 12), sm.scan);
       uint32_t ps = packed & 0xfffu, pcand = packed >> 12;
-      if (tid == kRowThreads - 1) sm.misc[5] = pcand + nc;  // total candidates
+      if (tid == NT - 1) sm.misc[5] = pcand + nc;  // total candidates
 #pragma unroll
       for (int u = 0; u < REGS; ++u) {
         if (rv[u] >= lo) {
-          const int32_t j = tid + u * kRowThreads;
+          const int32_t j = tid + u * NT;
           if (rv[u] >= hi) {
             if (ps < static_cast<uint32_t>(kMaxK)) sm.sel[ps] = j;
             ++ps;
           } else {
-            if (pcand < static_cast<uint32_t>(kCandCap)) {
+            if (pcand < static_cast<uint32_t>(SM::kCand)) {
               sm.ckey[pcand] = score_key(rv[u]);
               sm.cidx[pcand] = j;
             }
@@ -317,7 +337,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
           }
         }
       }
-      if (tid == kRowThreads - 1) sm.misc[4] = ps;  // sure entries (== above)
+      if (tid == NT - 1) sm.misc[4] = ps;  // sure entries (== above)
     } else {
       // The same float bucket tests batch by batch: each thread counts its
       // batch's sure entries and candidates and takes its slots in the two
@@ -328,7 +348,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
       const float hi = key_floor_float((bk + 1u) << sh);
       const float mid = key_floor_float(((2u * bk + 1u) << (sh - 1)));
       uint32_t nup = 0;  // entries at or above mid, less the sure ones
-      constexpr int64_t kStep = static_cast<int64_t>(kRowThreads) * kRowBatch;
+      constexpr int64_t kStep = static_cast<int64_t>(NT) * kRowBatch;
       // (the loads are unconditional: past the row's end a lane reads entry
       // V - 1, and its value is replaced; 32-bit indices, V < 2^31)
       const int V32 = static_cast<int>(V);
@@ -336,11 +356,11 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
         const int j0 = static_cast<int>(base) + tid;
         float v[kRowBatch];
 #pragma unroll
-        for (int u = 0; u < kRowBatch; ++u) v[u] = srow[min(j0 + u * kRowThreads, V32 - 1)];
+        for (int u = 0; u < kRowBatch; ++u) v[u] = srow[min(j0 + u * NT, V32 - 1)];
         uint32_t ns = 0, nc = 0;
 #pragma unroll
         for (int u = 0; u < kRowBatch; ++u) {
-          if (j0 + u * kRowThreads >= V32) v[u] = -INFINITY;  // below every finite bucket
+          if (j0 + u * NT >= V32) v[u] = -INFINITY;  // below every finite bucket
           ns += v[u] >= hi ? 1u : 0u;
           nc += v[u] >= lo ? 1u : 0u;
           nup += v[u] >= mid ? 1u : 0u;
@@ -352,12 +372,12 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
 #pragma unroll
         for (int u = 0; u < kRowBatch; ++u) {
           if (v[u] >= lo) {
-            const int32_t j = j0 + u * kRowThreads;
+            const int32_t j = j0 + u * NT;
             if (v[u] >= hi) {
               if (ps < static_cast<uint32_t>(kMaxK)) sm.sel[ps] = j;
               ++ps;
             } else {
-              if (pc < static_cast<uint32_t>(kCandCap)) {
+              if (pc < static_cast<uint32_t>(SM::kCand)) {
                 sm.ckey[pc] = score_key(v[u]);
                 sm.cidx[pc] = j;
               }
@@ -383,12 +403,12 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
     const bool up = above0 + n_up >= static_cast<uint32_t>(k);
     b1 = 2u * bk0 + (up ? 1u : 0u);
     above = up ? above0 : above0 + n_up;
-    if (nc <= static_cast<uint32_t>(kCandCap)) {
+    if (nc <= static_cast<uint32_t>(SM::kCand)) {
       // narrow the LDS candidates to bucket b1 (in place: every thread
       // reads its run, then the barrier, then the kept ones are written
       // at their compacted positions); the other half is dropped or, when
       // the cut lies in the lower half, joins the sure entries
-      constexpr int kRun = kCandCap / kRowThreads;
+      constexpr int kRun = SM::kCand / NT;
       const uint32_t c0 = min(nc, static_cast<uint32_t>(tid * kRun));
       const uint32_t c1 = min(nc, c0 + kRun);
       uint32_t rk[kRun];
@@ -401,8 +421,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
         rj[u] = i < c1 ? sm.cidx[i] : 0;
         kept += i < c1 && (rk[u] >> kTopkDigit1Shift) == b1 ? 1u : 0u;
       }
-      uint32_t pos = block_excl_scan<kRowThreads>(kept, sm.scan);
-      if (tid == kRowThreads - 1) sm.misc[5] = pos + kept;
+      uint32_t pos = block_excl_scan<NT>(kept, sm.scan);
+      if (tid == NT - 1) sm.misc[5] = pos + kept;
 #pragma unroll
       for (int u = 0; u < kRun; ++u) {
         if (c0 + u >= c1) continue;
@@ -425,7 +445,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(
       nc = sm.misc[5];
     }
   }
-  finish_row<kRowThreads>(sm, srow, V, b1, static_cast<uint32_t>(k) - above, nc, k, out);
+  finish_row<NT>(sm, srow, V, b1, static_cast<uint32_t>(k) - above, nc, k, out);
 }
 
 // ------------------------------------------------------------ split path
@@ -891,12 +911,12 @@ static void launch_row_kernel(const float* scores, const int64_t* pos0, int64_t 
                               int64_t rows, hipStream_t s) {
   const unsigned g = static_cast<unsigned>(rows);
   const bool regs = n_cap <= static_cast<int64_t>(kRowThreads) * kRowRegs;
-#define CSA_ROW_GO(R, C) \
-  topk_row_kernel<R, C><<<g, kRowThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, idx, hist, ch)
+#define CSA_ROW_GO(R, C, NT) \
+  topk_row_kernel<R, C, NT><<<g, NT, 0, s>>>(scores, pos0, T, n_cap, m, k, idx, hist, ch)
   if (ch.flag) {
-    if (regs) CSA_ROW_GO(kRowRegs, true); else CSA_ROW_GO(0, true);
+    if (regs) CSA_ROW_GO(kRowRegs, true, kRowThreads); else CSA_ROW_GO(0, true, kRowBatchedThreads);
   } else {
-    if (regs) CSA_ROW_GO(kRowRegs, false); else CSA_ROW_GO(0, false);
+    if (regs) CSA_ROW_GO(kRowRegs, false, kRowThreads); else CSA_ROW_GO(0, false, kRowBatchedThreads);
   }
 #undef CSA_ROW_GO
 }
