@@ -30,7 +30,9 @@
 //     L2; measured on the 32 x 32768 decode rows, such a fused kernel took
 //     three times as long as the two launches.)
 //   * row path (many rows, prefill; short rows): one workgroup per row;
-//     rows of up to 32768 entries are held in registers and read once.
+//     rows of up to 32768 entries are held in registers and read once;
+//     rows of up to 16384, and rows read in batches, run two 512-thread
+//     workgroups per CU.
 #include "common.h"
 #include "kernels.h"
 #include "select.h"
@@ -910,14 +912,21 @@ static void launch_row_kernel(const float* scores, const int64_t* pos0, int64_t 
                               int m, int k, int32_t* idx, uint32_t* hist, const CoarseHist& ch,
                               int64_t rows, hipStream_t s) {
   const unsigned g = static_cast<unsigned>(rows);
+  // register rows of up to 512 x 32 entries also run two 512-thread
+  // workgroups per CU; up to 1024 x 32, one 1024-thread workgroup
   const bool regs = n_cap <= static_cast<int64_t>(kRowThreads) * kRowRegs;
+  const bool regs_small = n_cap <= static_cast<int64_t>(kRowBatchedThreads) * kRowRegs;
 #define CSA_ROW_GO(R, C, NT) \
   topk_row_kernel<R, C, NT><<<g, NT, 0, s>>>(scores, pos0, T, n_cap, m, k, idx, hist, ch)
-  if (ch.flag) {
-    if (regs) CSA_ROW_GO(kRowRegs, true, kRowThreads); else CSA_ROW_GO(0, true, kRowBatchedThreads);
-  } else {
-    if (regs) CSA_ROW_GO(kRowRegs, false, kRowThreads); else CSA_ROW_GO(0, false, kRowBatchedThreads);
-  }
+#define CSA_ROW_CASE(C)                                                  \
+  do {                                                                   \
+    if (regs_small) CSA_ROW_GO(kRowRegs, C, kRowBatchedThreads);         \
+    else if (regs) CSA_ROW_GO(kRowRegs, C, kRowThreads);                 \
+    else CSA_ROW_GO(0, C, kRowBatchedThreads);                           \
+  } while (0)
+  if (ch.flag) CSA_ROW_CASE(true);
+  else CSA_ROW_CASE(false);
+#undef CSA_ROW_CASE
 #undef CSA_ROW_GO
 }
 
