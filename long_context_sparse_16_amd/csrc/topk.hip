@@ -33,6 +33,8 @@
 //     rows of up to 32768 entries are held in registers and read once;
 //     rows of up to 16384, and rows read in batches, run two 512-thread
 //     workgroups per CU.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "select.h"
@@ -353,16 +355,19 @@ __global__ __launch_bounds__(NT) void topk_row_kernel(
       constexpr int64_t kStep = static_cast<int64_t>(NT) * kRowBatch;
       // (the loads are unconditional: past the row's end a lane reads entry
       // V - 1, and its value is replaced; 32-bit indices, V < 2^31)
+      // Full batches need no bounds: only the last one is clamped and masked.
       const int V32 = static_cast<int>(V);
-      for (int64_t base = 0; base < V; base += kStep) {
+      const __amdgpu_buffer_rsrc_t rs = store_rsrc(srow, V32 * 4);
+      auto batch = [&](int64_t base, auto tail) __attribute__((always_inline)) {
+        constexpr bool TAIL = decltype(tail)::value;
         const int j0 = static_cast<int>(base) + tid;
         float v[kRowBatch];
 #pragma unroll
-        for (int u = 0; u < kRowBatch; ++u) v[u] = srow[min(j0 + u * NT, V32 - 1)];
+        for (int u = 0; u < kRowBatch; ++u) v[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, j0 * 4, u * NT * 4, 0));
         uint32_t ns = 0, nc = 0;
 #pragma unroll
         for (int u = 0; u < kRowBatch; ++u) {
-          if (j0 + u * NT >= V32) v[u] = -INFINITY;  // below every finite bucket
+          if (TAIL && j0 + u * NT >= V32) v[u] = -INFINITY;  // below every finite bucket
           ns += v[u] >= hi ? 1u : 0u;
           nc += v[u] >= lo ? 1u : 0u;
           nup += v[u] >= mid ? 1u : 0u;
@@ -387,7 +392,10 @@ __global__ __launch_bounds__(NT) void topk_row_kernel(
             }
           }
         }
-      }
+      };
+      int64_t base = 0;
+      for (; base + kStep <= V; base += kStep) batch(base, std::false_type{});
+      if (base < V) batch(base, std::true_type{});
       if (count_up) {
         for (int o = 1; o < 64; o <<= 1) nup += __shfl_xor(nup, o);
         if ((tid & 63) == 0) atomicAdd(&sm.misc[6], nup);
