@@ -67,7 +67,7 @@ struct FinishSharedT {
   uint32_t misc[8];  // [0] bin [1] above [2] [3] cut [4] selected [5] candidates [6] flag [7] count
 };
 using FinishShared = FinishSharedT<kCandCap, kBitmapMaxEntries>;
-// The 512-thread row kernel, two workgroups per CU: 72.6 KB of LDS
+// The 512-thread row kernel, two workgroups per CU: 74,400 bytes of LDS
 // (4096 candidates; the bitmap area still holds the 4096-bin histogram).
 using RowShared2 = FinishSharedT<4096, 131072>;
 static_assert(131072 / 32 >= kHistBins, "the bitmap area holds the first-digit histogram");
@@ -176,7 +176,7 @@ __device__ void finish_row(SM& sm, const float* srow, int64_t V, uint32_t b1,
 
 // ------------------------------------------------------------- row path
 
-// Rows of up to kRowThreads * REGS entries are held in registers (REGS > 0):
+// Rows of up to NT * REGS entries are held in registers (REGS > 0):
 // the histogram loads go out first, then the row's, so the histogram is
 // usable before the row has arrived, and the row is read once.  Longer rows
 // (REGS == 0) are read in batches of kRowBatch independent loads per thread
@@ -188,7 +188,9 @@ constexpr int kRowBatch = 32;
 // Batched rows run 512-thread workgroups with the small LDS layout, two per
 // CU, so one row's cut and output phases overlap the other's reads.
 constexpr int kRowBatchedThreads = 512;
-constexpr int kRowRegs = 32;  // register-resident rows: V <= 32768 (1024 threads x 32)
+// register-resident rows: 32 per thread, V <= 16384 at 512 threads and
+// V <= 32768 at 1024
+constexpr int kRowRegs = 32;
 
 // LDS layout of the row kernel by workgroup size: 1024 threads (one
 // workgroup per CU) use the full layout, 512 threads (two per CU) the small
