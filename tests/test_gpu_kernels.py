@@ -294,12 +294,15 @@ def _topk_case(scores, V, k):
     return got
 
 
-@pytest.mark.parametrize("path", ["split", "few_rows", "row", "row_long", "row_longer"])
+@pytest.mark.parametrize("path", ["split", "few_rows", "row", "row_long", "row_longer",
+                                  "row_sorted"])
 def test_topk_random_and_ties(path):
     """split: few rows longer than one workgroup handles (classify + finish
     kernels); few_rows: few short rows, one workgroup each; row: many rows
     (short ones, held in registers); row_long, row_longer: many rows read
-    in batches of 32768 entries (two and three batches, the last ragged)."""
+    in batches of 32768 entries (two and three batches, the last ragged);
+    row_sorted: many rows longer than the row kernel's output bitmap, whose
+    selection is put in order by the sorting network instead."""
     say("topk", path)
     rng = np.random.default_rng(500)
     k = 100
@@ -311,8 +314,10 @@ def test_topk_random_and_ties(path):
         B, T, n_cap = 1, 300, 3000
     elif path == "row_long":
         B, T, n_cap = 1, 264, 40000
-    else:
+    elif path == "row_longer":
         B, T, n_cap = 1, 260, 72000
+    else:
+        B, T, n_cap = 1, 258, 140000
     s = rng.standard_normal((B, T, n_cap)).astype(np.float32) * 30 + 140
     s[:, 1] = rng.integers(0, 40, size=s[:, 1].shape)          # heavy ties
     s[:, 2] = np.where(rng.random(s[:, 2].shape) < 0.5, -0.0, 0.0)  # signed zeros
