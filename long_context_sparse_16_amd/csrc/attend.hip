@@ -770,6 +770,39 @@ __device__ __forceinline__ void attend_body(const AttParams& p) {
   // (raw_pos0 may be NULL when W == 0; its value is then unused)
   const int64_t t = p.pos0[b] + (row - b * p.T);
   const int64_t rp0 = (p.W > 0 ? p.raw_pos0 : p.pos0)[b];
+  // the register slots of the chunk gathers (see below)
+  const uint8_t* kc_b = p.kc + b * p.n_cap * RB;
+  const uint8_t* vc_b = p.vc + b * p.n_cap * RB;
+  const int pc = tid % kPieces;
+  const int key0 = tid / kPieces;
+  struct Slot {
+    u32x4 k[kPerThread], v[kPerThread];
+    bool ok[kPerThread];
+  };
+  Slot ring0, ring1;
+  auto pick = [&](auto slot) __attribute__((always_inline)) -> Slot& {
+    if constexpr (decltype(slot)::value == 0) return ring0;
+    else return ring1;
+  };
+  if constexpr (HCA) {
+    // HCA: the split's first two chunks are loaded before the row's
+    // position arrives, as if every slot were a visible entry (addresses
+    // clamped into the cache, so always in bounds); kept when that holds
+    // (spec_ok), which saves the position's round trip to memory
+    const int64_t sc0 = static_cast<int64_t>(split) * p.chunks_per_split;
+    auto spec = [&](Slot& S, int64_t chunk) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < kPerThread; ++r) {
+        const int64_t e =
+            min(chunk * kAttChunk + key0 + r * (kAttThreads / kPieces), p.n_cap - 1);
+        S.ok[r] = true;
+        S.k[r] = *reinterpret_cast<const u32x4*>(kc_b + e * RB + pc * 16);
+        S.v[r] = *reinterpret_cast<const u32x4*>(vc_b + e * RB + pc * 16);
+      }
+    };
+    spec(ring0, sc0);
+    spec(ring1, sc0 + 1);
+  }
   const int64_t n_ent =
       HCA ? uniform64(visible_entries(t, p.m, p.n_cap)) : static_cast<int64_t>(p.k);
   const int64_t n_slots = n_ent + p.W;
@@ -839,19 +872,6 @@ __device__ __forceinline__ void attend_body(const AttParams& p) {
   // split's end re-read its last chunk, so every load is issued
   // unconditionally (which keeps the compiler's wait counts partial); absent
   // keys are masked out of the softmax.
-  const uint8_t* kc_b = p.kc + b * p.n_cap * RB;
-  const uint8_t* vc_b = p.vc + b * p.n_cap * RB;
-  const int pc = tid % kPieces;
-  const int key0 = tid / kPieces;
-  struct Slot {
-    u32x4 k[kPerThread], v[kPerThread];
-    bool ok[kPerThread];
-  };
-  Slot ring0, ring1;
-  auto pick = [&](auto slot) __attribute__((always_inline)) -> Slot& {
-    if constexpr (decltype(slot)::value == 0) return ring0;
-    else return ring1;
-  };
   auto gather = [&](auto slot, int64_t chunk) __attribute__((always_inline)) {
     Slot& S = pick(slot);
     const int64_t s0 = chunk * kAttChunk;
@@ -1043,12 +1063,20 @@ __device__ __forceinline__ void attend_body(const AttParams& p) {
   auto clamp_chunk = [&](int i) __attribute__((always_inline)) {
     return c_begin + min(i, n_chunks - 1);
   };
+  // the speculative HCA chunk i is what gather() would load: every slot a
+  // visible entry and the chunk one of the split's
+  auto spec_ok = [&](int i) __attribute__((always_inline)) {
+    return i < n_chunks && (c_begin + i + 1) * kAttChunk <= n_ent;
+  };
   if (n_chunks > 0) {
     // HCA gathers need nothing from LDS: their first loads go out before the
-    // barrier that publishes s_ent / s_partial.
+    // barrier that publishes s_ent / s_partial.  The two speculative chunks
+    // loaded at the top are kept when they hold only visible entries of
+    // this split (the usual case); otherwise they are gathered again now
+    // that the row's position is known.
     if (HCA) {
-      gather(I0{}, clamp_chunk(0));
-      gather(I1{}, clamp_chunk(1));
+      if (!spec_ok(0)) gather(I0{}, clamp_chunk(0));
+      if (!spec_ok(1)) gather(I1{}, clamp_chunk(1));
     }
     __syncthreads();
     if (!HCA) {
@@ -1148,13 +1176,16 @@ __global__ __launch_bounds__(kAttThreads, 4) void attend_wide_kernel(AttParams p
 // batch (maxima, sums, partial outputs; indices clamped so none is
 // conditional) is issued before any is used, and the batch is folded into a
 // running (max, sum, O) in split order, so the result does not depend on
-// scheduling.
+// scheduling.  Workgroups of NT threads: 256, or one wave when rows x
+// head tiles of 256 threads would leave CUs idle (few rows), so that the
+// loads of a row's partials are issued from more CUs.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeThreadsSmall = 64;
 
-template <int D, int MB>
-__global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(AttParams p) {
+template <int D, int MB, int NT>
+__global__ __launch_bounds__(NT) void attend_merge_kernel(AttParams p) {
   constexpr int kTPH = D / 4;  // threads per head
-  constexpr int kHPB = kMergeThreads / kTPH;
+  constexpr int kHPB = NT / kTPH;
   const int n_tiles = static_cast<int>((p.H + kHPB - 1) / kHPB);
   int64_t row;
   int tile;
@@ -1168,7 +1199,7 @@ __global__ __launch_bounds__(kMergeThreads) void attend_merge_kernel(AttParams p
   const int d4 = threadIdx.x % kTPH;
   if (p.hist_zero) {  // the row's top-k histogram, read by every split of the attention launch
     uint32_t* hz = p.hist_zero + row * kTopkHistBins;
-    for (int i = tile * kMergeThreads + threadIdx.x; i < kTopkHistBins; i += n_tiles * kMergeThreads)
+    for (int i = tile * NT + threadIdx.x; i < kTopkHistBins; i += n_tiles * NT)
       hz[i] = 0u;
   }
   if (h >= p.H) return;
@@ -1242,6 +1273,20 @@ size_t attend_workspace_bytes(int64_t rows, int64_t H, int64_t D, int64_t n_slot
   return static_cast<size_t>(rows) * s.splits * H * (D + 2) * sizeof(float);
 }
 
+template <int D>
+void launch_merge(int splits, bool small, dim3 grid, const AttParams& p, hipStream_t stream) {
+  // the smallest batch that holds the row's splits
+  if (small) {
+    if (splits > 16) attend_merge_kernel<D, 32, kMergeThreadsSmall><<<grid, kMergeThreadsSmall, 0, stream>>>(p);
+    else if (splits > 8) attend_merge_kernel<D, 16, kMergeThreadsSmall><<<grid, kMergeThreadsSmall, 0, stream>>>(p);
+    else attend_merge_kernel<D, 8, kMergeThreadsSmall><<<grid, kMergeThreadsSmall, 0, stream>>>(p);
+  } else {
+    if (splits > 16) attend_merge_kernel<D, 32, kMergeThreads><<<grid, kMergeThreads, 0, stream>>>(p);
+    else if (splits > 8) attend_merge_kernel<D, 16, kMergeThreads><<<grid, kMergeThreads, 0, stream>>>(p);
+    else attend_merge_kernel<D, 8, kMergeThreads><<<grid, kMergeThreads, 0, stream>>>(p);
+  }
+}
+
 int launch_attend(const void* q, int dtype, const void* kc, const void* vc, const int32_t* idx,
                   int k, int hca_m, const void* kr, const void* vr, const int64_t* raw_pos0,
                   int64_t R, const int64_t* pos0, int64_t B, int64_t T, int64_t H, int64_t D,
@@ -1289,7 +1334,9 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
                                : dim3(static_cast<unsigned>(sp.splits), static_cast<unsigned>(rows));
   // (bf16 keys, d 128, given indices: its LDS fits twice in a CU)
   const bool wide = static_cast<int64_t>(grid.x) * grid.y >= kAttWideGroups;
-  const int64_t m_tiles = (H + kMergeThreads / (D / 4) - 1) / (kMergeThreads / (D / 4));
+  const bool m_small = rows * ((H + kMergeThreads / (D / 4) - 1) / (kMergeThreads / (D / 4))) < 256;
+  const int m_nt = m_small ? kMergeThreadsSmall : kMergeThreads;
+  const int64_t m_tiles = (H + m_nt / (D / 4) - 1) / (m_nt / (D / 4));
   const dim3 mgrid = p.xcd_rows ? dim3(static_cast<unsigned>(xcd_grid_size(rows, m_tiles)))
                                 : dim3(static_cast<unsigned>(m_tiles), static_cast<unsigned>(rows));
 #define CSA_ATT_CASE(DT, DD)                                                        \
@@ -1304,12 +1351,7 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
       attend_wide_kernel<1, 128, false, 0><<<grid, kAttThreads, 0, stream>>>(p);    \
     else                                                                            \
       attend_kernel<DT, DD, false, 0><<<grid, kAttThreads, 0, stream>>>(p);         \
-    if (sp.splits > 16)                                                             \
-      attend_merge_kernel<DD, 32><<<mgrid, kMergeThreads, 0, stream>>>(p);          \
-    else if (sp.splits > 8)                                                         \
-      attend_merge_kernel<DD, 16><<<mgrid, kMergeThreads, 0, stream>>>(p);          \
-    else if (sp.splits > 1)                                                         \
-      attend_merge_kernel<DD, 8><<<mgrid, kMergeThreads, 0, stream>>>(p);           \
+    if (sp.splits > 1) launch_merge<DD>(sp.splits, m_small, mgrid, p, stream);      \
     return hipGetLastError() == hipSuccess ? 0 : -1;                                \
   }
   CSA_ATT_CASE(0, 64)
