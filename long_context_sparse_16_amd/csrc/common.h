@@ -97,6 +97,10 @@ __device__ __forceinline__ float relu(float x) {
 
 // ----------------------------------------------------- range-checked stores
 
+// Cache-policy operand of the raw buffer stores: sc1 makes a store
+// device-scope, written through the XCD's L2 to memory.
+constexpr int kCachePolicySc1 = 16;
+
 // Raw buffer descriptor over [base, base + nbytes): stores at byte offsets
 // >= nbytes are dropped by the hardware range check.  The caller passes
 // wave-uniform values; they are moved to scalar registers explicitly so the
