@@ -183,6 +183,33 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const auto& wq = qf.wq;
 
   const int64_t b = seq_of_row(row, T);
+  // FP8: each lane also fetches the fp32 scale of its column's entry with
+  // the group's keys; MXFP4: the entry's four E8M0 block scales as one
+  // word, whose byte g the MFMA step shifts into place.  (KScale holds
+  // either.)
+  using KScale = std::conditional_t<DTYPE == 3, uint32_t, float>;
+  constexpr int kGroupEnt = kGroup * kIdxTile;
+  u32x4 buf0[kGroup][kVec], buf1[kGroup][kVec];
+  KScale ks0[kGroup], ks1[kGroup];
+  {
+    // This wave's first group is loaded before the row's position arrives,
+    // as if every entry of the workgroup's range were visible (addresses
+    // clamped into the cache, so always in bounds): kept when the group is
+    // full (the same addresses), which takes the position's round trip to
+    // memory off the start of the scan.
+    const int64_t e_first = static_cast<int64_t>(blockIdx.x) * tiles_per_wg * kIdxTile +
+                            static_cast<int64_t>(wave) * kGroupEnt;
+#pragma unroll
+    for (int tt = 0; tt < kGroup; ++tt) {
+      const int64_t e = min(e_first + tt * kIdxTile + col, n_cap - 1);
+      const u32x4* src = reinterpret_cast<const u32x4*>(ki + (b * n_cap + e) * kRowBytes +
+                                                        g * Tr::kLaneBytes);
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) buf0[tt][v] = src[v];
+      if constexpr (DTYPE == 2) ks0[tt] = ki_scale[b * n_cap + e];
+      if constexpr (DTYPE == 3) ks0[tt] = reinterpret_cast<const uint32_t*>(ki_scale)[b * n_cap + e];
+    }
+  }
   const int64_t t = pos0[b] + (row - b * T);
   const int64_t V = uniform64(visible_entries(t, m, n_cap));
   const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * tiles_per_wg;
@@ -204,7 +231,6 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   // loop body is straight-line code with static wait counts.  A trailing
   // partial group is loaded once with clamped addresses (past-the-end
   // columns are computed from a valid row and never stored).
-  constexpr int kGroupEnt = kGroup * kIdxTile;
   const int n_ent_wg =
       static_cast<int>(min<int64_t>(V - e_begin, static_cast<int64_t>(tiles_per_wg) * kIdxTile));
   const int n_full = n_ent_wg / kGroupEnt;
@@ -249,11 +275,6 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     }
   }
 
-  // FP8: each lane also fetches the fp32 scale of its column's entry with
-  // the group's keys; MXFP4: the entry's four E8M0 block scales as one
-  // word, whose byte g the MFMA step shifts into place.  (KScale holds
-  // either.)
-  using KScale = std::conditional_t<DTYPE == 3, uint32_t, float>;
   const float* ksc = DTYPE == 2 ? ki_scale + b * n_cap + e_begin : nullptr;
   const uint32_t* ksw =
       DTYPE == 3 ? reinterpret_cast<const uint32_t*>(ki_scale) + b * n_cap + e_begin : nullptr;
@@ -392,15 +413,13 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     for (int i = threadIdx.x; i < kTopkHistBins; i += 256) s_hist[i] = 0u;
     __syncthreads();
   }
-  u32x4 buf0[kGroup][kVec], buf1[kGroup][kVec];
-  KScale ks0[kGroup], ks1[kGroup];
   // This wave's full groups are wave, wave + 4, ...: n_my of them, taken in
   // pairs (one per buffer) with a single trailing group when n_my is odd.
   // Every loop iteration runs both halves, so the body is straight-line.
   const int n_my = wave < n_full ? (n_full - 1 - wave) / kIdxWaves + 1 : 0;
-  // (first group through clamped addresses, unconditionally, so the wait
-  // for the query loads below leaves it in flight; same data when full)
-  load_tail(wave, buf0, ks0);
+  // (the first group was loaded speculatively at the top; a group that is
+  // not full, or past the end, is loaded again through clamped addresses)
+  if (wave >= n_full) load_tail(wave, buf0, ks0);
   qf.finish(H_I, true, g);
   int j = 0;
   for (; j + 2 <= n_my; j += 2) {

@@ -558,27 +558,40 @@ struct ClassifyShared {
   uint32_t tab[kSelPer * kSelWaves];  // (pass, wave) counts, sure | cand << 16
 };
 
-// Classify slice sl of row `row` (entries [j0, j1), j0 < V, V > k): writes
-// the slice's lists and counts and returns the bucket b1.
-__device__ uint32_t classify_slice(ClassifyShared& cs, const float* __restrict__ srow,
-                                   int64_t row, int sl, int64_t j0, int64_t j1, int k,
-                                   SplitWs ws) {
+// The slice's histogram and score loads (issued by classify_load before
+// the row's length is known: scores past the row's end are read from
+// clamped, in-bounds addresses and never used).
+struct ClassifyLoads {
+  u32x4 hq[kHistPerSel / 4];
+  float sv[kSelPer];
+};
+
+__device__ __forceinline__ void classify_load(ClassifyLoads& ld, const float* __restrict__ srow,
+                                              int64_t row, int64_t j0, int64_t n_cap,
+                                              const SplitWs& ws) {
+  const int tid = threadIdx.x;
+  // bins [kHistBins - 16 (tid + 1), kHistBins - 16 tid), 64-byte aligned
+  const uint32_t* gh = ws.hist + row * kHistBins + (kHistBins - kHistPerSel * (tid + 1));
+#pragma unroll
+  for (int q = 0; q < kHistPerSel / 4; ++q) ld.hq[q] = reinterpret_cast<const u32x4*>(gh)[q];
+#pragma unroll
+  for (int it = 0; it < kSelPer; ++it) {
+    const int64_t j = j0 + it * kSelThreads + tid;
+    ld.sv[it] = srow[j < n_cap ? j : n_cap - 1];
+  }
+}
+
+// Classify slice sl of row `row` (entries [j0, j1), j0 < V, V > k) from its
+// loads: writes the slice's lists and counts and returns the bucket b1.
+__device__ uint32_t classify_slice(ClassifyShared& cs, const ClassifyLoads& ld, int64_t row,
+                                   int sl, int64_t j0, int64_t j1, int k, SplitWs ws) {
   uint32_t* scan = cs.scan;
   uint32_t* res = cs.res;
   uint32_t* tab = cs.tab;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  // bins [kHistBins - 16 (tid + 1), kHistBins - 16 tid), 64-byte aligned
-  const uint32_t* gh = ws.hist + row * kHistBins + (kHistBins - kHistPerSel * (tid + 1));
-  u32x4 hq[kHistPerSel / 4];
-#pragma unroll
-  for (int q = 0; q < kHistPerSel / 4; ++q) hq[q] = reinterpret_cast<const u32x4*>(gh)[q];
-  float sv[kSelPer];
-#pragma unroll
-  for (int it = 0; it < kSelPer; ++it) {
-    const int64_t j = j0 + it * kSelThreads + tid;
-    sv[it] = srow[j < j1 ? j : j1 - 1];
-  }
+  const auto& hq = ld.hq;
+  const auto& sv = ld.sv;
   uint32_t local = 0;
 #pragma unroll
   for (int q = 0; q < kHistPerSel / 4; ++q) local += hq[q][0] + hq[q][1] + hq[q][2] + hq[q][3];
@@ -667,11 +680,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_classify_kernel(
     sl = blockIdx.x;
   }
   const int64_t b = seq_of_row(row, T);
+  const int64_t j0 = static_cast<int64_t>(sl) * kSelEntries;
+  // the slice's loads go out before the row's position arrives
+  ClassifyLoads ld;
+  if (j0 < n_cap) classify_load(ld, scores + row * n_cap, row, j0, n_cap, ws);
   const int64_t t = pos0[b] + (row - b * T);
   const int64_t V = uniform64(visible_entries(t, m, n_cap));
-  const int64_t j0 = static_cast<int64_t>(sl) * kSelEntries;
   if (V <= k || j0 >= V) return;
-  classify_slice(cs, scores + row * n_cap, row, sl, j0, min(V, j0 + kSelEntries), k, ws);
+  classify_slice(cs, ld, row, sl, j0, min(V, j0 + kSelEntries), k, ws);
 }
 
 static void launch_classify(const float* scores, const int64_t* pos0, int64_t T, int64_t n_cap,
