@@ -197,6 +197,13 @@ def hca_bytes(cfg) -> int:
     return step_bytes(cfg)
 
 
+def hca_splits(cfg) -> int:
+    """More than one when the HCA attention splits its rows over workgroups
+    (a merge launch follows): the library then needs a partials workspace."""
+    import long_context_sparse_16_amd as csa
+    return 2 if csa.hca_attend_workspace_size(cfg.B, cfg.T, cfg.H, cfg.d, cfg.n_cap, cfg.W) > 0 else 1
+
+
 # ------------------------------------------------------------ CPU baseline
 
 def cpu_model() -> str:
@@ -373,6 +380,33 @@ class Timer:
                 for i, (name, _) in enumerate(stages)}
 
 
+    def kernel_samples(self, stages, target, n_kernels, n):
+        """Kernel durations (us) of n cold passes over `stages`: from the
+        start of the first to the end of the n_kernels-th kernel that stage
+        `target` launches, recorded by those kernels' own launches
+        (csa_time_next_kernels: hipExtLaunchKernelGGL start / stop events on
+        the kernels' stream), so without the dispatch around the call."""
+        import long_context_sparse_16_amd as csa
+        torch = self.torch
+        out = []
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)  # creates the HIP events the launches record into
+        b.record(self.stream)
+        try:
+            for _ in range(n):
+                self.flush()
+                for name, fn in stages:
+                    if name == target:
+                        csa.csa_time_next_kernels(a, b, n_kernels)
+                    fn()
+                torch.cuda.synchronize()
+                out.append(a.elapsed_time(b) * 1e3)
+        finally:
+            csa.csa_time_next_kernels(None, None, 0)
+        return out
+
+
 def stats(xs) -> dict:
     import numpy as np
     a = np.asarray(xs, dtype=np.float64)
@@ -440,8 +474,14 @@ def measure(cfg, K, W, timer, torch):
     n_indexed = (sum(1 for k in cfg.layers if k == "csa") if cfg.layers else 1) if cfg.k > 0 else 0
     if n_indexed and not cfg.backward:
         res["entries_scored_per_s"] = n_indexed * cfg.B * visible_sum(cfg) / (med * 1e-6)
-    # roofline of the dominant kernel (mean of its event-timed cold launches,
-    # which is what a rocprofv3 kernel trace of this run averages)
+    # roofline of the dominant kernel: the mean of its cold launches, timed
+    # by the launches' own start / stop events (the kernel time a rocprofv3
+    # kernel trace of this run averages); `call_frac` is the same bytes over
+    # the event pair around the whole call (dispatch included)
+    def kernel_mean(stage, n_kernels=1):
+        return stats(timer.kernel_samples(stages, stage, n_kernels, max(10, K // 2)))["mean"]
+
+    call_us = None
     if cfg.backward:
         fl = backward_flops(cfg)
         t_us = st_stats["backward"]["mean"]
@@ -459,24 +499,33 @@ def measure(cfg, K, W, timer, torch):
                 "peak": HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": step_bytes(lay)}
     elif cfg.hca:
         kb = hca_bytes(cfg)
-        roof = {"kernel": "attend_kernel (HCA) + merge", "bound": "hbm",
-                "achieved": kb / (st_stats["attend"]["mean"] * 1e3), "peak": HBM_PEAK_GBS,
+        # the attention launch and, when the rows are split, the merge
+        n_k = 2 if hca_splits(cfg) > 1 else 1
+        t_us, call_us = kernel_mean("attend", n_k), st_stats["attend"]["mean"]
+        roof = {"kernel": "attend_kernel (HCA) + merge" if n_k == 2 else "attend_kernel (HCA)",
+                "bound": "hbm", "achieved": kb / (t_us * 1e3), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "traffic": measured_traffic(cfg.name, "attend_kernel"),
                 "algorithmic_bytes": kb}
     elif cfg.T >= 8:
         fl = indexer_flops(cfg)
+        t_us, call_us = kernel_mean("index"), st_stats["index"]["mean"]
         roof = {"kernel": "indexer_prefill_kernel", "bound": "mfma",
-                "achieved": fl / (st_stats["index"]["mean"] * 1e6),
+                "achieved": fl / (t_us * 1e6),
                 "peak": MFMA_PEAK_TFLOPS[index_dtype(cfg)], "unit": "TFLOP/s",
                 "traffic": None, "algorithmic_flops": fl}
     else:
         ib = indexer_bytes(cfg)
         stage = "index" if "index" in st_stats else "select"
+        t_us, call_us = kernel_mean(stage), st_stats[stage]["mean"]
         roof = {"kernel": "indexer_kernel", "bound": "hbm",
-                "achieved": ib / (st_stats[stage]["mean"] * 1e3), "peak": HBM_PEAK_GBS,
+                "achieved": ib / (t_us * 1e3), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "traffic": measured_traffic(cfg.name, "indexer_kernel"),
                 "algorithmic_bytes": ib}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    if call_us is not None:
+        roof["kernel_us"] = t_us
+        roof["call_us"] = call_us
+        roof["call_frac"] = roof["frac"] * t_us / call_us
     if cfg.T == 1 and not cfg.backward:
         sb = step_bytes(cfg) if not cfg.layers else sum(
             step_bytes(WL_layer(cfg, i)) for i in range(len(cfg.layers)))

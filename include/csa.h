@@ -95,6 +95,22 @@ const char* csa_build_digest(void);
  * may be captured in a HIP graph).  ws 16-byte aligned, ws_bytes % 4 == 0. */
 int csa_workspace_clear(void* ws, size_t ws_bytes, void* stream);
 
+/* Kernel timing, for callers that measure one kernel of a call rather than
+ * the call with the dispatch around it.  The next n kernels that library
+ * calls made on the calling host thread launch (the kernels of csa_compress,
+ * the quantizers, csa_index_scores / csa_topk / csa_index_topk,
+ * csa_decode_index_topk, csa_select_attend, csa_decode, csa_decode_noalloc,
+ * csa_attend and hca_attend; the backward calls' kernels and
+ * csa_workspace_clear do not count) are launched with hipExtLaunchKernelGGL:
+ * the first records start_event when it starts, the n-th records stop_event
+ * when it ends, so hipEventElapsedTime(start_event, stop_event) is the time
+ * from the first kernel's start to the n-th kernel's end.  start_event and
+ * stop_event are hipEvent_t created by the caller (non-NULL when n > 0), not
+ * owned by the library.  n = 0 cancels a pending request; a request stays
+ * pending until n kernels have been launched.  Returns CSA_OK, or
+ * CSA_ERR_NULL / CSA_ERR_SHAPE for missing events or n < 0. */
+int csa_time_next_kernels(void* start_event, void* stop_event, int n);
+
 /*
  * csa_compress -- the token-level compressor (takeshell.com 2.1: every m
  * tokens' KV entries are compressed into one entry by weighted

@@ -49,6 +49,7 @@ _SIGNATURES = {
     "csa_abi_version": (_i, []),
     "csa_build_digest": (ctypes.c_char_p, []),
     "csa_workspace_clear": (_i, [_vp, _sz, _vp]),
+    "csa_time_next_kernels": (_i, [_vp, _vp, _i]),
     "csa_compress": (_i, [_vp, _i, _vp, _i64, _i64, _i64, _i, _i64, _i64, _vp, _i, _i64, _i64, _vp]),
     "csa_quantize_fp8_rows": (_i, [_vp, _i, _i64, _i64, _vp, _vp, _vp]),
     "csa_quantize_mxfp4_rows": (_i, [_vp, _i, _i64, _i64, _vp, _vp, _vp]),
@@ -305,6 +306,19 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 def csa_workspace_clear(ws: torch.Tensor, stream=None) -> None:
     _check("csa_workspace_clear", _lib.csa_workspace_clear(
         _ptr(ws), ws.numel() * ws.element_size() // 4 * 4, _stream(stream, ws.device)))
+
+
+def csa_time_next_kernels(start_event, stop_event, n: int) -> None:
+    """Record start_event when the next library kernel starts and stop_event
+    when the n-th ends (torch.cuda.Event objects with enable_timing, already
+    recorded once so that their HIP events exist, or raw hipEvent_t values);
+    n = 0 cancels."""
+    def handle(e):
+        if e is None:
+            return None
+        return ctypes.c_void_p(e.cuda_event if hasattr(e, "cuda_event") else int(e))
+    _check("csa_time_next_kernels",
+           _lib.csa_time_next_kernels(handle(start_event), handle(stop_event), int(n)))
 
 
 def _workspace(ws, need, dev):

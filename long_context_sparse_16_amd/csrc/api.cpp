@@ -131,6 +131,27 @@ int check_attend_args(const void* q, int q_dtype, const void* kc, const void* vc
 
 }  // namespace
 
+namespace csa {
+
+// The calling thread's pending kernel-timing request (csa_time_next_kernels).
+struct TimingRequest {
+  hipEvent_t start = nullptr, stop = nullptr;
+  int remaining = 0, total = 0;
+};
+thread_local TimingRequest g_timing;
+
+LaunchEvents take_launch_events() {
+  TimingRequest& r = g_timing;
+  LaunchEvents ev{nullptr, nullptr};
+  if (r.remaining <= 0) return ev;
+  if (r.remaining == r.total) ev.start = r.start;
+  if (r.remaining == 1) ev.stop = r.stop;
+  if (--r.remaining == 0) r = TimingRequest{};
+  return ev;
+}
+
+}  // namespace csa
+
 extern "C" {
 
 const char* csa_status_string(int status) {
@@ -158,6 +179,16 @@ int csa_abi_version(void) { return 4; }
 static const char kSourceDigest[] = "csa-source-digest:" CSA_SOURCE_DIGEST;
 
 const char* csa_build_digest(void) { return kSourceDigest + sizeof("csa-source-digest:") - 1; }
+
+int csa_time_next_kernels(void* start_event, void* stop_event, int n) {
+  const char* fn = "csa_time_next_kernels";
+  CSA_REQUIRE(n >= 0, CSA_ERR_SHAPE, "%s: n must be >= 0", fn);
+  CSA_REQUIRE(n == 0 || (start_event && stop_event), CSA_ERR_NULL,
+              "%s: start_event and stop_event must be non-NULL", fn);
+  csa::g_timing = csa::TimingRequest{static_cast<hipEvent_t>(start_event),
+                                     static_cast<hipEvent_t>(stop_event), n, n};
+  return ok();
+}
 
 int csa_workspace_clear(void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "csa_workspace_clear";

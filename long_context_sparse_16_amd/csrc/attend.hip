@@ -1285,13 +1285,13 @@ template <int D>
 void launch_merge(int splits, bool small, dim3 grid, const AttParams& p, hipStream_t stream) {
   // the smallest batch that holds the row's splits
   if (small) {
-    if (splits > 16) attend_merge_kernel<D, 32, kMergeThreadsSmall><<<grid, kMergeThreadsSmall, 0, stream>>>(p);
-    else if (splits > 8) attend_merge_kernel<D, 16, kMergeThreadsSmall><<<grid, kMergeThreadsSmall, 0, stream>>>(p);
-    else attend_merge_kernel<D, 8, kMergeThreadsSmall><<<grid, kMergeThreadsSmall, 0, stream>>>(p);
+    if (splits > 16) launch_kernel(attend_merge_kernel<D, 32, kMergeThreadsSmall>, grid, kMergeThreadsSmall, stream, p);
+    else if (splits > 8) launch_kernel(attend_merge_kernel<D, 16, kMergeThreadsSmall>, grid, kMergeThreadsSmall, stream, p);
+    else launch_kernel(attend_merge_kernel<D, 8, kMergeThreadsSmall>, grid, kMergeThreadsSmall, stream, p);
   } else {
-    if (splits > 16) attend_merge_kernel<D, 32, kMergeThreads><<<grid, kMergeThreads, 0, stream>>>(p);
-    else if (splits > 8) attend_merge_kernel<D, 16, kMergeThreads><<<grid, kMergeThreads, 0, stream>>>(p);
-    else attend_merge_kernel<D, 8, kMergeThreads><<<grid, kMergeThreads, 0, stream>>>(p);
+    if (splits > 16) launch_kernel(attend_merge_kernel<D, 32, kMergeThreads>, grid, kMergeThreads, stream, p);
+    else if (splits > 8) launch_kernel(attend_merge_kernel<D, 16, kMergeThreads>, grid, kMergeThreads, stream, p);
+    else launch_kernel(attend_merge_kernel<D, 8, kMergeThreads>, grid, kMergeThreads, stream, p);
   }
 }
 
@@ -1350,15 +1350,15 @@ int launch_attend(const void* q, int dtype, const void* kc, const void* vc, cons
 #define CSA_ATT_CASE(DT, DD)                                                        \
   if (dtype == DT && D == DD) {                                                     \
     if (hca)                                                                        \
-      attend_kernel<DT, DD, true, 0><<<grid, kAttThreads, 0, stream>>>(p);          \
+      launch_kernel(attend_kernel<DT, DD, true, 0>, grid, kAttThreads, stream, p);          \
     else if (sel && sel->regs)                                                      \
-      attend_kernel<DT, DD, false, 2><<<grid, kAttThreads, 0, stream>>>(p);         \
+      launch_kernel(attend_kernel<DT, DD, false, 2>, grid, kAttThreads, stream, p);         \
     else if (sel)                                                                   \
-      attend_kernel<DT, DD, false, 1><<<grid, kAttThreads, 0, stream>>>(p);         \
+      launch_kernel(attend_kernel<DT, DD, false, 1>, grid, kAttThreads, stream, p);         \
     else if (DT == 1 && DD == 128 && wide)                                          \
-      attend_wide_kernel<1, 128, false, 0><<<grid, kAttThreads, 0, stream>>>(p);    \
+      launch_kernel(attend_wide_kernel<1, 128, false, 0>, grid, kAttThreads, stream, p);    \
     else                                                                            \
-      attend_kernel<DT, DD, false, 0><<<grid, kAttThreads, 0, stream>>>(p);         \
+      launch_kernel(attend_kernel<DT, DD, false, 0>, grid, kAttThreads, stream, p);         \
     if (sp.splits > 1) launch_merge<DD>(sp.splits, m_small, mgrid, p, stream);      \
     return hipGetLastError() == hipSuccess ? 0 : -1;                                \
   }

@@ -74,10 +74,10 @@ int launch_compress_bwd(const void* x, int dtype, const float* z, const float* d
   const int64_t nb = n_tok / m;
   dim3 grid(static_cast<unsigned>((nb * d + 255) / 256), static_cast<unsigned>(B));
   if (dtype == 0)
-    compress_bwd_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), z, dc, dx, dz,
+    launch_kernel(compress_bwd_kernel<float>, grid, 256, s, static_cast<const float*>(x), z, dc, dx, dz,
                                                     nb, d, m, x_sb, z_sb);
   else
-    compress_bwd_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), z, dc,
+    launch_kernel(compress_bwd_kernel<uint16_t>, grid, 256, s, static_cast<const uint16_t*>(x), z, dc,
                                                        dx, dz, nb, d, m, x_sb, z_sb);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
@@ -89,11 +89,11 @@ int launch_compress(const void* x, int dtype, const float* z, int64_t B, int64_t
   const int64_t total = nb * d;
   dim3 grid(static_cast<unsigned>((total + 255) / 256), static_cast<unsigned>(B));
   if (dtype == 0) {
-    compress_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), z,
+    launch_kernel(compress_kernel<float>, grid, 256, s, static_cast<const float*>(x), z,
                                                 static_cast<float*>(cache), nb, d, m, x_sb,
                                                 z_sb, n_cap, first_entry);
   } else {
-    compress_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), z,
+    launch_kernel(compress_kernel<uint16_t>, grid, 256, s, static_cast<const uint16_t*>(x), z,
                                                    static_cast<uint16_t*>(cache), nb, d, m,
                                                    x_sb, z_sb, n_cap, first_entry);
   }
@@ -169,10 +169,10 @@ int launch_quantize_mxfp4_rows(const void* x, int dtype, int64_t rows, int64_t d
                                uint8_t* scales, hipStream_t s) {
   dim3 grid(static_cast<unsigned>((rows + 3) / 4));
   if (dtype == 0) {
-    quantize_mxfp4_rows_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), codes,
+    launch_kernel(quantize_mxfp4_rows_kernel<float>, grid, 256, s, static_cast<const float*>(x), codes,
                                                            scales, rows, static_cast<int>(d));
   } else {
-    quantize_mxfp4_rows_kernel<uint16_t><<<grid, 256, 0, s>>>(
+    launch_kernel(quantize_mxfp4_rows_kernel<uint16_t>, grid, 256, s, 
         static_cast<const uint16_t*>(x), codes, scales, rows, static_cast<int>(d));
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -182,10 +182,10 @@ int launch_quantize_fp8_rows(const void* x, int dtype, int64_t rows, int64_t d,
                              uint8_t* codes, float* scales, hipStream_t s) {
   dim3 grid(static_cast<unsigned>((rows + 3) / 4));
   if (dtype == 0) {
-    quantize_rows_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), codes,
+    launch_kernel(quantize_rows_kernel<float>, grid, 256, s, static_cast<const float*>(x), codes,
                                                      scales, rows, static_cast<int>(d));
   } else {
-    quantize_rows_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x),
+    launch_kernel(quantize_rows_kernel<uint16_t>, grid, 256, s, static_cast<const uint16_t*>(x),
                                                         codes, scales, rows,
                                                         static_cast<int>(d));
   }

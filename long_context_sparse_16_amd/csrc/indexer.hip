@@ -694,7 +694,7 @@ static void launch_idx_t(const void* qi, const float* qs, const float* w, const 
     dim3 pgrid(static_cast<unsigned>((T + kPfTok - 1) / kPfTok), static_cast<unsigned>(B));
     const CoarseHist ch = coarse ? *coarse : CoarseHist{nullptr, nullptr};
 #define CSA_PF_GO(R, H)                                                                        \
-  indexer_prefill_kernel<DT, R, H><<<pgrid, kPfThreads, 0, s>>>(q8, qs, w, k8, ks, pos0, T, H_I, \
+  launch_kernel(indexer_prefill_kernel<DT, R, H>, pgrid, kPfThreads, s, q8, qs, w, k8, ks, pos0, T, H_I, \
                                                                 n_cap, m, scores, ch)
     if (ch.hist) {
       if (relu) CSA_PF_GO(true, true); else CSA_PF_GO(false, true);
@@ -713,10 +713,10 @@ static void launch_idx_t(const void* qi, const float* qs, const float* w, const 
 #define CSA_IDX_GO(R, HST)                                                                   \
   do {                                                                                       \
     if (DTYPE == 1 && fc.kr != nullptr)                                                      \
-      indexer_kernel<DTYPE, DI, R, HST, DTYPE == 1><<<grid, 256, 0, s>>>(                    \
+      launch_kernel(indexer_kernel<DTYPE, DI, R, HST, DTYPE == 1>, grid, 256, s,                     \
           q8, qs, w, k8, ks, pos0, T, H_I, n_cap, m, tiles_per_wg, scores, hist, k, fc);     \
     else                                                                                     \
-      indexer_kernel<DTYPE, DI, R, HST, false><<<grid, 256, 0, s>>>(                         \
+      launch_kernel(indexer_kernel<DTYPE, DI, R, HST, false>, grid, 256, s,                          \
           q8, qs, w, k8, ks, pos0, T, H_I, n_cap, m, tiles_per_wg, scores, hist, k, fc);     \
   } while (0)
   if (relu) {

@@ -3,11 +3,36 @@
 // -2 if no kernel variant matches the (already validated) arguments.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace csa {
+
+// Kernel timing (csa_time_next_kernels): the events a launch records
+// around itself, taken from the calling host thread's pending request;
+// both null when there is none.
+struct LaunchEvents {
+  hipEvent_t start;  // recorded when the kernel starts
+  hipEvent_t stop;   // recorded when the kernel ends
+};
+LaunchEvents take_launch_events();
+
+// Every kernel of the forward calls is launched through here: a plain
+// launch, or, when a timing request is pending, hipExtLaunchKernelGGL with
+// the request's events (the kernel's own start / end, without the dispatch
+// around it).  Arguments are converted to the kernel's parameter types.
+template <typename... P, typename... A>
+inline void launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s,
+                          A... args) {
+  const LaunchEvents ev = take_launch_events();
+  if (ev.start != nullptr || ev.stop != nullptr)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0u, s, ev.start, ev.stop, 0u,
+                          static_cast<P>(args)...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0u, s, static_cast<P>(args)...);
+}
 
 // Block compression fused into the decode indexer (bf16 caches): when the
 // new token at t completes a block ((t + 1) % m == 0), the block's K and V

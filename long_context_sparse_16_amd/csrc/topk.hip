@@ -693,11 +693,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_classify_kernel(
 static void launch_classify(const float* scores, const int64_t* pos0, int64_t T, int64_t n_cap,
                             int m, int k, const SplitWs& w, int64_t rows, hipStream_t s) {
   if (xcd_mappable(rows))
-    topk_classify_kernel<<<dim3(static_cast<unsigned>(xcd_grid_size(rows, w.n_sl))), kSelThreads,
-                           0, s>>>(scores, pos0, T, n_cap, m, k, w, rows);
+    launch_kernel(topk_classify_kernel, dim3(static_cast<unsigned>(xcd_grid_size(rows, w.n_sl))), kSelThreads, s, scores, pos0, T, n_cap, m, k, w, rows);
   else
-    topk_classify_kernel<<<dim3(static_cast<unsigned>(w.n_sl), static_cast<unsigned>(rows)),
-                           kSelThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, w, 0);
+    launch_kernel(topk_classify_kernel, dim3(static_cast<unsigned>(w.n_sl), static_cast<unsigned>(rows)), kSelThreads, s, scores, pos0, T, n_cap, m, k, w, 0);
 }
 
 // Resolve one row from its slices' lists and return its histogram and
@@ -943,7 +941,7 @@ static void launch_row_kernel(const float* scores, const int64_t* pos0, int64_t 
   const bool regs = n_cap <= static_cast<int64_t>(kRowThreads) * kRowRegs;
   const bool regs_small = n_cap <= static_cast<int64_t>(kRowBatchedThreads) * kRowRegs;
 #define CSA_ROW_GO(R, C, NT) \
-  topk_row_kernel<R, C, NT><<<g, NT, 0, s>>>(scores, pos0, T, n_cap, m, k, idx, hist, ch)
+  launch_kernel(topk_row_kernel<R, C, NT>, g, NT, s, scores, pos0, T, n_cap, m, k, idx, hist, ch)
 #define CSA_ROW_CASE(C)                                                  \
   do {                                                                   \
     if (regs_small) CSA_ROW_GO(kRowRegs, C, kRowBatchedThreads);         \
@@ -965,9 +963,9 @@ int launch_topk(const float* scores, const int64_t* pos0, int64_t B, int64_t T, 
     // finishes
     SplitWs w = split_ws(ws, rows, n_cap);
     dim3 grid(static_cast<unsigned>(w.n_sl), static_cast<unsigned>(rows));
-    if (!hist_ready) topk_hist_kernel<<<grid, kSelThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, w);
+    if (!hist_ready) launch_kernel(topk_hist_kernel, grid, kSelThreads, s, scores, pos0, T, n_cap, m, k, w);
     launch_classify(scores, pos0, T, n_cap, m, k, w, rows, s);
-    topk_finish_kernel<<<static_cast<unsigned>(rows), kFinThreads, 0, s>>>(scores, pos0, T, n_cap,
+    launch_kernel(topk_finish_kernel, static_cast<unsigned>(rows), kFinThreads, s, scores, pos0, T, n_cap,
                                                                            m, k, w, idx);
   } else {
     // one workgroup per row, using the indexer's histogram when it built
@@ -987,7 +985,7 @@ int launch_topk_lists(const float* scores, const int64_t* pos0, int64_t B, int64
     return 1;
   SplitWs w = split_ws(ws, rows, n_cap);
   dim3 grid(static_cast<unsigned>(w.n_sl), static_cast<unsigned>(rows));
-  if (!hist_ready) topk_hist_kernel<<<grid, kSelThreads, 0, s>>>(scores, pos0, T, n_cap, m, k, w);
+  if (!hist_ready) launch_kernel(topk_hist_kernel, grid, kSelThreads, s, scores, pos0, T, n_cap, m, k, w);
   // rows that fit the attention workgroup's registers need no lists
   lists->regs = n_cap <= kSelRegEntries && n_cap % 4 == 0 &&
                 (reinterpret_cast<uintptr_t>(scores) & 15u) == 0;
@@ -1007,7 +1005,7 @@ int launch_clear(void* p, size_t bytes, hipStream_t s) {
   const int64_t n = static_cast<int64_t>(bytes / 4);
   if (n == 0) return 0;
   const int64_t blocks = (n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048;
-  fill_zero_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(static_cast<uint32_t*>(p), n);
+  launch_kernel(fill_zero_kernel, static_cast<unsigned>(blocks), 256, s, static_cast<uint32_t*>(p), n);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

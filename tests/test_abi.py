@@ -65,6 +65,16 @@ def test_workspace_clear_validation():
                                 0, FAKE, 1024, FAKE, 16, NULL) == -5
 
 
+def test_time_next_kernels_validation():
+    assert lib.csa_time_next_kernels(NULL, NULL, -1) == -2
+    assert "n must be" in _last()
+    assert lib.csa_time_next_kernels(NULL, FAKE, 1) == -1
+    assert lib.csa_time_next_kernels(FAKE, NULL, 2) == -1
+    # n = 0 cancels (nothing is pending afterwards), with or without events
+    assert lib.csa_time_next_kernels(NULL, NULL, 0) == 0
+    assert lib.csa_time_next_kernels(FAKE, FAKE, 0) == 0
+
+
 def test_quantize_validation():
     assert lib.csa_quantize_fp8_rows(NULL, 1, 4, 128, FAKE, FAKE, NULL) == -1
     assert lib.csa_quantize_fp8_rows(FAKE, 2, 4, 128, FAKE, FAKE, NULL) == -3
