@@ -35,8 +35,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 10100.0, "f32": 157.3}
 FLUSH_BYTES = 1 << 30
 DEFAULT_WORKLOAD = "csa_decode_128k_bf16"
-# timed in the same run as the default workload (the 1M-token half of the metric)
-EXTRA_WORKLOADS = ("csa_decode_1m_fp8", "hca_decode_1m_bf16")
+# timed in the same run as the default workload: the 1M-token half of the
+# metric, and the chunked prefill (the indexer's MFMA fraction)
+EXTRA_WORKLOADS = ("csa_decode_1m_fp8", "hca_decode_1m_bf16", "csa_chunked_prefill_256k_8k_bf16")
 
 
 def parse():
@@ -46,7 +47,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-extra", action="store_true",
-                    help="time only --workload (not the 1M-token decode workloads)")
+                    help="time only --workload (not the 1M-token decode and chunked-prefill workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the CPU oracle sample")
